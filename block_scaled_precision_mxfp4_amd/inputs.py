@@ -1,0 +1,154 @@
+"""Seeded synthetic inputs for the MXFP4 GEMM workloads.
+
+This module only draws random bytes and values; it contains none of the
+GEMM's arithmetic and is the one piece of code that the GPU path's callers
+(tests, benchmark) and the CPU oracle's callers share.
+
+Generator: SplitMix64 (Steele, Lea, Flood, "Fast splittable pseudorandom
+number generators", OOPSLA 2014; public-domain reference by S. Vigna), used
+in its counter form: output i of a stream with seed s is mix(s + (i+1)*gamma).
+Every tensor draws from its own stream (seed XOR a per-tensor tag), so the
+shape of one tensor never shifts the values of another.
+
+Storage formats follow the asm_f4gemm README ("Data layouts"):
+  - A, B: row-major packed fp4x2 bytes [rows, K/2]; byte i holds element 2i
+    in the low nibble and 2i+1 in the high nibble; codes are E2M1 nibbles.
+  - SA, SB: E8M0 bytes [rows, K/32], one per 32 consecutive K elements.
+  - C: bf16 [M, N] (stored here as uint16 bit patterns).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+SEED_BASE = 0x4D5846500000
+
+_TAGS = {"A": 0x41 << 40, "B": 0x42 << 40, "SA": 0x5341 << 40, "SB": 0x5342 << 40,
+         "C": 0x43 << 40}
+
+_CHUNK = 1 << 22  # draws per numpy batch (bounds temporary memory)
+
+
+def splitmix64(seed: int, n: int, start: int = 0) -> np.ndarray:
+    """n consecutive SplitMix64 outputs (uint64) of stream `seed`, from index `start`."""
+    out = np.empty(n, dtype=np.uint64)
+    s = np.uint64(seed & 0xFFFFFFFFFFFFFFFF)
+    with np.errstate(over="ignore"):
+        for c0 in range(0, n, _CHUNK):
+            c1 = min(n, c0 + _CHUNK)
+            z = s + np.arange(start + c0 + 1, start + c1 + 1, dtype=np.uint64) * GAMMA
+            z = (z ^ (z >> np.uint64(30))) * _M1
+            z = (z ^ (z >> np.uint64(27))) * _M2
+            out[c0:c1] = z ^ (z >> np.uint64(31))
+    return out
+
+
+def _stream(seed: int, tag: str) -> int:
+    return (seed ^ _TAGS[tag]) & 0xFFFFFFFFFFFFFFFF
+
+
+def _u32(seed: int, n: int) -> np.ndarray:
+    """n uniform 32-bit draws (both halves of each 64-bit output)."""
+    w = splitmix64(seed, (n + 1) // 2)
+    return w.view(np.uint32)[:n]
+
+
+def fp4_codes_packed(seed: int, rows: int, K: int, dist: str = "uniform") -> np.ndarray:
+    """Packed fp4x2 matrix [rows, K/2] of E2M1 codes.
+
+    dist = "uniform":   every nibble uniform over the 16 codes (a uniform
+                        random byte is two independent uniform nibbles).
+    dist = "half_zero": each nibble is 0x0 with probability 1/2, otherwise
+                        uniform over 0x1..0xF (0x8, i.e. -0, included).
+    """
+    nbytes = rows * (K // 2)
+    if dist == "uniform":
+        w = splitmix64(seed, (nbytes + 7) // 8)
+        return w.view(np.uint8)[:nbytes].reshape(rows, K // 2).copy()
+    if dist == "half_zero":
+        out = np.empty(nbytes, dtype=np.uint8)
+        half = np.uint64(1 << 31)
+        for b0 in range(0, nbytes, _CHUNK):
+            b1 = min(nbytes, b0 + _CHUNK)
+            # two 32-bit draws per byte: low nibble then high nibble
+            w = splitmix64(seed, b1 - b0, start=b0).view(np.uint32).astype(np.uint64)
+            nz = w >= half
+            code = np.where(nz, np.uint64(1) + (((w - half) * np.uint64(15)) >> np.uint64(31)),
+                            np.uint64(0)).astype(np.uint8)
+            out[b0:b1] = code[0::2] | (code[1::2] << np.uint8(4))
+        return out.reshape(rows, K // 2)
+    raise ValueError("unknown code distribution %r" % dist)
+
+
+def e8m0_scales(seed: int, rows: int, K: int, lo: int, hi: int) -> np.ndarray:
+    """E8M0 bytes [rows, K/32], exponents uniform over lo..hi inclusive."""
+    n = rows * (K // 32)
+    span = np.uint64(hi - lo + 1)
+    h = _u32(seed, n).astype(np.uint64)
+    e = np.uint64(lo) + ((h * span) >> np.uint64(32))
+    return e.astype(np.uint8).reshape(rows, K // 32)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (input preparation)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    nan = np.isnan(x)
+    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    r = r.astype(np.uint16)
+    r[nan] = np.uint16(0x7FC0)
+    return r
+
+
+def gaussian_bf16(seed: int, rows: int, cols: int, sigma: float) -> np.ndarray:
+    """bf16 bit patterns [rows, cols] of N(0, sigma^2) draws (Box-Muller)."""
+    n = rows * cols
+    w = splitmix64(seed, 2 * n)
+    u1 = ((w[0::2] >> np.uint64(11)).astype(np.float64) + 1.0) * 2.0 ** -53
+    u2 = (w[1::2] >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
+    z = np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2) * sigma
+    return f32_to_bf16_bits(z.astype(np.float32)).reshape(rows, cols)
+
+
+# The five workloads.  Sizes, code and exponent distributions, alpha, beta
+# and C follow the statement of each case; `b_packed` marks the case that is
+# run on the pre-shuffled B layout.
+WORKLOADS = {
+    "tiny_128x256x512": dict(index=0, M=128, N=256, K=512, dist="uniform", e=(123, 131),
+                             alpha=1.0, beta=0.0, c_sigma=None, b_packed=False),
+    "mid_512x1024x2048": dict(index=1, M=512, N=1024, K=2048, dist="uniform", e=(123, 131),
+                              alpha=1.0, beta=1.0, c_sigma=1.0, b_packed=False),
+    "gemv_1x8192x8192": dict(index=2, M=1, N=8192, K=8192, dist="uniform", e=(120, 134),
+                             alpha=0.5, beta=0.0, c_sigma=None, b_packed=False),
+    "square_8192": dict(index=3, M=8192, N=8192, K=8192, dist="uniform", e=(123, 131),
+                        alpha=1.0, beta=0.0, c_sigma=None, b_packed=True),
+    "skinny_64x7168x16384": dict(index=4, M=64, N=7168, K=16384, dist="half_zero", e=(110, 140),
+                                 alpha=1.0, beta=1.0, c_sigma=2.0, b_packed=False),
+}
+
+
+def make_problem(M: int, N: int, K: int, *, seed: int, dist: str = "uniform",
+                 e=(123, 131), alpha: float = 1.0, beta: float = 0.0,
+                 c_sigma: float | None = None) -> dict:
+    """Dense (unpadded) operands for one GEMM problem."""
+    lo, hi = e
+    p = dict(M=M, N=N, K=K, alpha=float(alpha), beta=float(beta), seed=seed)
+    p["A"] = fp4_codes_packed(_stream(seed, "A"), M, K, dist)
+    p["B"] = fp4_codes_packed(_stream(seed, "B"), N, K, dist)
+    p["SA"] = e8m0_scales(_stream(seed, "SA"), M, K, lo, hi)
+    p["SB"] = e8m0_scales(_stream(seed, "SB"), N, K, lo, hi)
+    if c_sigma is not None:
+        p["C"] = gaussian_bf16(_stream(seed, "C"), M, N, c_sigma)
+    else:
+        p["C"] = None
+    return p
+
+
+def make_workload(name: str) -> dict:
+    w = WORKLOADS[name]
+    p = make_problem(w["M"], w["N"], w["K"], seed=SEED_BASE + w["index"], dist=w["dist"],
+                     e=w["e"], alpha=w["alpha"], beta=w["beta"], c_sigma=w["c_sigma"])
+    p["name"] = name
+    p["b_packed"] = w["b_packed"]
+    return p
