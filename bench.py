@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""MXFP4 block-scaled GEMM benchmark on one MI355X (gfx950).
+
+One step = one mxgemm_run call, i.e. the whole GEMM path (tile/split choice,
+operand streaming, scaled FP4 matrix instructions, split-K reduction when
+planned, fused alpha/beta bf16 epilogue) over one set of synthetic inputs
+already resident in HBM.  The B pre-shuffle (mxgemm_pack_b) is per-weight
+preparation and runs before timing, for the workload that uses it.
+
+Headline line: the 8192^3 workload (packed B), TFLOP/s = 2MNK / time, with
+the roofline of its kernel against the MI355X dense MXFP4 peak; the M = 1
+decode workload is reported next to it in GB/s against HBM, and the other
+workloads in a list.  Steps are launched from a HIP graph (captured once,
+replayed) so that kernel-launch overhead of the Python caller does not show
+up as GPU idle time; every kernel in the graph is a real mxgemm_run launch.
+For HBM-bound workloads the inputs rotate over enough copies that each
+step's operands are not resident in the last-level cache.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP4 GEMM TFLOPS (2MNK/s) + % of MXFP4 MFMA peak; GB/s at M=1"
+PEAK_MXFP4_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix peak (published)
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E (published)
+PAGE_TFLOPS_8192 = 4245.0    # asm_f4gemm README, "Measured": 8192^3 on MI355X
+LLC_BYTES = 256 << 20        # MI355X last-level (Infinity) cache
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(M, N, K, beta):
+    b = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + 2 * M * N
+    if beta != 0.0:
+        b += 2 * M * N
+    return b
+
+
+def time_workload(name, steps, warmup, split_k=-1, rotate=True):
+    import numpy as np
+    import torch
+
+    import block_scaled_precision_mxfp4_amd as mx
+    from block_scaled_precision_mxfp4_amd import inputs
+
+    p = inputs.make_workload(name)
+    M, N, K, alpha, beta = p["M"], p["N"], p["K"], p["alpha"], p["beta"]
+    packed = p["b_packed"]
+    info = mx.mxgemm_query(M, N, K, int(packed), split_k)
+    ws_bytes = algorithmic_bytes(M, N, K, beta)
+    copies = 1
+    if rotate and ws_bytes < 2 * LLC_BYTES:
+        copies = min(64, math.ceil(2.5 * LLC_BYTES / ws_bytes))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    A0, SA0, B0, SB0 = dev(p["A"]), dev(p["SA"]), dev(p["B"]), dev(p["SB"])
+    C0 = None
+    if p["C"] is not None:
+        C0 = torch.from_numpy(p["C"].view(np.int16)).cuda().view(torch.bfloat16)
+    sets = []
+    for c in range(copies):
+        A, SA = A0.clone(), SA0.clone()
+        B, SB = B0.clone(), SB0.clone()
+        C = C0.clone() if C0 is not None else None
+        D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        if packed:
+            Bp = torch.empty(info["packed_b_bytes"], dtype=torch.uint8, device="cuda")
+            SBp = torch.empty(info["packed_sb_bytes"], dtype=torch.uint8, device="cuda")
+            mx.mxgemm_pack_b(Bp, SBp, B, SB, N, K)
+            B, SB = Bp, SBp
+        sets.append((D, C, A, B, SA, SB))
+    del A0, SA0, B0, SB0, C0
+    wsp = torch.zeros(max(info["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
+    strides = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32,
+                              b_packed=int(packed), workspace=wsp, workspace_bytes=wsp.numel())
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+
+    def launch(i):
+        D, C, A, B, SA, SB = sets[i % copies]
+        mx.mxgemm_run(D, C if beta != 0.0 else None, A, B, SA, SB, alpha, beta, M, N, K,
+                      strides=strides, split_k=split_k, stream=stream.cuda_stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            launch(i)
+    torch.cuda.synchronize()
+
+    timing = "hipgraph"
+    graph = None
+    try:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                launch(i)
+        graph.replay()
+        torch.cuda.synchronize()
+    except Exception as e:  # capture unsupported: fall back to eager launches
+        log("graph capture failed (%s); timing eager launches" % e)
+        graph, timing = None, "eager"
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(steps):
+            launch(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    per = gpu_ms / 1e3 / steps
+    flops = 2.0 * M * N * K
+    r = dict(workload=name, M=M, N=N, K=K, alpha=alpha, beta=beta, b_packed=bool(packed),
+             kernel=info["kernel_name"], tile="%dx%d" % (info["tile_m"], info["tile_n"]),
+             split_k=info["split_k"], grid=info["grid"], copies=copies, timing=timing,
+             us_per_step=per * 1e6, tflops=flops / per / 1e12,
+             gbs=algorithmic_bytes(M, N, K, beta) / per / 1e9,
+             algorithmic_bytes=algorithmic_bytes(M, N, K, beta), wall_s=wall, gpu_ms=gpu_ms,
+             peak_flops_device=info["peak_flops"], clock_hz=info["clock_hz"], num_cu=info["num_cu"],
+             arch=info["arch"])
+    del sets, wsp
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log("%-24s %-22s split %2d  %9.2f us  %8.1f TFLOP/s  %8.1f GB/s  (%s, %d copies)" % (
+        name, r["kernel"], r["split_k"], r["us_per_step"], r["tflops"], r["gbs"], timing, copies))
+    return r
+
+
+def cpu_baseline(name, target_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the workload's outputs."""
+    import numpy as np
+
+    import oracle
+    from block_scaled_precision_mxfp4_amd import inputs
+
+    p = inputs.make_workload(name)
+    M, N, K = p["M"], p["N"], p["K"]
+    threads = max(1, min(16, os.cpu_count() or 1))
+    # calibrate on a small block, then size the sample for ~target_s seconds
+    rows = np.arange(min(M, 4), dtype=np.int64)
+    cols = np.arange(min(N, 256), dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.mxgemm(p["A"], p["SA"], p["B"], p["SB"], K, p["alpha"], p["beta"], p["C"],
+                  rows=rows, cols=cols, threads=threads)
+    dt = max(time.perf_counter() - t0, 1e-3)
+    rate = len(rows) * len(cols) / dt  # outputs per second
+    n_out = int(min(M * N, max(1, rate * target_s)))
+    n_cols = int(min(N, max(threads, n_out // min(M, 64))))
+    n_rows = int(min(M, max(1, n_out // n_cols)))
+    rows = np.arange(n_rows, dtype=np.int64)
+    cols = np.arange(n_cols, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.mxgemm(p["A"], p["SA"], p["B"], p["SB"], K, p["alpha"], p["beta"], p["C"],
+                  rows=rows, cols=cols, threads=threads)
+    dt = time.perf_counter() - t0
+    macs = n_rows * n_cols * K
+    return {"value": 2.0 * macs / dt / 1e9, "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d rows x %d cols of %s (%.3g MACs, fp64) in %.2f s" % (
+                n_rows, n_cols, name, macs, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="square_8192")
+    ap.add_argument("--split-k", type=int, default=-1)
+    ap.add_argument("--only", action="store_true", help="time only --workload (profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the GEMM runs on a single MI355X and this build has "
+              "no multi-GPU path (requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_precision_mxfp4_amd as mx
+    from block_scaled_precision_mxfp4_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    mx.lib()
+
+    head = time_workload(args.workload, args.steps, args.warmup, split_k=args.split_k)
+    others = []
+    if not args.only:
+        for name in inputs.WORKLOADS:
+            if name != args.workload:
+                others.append(time_workload(name, args.steps, args.warmup))
+    gemv = next((o for o in [head] + others if o["M"] == 1), None)
+
+    m1 = None
+    if gemv is not None:
+        m1 = {"workload": gemv["workload"], "value": gemv["gbs"], "unit": "GB/s",
+              "us_per_step": gemv["us_per_step"], "split_k": gemv["split_k"],
+              "roofline": {"bound": "hbm", "achieved": gemv["gbs"], "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": gemv["gbs"] / PEAK_HBM_GBS, "traffic": None}}
+
+    base = None
+    if not args.no_cpu_baseline:
+        base = cpu_baseline(args.workload)
+        log("cpu baseline:", base)
+
+    hbm_bound = head["M"] <= 64
+    if hbm_bound:
+        value, unit = head["gbs"], "GB/s"
+        roof = {"bound": "hbm", "achieved": head["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": head["gbs"] / PEAK_HBM_GBS, "traffic": None}
+    else:
+        value, unit = head["tflops"], "TFLOP/s"
+        roof = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_MXFP4_TFLOPS,
+                "unit": "TFLOP/s", "frac": head["tflops"] / PEAK_MXFP4_TFLOPS, "traffic": None}
+    vs = value / PAGE_TFLOPS_8192 if head["workload"] == "square_8192" and unit == "TFLOP/s" else None
+    line = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["us_per_step"] / 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": vs, "dtype": "mxfp4", "data": "synthetic",
+        "config": {"workload": head["workload"], "M": head["M"], "N": head["N"], "K": head["K"],
+                   "b_packed": head["b_packed"], "kernel": head["kernel"], "tile": head["tile"],
+                   "split_k": head["split_k"], "timing": head["timing"]},
+        "roofline": roof,
+        "cpu_baseline": base,
+        "m1": m1,
+        "device": {"arch": head["arch"], "num_cu": head["num_cu"], "clock_hz": head["clock_hz"],
+                   "derived_peak_tflops": head["peak_flops_device"] / 1e12},
+        "workloads": [{k: o[k] for k in ("workload", "kernel", "tile", "split_k", "us_per_step",
+                                         "tflops", "gbs", "copies", "timing")} for o in [head] + others],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+"""Python binding of libmxgemm (MXFP4 block-scaled GEMM for gfx950).
+
+Argument marshalling only: every function below calls the C-ABI entry point
+of the same name in libmxgemm.so (declared in include/libmxgemm.h) and every
+step of the computation runs in the library's HIP kernels.  Tensors may be
+passed as torch tensors (their data_ptr() is used) or as raw device
+addresses (int).  The stream defaults to torch's current stream.
+
+There is no fallback: if libmxgemm.so is missing or fails to load, every
+call raises MxGemmError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
+
+# C-ABI entry points declared in include/libmxgemm.h
+EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_pack_b", "mxgemm_query",
+           "mxgemm_plan", "mxgemm_release_workspaces")
+
+STATUS = {0: "MXGEMM_OK", -1: "MXGEMM_ERR_INVALID_ARG", -2: "MXGEMM_ERR_SHAPE",
+          -3: "MXGEMM_ERR_ALIGN", -4: "MXGEMM_ERR_UNSUPPORTED_DEVICE", -5: "MXGEMM_ERR_HIP",
+          -6: "MXGEMM_ERR_WORKSPACE"}
+
+
+class MxGemmError(RuntimeError):
+    def __init__(self, status, where=""):
+        self.status = status
+        name = STATUS.get(status, str(status))
+        super().__init__("%s failed: %s (%s)" % (where, name, _status_text(status)))
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("ldd", ctypes.c_int64), ("ldc", ctypes.c_int64), ("lda", ctypes.c_int64),
+                ("ldb", ctypes.c_int64), ("ldsa", ctypes.c_int64), ("ldsb", ctypes.c_int64),
+                ("b_packed", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class Info(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("split_k", ctypes.c_int32), ("grid", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t), ("packed_b_bytes", ctypes.c_size_t),
+                ("packed_sb_bytes", ctypes.c_size_t), ("num_cu", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("kernel_name", ctypes.c_char * 64),
+                ("arch", ctypes.c_char * 32), ("peak_flops", ctypes.c_double),
+                ("clock_hz", ctypes.c_double)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        d["kernel_name"] = self.kernel_name.decode()
+        d["arch"] = self.arch.decode()
+        return d
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmxgemm.so (raises MxGemmError if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MxGemmError(-5, "loading %s (not built; run __graft_entry__.build())" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        L.mxgemm_status_string.argtypes = [i32]
+        L.mxgemm_status_string.restype = ctypes.c_char_p
+        L.mxgemm_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, i32, i32, i32,
+                                 ctypes.POINTER(Strides), i32, vp]
+        L.mxgemm_run.restype = i32
+        L.mxgemm_pack_b.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, vp]
+        L.mxgemm_pack_b.restype = i32
+        L.mxgemm_query.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(Info)]
+        L.mxgemm_query.restype = i32
+        L.mxgemm_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(Info)]
+        L.mxgemm_plan.restype = i32
+        L.mxgemm_release_workspaces.argtypes = []
+        L.mxgemm_release_workspaces.restype = i32
+        _lib = L
+    return _lib
+
+
+def _status_text(status):
+    try:
+        return lib().mxgemm_status_string(status).decode()
+    except Exception:
+        return "?"
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, where):
+    if status != 0:
+        raise MxGemmError(status, where)
+
+
+def make_strides(*, ldd, ldc, lda, ldb, ldsa, ldsb, b_packed=0, workspace=None, workspace_bytes=0):
+    return Strides(ldd, ldc, lda, ldb, ldsa, ldsb, b_packed, 0, _ptr(workspace), workspace_bytes)
+
+
+def mxgemm_status_string(status: int) -> str:
+    return lib().mxgemm_status_string(status).decode()
+
+
+def mxgemm_run(D, C, A, B, scaleA, scaleB, alpha, beta, M, N, K, strides=None, split_k=-1,
+               stream=None, check=True):
+    """D = bf16(alpha * A * B^T + beta * C) on `stream` (asynchronous)."""
+    sp = ctypes.byref(strides) if strides is not None else None
+    st = lib().mxgemm_run(_ptr(D), _ptr(C), _ptr(A), _ptr(B), _ptr(scaleA), _ptr(scaleB),
+                          float(alpha), float(beta), int(M), int(N), int(K), sp, int(split_k),
+                          _stream(stream))
+    if check:
+        _check(st, "mxgemm_run")
+    return st
+
+
+def mxgemm_pack_b(Bp, SBp, B, scaleB, N, K, ldb=None, ldsb=None, stream=None, check=True):
+    """Pre-shuffle B and its scales into the kernels' layout (asynchronous)."""
+    ldb = K if ldb is None else ldb
+    ldsb = K // 32 if ldsb is None else ldsb
+    st = lib().mxgemm_pack_b(_ptr(Bp), _ptr(SBp), _ptr(B), _ptr(scaleB), int(N), int(K),
+                             int(ldb), int(ldsb), _stream(stream))
+    if check:
+        _check(st, "mxgemm_pack_b")
+    return st
+
+
+def mxgemm_query(M, N, K, b_packed=0, split_k=-1) -> dict:
+    info = Info()
+    _check(lib().mxgemm_query(int(M), int(N), int(K), int(b_packed), int(split_k),
+                              ctypes.byref(info)), "mxgemm_query")
+    return info.as_dict()
+
+
+def mxgemm_plan(M, N, K, b_packed=0, split_k=-1, num_cu=256) -> dict:
+    info = Info()
+    _check(lib().mxgemm_plan(int(M), int(N), int(K), int(b_packed), int(split_k), int(num_cu),
+                             ctypes.byref(info)), "mxgemm_plan")
+    return info.as_dict()
+
+
+def mxgemm_release_workspaces():
+    _check(lib().mxgemm_release_workspaces(), "mxgemm_release_workspaces")

@@ -1,0 +1,60 @@
+// Kernel arguments and launcher table shared by the host library and the
+// gfx950 kernels.  Host-side only plain types; no torch, no device code.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mx {
+
+struct GemmArgs {
+    uint16_t *D;          // bf16 [M][ldd]
+    const uint16_t *C;    // bf16 [M][ldc], read only when beta != 0
+    const uint8_t *A;     // fp4x2 [M][lda_b]
+    const uint8_t *B;     // fp4x2 [N][ldb_b], or the packed layout
+    const uint8_t *SA;    // E8M0 [M][ldsa]
+    const uint8_t *SB;    // E8M0 [N][ldsb], or the packed layout
+    float *ws;            // split-K fp32 partials
+    int *counters;        // split-K arrival counters, one per output tile, zero between calls
+    float alpha, beta;
+    int M, N, K;
+    int KB;               // K / 32 scale blocks
+    int64_t lda_b, ldb_b; // byte pitch of A and B rows
+    int64_t ldsa, ldsb;   // byte pitch of scale rows
+    int64_t ldc, ldd;     // element pitch of C and D rows
+    int split;            // K chunks (1 = no split)
+    int kb_per_split;     // K-blocks per chunk, a multiple of 8
+    int tiles_m, tiles_n; // output tiles per dimension
+    int ks_total;         // packed B: 128-K steps per 16-row group, ceil(KB/4)
+    int sn8;              // packed scales: (KB rounded up to 8) / 8
+    int sa_fast, sb_fast; // scale rows allow aligned 8-byte loads
+    int d_vec, c_vec;     // 8-byte D stores / C loads allowed
+    int group_m;          // tile-order grouping along M
+};
+
+typedef void (*LaunchFn)(const GemmArgs &, int grid, hipStream_t);
+
+// Tiled kernel (operands staged through LDS): tile shapes available.
+struct TileKernel {
+    int bm, bn;
+    int occupancy;        // workgroups per CU the kernel's LDS allows
+    LaunchFn plain, packed;
+    const char *name;
+};
+// Host-side table of the tiled kernels, in the planner's preference order.
+const TileKernel *tile_kernels(int *count);
+
+// Skinny kernel (M <= 64, B streamed from memory into registers).
+// index: (mg - 1) * 3 + nr_index with nr in {1, 2, 4}.
+struct SkinnyKernel {
+    int mg, nr;
+    LaunchFn plain, packed;
+    const char *name;
+};
+const SkinnyKernel *skinny_kernels(int *count);
+
+void launch_pack_b(uint8_t *Bp, const uint8_t *B, int N, int KB, int64_t ldb_b, hipStream_t s);
+void launch_pack_sb(uint32_t *SBp, const uint8_t *SB, int N, int KB, int64_t ldsb, hipStream_t s);
+
+}  // namespace mx

@@ -1,0 +1,187 @@
+// Device-side building blocks shared by the MXFP4 GEMM kernels (gfx950).
+//
+// Operand fragments.  The 16x16x128 scaled matrix instruction ("CDNA4 dense
+// MFMA builtins", section "Mixed-precision with scaling") takes, for FP4
+// (format selector 4), 32 E2M1 values per lane: lane l holds row l % 16 of
+// its operand and the 32 consecutive K elements of K-block l / 16, i.e. 16
+// bytes.  One such fragment is therefore exactly 16 rows x 128 K = 1 KiB,
+// and "lane-linear" 1 KiB chunks (lane l's 16 bytes at offset 16*l) are the
+// unit in which the kernels move operands: it is also the unit of the
+// 16x16 tile-transposed B layout of the asm_f4gemm README ("Data layouts").
+// Each lane passes one 32-bit scale register per operand; the 2-bit op_sel
+// immediate picks which of its four E8M0 bytes applies to that lane's
+// K-block.
+//
+// Result layout ("CDNA4 dense MFMA builtins", "Accumulator layout", 16x16):
+// lane l, accumulator g holds row 4*(l/16) + g, column l % 16.  The kernels
+// feed B as the instruction's first operand and A as its second, so the
+// instruction's rows are columns n of D and its columns are rows m of D:
+// every lane ends up with four consecutive n of one row m.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Format selector of E2M1 for the scaled matrix instructions (the fifth
+// entry of the format table, codes 0..4).
+constexpr int kFmtFp4 = 4;
+// Buffer-resource word 3 for gfx9-family raw buffers (no swizzle, range
+// checked against num_records).
+constexpr int kRsrcWord3 = 0x00020000;
+// A byte offset that is always outside any buffer resource's range: loads
+// from it return zero and do not touch memory.
+constexpr uint32_t kOOB = 0xFFFFFF00u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+__device__ __forceinline__ v4i load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ v2u load8(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t load1(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+// 16 bytes per lane straight from global memory into LDS at lds + 16*lane
+// (lds must be wave-uniform).  Out-of-range lanes write zeros.
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, lds_void *lds, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, 0, 0, 0);
+}
+
+// acc += (B fragment, scaled) x (A fragment, scaled) over 128 K.
+template <int OPSEL_B, int OPSEL_A>
+__device__ __forceinline__ v4f mfma_fp4(v4i bfrag, v4i afrag, v4f acc, int sb, int sa)
+{
+    v8i b = {bfrag[0], bfrag[1], bfrag[2], bfrag[3], 0, 0, 0, 0};
+    v8i a = {afrag[0], afrag[1], afrag[2], afrag[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, acc, kFmtFp4, kFmtFp4,
+                                                           OPSEL_B, sb, OPSEL_A, sa);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint32_t bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return (u >> 16) | 0x40u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h)
+{
+    return __uint_as_float(h << 16);
+}
+
+// Epilogue parameters shared by all kernels.
+struct Epilogue {
+    uint16_t *D;
+    const uint16_t *C;
+    float alpha, beta;
+    int M, N;
+    int64_t ldd, ldc;
+    int d_vec;  // D rows and base allow 8-byte stores of 4 consecutive n
+    int c_vec;  // C rows and base allow 8-byte loads
+};
+
+// Writes D[m][n..n+3] = bf16(alpha*acc[g] + beta*C[m][n+g]) for the
+// elements inside the matrix.  One rounding per element.
+__device__ __forceinline__ void store_quad(const Epilogue &ep, int m, int n, v4f acc)
+{
+    if (m >= ep.M || n >= ep.N)
+        return;
+    float r[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+        r[g] = ep.alpha * acc[g];
+    const bool full = n + 3 < ep.N;
+    if (ep.beta != 0.0f) {
+        const uint16_t *crow = ep.C + (int64_t)m * ep.ldc + n;
+        if (full && ep.c_vec) {
+            v2u c2 = *reinterpret_cast<const v2u *>(crow);
+            r[0] = fmaf(ep.beta, bf16_to_f32(c2[0] & 0xFFFFu), r[0]);
+            r[1] = fmaf(ep.beta, bf16_to_f32(c2[0] >> 16), r[1]);
+            r[2] = fmaf(ep.beta, bf16_to_f32(c2[1] & 0xFFFFu), r[2]);
+            r[3] = fmaf(ep.beta, bf16_to_f32(c2[1] >> 16), r[3]);
+        } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                if (n + g < ep.N)
+                    r[g] = fmaf(ep.beta, bf16_to_f32(crow[g]), r[g]);
+        }
+    }
+    uint16_t *drow = ep.D + (int64_t)m * ep.ldd + n;
+    if (full && ep.d_vec) {
+        v2u o;
+        o[0] = bf16_rne(r[0]) | (bf16_rne(r[1]) << 16);
+        o[1] = bf16_rne(r[2]) | (bf16_rne(r[3]) << 16);
+        *reinterpret_cast<v2u *>(drow) = o;
+    } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            if (n + g < ep.N)
+                drow[g] = (uint16_t)bf16_rne(r[g]);
+    }
+}
+
+// Map a hardware workgroup id to a logical one so that the workgroups the
+// dispatcher sends to the same XCD (ids congruent mod 8) receive
+// consecutive logical ids, i.e. neighbouring output tiles sharing operand
+// rows in that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int wg, int total)
+{
+    constexpr int kXcds = 8;
+    const int xcd = wg % kXcds, idx = wg / kXcds;
+    const int q = total / kXcds, r = total % kXcds;
+    return xcd * q + (xcd < r ? xcd : r) + idx;
+}
+
+// Split-K arrival: every workgroup of a tile has written its fp32 partial;
+// returns true in exactly one of them (the last to arrive), which then owns
+// the reduction.  The counter is returned to zero for the next call.
+__device__ __forceinline__ bool split_arrive_last(int *counter, int splits)
+{
+    __shared__ int s_last;
+    __threadfence();  // release this workgroup's partial at device scope
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int prev = atomicAdd(counter, 1);
+        int last = prev == splits - 1;
+        if (last)
+            atomicExch(counter, 0);
+        s_last = last;
+    }
+    __syncthreads();
+    const bool last = s_last != 0;
+    if (last)
+        __threadfence();  // acquire the other workgroups' partials
+    return last;
+}
+
+}  // namespace mx

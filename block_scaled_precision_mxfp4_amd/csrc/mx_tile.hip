@@ -1,0 +1,347 @@
+// Tiled MXFP4 GEMM kernel for gfx950: each 256-thread workgroup (4 wave64)
+// computes a BM x BN tile of D over one K chunk.
+//
+// Data movement per 256-K stage:
+//   - operand tiles go from HBM/L2 straight into LDS with 16-byte-per-lane
+//     buffer loads (no VGPR round trip), double-buffered;
+//   - LDS holds each operand as lane-linear 1 KiB chunks (16 rows x 128 K,
+//     one instruction operand each), so every fragment read is one
+//     conflict-free 16-byte ds_read per lane at chunk + 16*lane;
+//   - scales are staged through registers into LDS words that already hold
+//     the four bytes one lane needs for two 16-row groups x two 128-K steps
+//     (the word layout of the asm_f4gemm README's scale shuffle, "Data
+//     layouts"), so one 4-byte LDS read feeds four matrix instructions and
+//     op_sel picks the byte.
+// Out-of-range rows and K blocks are zero-filled by the buffer loads'
+// range check, so no caller padding is needed.
+//
+// Split K: workgroup (tile, z) reduces K-blocks [z*kb_per_split, ...).  With
+// more than one chunk every workgroup stores its fp32 partial tile; the last
+// one to arrive adds the partials in the fixed order z = 0, 1, ... and runs
+// the epilogue, so results do not depend on arrival order.
+#include "mx_args.hpp"
+#include "mx_device.hpp"
+
+#include <type_traits>
+
+namespace mx {
+
+// op_sel must be an immediate: select among the 16 (B byte, A byte) forms.
+// With fully unrolled loops the selector is a constant and the switch folds.
+__device__ __forceinline__ v4f mma_sel(int ob, int oa, v4i b, v4i a, v4f c, int sb, int sa)
+{
+#define MX_CASE(OB, OA) \
+    case OB * 4 + OA: return mfma_fp4<OB, OA>(b, a, c, sb, sa);
+    switch (ob * 4 + oa) {
+        MX_CASE(0, 0) MX_CASE(0, 1) MX_CASE(0, 2) MX_CASE(0, 3)
+        MX_CASE(1, 0) MX_CASE(1, 1) MX_CASE(1, 2) MX_CASE(1, 3)
+        MX_CASE(2, 0) MX_CASE(2, 1) MX_CASE(2, 2) MX_CASE(2, 3)
+        MX_CASE(3, 0) MX_CASE(3, 1) MX_CASE(3, 2) MX_CASE(3, 3)
+    }
+#undef MX_CASE
+    return c;
+}
+
+// s_waitcnt with vmcnt(0) only (expcnt and lgkmcnt left at their maxima):
+// waits for this wave's outstanding memory loads, including LDS-direct ones.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Scale bytes of one stage for one 32-row group, as loaded: rows r0 and
+// r0+16, 8 K-blocks each (word 0 = blocks 0..3, word 1 = blocks 4..7).
+struct ScaleRows {
+    v2u r0, r1;
+};
+
+// Loads the two rows' 8 stage scale bytes.  SVEC: one 8-byte load per row
+// (K-block count and row pitch multiples of 8, so a stage is never partly
+// outside the chunk).  Otherwise byte loads, blocks at or past kb_end read
+// from an out-of-range offset (zero).  `own` false turns every load into an
+// out-of-range one; nothing branches.
+template <bool SVEC>
+__device__ __forceinline__ ScaleRows load_scale_rows(__amdgpu_buffer_rsrc_t r, int64_t ld, int row0,
+                                                     int kb_s, int kb_end, bool own)
+{
+    ScaleRows s;
+    const uint32_t o0 = own ? (uint32_t)(row0 * ld + kb_s) : kOOB;
+    const uint32_t o1 = own ? (uint32_t)((row0 + 16) * ld + kb_s) : kOOB;
+    if constexpr (SVEC) {
+        s.r0 = load8(r, o0);
+        s.r1 = load8(r, o1);
+    } else {
+        uint32_t b0[2] = {0, 0}, b1[2] = {0, 0};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool ok = kb_s + j < kb_end;
+            b0[j >> 2] |= load1(r, ok ? o0 + j : kOOB) << (8 * (j & 3));
+            b1[j >> 2] |= load1(r, ok ? o1 + j : kOOB) << (8 * (j & 3));
+        }
+        s.r0 = v2u{b0[0], b0[1]};
+        s.r1 = v2u{b1[0], b1[1]};
+    }
+    return s;
+}
+
+// Word for lane (K-block d5 of the step, row d2): bytes
+// [step0 row r0, step0 row r0+16, step1 row r0, step1 row r0+16].
+__device__ __forceinline__ uint32_t scale_word(const ScaleRows &s, int d5)
+{
+    const int sh = 8 * d5;
+    return ((s.r0[0] >> sh) & 0xFFu) | (((s.r1[0] >> sh) & 0xFFu) << 8) |
+           (((s.r0[1] >> sh) & 0xFFu) << 16) | (((s.r1[1] >> sh) & 0xFFu) << 24);
+}
+
+template <int BM, int BN, int WM, int WN, bool BPACK, bool SVEC>
+__global__ void __launch_bounds__(256) mx_tile_kernel(GemmArgs g)
+{
+    constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+    constexpr int FM = TM / 16, FN = TN / 16;  // 16-row fragments per wave
+    static_assert(WM * WN == 4, "four waves");
+    static_assert(FM % 2 == 0 && FN % 2 == 0, "scale words cover 32-row groups");
+    constexpr int A_CH = BM / 8, B_CH = BN / 8;  // 1 KiB chunks per stage
+    static_assert(A_CH % 4 == 0 && B_CH % 4 == 0, "chunks split evenly over waves");
+    constexpr int A_STAGE = BM * 128, B_STAGE = BN * 128;    // bytes per stage
+    constexpr int SA_W = BM / 32 * 64, SB_W = BN / 32 * 64;  // scale words per stage
+    constexpr int SC_W = SA_W + SB_W + 64;                   // + a scratch row for idle threads
+    constexpr int SBP_PER_THREAD = (SB_W + 255) / 256;       // packed-scale words per thread
+    static_assert(BM / 2 + BN / 2 <= 256, "one scale row pair per thread");
+
+    // The two halves of each double buffer are distinct LDS objects and every
+    // access names one of them at compile time: the compiler can then tell
+    // the next stage's direct-to-LDS loads from this stage's fragment reads
+    // and does not make the reads wait for the loads.
+    __shared__ __attribute__((aligned(1024))) uint8_t s_a0[A_STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_a1[A_STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_b0[B_STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_b1[B_STAGE];
+    __shared__ uint32_t s_sc0[SC_W];  // [SA words | SB words | scratch]
+    __shared__ uint32_t s_sc1[SC_W];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_m = wave % WM, wave_n = wave / WM;
+
+    // ---- which tile and K chunk
+    const int tiles = g.tiles_m * g.tiles_n;
+    const int lg = xcd_remap(blockIdx.x, gridDim.x);
+    const int z = lg / tiles;
+    const int t = lg - z * tiles;
+    const int per_group = g.group_m * g.tiles_n;
+    const int grp = t / per_group;
+    const int first_m = grp * g.group_m;
+    const int gsz = min(g.tiles_m - first_m, g.group_m);
+    const int within = t - grp * per_group;
+    const int tm = first_m + within % gsz;
+    const int tn = within / gsz;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    const int kb_begin = z * g.kb_per_split;
+    const int kb_end = min(g.KB, kb_begin + g.kb_per_split);
+    const int nst = (kb_end - kb_begin + 7) >> 3;
+
+    // ---- buffer resources, rebased at the tile (offsets stay below 2^31)
+    const int rows_a = min(BM, g.M - m0);
+    const auto ra = make_rsrc(g.A + (int64_t)m0 * g.lda_b, (uint32_t)(rows_a * g.lda_b));
+    const auto rsa = make_rsrc(g.SA + (int64_t)m0 * g.ldsa, (uint32_t)(rows_a * g.ldsa));
+    __amdgpu_buffer_rsrc_t rb, rsb;
+    if constexpr (BPACK) {
+        const int n16 = n0 / 16, grp16 = min(BN / 16, (g.N + 15) / 16 - n16);
+        rb = make_rsrc(g.B + (int64_t)n16 * g.ks_total * 1024, (uint32_t)(grp16 * g.ks_total * 1024));
+        const int n32 = n0 / 32, grp32 = min(BN / 32, (g.N + 31) / 32 - n32);
+        rsb = make_rsrc(g.SB + (int64_t)n32 * g.sn8 * 256, (uint32_t)(grp32 * g.sn8 * 256));
+    } else {
+        const int rows_b = min(BN, g.N - n0);
+        rb = make_rsrc(g.B + (int64_t)n0 * g.ldb_b, (uint32_t)(rows_b * g.ldb_b));
+        rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)(rows_b * g.ldsb));
+    }
+
+    // ---- stage loaders; `on` false makes every load out of range (no traffic)
+    auto issue_operands = [&](int kt, bool on, auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
+        uint8_t *dst_a = BUF ? s_a1 : s_a0;
+        uint8_t *dst_b = BUF ? s_b1 : s_b0;
+        const int kb_s = kb_begin + kt * 8;
+#pragma unroll
+        for (int i = 0; i < A_CH / 4; ++i) {
+            const int c = i * 4 + wave;
+            const int rg = c >> 1, ks = c & 1;
+            const int kb = kb_s + ks * 4 + (lane >> 4);
+            const int row = rg * 16 + (lane & 15);
+            const uint32_t off = on && kb < kb_end ? (uint32_t)(row * g.lda_b + kb * 16) : kOOB;
+            load16_to_lds(ra, (lds_void *)(dst_a + c * 1024), off);
+        }
+#pragma unroll
+        for (int i = 0; i < B_CH / 4; ++i) {
+            const int c = i * 4 + wave;
+            const int rg = c >> 1, ks = c & 1;
+            const int kb = kb_s + ks * 4 + (lane >> 4);
+            uint32_t off;
+            if constexpr (BPACK)
+                off = on && kb < kb_end ? (uint32_t)(((rg * g.ks_total + (kb_s >> 2) + ks) * 64 + lane) * 16) : kOOB;
+            else
+                off = on && kb < kb_end ? (uint32_t)((rg * 16 + (lane & 15)) * g.ldb_b + kb * 16) : kOOB;
+            load16_to_lds(rb, (lds_void *)(dst_b + c * 1024), off);
+        }
+    };
+
+    // scale-row ownership: thread < BM/2 owns A row pair tid; the next BN/2
+    // threads own B row pairs (row-major B scales only)
+    const bool own_a = tid < BM / 2;
+    const int ua = own_a ? tid : 0;
+    const bool own_b = !BPACK && tid >= BM / 2 && tid < BM / 2 + BN / 2;
+    const int ub = own_b ? tid - BM / 2 : 0;
+    // LDS word index (per d5 add 16*d5) each thread commits its A / B words to
+    const int wa = own_a ? (ua >> 4) * 64 + (ua & 15) : SA_W + SB_W + lane;
+    const int wb = own_b ? SA_W + (ub >> 4) * 64 + (ub & 15) : SA_W + SB_W + lane;
+
+    ScaleRows sa_rows, sb_rows;
+    uint32_t sbp[SBP_PER_THREAD];
+    auto issue_scales = [&](int kt, bool on) {
+        const int kb_s = kb_begin + kt * 8;
+        sa_rows = load_scale_rows<SVEC>(rsa, g.ldsa, (ua >> 4) * 32 + (ua & 15), kb_s, kb_end, on && own_a);
+        if constexpr (BPACK) {
+#pragma unroll
+            for (int i = 0; i < SBP_PER_THREAD; ++i) {
+                const int q = i * 256 + tid;
+                const uint32_t off = on && q < SB_W
+                                         ? (uint32_t)((((q >> 6) * g.sn8 + (kb_s >> 3)) * 64 + (q & 63)) * 4)
+                                         : kOOB;
+                sbp[i] = load4(rsb, off);
+            }
+        } else {
+            sb_rows = load_scale_rows<SVEC>(rsb, g.ldsb, (ub >> 4) * 32 + (ub & 15), kb_s, kb_end, on && own_b);
+        }
+    };
+    auto commit_scales = [&](auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
+        uint32_t *dsc = BUF ? s_sc1 : s_sc0;
+#pragma unroll
+        for (int d5 = 0; d5 < 4; ++d5)
+            dsc[wa + (own_a ? 16 * d5 : 0)] = scale_word(sa_rows, d5);
+        if constexpr (BPACK) {
+#pragma unroll
+            for (int i = 0; i < SBP_PER_THREAD; ++i) {
+                const int q = i * 256 + tid;
+                dsc[q < SB_W ? SA_W + q : SA_W + SB_W + lane] = sbp[i];
+            }
+        } else {
+#pragma unroll
+            for (int d5 = 0; d5 < 4; ++d5)
+                dsc[wb + (own_b ? 16 * d5 : 0)] = scale_word(sb_rows, d5);
+        }
+    };
+
+    // ---- main loop
+    v4f acc[FN][FM];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            acc[fn][fm] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+
+    // One stage, one basic block: prefetch stage kt+1 into the other buffer,
+    // multiply stage kt, then wait for the prefetch and publish its scales.
+    auto stage = [&](int kt, auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
+        using Next = std::integral_constant<int, BUF ^ 1>;
+        const bool more = kt + 1 < nst;
+        issue_operands(kt + 1, more, Next{});
+        issue_scales(kt + 1, more);
+        const uint8_t *sa_tile = BUF ? s_a1 : s_a0;
+        const uint8_t *sb_tile = BUF ? s_b1 : s_b0;
+        const uint32_t *ssc = BUF ? s_sc1 : s_sc0;
+        uint32_t saw[FM / 2], sbw[FN / 2];
+#pragma unroll
+        for (int p = 0; p < FM / 2; ++p)
+            saw[p] = ssc[(wave_m * (FM / 2) + p) * 64 + lane];
+#pragma unroll
+        for (int p = 0; p < FN / 2; ++p)
+            sbw[p] = ssc[SA_W + (wave_n * (FN / 2) + p) * 64 + lane];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            v4i af[FM];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                af[fm] = *reinterpret_cast<const v4i *>(sa_tile + ((wave_m * FM + fm) * 2 + ks) * 1024 + lane * 16);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const v4i bf = *reinterpret_cast<const v4i *>(sb_tile + ((wave_n * FN + fn) * 2 + ks) * 1024 + lane * 16);
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+                    acc[fn][fm] = mma_sel(ks * 2 + (fn & 1), ks * 2 + (fm & 1), bf, af[fm],
+                                          acc[fn][fm], (int)sbw[fn >> 1], (int)saw[fm >> 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_vmem();
+        commit_scales(Next{});
+        __syncthreads();
+    };
+
+    issue_operands(0, true, B0{});
+    issue_scales(0, true);
+    wait_vmem();
+    commit_scales(B0{});
+    __syncthreads();
+    for (int kt = 0; kt < nst; kt += 2) {
+        stage(kt, B0{});
+        if (kt + 1 < nst)
+            stage(kt + 1, B1{});
+    }
+
+    // ---- epilogue
+    Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec};
+    const int mb = m0 + wave_m * TM + (lane & 15);
+    const int nb = n0 + wave_n * TN + 4 * (lane >> 4);
+    if (g.split == 1) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                store_quad(ep, mb + fm * 16, nb + fn * 16, acc[fn][fm]);
+        return;
+    }
+    v4f *part = reinterpret_cast<v4f *>(g.ws + ((size_t)t * g.split + z) * (size_t)(BM * BN));
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+            part[((wave * FN + fn) * FM + fm) * 64 + lane] = acc[fn][fm];
+    if (!split_arrive_last(g.counters + t, g.split))
+        return;
+    const v4f *base = reinterpret_cast<const v4f *>(g.ws + (size_t)t * g.split * (size_t)(BM * BN));
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int idx = ((wave * FN + fn) * FM + fm) * 64 + lane;
+            v4f s = base[idx];
+            for (int zz = 1; zz < g.split; ++zz)
+                s += base[(size_t)zz * (BM * BN / 4) + idx];
+            store_quad(ep, mb + fm * 16, nb + fn * 16, s);
+        }
+}
+
+template <int BM, int BN, int WM, int WN, bool BPACK>
+static void launch_tile(const GemmArgs &g, int grid, hipStream_t s)
+{
+    if (g.sa_fast && (BPACK || g.sb_fast))
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, true>), dim3(grid), dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, false>), dim3(grid), dim3(256), 0, s, g);
+}
+
+const TileKernel *tile_kernels(int *count)
+{
+    static const TileKernel table[] = {
+        {256, 256, 1, launch_tile<256, 256, 2, 2, false>, launch_tile<256, 256, 2, 2, true>, "tile_256x256"},
+        {256, 128, 1, launch_tile<256, 128, 2, 2, false>, launch_tile<256, 128, 2, 2, true>, "tile_256x128"},
+        {128, 128, 2, launch_tile<128, 128, 2, 2, false>, launch_tile<128, 128, 2, 2, true>, "tile_128x128"},
+        {64, 64, 4, launch_tile<64, 64, 2, 2, false>, launch_tile<64, 64, 2, 2, true>, "tile_64x64"},
+    };
+    *count = (int)(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+
+}  // namespace mx

@@ -1,0 +1,464 @@
+// libmxgemm host library: argument validation, kernel/tile/split planning,
+// split-K workspace management and the C-ABI entry points of libmxgemm.h.
+//
+// Planning follows the idea of the asm_f4gemm README's "Tile selection
+// heuristic" (count how many rounds of workgroups the compute units need
+// for each tile shape and prefer fewer, larger-tile rounds, iterating
+// candidates in a fixed order so the choice is reproducible), extended with
+// a per-tile cost so that tiles of different sizes and the split-K
+// reduction can be compared, and with the skinny streaming kernel for
+// M <= 64.
+#include "libmxgemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "mx_args.hpp"
+
+namespace {
+
+using mx::GemmArgs;
+
+constexpr int kMaxK = 1 << 24;
+constexpr int kMaxDevices = 64;
+constexpr int kSplits[] = {1, 2, 4, 8, 16};
+
+struct Plan {
+    int family = 0;  // 0 tiled, 1 skinny
+    int index = 0;   // index into the kernel table of the family
+    int bm = 0, bn = 0;
+    int split = 1;
+    int kb_per_split = 0;
+    int tiles_m = 0, tiles_n = 0;
+    int64_t grid = 0;
+    size_t counter_bytes = 0;
+    size_t ws_bytes = 0;
+    const char *name = "";
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Split s over KB scale blocks: chunks are whole 256-K stages (8 blocks);
+// returns blocks per chunk and the number of non-empty chunks.
+std::pair<int, int> split_chunks(int KB, int s)
+{
+    int per = cdiv(cdiv(KB, s), 8) * 8;
+    return {per, cdiv(KB, per)};
+}
+
+// Sustained rates the cost model uses (per device, not per call): the
+// matrix peak of one CU at 2.4 GHz, a streaming HBM rate and an L2 read rate
+// per CU.  They only rank candidates; the bench reports measured numbers.
+constexpr double kCuFlops = 4.0 * 4096.0 * 2.4e9;
+constexpr double kHbm = 5.0e12;
+constexpr double kCuL2 = 64.0 * 2.4e9;
+
+double tile_efficiency(int bm, int bn)
+{
+    // fraction of the matrix peak a tile can sustain, from its operand bytes
+    // per multiply (smaller tiles re-read more)
+    const double ai = (double)bm * bn / (bm + bn);  // flops per operand byte, up to a constant
+    return ai / (ai + 24.0);
+}
+
+Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
+{
+    const int KB = K / 32;
+    if (num_cu <= 0)
+        num_cu = 256;
+    Plan best;
+    double best_t = 1e300;
+
+    auto consider_split = [&](int s) { return split_req <= 0 || s == split_req; };
+
+    int n_tile = 0, n_skinny = 0;
+    const mx::TileKernel *tile = mx::tile_kernels(&n_tile);
+    const mx::SkinnyKernel *skinny = mx::skinny_kernels(&n_skinny);
+    if (M <= 64) {
+        const int mg = cdiv(M, 16);
+        const int nr = mg >= 3 ? 4 : (mg == 2 ? 2 : 1);
+        const int nri = nr == 1 ? 0 : (nr == 2 ? 1 : 2);
+        const int rows_wg = 64 * nr;
+        const int tiles = cdiv(N, rows_wg);
+        for (int s : kSplits) {
+            if (!consider_split(s))
+                continue;
+            auto [per, eff] = split_chunks(KB, s);
+            if (split_req <= 0 && s > 1 && eff < s)
+                continue;  // heuristic: never pick a split that collapses
+            const int64_t wgs = (int64_t)tiles * eff;
+            // HBM-bound: time ~ bytes / rate, but a launch needs enough
+            // workgroups in flight to reach the rate (about 4 per CU)
+            const double bytes = (double)N * K / 2 * 1.0625 + (double)M * N * 2;
+            const double fill = std::min(1.0, (double)wgs / (4.0 * num_cu));
+            double t = bytes / (kHbm * fill);
+            if (eff > 1)
+                t += (double)tiles * eff * rows_wg * mg * 16 * 4 * 2 / kHbm + 1e-6;
+            if (t < best_t * 0.97 || (split_req > 0)) {
+                best_t = t;
+                best.family = 1;
+                best.index = (mg - 1) * 3 + nri;
+                best.bm = mg * 16;
+                best.bn = rows_wg;
+                best.split = eff;
+                best.kb_per_split = per;
+                best.tiles_m = 1;
+                best.tiles_n = tiles;
+                best.grid = wgs;
+                best.name = skinny[best.index].name;
+            }
+        }
+        const size_t part = (size_t)rows_wg * mg * 16 * 4;
+        best.counter_bytes = best.split > 1 ? align_up((size_t)tiles * 4, 256) : 0;
+        best.ws_bytes = best.split > 1 ? best.counter_bytes + (size_t)tiles * best.split * part : 0;
+        return best;
+    }
+
+    for (int k = 0; k < n_tile; ++k) {
+        const mx::TileKernel &tk = tile[k];
+        const int tm = cdiv(M, tk.bm), tn = cdiv(N, tk.bn);
+        const int64_t tiles = (int64_t)tm * tn;
+        for (int s : kSplits) {
+            if (!consider_split(s))
+                continue;
+            auto [per, eff] = split_chunks(KB, s);
+            if (split_req <= 0 && s > 1 && eff < s)
+                continue;
+            const int64_t wgs = tiles * eff;
+            const double rounds = (double)((wgs + (int64_t)num_cu * tk.occupancy - 1) / ((int64_t)num_cu * tk.occupancy));
+            const double t_tile = 2.0 * tk.bm * tk.bn * (double)per * 32 * tk.occupancy /
+                                  (kCuFlops * tile_efficiency(tk.bm, tk.bn));
+            double t = rounds * t_tile;
+            if (eff > 1)
+                t += (double)tiles * eff * tk.bm * tk.bn * 4 * 2 / kHbm +
+                     (double)eff * tk.bm * tk.bn * 4 / kCuL2;
+            if (t < best_t * 0.97 || split_req > 0) {
+                if (split_req > 0 && t >= best_t)
+                    continue;
+                best_t = t;
+                best.family = 0;
+                best.index = k;
+                best.bm = tk.bm;
+                best.bn = tk.bn;
+                best.split = eff;
+                best.kb_per_split = per;
+                best.tiles_m = tm;
+                best.tiles_n = tn;
+                best.grid = wgs;
+                best.name = tk.name;
+            }
+        }
+    }
+    const int64_t tiles = (int64_t)best.tiles_m * best.tiles_n;
+    best.counter_bytes = best.split > 1 ? align_up((size_t)tiles * 4, 256) : 0;
+    best.ws_bytes = best.split > 1 ? best.counter_bytes + (size_t)tiles * best.split * best.bm * best.bn * 4 : 0;
+    return best;
+}
+
+size_t packed_b_bytes(int N, int K) { return (size_t)cdiv(N, 16) * 16 * (size_t)cdiv(K / 32, 4) * 64; }
+size_t packed_sb_bytes(int N, int K) { return (size_t)cdiv(N, 32) * 32 * (size_t)cdiv(K / 32, 8) * 8; }
+
+// ---- device facts, queried once per device
+
+struct DeviceInfo {
+    bool known = false;
+    bool gfx950 = false;
+    int num_cu = 0;
+    double clock_hz = 0;
+    char arch[32] = {0};
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_mutex;
+
+mxgemm_status device_info(DeviceInfo **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return MXGEMM_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceInfo &d = g_dev[dev];
+    if (!d.known) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess)
+            return MXGEMM_ERR_HIP;
+        std::snprintf(d.arch, sizeof d.arch, "%s", p.gcnArchName);
+        d.gfx950 = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+        d.num_cu = p.multiProcessorCount;
+        d.clock_hz = (double)p.clockRate * 1e3;
+        d.known = true;
+    }
+    *out = &d;
+    return d.gfx950 ? MXGEMM_OK : MXGEMM_ERR_UNSUPPORTED_DEVICE;
+}
+
+// ---- library-owned split-K workspaces, one per (device, stream)
+
+struct Workspace {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+mxgemm_status get_workspace(hipStream_t stream, size_t need, void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return MXGEMM_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    Workspace &w = g_ws[{dev, stream}];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            if (hipStreamSynchronize(stream) != hipSuccess || hipFree(w.ptr) != hipSuccess)
+                return MXGEMM_ERR_HIP;
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        size_t sz = align_up(need, (size_t)1 << 20);
+        void *p = nullptr;
+        if (hipMalloc(&p, sz) != hipSuccess)
+            return MXGEMM_ERR_HIP;
+        // arrival counters must start at zero; the kernels leave them zero
+        if (hipMemset(p, 0, sz) != hipSuccess) {
+            (void)hipFree(p);
+            return MXGEMM_ERR_HIP;
+        }
+        w.ptr = p;
+        w.bytes = sz;
+    }
+    *out = w.ptr;
+    return MXGEMM_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+mxgemm_status check_shape(int M, int N, int K)
+{
+    if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || K > kMaxK)
+        return MXGEMM_ERR_SHAPE;
+    return MXGEMM_OK;
+}
+
+bool valid_split(int s) { return s == 0 || s == -1 || s == 1 || s == 2 || s == 4 || s == 8 || s == 16; }
+
+}  // namespace
+
+extern "C" {
+
+const char *mxgemm_status_string(mxgemm_status s)
+{
+    switch (s) {
+    case MXGEMM_OK: return "ok";
+    case MXGEMM_ERR_INVALID_ARG: return "invalid argument";
+    case MXGEMM_ERR_SHAPE: return "unsupported shape";
+    case MXGEMM_ERR_ALIGN: return "misaligned pointer or stride";
+    case MXGEMM_ERR_UNSUPPORTED_DEVICE: return "device is not gfx950";
+    case MXGEMM_ERR_HIP: return "HIP runtime error";
+    case MXGEMM_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+    }
+}
+
+mxgemm_status mxgemm_plan(int M, int N, int K, int b_packed, int split_k, int num_cu, mxgemm_info *out)
+{
+    if (!out || !valid_split(split_k) || (b_packed != 0 && b_packed != 1) || num_cu < 1)
+        return MXGEMM_ERR_INVALID_ARG;
+    mxgemm_status st = check_shape(M, N, K);
+    if (st != MXGEMM_OK)
+        return st;
+    Plan p = plan_for(M, N, K, b_packed, split_k, num_cu);
+    std::memset(out, 0, sizeof *out);
+    out->kernel = p.family;
+    out->tile_m = p.bm;
+    out->tile_n = p.bn;
+    out->split_k = p.split;
+    out->grid = p.grid;
+    out->workspace_bytes = p.ws_bytes;
+    out->packed_b_bytes = packed_b_bytes(N, K);
+    out->packed_sb_bytes = packed_sb_bytes(N, K);
+    out->num_cu = num_cu;
+    std::snprintf(out->kernel_name, sizeof out->kernel_name, "%s", p.name);
+    return MXGEMM_OK;
+}
+
+mxgemm_status mxgemm_query(int M, int N, int K, int b_packed, int split_k, mxgemm_info *out)
+{
+    if (!out || !valid_split(split_k) || (b_packed != 0 && b_packed != 1))
+        return MXGEMM_ERR_INVALID_ARG;
+    mxgemm_status st = check_shape(M, N, K);
+    if (st != MXGEMM_OK)
+        return st;
+    DeviceInfo *d = nullptr;
+    st = device_info(&d);
+    if (st != MXGEMM_OK)
+        return st;
+    st = mxgemm_plan(M, N, K, b_packed, split_k, d->num_cu, out);
+    if (st != MXGEMM_OK)
+        return st;
+    std::snprintf(out->arch, sizeof out->arch, "%s", d->arch);
+    out->clock_hz = d->clock_hz;
+    // 16x16x128 FP4: 65536 flop per 16 cycles per matrix core ("CDNA4 dense
+    // MFMA builtins", "Instruction throughput"), four matrix cores per CU.
+    out->peak_flops = 65536.0 / 16.0 * 4.0 * d->num_cu * d->clock_hz;
+    return MXGEMM_OK;
+}
+
+mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, const void *scaleA,
+                         const void *scaleB, float alpha, float beta, int M, int N, int K,
+                         const mxgemm_strides *strides, int split_k, hipStream_t stream)
+{
+    // ---- host-only validation (no HIP call before it passes)
+    if (!D || !A || !B || !scaleA || !scaleB || !valid_split(split_k))
+        return MXGEMM_ERR_INVALID_ARG;
+    if (beta != 0.0f && !C)
+        return MXGEMM_ERR_INVALID_ARG;
+    mxgemm_status st = check_shape(M, N, K);
+    if (st != MXGEMM_OK)
+        return st;
+    mxgemm_strides s;
+    if (strides) {
+        s = *strides;
+        if (s.reserved != 0 || (s.b_packed != 0 && s.b_packed != 1))
+            return MXGEMM_ERR_INVALID_ARG;
+    } else {
+        std::memset(&s, 0, sizeof s);
+        s.ldd = s.ldc = N;
+        s.lda = s.ldb = K;
+        s.ldsa = s.ldsb = K / 32;
+    }
+    const int KB = K / 32;
+    if (s.ldd < N || s.lda < K || s.ldsa < KB || (beta != 0.0f && s.ldc < N))
+        return MXGEMM_ERR_SHAPE;
+    if (!s.b_packed && (s.ldb < K || s.ldsb < KB))
+        return MXGEMM_ERR_SHAPE;
+    if (s.lda % 2 || (!s.b_packed && s.ldb % 2))
+        return MXGEMM_ERR_ALIGN;
+    if (!aligned(A, 16) || !aligned(B, 16) || (s.lda / 2) % 16 || (!s.b_packed && (s.ldb / 2) % 16))
+        return MXGEMM_ERR_ALIGN;
+    if (s.b_packed && !aligned(scaleB, 4))
+        return MXGEMM_ERR_ALIGN;
+    if (!aligned(D, 2) || (C && beta != 0.0f && !aligned(C, 2)))
+        return MXGEMM_ERR_ALIGN;
+    // byte offsets inside a tile must stay below 2^31
+    if ((int64_t)256 * (s.lda / 2) >= ((int64_t)1 << 31) || (!s.b_packed && (int64_t)256 * (s.ldb / 2) >= ((int64_t)1 << 31)))
+        return MXGEMM_ERR_SHAPE;
+
+    // ---- device and plan
+    DeviceInfo *d = nullptr;
+    st = device_info(&d);
+    if (st != MXGEMM_OK)
+        return st;
+    Plan p = plan_for(M, N, K, s.b_packed, split_k, d->num_cu);
+
+    GemmArgs g;
+    std::memset(&g, 0, sizeof g);
+    g.D = (uint16_t *)D;
+    g.C = (const uint16_t *)C;
+    g.A = (const uint8_t *)A;
+    g.B = (const uint8_t *)B;
+    g.SA = (const uint8_t *)scaleA;
+    g.SB = (const uint8_t *)scaleB;
+    g.alpha = alpha;
+    g.beta = beta;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.KB = KB;
+    g.lda_b = s.lda / 2;
+    g.ldb_b = s.ldb / 2;
+    g.ldsa = s.ldsa;
+    g.ldsb = s.ldsb;
+    g.ldc = s.ldc;
+    g.ldd = s.ldd;
+    g.split = p.split;
+    g.kb_per_split = p.kb_per_split;
+    g.tiles_m = p.tiles_m;
+    g.tiles_n = p.tiles_n;
+    g.ks_total = cdiv(KB, 4);
+    g.sn8 = cdiv(KB, 8);
+    g.sa_fast = aligned(scaleA, 8) && s.ldsa % 8 == 0 && KB % 8 == 0;
+    g.sb_fast = !s.b_packed && aligned(scaleB, 8) && s.ldsb % 8 == 0 && KB % 8 == 0;
+    g.d_vec = aligned(D, 8) && s.ldd % 4 == 0;
+    g.c_vec = C && aligned(C, 8) && s.ldc % 4 == 0;
+    g.group_m = 4;
+
+    if (p.split > 1) {
+        void *ws = nullptr;
+        if (s.workspace) {
+            if (s.workspace_bytes < p.ws_bytes)
+                return MXGEMM_ERR_WORKSPACE;
+            ws = s.workspace;
+        } else {
+            st = get_workspace(stream, p.ws_bytes, &ws);
+            if (st != MXGEMM_OK)
+                return st;
+        }
+        g.counters = (int *)ws;
+        g.ws = (float *)((char *)ws + p.counter_bytes);
+    }
+
+    if (p.grid > 0x7FFFFFFF)
+        return MXGEMM_ERR_SHAPE;
+    if (p.family == 0) {
+        int n = 0;
+        const mx::TileKernel &k = mx::tile_kernels(&n)[p.index];
+        (s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
+    } else {
+        int n = 0;
+        const mx::SkinnyKernel &k = mx::skinny_kernels(&n)[p.index];
+        (s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
+    }
+    if (hipGetLastError() != hipSuccess)
+        return MXGEMM_ERR_HIP;
+    return MXGEMM_OK;
+}
+
+mxgemm_status mxgemm_pack_b(void *Bp, void *SBp, const void *B, const void *scaleB, int N, int K, int64_t ldb,
+                            int64_t ldsb, hipStream_t stream)
+{
+    if (!Bp || !SBp || !B || !scaleB)
+        return MXGEMM_ERR_INVALID_ARG;
+    mxgemm_status st = check_shape(1, N, K);
+    if (st != MXGEMM_OK)
+        return st;
+    if (ldb < K || ldsb < K / 32)
+        return MXGEMM_ERR_SHAPE;
+    if (ldb % 2 || (ldb / 2) % 16 || !aligned(B, 16) || !aligned(Bp, 16) || !aligned(SBp, 4))
+        return MXGEMM_ERR_ALIGN;
+    DeviceInfo *d = nullptr;
+    st = device_info(&d);
+    if (st != MXGEMM_OK)
+        return st;
+    mx::launch_pack_b((uint8_t *)Bp, (const uint8_t *)B, N, K / 32, ldb / 2, stream);
+    mx::launch_pack_sb((uint32_t *)SBp, (const uint8_t *)scaleB, N, K / 32, ldsb, stream);
+    if (hipGetLastError() != hipSuccess)
+        return MXGEMM_ERR_HIP;
+    return MXGEMM_OK;
+}
+
+mxgemm_status mxgemm_release_workspaces(void)
+{
+    std::lock_guard<std::mutex> lock(g_mutex);
+    mxgemm_status st = MXGEMM_OK;
+    for (auto &kv : g_ws) {
+        if (kv.second.ptr) {
+            int cur = 0;
+            (void)hipGetDevice(&cur);
+            if (hipSetDevice(kv.first.first) != hipSuccess || hipStreamSynchronize(kv.first.second) != hipSuccess ||
+                hipFree(kv.second.ptr) != hipSuccess)
+                st = MXGEMM_ERR_HIP;
+            (void)hipSetDevice(cur);
+        }
+    }
+    g_ws.clear();
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,190 @@
+/*
+ * libmxgemm — MXFP4 block-scaled GEMM for AMD Instinct MI355X (gfx950).
+ *
+ *     D[M,N] = bf16( alpha * A[M,K] * B[N,K]^T + beta * C[M,N] )
+ *
+ * A and B hold OCP E2M1 (fp4) codes packed two per byte; every run of 32
+ * consecutive K elements of a row carries one E8M0 scale byte.  This is the
+ * problem the asm_f4gemm README ("asm_f4gemm -- driving aiter's gfx950
+ * MXFP4 GEMM code objects") states at its top; operand formats follow its
+ * section "Data layouts":
+ *
+ *   A      [M][lda/2] bytes, row-major.  Byte i of a row holds element 2i in
+ *          its low nibble and element 2i+1 in its high nibble.  A code's
+ *          value is one of {0, .5, 1, 1.5, 2, 3, 4, 6}, sign in bit 3.
+ *   B      [N][ldb/2] bytes, same encoding (B is used transposed: D = A B^T).
+ *   scaleA [M][ldsa] bytes: scaleA[i][k/32] is the E8M0 scale of A[i][k];
+ *          its value is 2^(e-127) (0xFF is NaN).
+ *   scaleB [N][ldsb] bytes, likewise for B.
+ *   C, D   [M][ldc], [M][ldd] bf16, row-major.
+ *
+ * Arithmetic: the scaled products are accumulated in fp32 by the CDNA4
+ * scaled matrix instructions ("CDNA4 dense MFMA builtins", section
+ * "Mixed-precision with scaling"), partial sums of a split K are added in
+ * fp32 in a fixed order, and the epilogue forms alpha*acc + beta*C in fp32
+ * and rounds once to bf16 (nearest, ties to even).  When beta == 0, C is not
+ * read (it may be NULL and may hold NaNs).
+ *
+ * Every pointer passed to libmxgemm is a DEVICE pointer on the current HIP
+ * device, owned by the caller; the library never frees, retains or
+ * reallocates caller memory.  All calls are asynchronous on `stream` (NULL
+ * means the null stream) and return after enqueueing.  No call throws or
+ * aborts: every failure is a negative status code.  Argument validation
+ * happens on the host before any HIP call is made.
+ */
+#ifndef LIBMXGEMM_H
+#define LIBMXGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+
+typedef int mxgemm_status;
+
+#define MXGEMM_OK                      0
+#define MXGEMM_ERR_INVALID_ARG        -1  /* NULL pointer, bad split_k, C == NULL with beta != 0, ... */
+#define MXGEMM_ERR_SHAPE              -2  /* M, N < 1; K < 32; K % 32 != 0; K > 2^24; stride < extent */
+#define MXGEMM_ERR_ALIGN              -3  /* A/B base not 16-byte aligned, or row pitch lda/2, ldb/2 not a multiple of 16 bytes */
+#define MXGEMM_ERR_UNSUPPORTED_DEVICE -4  /* current device is not gfx950 */
+#define MXGEMM_ERR_HIP                -5  /* a HIP runtime call failed (launch, allocation) */
+#define MXGEMM_ERR_WORKSPACE          -6  /* caller workspace smaller than mxgemm_query's workspace_bytes */
+
+/* Static string naming a status code (never NULL). */
+const char *mxgemm_status_string(mxgemm_status status);
+
+/* ---- strides and options --------------------------------------------------- */
+
+/*
+ * Row strides of the operands.  Passing NULL for the whole struct means
+ * dense rows: ldd = ldc = N, lda = ldb = K, ldsa = ldsb = K/32, b_packed = 0,
+ * library-owned workspace.
+ *
+ * Units follow the asm_f4gemm README ("Kernel ABI", kernarg notes): A and B
+ * strides count fp4 ELEMENTS (twice the byte pitch) and must be even; scale
+ * strides count bytes; C and D strides count bf16 elements.  ldc and ldd are
+ * honoured separately, so D may alias C (in place) when ldc == ldd.
+ */
+typedef struct mxgemm_strides {
+    int64_t ldd;      /* bf16 elements between rows of D, >= N */
+    int64_t ldc;      /* bf16 elements between rows of C, >= N (ignored if beta == 0) */
+    int64_t lda;      /* fp4 elements between rows of A, >= K, even */
+    int64_t ldb;      /* fp4 elements between rows of B, >= K, even (ignored if b_packed) */
+    int64_t ldsa;     /* bytes between rows of scaleA, >= K/32 */
+    int64_t ldsb;     /* bytes between rows of scaleB, >= K/32 (ignored if b_packed) */
+    int32_t b_packed; /* 0: B, scaleB row-major as above; 1: outputs of mxgemm_pack_b */
+    int32_t reserved; /* must be 0 */
+    void *workspace;  /* optional device buffer for split-K partials; NULL = library-owned */
+    size_t workspace_bytes;
+} mxgemm_strides;
+
+/* ---- the GEMM ------------------------------------------------------------- */
+
+/*
+ * D = bf16(alpha * A * B^T + beta * C).  Enqueued on `stream`.
+ *
+ * split_k: 0 or -1 lets the library choose (the "-1 lets the heuristic try"
+ *          convention of the asm_f4gemm CLI, section "Build and run");
+ *          1 = no split; 2, 4, 8 or 16 = split the K range into that many
+ *          chunks whose fp32 partial sums are added in a fixed order (the
+ *          result is bitwise reproducible run to run).  Other values:
+ *          MXGEMM_ERR_INVALID_ARG.  A split that would leave a chunk empty is
+ *          reduced to the largest allowed value that does not.
+ *
+ * Shapes: M, N >= 1; K >= 32, K % 32 == 0, K <= 2^24.  M and N need not be
+ * multiples of any tile size and K need not be a multiple of 128: edges are
+ * handled inside the kernels (no caller padding as in the asm_f4gemm README's
+ * "D -- output" note).
+ *
+ * Alignment: A and B base addresses 16-byte aligned and lda/2, ldb/2 (the
+ * byte pitches) multiples of 16.  Scales, C and D need only natural
+ * alignment (C and D: 2 bytes).
+ *
+ * Split-K (split_k > 1, chosen or forced) needs a workspace of
+ * mxgemm_query(...).workspace_bytes.  With strides->workspace == NULL the
+ * library allocates one per (device, stream) on first use and keeps it
+ * until mxgemm_release_workspaces(); the first call with a new (device,
+ * stream, size) therefore allocates.  A caller workspace must be at least
+ * that size and must not be used by two calls that can run concurrently.
+ */
+mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B,
+                         const void *scaleA, const void *scaleB,
+                         float alpha, float beta, int M, int N, int K,
+                         const mxgemm_strides *strides, int split_k,
+                         hipStream_t stream);
+
+/* ---- B pre-shuffle ----------------------------------------------------------- */
+
+/*
+ * Rewrite B [N][ldb/2] and scaleB [N][ldsb] into the layout the kernels read
+ * directly (b_packed = 1).  The byte permutation is the "16x16
+ * tile-transposed" B shuffle of the asm_f4gemm README ("Data layouts", B):
+ *
+ *   B[n0*16 + n1][k-byte k0*32 + k1*16 + k2]
+ *       -> Bp[(((n0 * Kp/32 + k0) * 2 + k1) * 16 + n1) * 16 + k2],
+ *
+ * with Kp = (K rounded up to 128)/2 bytes and N rounded up to 16 rows, so
+ * that every 1 KiB of Bp is one matrix-instruction operand (16 rows x 128
+ * K), and the scale shuffle of the same section (its "A_scale / B_scale"
+ * part), over scaleB padded to [N rounded up to 32][K/32 rounded up to 8]:
+ *
+ *   scaleB[d0*32 + d1*16 + d2][d3*8 + d4*4 + d5]
+ *       -> SBp[((((d0 * sn/8 + d3) * 4 + d5) * 16 + d2) * 2 + d4) * 2 + d1],
+ *
+ * sn = padded K/32.  Padding bytes are code 0 for Bp and 0x7F (2^0) for SBp.
+ * Bp and SBp are caller buffers of mxgemm_query's packed_b_bytes and
+ * packed_sb_bytes; they must not overlap B or scaleB.  Bp 16-byte aligned,
+ * SBp 4-byte aligned, B as for mxgemm_run.  Same shape rules as mxgemm_run.
+ */
+mxgemm_status mxgemm_pack_b(void *Bp, void *SBp, const void *B, const void *scaleB,
+                            int N, int K, int64_t ldb, int64_t ldsb,
+                            hipStream_t stream);
+
+/* ---- plan / query ------------------------------------------------------------- */
+
+typedef struct mxgemm_info {
+    int32_t kernel;          /* kernel family: 0 = tiled (LDS), 1 = skinny (M <= 64, streams B) */
+    int32_t tile_m, tile_n;  /* output tile per workgroup */
+    int32_t split_k;         /* K chunks the plan uses */
+    int64_t grid;            /* workgroups launched */
+    size_t workspace_bytes;  /* split-K workspace needed (0 if split_k == 1) */
+    size_t packed_b_bytes;   /* size of mxgemm_pack_b's Bp for this N, K */
+    size_t packed_sb_bytes;  /* size of mxgemm_pack_b's SBp for this N, K */
+    int32_t num_cu;          /* compute units the plan assumed */
+    int32_t reserved;
+    char kernel_name[64];
+    char arch[32];           /* device architecture (mxgemm_query only) */
+    double peak_flops;       /* dense MXFP4 matrix peak, flop/s, from the device clock and CU count */
+    double clock_hz;         /* peak engine clock used for peak_flops */
+} mxgemm_info;
+
+/*
+ * Plan for the current device: the kernel, tile and split mxgemm_run would
+ * use for these arguments, and the buffer sizes it needs.  Returns
+ * MXGEMM_ERR_UNSUPPORTED_DEVICE unless the current device is gfx950.
+ * split_k as for mxgemm_run.
+ */
+mxgemm_status mxgemm_query(int M, int N, int K, int b_packed, int split_k,
+                           mxgemm_info *out);
+
+/*
+ * The same plan for a device with num_cu compute units, computed on the
+ * host without touching any device (arch, peak_flops, clock_hz left 0).
+ */
+mxgemm_status mxgemm_plan(int M, int N, int K, int b_packed, int split_k, int num_cu,
+                          mxgemm_info *out);
+
+/* Free the library-owned split-K workspaces (after synchronizing their
+ * streams).  Later calls allocate again. */
+mxgemm_status mxgemm_release_workspaces(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMXGEMM_H */

@@ -1,0 +1,162 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no compute calls).
+
+- libmxgemm.so loads and exports every function include/libmxgemm.h declares;
+- every argument error is reported before any HIP call is made;
+- the planner (mxgemm_plan, pure host logic) makes choices that respect its
+  contract on the five workloads and on edge shapes.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_precision_mxfp4_amd as mx
+from block_scaled_precision_mxfp4_amd import build as mxbuild
+from block_scaled_precision_mxfp4_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmxgemm.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if mxbuild.is_stale():
+        mxbuild.build()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxgemm_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(mx.EXPORTS) == declared_functions()
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mx.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = mx.mxgemm_status_string(code)
+        assert s and s != "unknown status"
+    assert mx.mxgemm_status_string(-99) == "unknown status"
+
+
+def _run(**kw):
+    args = dict(D=0x1000, C=None, A=0x2000, B=0x3000, scaleA=0x4000, scaleB=0x5000,
+                alpha=1.0, beta=0.0, M=128, N=256, K=512, strides=None, split_k=-1, stream=0)
+    args.update(kw)
+    return mx.mxgemm_run(**args, check=False)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=None), -1), (dict(A=None), -1), (dict(B=None), -1), (dict(scaleA=None), -1),
+    (dict(scaleB=None), -1), (dict(beta=1.0, C=None), -1), (dict(split_k=3), -1),
+    (dict(split_k=32), -1), (dict(split_k=-2), -1),
+    (dict(M=0), -2), (dict(N=0), -2), (dict(K=0), -2), (dict(K=16), -2), (dict(K=48), -2),
+    (dict(K=(1 << 24) + 32), -2),
+    (dict(A=0x2008), -3), (dict(B=0x3004), -3), (dict(D=0x1001), -3),
+])
+def test_run_validation_before_any_hip_call(kw, code):
+    assert _run(**kw) == code
+
+
+def test_run_stride_validation():
+    def st(**kw):
+        d = dict(ldd=256, ldc=256, lda=512, ldb=512, ldsa=16, ldsb=16)
+        d.update(kw)
+        return mx.make_strides(**d)
+    assert _run(strides=st(ldd=255)) == -2
+    assert _run(strides=st(lda=480)) == -2
+    assert _run(strides=st(ldsa=15)) == -2
+    assert _run(strides=st(ldb=510)) == -2
+    assert _run(strides=st(ldsb=15)) == -2
+    assert _run(strides=st(ldc=255), beta=1.0, C=0x6000) == -2
+    assert _run(strides=st(lda=513)) == -3      # odd element stride
+    assert _run(strides=st(lda=528)) == -3      # 264-byte pitch: not a multiple of 16
+    assert _run(strides=st(ldb=528)) == -3
+    s = st()
+    s.reserved = 1
+    assert _run(strides=s) == -1
+    s = st()
+    s.b_packed = 2
+    assert _run(strides=s) == -1
+    # packed B: B strides are ignored, but scaleB must be 4-byte aligned
+    assert _run(strides=st(ldb=0, ldsb=0, b_packed=1), scaleB=0x5002) == -3
+
+
+def test_pack_validation_before_any_hip_call():
+    f = lambda **kw: mx.mxgemm_pack_b(**dict(dict(Bp=0x1000, SBp=0x2000, B=0x3000, scaleB=0x4000,
+                                                   N=64, K=256, stream=0), **kw), check=False)
+    assert f(Bp=None) == -1 and f(SBp=None) == -1 and f(B=None) == -1 and f(scaleB=None) == -1
+    assert f(N=0) == -2 and f(K=40) == -2 and f(ldb=128) == -2 and f(ldsb=4) == -2
+    assert f(Bp=0x1008) == -3 and f(SBp=0x2002) == -3 and f(B=0x3008) == -3 and f(ldb=272) == -3
+
+
+def test_query_and_plan_argument_errors():
+    info = mx.Info()
+    L = mx.lib()
+    assert L.mxgemm_plan(8, 8, 64, 0, -1, 256, None) == -1
+    assert L.mxgemm_plan(8, 8, 64, 2, -1, 256, ctypes.byref(info)) == -1
+    assert L.mxgemm_plan(8, 8, 64, 0, 5, 256, ctypes.byref(info)) == -1
+    assert L.mxgemm_plan(8, 8, 64, 0, -1, 0, ctypes.byref(info)) == -1
+    assert L.mxgemm_plan(8, 8, 40, 0, -1, 256, ctypes.byref(info)) == -2
+    assert L.mxgemm_query(0, 8, 64, 0, -1, ctypes.byref(info)) == -2
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_plan_for_workloads(name):
+    w = inputs.WORKLOADS[name]
+    M, N, K = w["M"], w["N"], w["K"]
+    for b_packed in (0, 1):
+        p = mx.mxgemm_plan(M, N, K, b_packed, -1, 256)
+        assert p["split_k"] in (1, 2, 4, 8, 16)
+        if M <= 64:
+            assert p["kernel"] == 1 and p["kernel_name"].startswith("skinny")
+            assert p["tile_m"] >= M
+        else:
+            assert p["kernel"] == 0 and p["kernel_name"].startswith("tile")
+        tiles = cdiv(M, p["tile_m"]) * cdiv(N, p["tile_n"]) if M > 64 else cdiv(N, p["tile_n"])
+        assert p["grid"] == tiles * p["split_k"]
+        if p["split_k"] > 1:
+            part = p["tile_m"] * p["tile_n"] * 4 if M > 64 else p["tile_n"] * cdiv(M, 16) * 16 * 4
+            counters = cdiv(tiles * 4, 256) * 256
+            assert p["workspace_bytes"] == counters + tiles * p["split_k"] * part
+        else:
+            assert p["workspace_bytes"] == 0
+        assert p["packed_b_bytes"] == cdiv(N, 16) * 16 * cdiv(K // 32, 4) * 64
+        assert p["packed_sb_bytes"] == cdiv(N, 32) * 32 * cdiv(K // 32, 8) * 8
+    # the large square case fills the machine with full tiles and no split
+    if name == "square_8192":
+        p = mx.mxgemm_plan(M, N, K, 1, -1, 256)
+        assert (p["tile_m"], p["tile_n"], p["split_k"]) == (256, 256, 1)
+    # the decode case splits K to get enough workgroups
+    if name == "gemv_1x8192x8192":
+        assert mx.mxgemm_plan(M, N, K, 0, -1, 256)["split_k"] > 1
+
+
+@pytest.mark.parametrize("s", [1, 2, 4, 8, 16])
+def test_forced_split_is_honoured_or_reduced(s):
+    # K = 4096: 128 blocks, every split up to 16 leaves chunks of >= 8 blocks
+    assert mx.mxgemm_plan(300, 500, 4096, 0, s, 256)["split_k"] == s
+    assert mx.mxgemm_plan(1, 500, 4096, 0, s, 256)["split_k"] == s
+    # K = 256: a single 256-K stage; any split collapses to 1
+    assert mx.mxgemm_plan(300, 500, 256, 0, s, 256)["split_k"] == 1
+    # K = 1024: 32 blocks -> at most 4 chunks of 8
+    assert mx.mxgemm_plan(300, 500, 1024, 0, s, 256)["split_k"] == min(s, 4)
+
+
+def test_plan_is_deterministic():
+    a = [mx.mxgemm_plan(m, n, k, 0, -1, 256) for m, n, k in [(77, 999, 2048), (4096, 4096, 4096)]]
+    b = [mx.mxgemm_plan(m, n, k, 0, -1, 256) for m, n, k in [(77, 999, 2048), (4096, 4096, 4096)]]
+    assert a == b
