@@ -105,7 +105,8 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True):
         with torch.cuda.graph(graph, stream=stream):
             for i in range(steps):
                 launch(i)
-        graph.replay()
+        with torch.cuda.stream(stream):
+            graph.replay()
         torch.cuda.synchronize()
     except Exception as e:  # capture unsupported: fall back to eager launches
         log("graph capture failed (%s); timing eager launches" % e)
@@ -115,13 +116,14 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True):
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(stream)
-    if graph is not None:
-        graph.replay()
-    else:
-        for i in range(steps):
-            launch(i)
-    e1.record(stream)
+    with torch.cuda.stream(stream):  # the graph replays on the current stream
+        e0.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(steps):
+                launch(i)
+        e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = e0.elapsed_time(e1)
@@ -153,23 +155,24 @@ def cpu_baseline(name, target_s=12.0):
     p = inputs.make_workload(name)
     M, N, K = p["M"], p["N"], p["K"]
     threads = max(1, min(16, os.cpu_count() or 1))
-    # calibrate on a small block, then size the sample for ~target_s seconds
-    rows = np.arange(min(M, 4), dtype=np.int64)
-    cols = np.arange(min(N, 256), dtype=np.int64)
-    t0 = time.perf_counter()
-    oracle.mxgemm(p["A"], p["SA"], p["B"], p["SB"], K, p["alpha"], p["beta"], p["C"],
-                  rows=rows, cols=cols, threads=threads)
-    dt = max(time.perf_counter() - t0, 1e-3)
-    rate = len(rows) * len(cols) / dt  # outputs per second
-    n_out = int(min(M * N, max(1, rate * target_s)))
-    n_cols = int(min(N, max(threads, n_out // min(M, 64))))
-    n_rows = int(min(M, max(1, n_out // n_cols)))
-    rows = np.arange(n_rows, dtype=np.int64)
-    cols = np.arange(n_cols, dtype=np.int64)
-    t0 = time.perf_counter()
-    oracle.mxgemm(p["A"], p["SA"], p["B"], p["SB"], K, p["alpha"], p["beta"], p["C"],
-                  rows=rows, cols=cols, threads=threads)
-    dt = time.perf_counter() - t0
+    # grow the sample (whole rows of the output, capped by its size) until a
+    # run takes a sizeable fraction of target_s, then scale it to target_s
+    n_cols = min(N, 1024)
+    n_rows = 1
+    while True:
+        rows = np.arange(n_rows, dtype=np.int64)
+        cols = np.arange(n_cols, dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.mxgemm(p["A"], p["SA"], p["B"], p["SB"], K, p["alpha"], p["beta"], p["C"],
+                      rows=rows, cols=cols, threads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 3 or n_rows * n_cols >= M * N:
+            break
+        grow = min(8.0, max(2.0, target_s / max(dt, 1e-3)))
+        if n_cols < N:
+            n_cols = min(N, int(n_cols * grow))
+        else:
+            n_rows = min(M, max(n_rows + 1, int(n_rows * grow)))
     macs = n_rows * n_cols * K
     return {"value": 2.0 * macs / dt / 1e9, "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "%d rows x %d cols of %s (%.3g MACs, fp64) in %.2f s" % (

@@ -162,26 +162,45 @@ __device__ __forceinline__ int xcd_remap(int wg, int total)
     return xcd * q + (xcd < r ? xcd : r) + idx;
 }
 
-// Split-K arrival: every workgroup of a tile has written its fp32 partial;
-// returns true in exactly one of them (the last to arrive), which then owns
-// the reduction.  The counter is returned to zero for the next call.
+// ---- split-K partials shared between workgroups
+//
+// Workgroups of one output tile may run on different XCDs, whose L2 caches
+// are not coherent with each other.  Partial sums are therefore written and
+// read with the device-coherent cache policy (sc1, the policy the compiler
+// uses for agent-scope atomic stores and loads): a store completes only once
+// it is visible device-wide, and a load never hits a stale L2 line.  That
+// makes the usual release/acquire fences, which write back and invalidate a
+// whole L2 each time, unnecessary here.
+constexpr int kCoherent = 16;  // cache-policy bits: sc1
+
+__device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, v4f v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCoherent);
+}
+
+__device__ __forceinline__ v4f load16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent);
+}
+
+// Called by every thread after storing its part of the workgroup's partial
+// with store16_coherent.  Returns true in exactly one workgroup of the tile
+// (the last to arrive), whose threads may then read all partials with
+// load16_coherent.  The counter is returned to zero for the next call.
 __device__ __forceinline__ bool split_arrive_last(int *counter, int splits)
 {
     __shared__ int s_last;
-    __threadfence();  // release this workgroup's partial at device scope
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are complete
+    __syncthreads();                      // ... and so are every other thread's
     if (threadIdx.x == 0) {
-        int prev = atomicAdd(counter, 1);
-        int last = prev == splits - 1;
+        const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = prev == splits - 1;
         if (last)
-            atomicExch(counter, 0);
+            __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = last;
     }
     __syncthreads();
-    const bool last = s_last != 0;
-    if (last)
-        __threadfence();  // acquire the other workgroups' partials
-    return last;
+    return s_last != 0;
 }
 
 }  // namespace mx

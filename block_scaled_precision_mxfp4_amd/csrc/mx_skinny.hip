@@ -3,15 +3,17 @@
 // Here the whole cost is reading B once from HBM, so the kernel streams B
 // straight from memory into registers (16 bytes per lane, one instruction
 // operand per 16 rows x 128 K) with several loads in flight per lane, and
-// keeps the tiny A in the L2.  Each wave owns 16*NR rows of B (= columns of
-// D); its accumulators cover all M <= 16*MG rows of D.  The scaled FP4
-// instruction still does the arithmetic: rows of A past M are zero lanes
-// (out-of-range loads return zero), which costs nothing here because the
-// matrix unit is far from busy when bytes arrive at HBM speed.
+// keeps the tiny A in the L2.  A workgroup owns 16*NR rows of B (= columns
+// of D) and one K chunk; its four waves take consecutive quarters of that
+// chunk and add their accumulators through LDS in a fixed order.  The
+// accumulators of a wave cover all M <= 16*MG rows of D.  The scaled FP4
+// instruction does the arithmetic: rows of A past M are zero lanes
+// (out-of-range loads return zero without memory traffic), which costs
+// nothing here because the matrix unit is far from busy at HBM speed.
 //
-// Split K spreads one row block over several workgroups; the partial sums
-// are combined in fp32 in a fixed order by the last workgroup to arrive (see
-// split_arrive_last), in the same launch.
+// Split K across workgroups (more workgroups than row blocks, to keep
+// enough bytes in flight) combines fp32 partials in a fixed order in the
+// last workgroup to arrive, in the same launch.
 #include "mx_args.hpp"
 #include "mx_device.hpp"
 
@@ -20,35 +22,41 @@ namespace mx {
 template <int MG, int NR, bool BPACK>
 __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
 {
-    constexpr int RW = 16 * NR;  // B rows per wave
-    constexpr int RWG = 4 * RW;  // B rows per workgroup
+    constexpr int R = 16 * NR;   // B rows per workgroup
     constexpr int U = 4;         // 128-K steps loaded per batch
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int NF = NR * MG;  // 16x16 result blocks per workgroup
+    __shared__ v4f s_red[4][NF][64];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
     const int lg = xcd_remap(blockIdx.x, gridDim.x);
     const int z = lg / g.tiles_n;
     const int t = lg - z * g.tiles_n;
-    const int nw = t * RWG + wave * RW;  // first row of B (column of D) of this wave
+    const int n0 = t * R;  // first row of B (column of D) of this workgroup
 
     const int kb_begin = z * g.kb_per_split;
     const int kb_end = min(g.KB, kb_begin + g.kb_per_split);
     const int ks_begin = kb_begin >> 2, ks_end = (kb_end + 3) >> 2;
+    const int q = (ks_end - ks_begin + 3) >> 2;  // k-steps per wave
+    const int w_begin = ks_begin + wave * q;
+    const int w_end = min(ks_end, w_begin + q);
 
     const auto ra = make_rsrc(g.A, (uint32_t)(g.M * g.lda_b));
     const auto rsa = make_rsrc(g.SA, (uint32_t)(g.M * g.ldsa));
     __amdgpu_buffer_rsrc_t rb, rsb;
-    int half0 = 0;  // packed scales: which 16-row half of its 32-row group row nw is
+    int half0 = 0;  // packed scales: which 16-row half of its 32-row group row n0 is
     if constexpr (BPACK) {
-        const int n16 = nw / 16, g16 = max(0, min(NR, (g.N + 15) / 16 - n16));
+        const int n16 = n0 / 16, g16 = max(0, min(NR, (g.N + 15) / 16 - n16));
         rb = make_rsrc(g.B + (int64_t)n16 * g.ks_total * 1024, (uint32_t)(g16 * g.ks_total * 1024));
-        const int n32 = nw / 32;
-        const int g32 = max(0, min((nw + RW + 31) / 32 - n32, (g.N + 31) / 32 - n32));
+        const int n32 = n0 / 32;
+        const int g32 = max(0, min((n0 + R + 31) / 32 - n32, (g.N + 31) / 32 - n32));
         rsb = make_rsrc(g.SB + (int64_t)n32 * g.sn8 * 256, (uint32_t)(g32 * g.sn8 * 256));
         half0 = n16 & 1;
     } else {
-        const int rows = max(0, min(RW, g.N - nw));
-        rb = make_rsrc(g.B + (int64_t)nw * g.ldb_b, (uint32_t)(rows * g.ldb_b));
-        rsb = make_rsrc(g.SB + (int64_t)nw * g.ldsb, (uint32_t)(rows * g.ldsb));
+        const int rows = max(0, min(R, g.N - n0));
+        rb = make_rsrc(g.B + (int64_t)n0 * g.ldb_b, (uint32_t)(rows * g.ldb_b));
+        rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)(rows * g.ldsb));
     }
 
     v4f acc[NR][MG];
@@ -58,14 +66,14 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
         for (int mg = 0; mg < MG; ++mg)
             acc[nr][mg] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int ks0 = ks_begin; ks0 < ks_end; ks0 += U) {
+    for (int ks0 = w_begin; ks0 < w_end; ks0 += U) {
         v4i bfr[U][NR], afr[U][MG];
         uint32_t sbv[U][NR], sav[U][MG];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int ks = ks0 + u;
             const int kb = ks * 4 + (lane >> 4);
-            const bool ok = ks < ks_end && kb < kb_end;
+            const bool ok = ks < w_end && kb < kb_end;
 #pragma unroll
             for (int nr = 0; nr < NR; ++nr) {
                 if constexpr (BPACK) {
@@ -97,37 +105,64 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
                                                  (int)sav[u][mg]);
     }
 
-    Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec};
-    const int mb = lane & 15;
-    const int nb = nw + 4 * (lane >> 4);
-    if (g.split == 1) {
-#pragma unroll
-        for (int nr = 0; nr < NR; ++nr)
-#pragma unroll
-            for (int mg = 0; mg < MG; ++mg)
-                store_quad(ep, mb + mg * 16, nb + nr * 16, acc[nr][mg]);
-        return;
-    }
-    constexpr int PART = RWG * MG * 16;  // floats per workgroup partial
-    v4f *part = reinterpret_cast<v4f *>(g.ws + ((size_t)t * g.split + z) * (size_t)PART);
+    // ---- the four waves' sums, added in wave order; wave w then owns blocks f = w, w+4, ...
 #pragma unroll
     for (int nr = 0; nr < NR; ++nr)
 #pragma unroll
         for (int mg = 0; mg < MG; ++mg)
-            part[((wave * NR + nr) * MG + mg) * 64 + lane] = acc[nr][mg];
+            s_red[wave][nr * MG + mg][lane] = acc[nr][mg];
+    __syncthreads();
+
+    Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec};
+    constexpr int FPW = (NF + 3) / 4;  // blocks per wave
+    v4f sum[FPW];
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) {
+        const int f = i * 4 + wave;
+        if (f < NF)
+            sum[i] = ((s_red[0][f][lane] + s_red[1][f][lane]) + s_red[2][f][lane]) + s_red[3][f][lane];
+    }
+    auto block_mn = [&](int f, int &m, int &n) {
+        const int nr = f / MG, mg = f - nr * MG;
+        m = mg * 16 + (lane & 15);
+        n = n0 + nr * 16 + 4 * (lane >> 4);
+    };
+    if (g.split == 1) {
+#pragma unroll
+        for (int i = 0; i < FPW; ++i) {
+            const int f = i * 4 + wave;
+            if (f < NF) {
+                int m, n;
+                block_mn(f, m, n);
+                store_quad(ep, m, n, sum[i]);
+            }
+        }
+        return;
+    }
+    // fp32 partials of this chunk: [tile][z][block][lane] float4s
+    constexpr uint32_t PART = NF * 64 * 16;  // bytes per workgroup partial
+    const auto rws = make_rsrc(g.ws + (size_t)t * g.split * (PART / 4), (uint32_t)(g.split * PART));
+#pragma unroll
+    for (int i = 0; i < FPW; ++i) {
+        const int f = i * 4 + wave;
+        if (f < NF)
+            store16_coherent(rws, z * PART + (uint32_t)((f * 64 + lane) * 16), sum[i]);
+    }
     if (!split_arrive_last(g.counters + t, g.split))
         return;
-    const v4f *base = reinterpret_cast<const v4f *>(g.ws + (size_t)t * g.split * (size_t)PART);
 #pragma unroll
-    for (int nr = 0; nr < NR; ++nr)
-#pragma unroll
-        for (int mg = 0; mg < MG; ++mg) {
-            const int idx = ((wave * NR + nr) * MG + mg) * 64 + lane;
-            v4f s = base[idx];
+    for (int i = 0; i < FPW; ++i) {
+        const int f = i * 4 + wave;
+        if (f < NF) {
+            const uint32_t idx = (uint32_t)((f * 64 + lane) * 16);
+            v4f tot = load16_coherent(rws, idx);
             for (int zz = 1; zz < g.split; ++zz)
-                s += base[(size_t)zz * (PART / 4) + idx];
-            store_quad(ep, mb + mg * 16, nb + nr * 16, s);
+                tot += load16_coherent(rws, zz * PART + idx);
+            int m, n;
+            block_mn(f, m, n);
+            store_quad(ep, m, n, tot);
         }
+    }
 }
 
 template <int MG, int NR, bool BPACK>
@@ -137,7 +172,7 @@ static void launch_skinny(const GemmArgs &g, int grid, hipStream_t s)
 }
 
 #define MX_SKINNY(MG, NR) \
-    {MG, NR, launch_skinny<MG, NR, false>, launch_skinny<MG, NR, true>, "skinny_m" #MG "x16_n" #NR "x64"}
+    {MG, NR, launch_skinny<MG, NR, false>, launch_skinny<MG, NR, true>, "skinny_m" #MG "x16_n" #NR "x16"}
 const SkinnyKernel *skinny_kernels(int *count)
 {
     static const SkinnyKernel table[] = {

@@ -1,5 +1,6 @@
-// Tiled MXFP4 GEMM kernel for gfx950: each 256-thread workgroup (4 wave64)
-// computes a BM x BN tile of D over one K chunk.
+// Tiled MXFP4 GEMM kernel for gfx950: each workgroup of 4 or 8 wave64s
+// (WM x WN waves, each owning a TM x TN sub-tile) computes a BM x BN tile of
+// D over one K chunk.
 //
 // Data movement per 256-K stage:
 //   - operand tiles go from HBM/L2 straight into LDS with 16-byte-per-lane
@@ -91,19 +92,21 @@ __device__ __forceinline__ uint32_t scale_word(const ScaleRows &s, int d5)
 }
 
 template <int BM, int BN, int WM, int WN, bool BPACK, bool SVEC>
-__global__ void __launch_bounds__(256) mx_tile_kernel(GemmArgs g)
+__global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
 {
+    constexpr int NW = WM * WN;                // waves per workgroup
+    constexpr int NT = 64 * NW;                // threads per workgroup
     constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
     constexpr int FM = TM / 16, FN = TN / 16;  // 16-row fragments per wave
-    static_assert(WM * WN == 4, "four waves");
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(FM % 2 == 0 && FN % 2 == 0, "scale words cover 32-row groups");
     constexpr int A_CH = BM / 8, B_CH = BN / 8;  // 1 KiB chunks per stage
-    static_assert(A_CH % 4 == 0 && B_CH % 4 == 0, "chunks split evenly over waves");
+    static_assert(A_CH % NW == 0 && B_CH % NW == 0, "chunks split evenly over waves");
     constexpr int A_STAGE = BM * 128, B_STAGE = BN * 128;    // bytes per stage
     constexpr int SA_W = BM / 32 * 64, SB_W = BN / 32 * 64;  // scale words per stage
     constexpr int SC_W = SA_W + SB_W + 64;                   // + a scratch row for idle threads
-    constexpr int SBP_PER_THREAD = (SB_W + 255) / 256;       // packed-scale words per thread
-    static_assert(BM / 2 + BN / 2 <= 256, "one scale row pair per thread");
+    constexpr int SBP_PER_THREAD = (SB_W + NT - 1) / NT;     // packed-scale words per thread
+    static_assert(BM / 2 + BN / 2 <= NT, "one scale row pair per thread");
 
     // The two halves of each double buffer are distinct LDS objects and every
     // access names one of them at compile time: the compiler can then tell
@@ -116,7 +119,8 @@ __global__ void __launch_bounds__(256) mx_tile_kernel(GemmArgs g)
     __shared__ uint32_t s_sc0[SC_W];  // [SA words | SB words | scratch]
     __shared__ uint32_t s_sc1[SC_W];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS/chunk math scalar
     const int wave_m = wave % WM, wave_n = wave / WM;
 
     // ---- which tile and K chunk
@@ -137,47 +141,63 @@ __global__ void __launch_bounds__(256) mx_tile_kernel(GemmArgs g)
     const int kb_end = min(g.KB, kb_begin + g.kb_per_split);
     const int nst = (kb_end - kb_begin + 7) >> 3;
 
-    // ---- buffer resources, rebased at the tile (offsets stay below 2^31)
+    // ---- operand sources, rebased at the tile (offsets stay below 2^31).
+    // Per stage the base advances by the stage's K offset and the range
+    // shrinks by the same amount, so a lane's offset inside a stage is its
+    // fixed lane part plus a wave-uniform chunk part.  A stage that must not
+    // load gets an empty range: every load returns zero without traffic.
     const int rows_a = min(BM, g.M - m0);
-    const auto ra = make_rsrc(g.A + (int64_t)m0 * g.lda_b, (uint32_t)(rows_a * g.lda_b));
+    const uint8_t *a_base = g.A + (int64_t)m0 * g.lda_b;
+    const uint32_t a_bytes = (uint32_t)(rows_a * g.lda_b);
+    const uint32_t a_lane = (uint32_t)((lane & 15) * g.lda_b + (lane >> 4) * 16);
     const auto rsa = make_rsrc(g.SA + (int64_t)m0 * g.ldsa, (uint32_t)(rows_a * g.ldsa));
-    __amdgpu_buffer_rsrc_t rb, rsb;
+    const uint8_t *b_base;
+    uint32_t b_bytes, b_lane, b_rg_stride;
+    __amdgpu_buffer_rsrc_t rsb;
     if constexpr (BPACK) {
         const int n16 = n0 / 16, grp16 = min(BN / 16, (g.N + 15) / 16 - n16);
-        rb = make_rsrc(g.B + (int64_t)n16 * g.ks_total * 1024, (uint32_t)(grp16 * g.ks_total * 1024));
+        b_base = g.B + (int64_t)n16 * g.ks_total * 1024;
+        b_bytes = (uint32_t)(grp16 * g.ks_total * 1024);
+        b_lane = (uint32_t)(lane * 16);
+        b_rg_stride = (uint32_t)(g.ks_total * 1024);
         const int n32 = n0 / 32, grp32 = min(BN / 32, (g.N + 31) / 32 - n32);
         rsb = make_rsrc(g.SB + (int64_t)n32 * g.sn8 * 256, (uint32_t)(grp32 * g.sn8 * 256));
     } else {
         const int rows_b = min(BN, g.N - n0);
-        rb = make_rsrc(g.B + (int64_t)n0 * g.ldb_b, (uint32_t)(rows_b * g.ldb_b));
+        b_base = g.B + (int64_t)n0 * g.ldb_b;
+        b_bytes = (uint32_t)(rows_b * g.ldb_b);
+        b_lane = (uint32_t)((lane & 15) * g.ldb_b + (lane >> 4) * 16);
+        b_rg_stride = (uint32_t)(16 * g.ldb_b);
         rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)(rows_b * g.ldsb));
     }
 
-    // ---- stage loaders; `on` false makes every load out of range (no traffic)
+    // ---- stage loaders
     auto issue_operands = [&](int kt, bool on, auto bufc) {
         constexpr int BUF = decltype(bufc)::value;
         uint8_t *dst_a = BUF ? s_a1 : s_a0;
         uint8_t *dst_b = BUF ? s_b1 : s_b0;
         const int kb_s = kb_begin + kt * 8;
+        // K offset of the stage: bytes along a row (row-major) or 1 KiB steps (packed)
+        const uint32_t a_k = (uint32_t)kb_s * 16;
+        const uint32_t b_k = BPACK ? (uint32_t)(kb_s >> 2) * 1024 : (uint32_t)kb_s * 16;
+        const auto ra = make_rsrc(a_base + a_k, on ? a_bytes - a_k : 0u);
+        const auto rb = make_rsrc(b_base + b_k, on ? b_bytes - b_k : 0u);
 #pragma unroll
-        for (int i = 0; i < A_CH / 4; ++i) {
-            const int c = i * 4 + wave;
+        for (int i = 0; i < A_CH / NW; ++i) {
+            const int c = i * NW + wave;
             const int rg = c >> 1, ks = c & 1;
-            const int kb = kb_s + ks * 4 + (lane >> 4);
-            const int row = rg * 16 + (lane & 15);
-            const uint32_t off = on && kb < kb_end ? (uint32_t)(row * g.lda_b + kb * 16) : kOOB;
+            uint32_t off = a_lane + (uint32_t)(rg * 16 * g.lda_b + ks * 64);
+            if constexpr (!SVEC)  // K tail: blocks at or past the chunk end read as zero
+                off = kb_s + ks * 4 + (lane >> 4) < kb_end ? off : kOOB;
             load16_to_lds(ra, (lds_void *)(dst_a + c * 1024), off);
         }
 #pragma unroll
-        for (int i = 0; i < B_CH / 4; ++i) {
-            const int c = i * 4 + wave;
+        for (int i = 0; i < B_CH / NW; ++i) {
+            const int c = i * NW + wave;
             const int rg = c >> 1, ks = c & 1;
-            const int kb = kb_s + ks * 4 + (lane >> 4);
-            uint32_t off;
-            if constexpr (BPACK)
-                off = on && kb < kb_end ? (uint32_t)(((rg * g.ks_total + (kb_s >> 2) + ks) * 64 + lane) * 16) : kOOB;
-            else
-                off = on && kb < kb_end ? (uint32_t)((rg * 16 + (lane & 15)) * g.ldb_b + kb * 16) : kOOB;
+            uint32_t off = b_lane + (uint32_t)rg * b_rg_stride + (uint32_t)(ks * (BPACK ? 1024 : 64));
+            if constexpr (!SVEC)
+                off = kb_s + ks * 4 + (lane >> 4) < kb_end ? off : kOOB;
             load16_to_lds(rb, (lds_void *)(dst_b + c * 1024), off);
         }
     };
@@ -200,7 +220,7 @@ __global__ void __launch_bounds__(256) mx_tile_kernel(GemmArgs g)
         if constexpr (BPACK) {
 #pragma unroll
             for (int i = 0; i < SBP_PER_THREAD; ++i) {
-                const int q = i * 256 + tid;
+                const int q = i * NT + tid;
                 const uint32_t off = on && q < SB_W
                                          ? (uint32_t)((((q >> 6) * g.sn8 + (kb_s >> 3)) * 64 + (q & 63)) * 4)
                                          : kOOB;
@@ -219,7 +239,7 @@ __global__ void __launch_bounds__(256) mx_tile_kernel(GemmArgs g)
         if constexpr (BPACK) {
 #pragma unroll
             for (int i = 0; i < SBP_PER_THREAD; ++i) {
-                const int q = i * 256 + tid;
+                const int q = i * NT + tid;
                 dsc[q < SB_W ? SA_W + q : SA_W + SB_W + lane] = sbp[i];
             }
         } else {
@@ -230,20 +250,20 @@ __global__ void __launch_bounds__(256) mx_tile_kernel(GemmArgs g)
     };
 
     // ---- main loop
+    // Accumulators get their first value from the first stage's matrix
+    // instructions (zero accumulator input), never from a register move, so
+    // the register allocator keeps them in the accumulation registers across
+    // the loop.
     v4f acc[FN][FM];
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-            acc[fn][fm] = v4f{0.f, 0.f, 0.f, 0.f};
 
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
 
     // One stage, one basic block: prefetch stage kt+1 into the other buffer,
     // multiply stage kt, then wait for the prefetch and publish its scales.
-    auto stage = [&](int kt, auto bufc) {
+    auto stage = [&](int kt, auto bufc, auto firstc) {
         constexpr int BUF = decltype(bufc)::value;
+        constexpr bool FIRST = decltype(firstc)::value;
         using Next = std::integral_constant<int, BUF ^ 1>;
         const bool more = kt + 1 < nst;
         issue_operands(kt + 1, more, Next{});
@@ -270,7 +290,8 @@ __global__ void __launch_bounds__(256) mx_tile_kernel(GemmArgs g)
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm)
                     acc[fn][fm] = mma_sel(ks * 2 + (fn & 1), ks * 2 + (fm & 1), bf, af[fm],
-                                          acc[fn][fm], (int)sbw[fn >> 1], (int)saw[fm >> 1]);
+                                          FIRST && ks == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : acc[fn][fm],
+                                          (int)sbw[fn >> 1], (int)saw[fm >> 1]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -284,11 +305,19 @@ __global__ void __launch_bounds__(256) mx_tile_kernel(GemmArgs g)
     wait_vmem();
     commit_scales(B0{});
     __syncthreads();
-    for (int kt = 0; kt < nst; kt += 2) {
-        stage(kt, B0{});
-        if (kt + 1 < nst)
-            stage(kt + 1, B1{});
+    // Stage 0 is peeled (it initialises the accumulators); then pairs of
+    // stages keep the buffer choice static, and an odd last stage is peeled
+    // so that the loop body has no branch (no join over the accumulators).
+    using First = std::true_type;
+    using Rest = std::false_type;
+    stage(0, B0{}, First{});
+    int kt = 1;
+    for (; kt + 2 <= nst; kt += 2) {
+        stage(kt, B1{}, Rest{});
+        stage(kt + 1, B0{}, Rest{});
     }
+    if (kt < nst)
+        stage(kt, B1{}, Rest{});
 
     // ---- epilogue
     Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec};
@@ -302,24 +331,26 @@ __global__ void __launch_bounds__(256) mx_tile_kernel(GemmArgs g)
                 store_quad(ep, mb + fm * 16, nb + fn * 16, acc[fn][fm]);
         return;
     }
-    v4f *part = reinterpret_cast<v4f *>(g.ws + ((size_t)t * g.split + z) * (size_t)(BM * BN));
+    // fp32 partial tile of this K chunk: [tile][z][wave][fn][fm][lane] float4s
+    constexpr uint32_t PART = BM * BN * 4;  // bytes per partial tile
+    const auto rws = make_rsrc(g.ws + (size_t)t * g.split * (BM * BN), (uint32_t)(g.split * PART));
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
-            part[((wave * FN + fn) * FM + fm) * 64 + lane] = acc[fn][fm];
+            store16_coherent(rws, z * PART + (uint32_t)((((wave * FN + fn) * FM + fm) * 64 + lane) * 16),
+                             acc[fn][fm]);
     if (!split_arrive_last(g.counters + t, g.split))
         return;
-    const v4f *base = reinterpret_cast<const v4f *>(g.ws + (size_t)t * g.split * (size_t)(BM * BN));
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            const int idx = ((wave * FN + fn) * FM + fm) * 64 + lane;
-            v4f s = base[idx];
+            const uint32_t idx = (uint32_t)((((wave * FN + fn) * FM + fm) * 64 + lane) * 16);
+            v4f sum = load16_coherent(rws, idx);
             for (int zz = 1; zz < g.split; ++zz)
-                s += base[(size_t)zz * (BM * BN / 4) + idx];
-            store_quad(ep, mb + fm * 16, nb + fn * 16, s);
+                sum += load16_coherent(rws, zz * PART + idx);
+            store_quad(ep, mb + fm * 16, nb + fn * 16, sum);
         }
 }
 
@@ -327,15 +358,15 @@ template <int BM, int BN, int WM, int WN, bool BPACK>
 static void launch_tile(const GemmArgs &g, int grid, hipStream_t s)
 {
     if (g.sa_fast && (BPACK || g.sb_fast))
-        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, true>), dim3(grid), dim3(256), 0, s, g);
+            hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, true>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
     else
-        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, false>), dim3(grid), dim3(256), 0, s, g);
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, false>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
 }
 
 const TileKernel *tile_kernels(int *count)
 {
     static const TileKernel table[] = {
-        {256, 256, 1, launch_tile<256, 256, 2, 2, false>, launch_tile<256, 256, 2, 2, true>, "tile_256x256"},
+        {256, 256, 1, launch_tile<256, 256, 2, 4, false>, launch_tile<256, 256, 2, 4, true>, "tile_256x256"},
         {256, 128, 1, launch_tile<256, 128, 2, 2, false>, launch_tile<256, 128, 2, 2, true>, "tile_256x128"},
         {128, 128, 2, launch_tile<128, 128, 2, 2, false>, launch_tile<128, 128, 2, 2, true>, "tile_128x128"},
         {64, 64, 4, launch_tile<64, 64, 2, 2, false>, launch_tile<64, 64, 2, 2, true>, "tile_64x64"},

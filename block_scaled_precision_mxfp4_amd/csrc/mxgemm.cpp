@@ -83,46 +83,58 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
     const mx::TileKernel *tile = mx::tile_kernels(&n_tile);
     const mx::SkinnyKernel *skinny = mx::skinny_kernels(&n_skinny);
     if (M <= 64) {
+        // Skinny kernel: a workgroup owns 16*nr rows of B and one K chunk.
+        // nr grows with M so that A (re-read from L2 per row block) stays
+        // below the B bytes streamed from HBM.  The split is the smallest
+        // that gives about four workgroups per CU (enough bytes in flight),
+        // keeping at least two 128-K steps per wave.
         const int mg = cdiv(M, 16);
-        const int nr = mg >= 3 ? 4 : (mg == 2 ? 2 : 1);
+        int nr = mg == 1 ? 1 : 2;
+        if (const char *e = std::getenv("MXGEMM_FORCE_NR"))
+            nr = std::atoi(e) >= 4 ? 4 : (std::atoi(e) >= 2 ? 2 : 1);
         const int nri = nr == 1 ? 0 : (nr == 2 ? 1 : 2);
-        const int rows_wg = 64 * nr;
+        const int rows_wg = 16 * nr;
         const int tiles = cdiv(N, rows_wg);
+        int chosen = -1;
         for (int s : kSplits) {
             if (!consider_split(s))
                 continue;
             auto [per, eff] = split_chunks(KB, s);
-            if (split_req <= 0 && s > 1 && eff < s)
-                continue;  // heuristic: never pick a split that collapses
-            const int64_t wgs = (int64_t)tiles * eff;
-            // HBM-bound: time ~ bytes / rate, but a launch needs enough
-            // workgroups in flight to reach the rate (about 4 per CU)
-            const double bytes = (double)N * K / 2 * 1.0625 + (double)M * N * 2;
-            const double fill = std::min(1.0, (double)wgs / (4.0 * num_cu));
-            double t = bytes / (kHbm * fill);
-            if (eff > 1)
-                t += (double)tiles * eff * rows_wg * mg * 16 * 4 * 2 / kHbm + 1e-6;
-            if (t < best_t * 0.97 || (split_req > 0)) {
-                best_t = t;
-                best.family = 1;
-                best.index = (mg - 1) * 3 + nri;
-                best.bm = mg * 16;
-                best.bn = rows_wg;
-                best.split = eff;
-                best.kb_per_split = per;
-                best.tiles_m = 1;
-                best.tiles_n = tiles;
-                best.grid = wgs;
-                best.name = skinny[best.index].name;
+            if (split_req <= 0) {
+                if (s > 1 && (eff < s || per < 32))
+                    break;  // chunks would collapse or leave waves idle
+                chosen = s;
+                if ((int64_t)tiles * eff >= 4LL * num_cu)
+                    break;
+            } else {
+                chosen = s;
             }
         }
+        if (chosen < 0)
+            chosen = 1;
+        auto [per, eff] = split_chunks(KB, chosen);
+        best.family = 1;
+        best.index = (mg - 1) * 3 + nri;
+        best.bm = mg * 16;
+        best.bn = rows_wg;
+        best.split = eff;
+        best.kb_per_split = per;
+        best.tiles_m = 1;
+        best.tiles_n = tiles;
+        best.grid = (int64_t)tiles * eff;
+        best.name = skinny[best.index].name;
         const size_t part = (size_t)rows_wg * mg * 16 * 4;
-        best.counter_bytes = best.split > 1 ? align_up((size_t)tiles * 4, 256) : 0;
-        best.ws_bytes = best.split > 1 ? best.counter_bytes + (size_t)tiles * best.split * part : 0;
+        best.counter_bytes = best.split > 1 ? (size_t)tiles * 4 : 0;
+        best.ws_bytes = best.split > 1 ? (size_t)tiles * best.split * part : 0;
         return best;
     }
 
+    int force_tile = -1;
+    if (const char *e = std::getenv("MXGEMM_FORCE_TILE"))
+        force_tile = std::atoi(e);
     for (int k = 0; k < n_tile; ++k) {
+        if (force_tile >= 0 && force_tile < n_tile && k != force_tile)
+            continue;
         const mx::TileKernel &tk = tile[k];
         const int tm = cdiv(M, tk.bm), tn = cdiv(N, tk.bn);
         const int64_t tiles = (int64_t)tm * tn;
@@ -158,8 +170,8 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
         }
     }
     const int64_t tiles = (int64_t)best.tiles_m * best.tiles_n;
-    best.counter_bytes = best.split > 1 ? align_up((size_t)tiles * 4, 256) : 0;
-    best.ws_bytes = best.split > 1 ? best.counter_bytes + (size_t)tiles * best.split * best.bm * best.bn * 4 : 0;
+    best.counter_bytes = best.split > 1 ? (size_t)tiles * 4 : 0;
+    best.ws_bytes = best.split > 1 ? (size_t)tiles * best.split * best.bm * best.bn * 4 : 0;
     return best;
 }
 
@@ -199,41 +211,66 @@ mxgemm_status device_info(DeviceInfo **out)
     return d.gfx950 ? MXGEMM_OK : MXGEMM_ERR_UNSUPPORTED_DEVICE;
 }
 
-// ---- library-owned split-K workspaces, one per (device, stream)
+// ---- library-owned split-K buffers, one set per (device, stream)
+//
+// Arrival counters live in a buffer of their own that only ever holds
+// counters: it is zeroed when allocated and every kernel that increments a
+// counter returns it to zero, so it is all zeros between calls whatever the
+// previous plan was.  Partial sums live in a separate buffer (or in the
+// caller's workspace), so stale partials can never be mistaken for counts.
 
-struct Workspace {
+struct DeviceBuffer {
     void *ptr = nullptr;
     size_t bytes = 0;
 };
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+struct StreamBuffers {
+    DeviceBuffer partials, counters;
+};
+std::map<std::pair<int, hipStream_t>, StreamBuffers> g_ws;
 
-mxgemm_status get_workspace(hipStream_t stream, size_t need, void **out)
+mxgemm_status grow(DeviceBuffer &b, size_t need, hipStream_t stream, bool zero)
+{
+    if (b.bytes >= need)
+        return MXGEMM_OK;
+    if (b.ptr) {
+        // earlier work on this stream may still use the old buffer
+        if (hipStreamSynchronize(stream) != hipSuccess || hipFree(b.ptr) != hipSuccess)
+            return MXGEMM_ERR_HIP;
+        b.ptr = nullptr;
+        b.bytes = 0;
+    }
+    const size_t sz = align_up(need, (size_t)1 << 16);
+    void *p = nullptr;
+    if (hipMalloc(&p, sz) != hipSuccess)
+        return MXGEMM_ERR_HIP;
+    if (zero && hipMemset(p, 0, sz) != hipSuccess) {
+        (void)hipFree(p);
+        return MXGEMM_ERR_HIP;
+    }
+    b.ptr = p;
+    b.bytes = sz;
+    return MXGEMM_OK;
+}
+
+// Counters (always library-owned) and, when part_need > 0, partials.
+mxgemm_status get_split_buffers(hipStream_t stream, size_t counter_need, size_t part_need, void **counters,
+                                void **partials)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return MXGEMM_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_mutex);
-    Workspace &w = g_ws[{dev, stream}];
-    if (w.bytes < need) {
-        if (w.ptr) {
-            if (hipStreamSynchronize(stream) != hipSuccess || hipFree(w.ptr) != hipSuccess)
-                return MXGEMM_ERR_HIP;
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
-        size_t sz = align_up(need, (size_t)1 << 20);
-        void *p = nullptr;
-        if (hipMalloc(&p, sz) != hipSuccess)
-            return MXGEMM_ERR_HIP;
-        // arrival counters must start at zero; the kernels leave them zero
-        if (hipMemset(p, 0, sz) != hipSuccess) {
-            (void)hipFree(p);
-            return MXGEMM_ERR_HIP;
-        }
-        w.ptr = p;
-        w.bytes = sz;
+    StreamBuffers &w = g_ws[{dev, stream}];
+    mxgemm_status st = grow(w.counters, counter_need, stream, true);
+    if (st != MXGEMM_OK)
+        return st;
+    *counters = w.counters.ptr;
+    if (part_need > 0) {
+        st = grow(w.partials, part_need, stream, false);
+        if (st != MXGEMM_OK)
+            return st;
+        *partials = w.partials.ptr;
     }
-    *out = w.ptr;
     return MXGEMM_OK;
 }
 
@@ -390,18 +427,14 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     g.group_m = 4;
 
     if (p.split > 1) {
-        void *ws = nullptr;
-        if (s.workspace) {
-            if (s.workspace_bytes < p.ws_bytes)
-                return MXGEMM_ERR_WORKSPACE;
-            ws = s.workspace;
-        } else {
-            st = get_workspace(stream, p.ws_bytes, &ws);
-            if (st != MXGEMM_OK)
-                return st;
-        }
-        g.counters = (int *)ws;
-        g.ws = (float *)((char *)ws + p.counter_bytes);
+        void *counters = nullptr, *partials = nullptr;
+        if (s.workspace && s.workspace_bytes < p.ws_bytes)
+            return MXGEMM_ERR_WORKSPACE;
+        st = get_split_buffers(stream, p.counter_bytes, s.workspace ? 0 : p.ws_bytes, &counters, &partials);
+        if (st != MXGEMM_OK)
+            return st;
+        g.counters = (int *)counters;
+        g.ws = (float *)(s.workspace ? s.workspace : partials);
     }
 
     if (p.grid > 0x7FFFFFFF)
@@ -447,16 +480,16 @@ mxgemm_status mxgemm_release_workspaces(void)
 {
     std::lock_guard<std::mutex> lock(g_mutex);
     mxgemm_status st = MXGEMM_OK;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
     for (auto &kv : g_ws) {
-        if (kv.second.ptr) {
-            int cur = 0;
-            (void)hipGetDevice(&cur);
-            if (hipSetDevice(kv.first.first) != hipSuccess || hipStreamSynchronize(kv.first.second) != hipSuccess ||
-                hipFree(kv.second.ptr) != hipSuccess)
+        if (hipSetDevice(kv.first.first) != hipSuccess || hipStreamSynchronize(kv.first.second) != hipSuccess)
+            st = MXGEMM_ERR_HIP;
+        for (DeviceBuffer *b : {&kv.second.partials, &kv.second.counters})
+            if (b->ptr && hipFree(b->ptr) != hipSuccess)
                 st = MXGEMM_ERR_HIP;
-            (void)hipSetDevice(cur);
-        }
     }
+    (void)hipSetDevice(cur);
     g_ws.clear();
     return st;
 }

@@ -105,12 +105,16 @@ typedef struct mxgemm_strides {
  * byte pitches) multiples of 16.  Scales, C and D need only natural
  * alignment (C and D: 2 bytes).
  *
- * Split-K (split_k > 1, chosen or forced) needs a workspace of
- * mxgemm_query(...).workspace_bytes.  With strides->workspace == NULL the
- * library allocates one per (device, stream) on first use and keeps it
- * until mxgemm_release_workspaces(); the first call with a new (device,
- * stream, size) therefore allocates.  A caller workspace must be at least
- * that size and must not be used by two calls that can run concurrently.
+ * Split-K (split_k > 1, chosen or forced) keeps fp32 partial sums in a
+ * workspace of mxgemm_query(...).workspace_bytes.  With strides->workspace
+ * == NULL the library allocates one per (device, stream) on first use and
+ * keeps it until mxgemm_release_workspaces(); a caller workspace must be at
+ * least that size and must not be used by two calls that can run
+ * concurrently.  The per-tile arrival counters of split-K are always
+ * library-owned: one zeroed buffer per (device, stream), allocated on first
+ * use and returned to all-zero by every call.  The first call with a new
+ * (device, stream) or a larger need therefore allocates; calls on one
+ * stream are ordered, calls on different streams use separate buffers.
  */
 mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B,
                          const void *scaleA, const void *scaleB,
@@ -152,7 +156,7 @@ typedef struct mxgemm_info {
     int32_t tile_m, tile_n;  /* output tile per workgroup */
     int32_t split_k;         /* K chunks the plan uses */
     int64_t grid;            /* workgroups launched */
-    size_t workspace_bytes;  /* split-K workspace needed (0 if split_k == 1) */
+    size_t workspace_bytes;  /* split-K fp32 partials workspace needed (0 if split_k == 1) */
     size_t packed_b_bytes;   /* size of mxgemm_pack_b's Bp for this N, K */
     size_t packed_sb_bytes;  /* size of mxgemm_pack_b's SBp for this N, K */
     int32_t num_cu;          /* compute units the plan assumed */

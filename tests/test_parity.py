@@ -95,6 +95,20 @@ def test_packed_b_matches_plain_b(shape):
     assert_parity(d_packed, ref, mag, "packed")
 
 
+def test_split_counters_survive_plan_changes():
+    """Split-K calls with different tile counts on one stream, back to back:
+    a call's partial sums must never be taken for another call's arrival
+    counters (regression: they once shared one buffer)."""
+    seq = [(63, 100, 4128, 8), (64, 4096, 2048, 2), (1, 64, 8192, 16), (700, 900, 2048, 4),
+           (64, 4096, 2048, 2), (300, 520, 4096, 16), (1, 8192, 4096, 4)]
+    for M, N, K, s in seq:
+        p = inputs.make_problem(M, N, K, seed=0xC0C0 + M + N, beta=1.0, c_sigma=1.0)
+        say("case counters", (M, N, K), "split", s)
+        d = gemm_gpu(p, split_k=s)
+        ref, mag, _ = oracle_ref(p)
+        assert_parity(d, ref, mag, "sequence %s" % ((M, N, K, s),))
+
+
 EDGE_SHAPES = [
     (1, 1, 32), (1, 17, 96), (2, 5, 64), (15, 31, 160), (16, 16, 128), (17, 33, 288),
     (63, 100, 4128), (64, 4096, 2048), (65, 257, 544), (127, 129, 1056), (129, 130, 288),
