@@ -41,6 +41,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed counter runs (profiles/traffic.json),
+    or None when the kernels have changed since those counters were taken."""
+    from block_scaled_precision_mxfp4_amd.kernel_hash import kernel_source_hash
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    w = t.get("workloads", {}).get(workload)
+    return None if w is None else w["traffic_bytes"]
+
+
 def algorithmic_bytes(M, N, K, beta):
     b = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + 2 * M * N
     if beta != 0.0:
@@ -48,7 +64,7 @@ def algorithmic_bytes(M, N, K, beta):
     return b
 
 
-def time_workload(name, steps, warmup, split_k=-1, rotate=True):
+def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False):
     import numpy as np
     import torch
 
@@ -100,7 +116,11 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True):
 
     timing = "hipgraph"
     graph = None
+    if eager:
+        timing = "eager"
     try:
+        if eager:
+            raise RuntimeError("eager launches requested")
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             for i in range(steps):
@@ -188,6 +208,9 @@ def main():
     ap.add_argument("--split-k", type=int, default=-1)
     ap.add_argument("--only", action="store_true", help="time only --workload (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch steps one by one (counter runs)")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES, 5 times (counter scaling)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -205,22 +228,33 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.calib_copy:
+        src = torch.randint(0, 255, (args.calib_copy,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": args.calib_copy, "copies": 5}), flush=True)
+        return
     mx.lib()
 
-    head = time_workload(args.workload, args.steps, args.warmup, split_k=args.split_k)
+    head = time_workload(args.workload, args.steps, args.warmup, split_k=args.split_k, eager=args.eager)
     others = []
     if not args.only:
         for name in inputs.WORKLOADS:
             if name != args.workload:
-                others.append(time_workload(name, args.steps, args.warmup))
+                others.append(time_workload(name, args.steps, args.warmup, eager=args.eager))
     gemv = next((o for o in [head] + others if o["M"] == 1), None)
 
     m1 = None
     if gemv is not None:
         m1 = {"workload": gemv["workload"], "value": gemv["gbs"], "unit": "GB/s",
               "us_per_step": gemv["us_per_step"], "split_k": gemv["split_k"],
+              "algorithmic_bytes": gemv["algorithmic_bytes"],
               "roofline": {"bound": "hbm", "achieved": gemv["gbs"], "peak": PEAK_HBM_GBS,
-                           "unit": "GB/s", "frac": gemv["gbs"] / PEAK_HBM_GBS, "traffic": None}}
+                           "unit": "GB/s", "frac": gemv["gbs"] / PEAK_HBM_GBS,
+                           "traffic": measured_traffic(gemv["workload"])}}
 
     base = None
     if not args.no_cpu_baseline:
@@ -231,11 +265,13 @@ def main():
     if hbm_bound:
         value, unit = head["gbs"], "GB/s"
         roof = {"bound": "hbm", "achieved": head["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": head["gbs"] / PEAK_HBM_GBS, "traffic": None}
+                "frac": head["gbs"] / PEAK_HBM_GBS, "traffic": measured_traffic(head["workload"])}
     else:
         value, unit = head["tflops"], "TFLOP/s"
         roof = {"bound": "mfma", "achieved": head["tflops"], "peak": PEAK_MXFP4_TFLOPS,
-                "unit": "TFLOP/s", "frac": head["tflops"] / PEAK_MXFP4_TFLOPS, "traffic": None}
+                "unit": "TFLOP/s", "frac": head["tflops"] / PEAK_MXFP4_TFLOPS,
+                "traffic": measured_traffic(head["workload"]),
+                "algorithmic_bytes": head["algorithmic_bytes"]}
     vs = value / PAGE_TFLOPS_8192 if head["workload"] == "square_8192" and unit == "TFLOP/s" else None
     line = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
