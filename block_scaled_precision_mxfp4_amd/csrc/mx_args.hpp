@@ -28,7 +28,8 @@ struct GemmArgs {
     int tiles_m, tiles_n; // output tiles per dimension
     int ks_total;         // packed B: 128-K steps per 16-row group, ceil(KB/4)
     int sn8;              // packed scales: (KB rounded up to 8) / 8
-    int sa_fast, sb_fast; // scale rows allow aligned 8-byte loads
+    int sa_fast, sb_fast; // scale rows allow aligned 8-byte loads (tiled kernel)
+    int scale16;          // both scale operands allow aligned 16-byte row groups (skinny kernel)
     int d_vec, c_vec;     // 8-byte D stores / C loads allowed
     int group_m;          // tile-order grouping along M
 };
@@ -39,9 +40,14 @@ typedef void (*LaunchFn)(const GemmArgs &, int grid, hipStream_t);
 struct TileKernel {
     int bm, bn;
     int occupancy;        // workgroups per CU the kernel's LDS allows
-    LaunchFn plain, packed;
+    LaunchFn plain, packed;            // two-stage kernel: any strides
+    LaunchFn deep_plain, deep_packed;  // four-slot ring: dword-aligned scale rows, K % 128 == 0
+    bool prefer_deep;                  // the ring kernel is the faster one for this tile
     const char *name;
 };
+
+template <int BM, int BN, int WM, int WN, bool BPACK>
+void launch_tile_deep(const GemmArgs &g, int grid, hipStream_t s);
 // Host-side table of the tiled kernels, in the planner's preference order.
 const TileKernel *tile_kernels(int *count);
 

@@ -84,6 +84,22 @@ __device__ __forceinline__ v4f mfma_fp4(v4i bfrag, v4i afrag, v4f acc, int sb, i
                                                            OPSEL_B, sb, OPSEL_A, sa);
 }
 
+// op_sel must be an immediate: select among the 16 (B byte, A byte) forms.
+// With fully unrolled loops the selector is a constant and the switch folds.
+__device__ __forceinline__ v4f mma_sel(int ob, int oa, v4i b, v4i a, v4f c, int sb, int sa)
+{
+#define MX_CASE(OB, OA) \
+    case OB * 4 + OA: return mfma_fp4<OB, OA>(b, a, c, sb, sa);
+    switch (ob * 4 + oa) {
+        MX_CASE(0, 0) MX_CASE(0, 1) MX_CASE(0, 2) MX_CASE(0, 3)
+        MX_CASE(1, 0) MX_CASE(1, 1) MX_CASE(1, 2) MX_CASE(1, 3)
+        MX_CASE(2, 0) MX_CASE(2, 1) MX_CASE(2, 2) MX_CASE(2, 3)
+        MX_CASE(3, 0) MX_CASE(3, 1) MX_CASE(3, 2) MX_CASE(3, 3)
+    }
+#undef MX_CASE
+    return c;
+}
+
 // fp32 -> bf16, round to nearest, ties to even; NaN stays NaN (quiet).
 __device__ __forceinline__ uint32_t bf16_rne(float f)
 {

@@ -19,12 +19,42 @@
 
 namespace mx {
 
-template <int MG, int NR, bool BPACK>
+// Scale bytes of 4 consecutive 128-K steps for one lane, packed into one
+// register: byte u is the scale of step u, so op_sel = u picks it.  The lane's
+// K-block within a step is lane/16; a row's 16 scale bytes for the 4 steps
+// are contiguous.  SVEC: one aligned 16-byte load per row (pitch and K-block
+// count multiples of 16, so a group is entirely inside or outside the chunk);
+// otherwise byte loads, blocks at or past kb_end reading as zero.
+template <bool SVEC>
+__device__ __forceinline__ uint32_t load_scale_group(__amdgpu_buffer_rsrc_t r, int64_t ld, int row, int kb0,
+                                                     int kb_end, int lane)
+{
+    const int j = lane >> 4;
+    if constexpr (SVEC) {
+        const v4i w = load16(r, kb0 < kb_end ? (uint32_t)(row * ld + kb0) : kOOB);
+        uint32_t out = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            out |= (((uint32_t)w[u] >> (8 * j)) & 0xFFu) << (8 * u);
+        return out;
+    } else {
+        uint32_t out = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int kb = kb0 + 4 * u + j;
+            out |= load1(r, kb < kb_end ? (uint32_t)(row * ld + kb) : kOOB) << (8 * u);
+        }
+        return out;
+    }
+}
+
+template <int MG, int NR, bool BPACK, bool SVEC>
 __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
 {
-    constexpr int R = 16 * NR;   // B rows per workgroup
-    constexpr int U = 4;         // 128-K steps loaded per batch
-    constexpr int NF = NR * MG;  // 16x16 result blocks per workgroup
+    constexpr int R = 16 * NR;                      // B rows per workgroup
+    constexpr int NF = NR * MG;                     // 16x16 result blocks per workgroup
+    constexpr int U = (NR + MG) <= 3 ? 8 : 4;       // 128-K steps per batch (two batches in flight)
+    constexpr int G = U / 4;                        // scale groups (4 steps) per batch
     __shared__ v4f s_red[4][NF][64];
 
     const int lane = threadIdx.x & 63;
@@ -35,12 +65,14 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
     const int t = lg - z * g.tiles_n;
     const int n0 = t * R;  // first row of B (column of D) of this workgroup
 
+    // K range: chunks are multiples of 16 K-blocks, wave ranges multiples of 4 steps
     const int kb_begin = z * g.kb_per_split;
     const int kb_end = min(g.KB, kb_begin + g.kb_per_split);
     const int ks_begin = kb_begin >> 2, ks_end = (kb_end + 3) >> 2;
-    const int q = (ks_end - ks_begin + 3) >> 2;  // k-steps per wave
+    const int q = (((ks_end - ks_begin + 3) >> 2) + 3) & ~3;  // steps per wave
     const int w_begin = ks_begin + wave * q;
     const int w_end = min(ks_end, w_begin + q);
+    const int kb_wend = min(kb_end, w_end * 4);  // K-blocks this wave may touch
 
     const auto ra = make_rsrc(g.A, (uint32_t)(g.M * g.lda_b));
     const auto rsa = make_rsrc(g.SA, (uint32_t)(g.M * g.ldsa));
@@ -59,6 +91,56 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
         rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)(rows * g.ldsb));
     }
 
+    struct Batch {
+        v4i b[U][NR], a[U][MG];
+        uint32_t sb[BPACK ? U / 2 : G][NR];  // packed: one word per step pair, else per group
+        uint32_t sa[G][MG];
+    };
+
+    auto load_batch = [&](int ks0, Batch &bt) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int ks = ks0 + u;
+            const int kb = ks * 4 + (lane >> 4);
+            const bool ok = kb < kb_wend;
+#pragma unroll
+            for (int nr = 0; nr < NR; ++nr) {
+                if constexpr (BPACK)
+                    bt.b[u][nr] = load16(rb, ok ? (uint32_t)(((nr * g.ks_total + ks) * 64 + lane) * 16) : kOOB);
+                else
+                    bt.b[u][nr] = load16(rb, ok ? (uint32_t)((nr * 16 + (lane & 15)) * g.ldb_b + kb * 16) : kOOB);
+            }
+#pragma unroll
+            for (int mg = 0; mg < MG; ++mg)
+                bt.a[u][mg] = load16(ra, ok ? (uint32_t)((mg * 16 + (lane & 15)) * g.lda_b + kb * 16) : kOOB);
+        }
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+            const int kb0 = (ks0 + 4 * gi) * 4;  // first K-block of the group
+#pragma unroll
+            for (int mg = 0; mg < MG; ++mg)
+                bt.sa[gi][mg] = load_scale_group<SVEC>(rsa, g.ldsa, mg * 16 + (lane & 15), kb0, kb_wend, lane);
+            if constexpr (!BPACK) {
+#pragma unroll
+                for (int nr = 0; nr < NR; ++nr)
+                    bt.sb[gi][nr] = load_scale_group<SVEC>(rsb, g.ldsb, nr * 16 + (lane & 15), kb0, kb_wend, lane);
+            }
+        }
+        if constexpr (BPACK) {
+#pragma unroll
+            for (int p = 0; p < U / 2; ++p) {
+                const int ks = ks0 + 2 * p;  // even: the word holds steps ks, ks+1 x both row halves
+#pragma unroll
+                for (int nr = 0; nr < NR; ++nr) {
+                    const int grp = (half0 + nr) >> 1, half = (half0 + nr) & 1;
+                    const uint32_t w =
+                        load4(rsb, ks * 4 < kb_wend ? (uint32_t)(((grp * g.sn8 + (ks >> 1)) * 64 + lane) * 4) : kOOB);
+                    bt.sb[p][nr] = w >> (8 * half);  // this row half's bytes at 0 and 2
+                }
+            }
+        }
+    };
+
     v4f acc[NR][MG];
 #pragma unroll
     for (int nr = 0; nr < NR; ++nr)
@@ -66,43 +148,28 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
         for (int mg = 0; mg < MG; ++mg)
             acc[nr][mg] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int ks0 = w_begin; ks0 < w_end; ks0 += U) {
-        v4i bfr[U][NR], afr[U][MG];
-        uint32_t sbv[U][NR], sav[U][MG];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int ks = ks0 + u;
-            const int kb = ks * 4 + (lane >> 4);
-            const bool ok = ks < w_end && kb < kb_end;
-#pragma unroll
-            for (int nr = 0; nr < NR; ++nr) {
-                if constexpr (BPACK) {
-                    bfr[u][nr] = load16(rb, ok ? (uint32_t)(((nr * g.ks_total + ks) * 64 + lane) * 16) : kOOB);
-                    const int grp = (half0 + nr) >> 1, half = (half0 + nr) & 1;
-                    const uint32_t w =
-                        load4(rsb, ok ? (uint32_t)(((grp * g.sn8 + (ks >> 1)) * 64 + lane) * 4) : kOOB);
-                    sbv[u][nr] = w >> (8 * ((ks & 1) * 2 + half));
-                } else {
-                    const int row = nr * 16 + (lane & 15);
-                    bfr[u][nr] = load16(rb, ok ? (uint32_t)(row * g.ldb_b + kb * 16) : kOOB);
-                    sbv[u][nr] = load1(rsb, ok ? (uint32_t)(row * g.ldsb + kb) : kOOB);
-                }
-            }
-#pragma unroll
-            for (int mg = 0; mg < MG; ++mg) {
-                const int row = mg * 16 + (lane & 15);
-                afr[u][mg] = load16(ra, ok ? (uint32_t)(row * g.lda_b + kb * 16) : kOOB);
-                sav[u][mg] = load1(rsa, ok ? (uint32_t)(row * g.ldsa + kb) : kOOB);
-            }
-        }
+    auto compute = [&](const Batch &bt) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int nr = 0; nr < NR; ++nr)
 #pragma unroll
-                for (int mg = 0; mg < MG; ++mg)
-                    acc[nr][mg] = mfma_fp4<0, 0>(bfr[u][nr], afr[u][mg], acc[nr][mg], (int)sbv[u][nr],
-                                                 (int)sav[u][mg]);
+                for (int mg = 0; mg < MG; ++mg) {
+                    const int ob = BPACK ? (u & 1) * 2 : (u & 3);
+                    const uint32_t sbr = BPACK ? bt.sb[u / 2][nr] : bt.sb[u / 4][nr];
+                    acc[nr][mg] = mma_sel(ob, u & 3, bt.b[u][nr], bt.a[u][mg], acc[nr][mg], (int)sbr,
+                                          (int)bt.sa[u / 4][mg]);
+                }
+    };
+
+    // two batches in flight: issue the next before multiplying the current
+    Batch cur, nxt;
+    load_batch(w_begin, cur);
+    for (int ks0 = w_begin; ks0 < w_end; ks0 += 2 * U) {
+        load_batch(ks0 + U, nxt);
+        compute(cur);
+        load_batch(ks0 + 2 * U, cur);
+        compute(nxt);
     }
 
     // ---- the four waves' sums, added in wave order; wave w then owns blocks f = w, w+4, ...
@@ -168,7 +235,11 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
 template <int MG, int NR, bool BPACK>
 static void launch_skinny(const GemmArgs &g, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK>), dim3(grid), dim3(256), 0, s, g);
+    // 16-byte scale groups need 16-aligned scale rows and whole 16-block groups
+    if (g.scale16)
+        hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, true>), dim3(grid), dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, false>), dim3(grid), dim3(256), 0, s, g);
 }
 
 #define MX_SKINNY(MG, NR) \

@@ -27,22 +27,6 @@
 
 namespace mx {
 
-// op_sel must be an immediate: select among the 16 (B byte, A byte) forms.
-// With fully unrolled loops the selector is a constant and the switch folds.
-__device__ __forceinline__ v4f mma_sel(int ob, int oa, v4i b, v4i a, v4f c, int sb, int sa)
-{
-#define MX_CASE(OB, OA) \
-    case OB * 4 + OA: return mfma_fp4<OB, OA>(b, a, c, sb, sa);
-    switch (ob * 4 + oa) {
-        MX_CASE(0, 0) MX_CASE(0, 1) MX_CASE(0, 2) MX_CASE(0, 3)
-        MX_CASE(1, 0) MX_CASE(1, 1) MX_CASE(1, 2) MX_CASE(1, 3)
-        MX_CASE(2, 0) MX_CASE(2, 1) MX_CASE(2, 2) MX_CASE(2, 3)
-        MX_CASE(3, 0) MX_CASE(3, 1) MX_CASE(3, 2) MX_CASE(3, 3)
-    }
-#undef MX_CASE
-    return c;
-}
-
 // s_waitcnt with vmcnt(0) only (expcnt and lgkmcnt left at their maxima):
 // waits for this wave's outstanding memory loads, including LDS-direct ones.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -366,10 +350,14 @@ static void launch_tile(const GemmArgs &g, int grid, hipStream_t s)
 const TileKernel *tile_kernels(int *count)
 {
     static const TileKernel table[] = {
-        {256, 256, 1, launch_tile<256, 256, 2, 4, false>, launch_tile<256, 256, 2, 4, true>, "tile_256x256"},
-        {256, 128, 1, launch_tile<256, 128, 2, 2, false>, launch_tile<256, 128, 2, 2, true>, "tile_256x128"},
-        {128, 128, 2, launch_tile<128, 128, 2, 2, false>, launch_tile<128, 128, 2, 2, true>, "tile_128x128"},
-        {64, 64, 4, launch_tile<64, 64, 2, 2, false>, launch_tile<64, 64, 2, 2, true>, "tile_64x64"},
+        {256, 256, 1, launch_tile<256, 256, 2, 4, false>, launch_tile<256, 256, 2, 4, true>,
+         launch_tile_deep<256, 256, 2, 4, false>, launch_tile_deep<256, 256, 2, 4, true>, false, "tile_256x256"},
+        {256, 128, 1, launch_tile<256, 128, 2, 2, false>, launch_tile<256, 128, 2, 2, true>,
+         launch_tile_deep<256, 128, 2, 2, false>, launch_tile_deep<256, 128, 2, 2, true>, true, "tile_256x128"},
+        {128, 128, 2, launch_tile<128, 128, 2, 2, false>, launch_tile<128, 128, 2, 2, true>,
+         launch_tile_deep<128, 128, 2, 2, false>, launch_tile_deep<128, 128, 2, 2, true>, false, "tile_128x128"},
+        {64, 64, 4, launch_tile<64, 64, 2, 2, false>, launch_tile<64, 64, 2, 2, true>,
+         launch_tile_deep<64, 64, 2, 2, false>, launch_tile_deep<64, 64, 2, 2, true>, true, "tile_64x64"},
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -46,11 +46,13 @@ struct Plan {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Split s over KB scale blocks: chunks are whole 256-K stages (8 blocks);
-// returns blocks per chunk and the number of non-empty chunks.
-std::pair<int, int> split_chunks(int KB, int s)
+// Split s over KB scale blocks in chunks of whole `gran`-block units (the
+// tiled kernel's 256-K stage: 8 blocks; the skinny kernel's 4-step scale
+// group: 16 blocks); returns blocks per chunk and the number of non-empty
+// chunks.
+std::pair<int, int> split_chunks(int KB, int s, int gran)
 {
-    int per = cdiv(cdiv(KB, s), 8) * 8;
+    int per = cdiv(cdiv(KB, s), gran) * gran;
     return {per, cdiv(KB, per)};
 }
 
@@ -85,11 +87,13 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
     if (M <= 64) {
         // Skinny kernel: a workgroup owns 16*nr rows of B and one K chunk.
         // nr grows with M so that A (re-read from L2 per row block) stays
-        // below the B bytes streamed from HBM.  The split is the smallest
-        // that gives about four workgroups per CU (enough bytes in flight),
-        // keeping at least two 128-K steps per wave.
+        // below the B bytes streamed from HBM.  Splitting K costs every
+        // split workgroup a serialized tail (partial write-back, counter,
+        // read-back), so the split is the smallest that gives most CUs a
+        // workgroup (measured on MI355X: 1x8192x8192 fastest unsplit,
+        // 64x7168x16384 with nr 4 fastest at split 2).
         const int mg = cdiv(M, 16);
-        int nr = mg == 1 ? 1 : 2;
+        int nr = mg == 1 ? 1 : (mg == 2 ? 2 : 4);
         if (const char *e = std::getenv("MXGEMM_FORCE_NR"))
             nr = std::atoi(e) >= 4 ? 4 : (std::atoi(e) >= 2 ? 2 : 1);
         const int nri = nr == 1 ? 0 : (nr == 2 ? 1 : 2);
@@ -99,12 +103,12 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
         for (int s : kSplits) {
             if (!consider_split(s))
                 continue;
-            auto [per, eff] = split_chunks(KB, s);
+            auto [per, eff] = split_chunks(KB, s, 16);
             if (split_req <= 0) {
                 if (s > 1 && (eff < s || per < 32))
                     break;  // chunks would collapse or leave waves idle
                 chosen = s;
-                if ((int64_t)tiles * eff >= 4LL * num_cu)
+                if ((int64_t)tiles * eff * 5 >= 4LL * num_cu)
                     break;
             } else {
                 chosen = s;
@@ -112,7 +116,7 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
         }
         if (chosen < 0)
             chosen = 1;
-        auto [per, eff] = split_chunks(KB, chosen);
+        auto [per, eff] = split_chunks(KB, chosen, 16);
         best.family = 1;
         best.index = (mg - 1) * 3 + nri;
         best.bm = mg * 16;
@@ -141,7 +145,7 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
         for (int s : kSplits) {
             if (!consider_split(s))
                 continue;
-            auto [per, eff] = split_chunks(KB, s);
+            auto [per, eff] = split_chunks(KB, s, 8);
             if (split_req <= 0 && s > 1 && eff < s)
                 continue;
             const int64_t wgs = tiles * eff;
@@ -422,6 +426,8 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     g.sn8 = cdiv(KB, 8);
     g.sa_fast = aligned(scaleA, 8) && s.ldsa % 8 == 0 && KB % 8 == 0;
     g.sb_fast = !s.b_packed && aligned(scaleB, 8) && s.ldsb % 8 == 0 && KB % 8 == 0;
+    g.scale16 = aligned(scaleA, 16) && s.ldsa % 16 == 0 && KB % 16 == 0 &&
+                (s.b_packed || (aligned(scaleB, 16) && s.ldsb % 16 == 0));
     g.d_vec = aligned(D, 8) && s.ldd % 4 == 0;
     g.c_vec = C && aligned(C, 8) && s.ldc % 4 == 0;
     g.group_m = 4;
@@ -442,7 +448,21 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     if (p.family == 0) {
         int n = 0;
         const mx::TileKernel &k = mx::tile_kernels(&n)[p.index];
-        (s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
+        // the four-slot ring kernel moves scales as 4-byte words and whole
+        // 128-K steps; otherwise the two-stage kernel handles any layout
+        const bool deep_ok = KB % 4 == 0 && aligned(scaleA, 4) && s.ldsa % 4 == 0 &&
+                             (s.b_packed || (aligned(scaleB, 4) && s.ldsb % 4 == 0));
+        bool deep = deep_ok && k.prefer_deep;
+        if (const char *e = std::getenv("MXGEMM_TILE_PIPELINE")) {  // "deep" or "two-stage"
+            if (std::strcmp(e, "two-stage") == 0)
+                deep = false;
+            else if (std::strcmp(e, "deep") == 0)
+                deep = deep_ok;
+        }
+        if (deep)
+            (s.b_packed ? k.deep_packed : k.deep_plain)(g, (int)p.grid, stream);
+        else
+            (s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
     } else {
         int n = 0;
         const mx::SkinnyKernel &k = mx::skinny_kernels(&n)[p.index];

@@ -93,8 +93,10 @@ typedef struct mxgemm_strides {
  *          1 = no split; 2, 4, 8 or 16 = split the K range into that many
  *          chunks whose fp32 partial sums are added in a fixed order (the
  *          result is bitwise reproducible run to run).  Other values:
- *          MXGEMM_ERR_INVALID_ARG.  A split that would leave a chunk empty is
- *          reduced to the largest allowed value that does not.
+ *          MXGEMM_ERR_INVALID_ARG.  Chunks are whole units of 256 K (tiled
+ *          kernel, M > 64) or 512 K (skinny kernel, M <= 64); a split that
+ *          needs smaller chunks is reduced to the number of such units
+ *          (mxgemm_query reports the split used).
  *
  * Shapes: M, N >= 1; K >= 32, K % 32 == 0, K <= 2^24.  M and N need not be
  * multiples of any tile size and K need not be a multiple of 128: edges are

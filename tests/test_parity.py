@@ -210,3 +210,32 @@ def test_strided_operands(M):
         d = host_bits(D)
         assert_parity(d[:, :N], ref, mag, "strided split %d" % s)
         assert (d[:, N:] == 0).all()  # padding columns untouched
+
+
+DEEP_SHAPES = [(65, 129, 128), (257, 511, 2048), (700, 300, 1152), (1000, 40, 384), (129, 1000, 640),
+               (512, 512, 4096)]
+
+
+@pytest.mark.parametrize("shape", DEEP_SHAPES, ids=lambda s: "%dx%dx%d" % s)
+def test_tile_pipelines_agree(shape, monkeypatch):
+    """Shapes with K % 128 == 0 and aligned scale rows can take the four-slot
+    ring kernel; the two-stage kernel must give bit-identical results (same
+    instruction sequence per accumulator), and both must match the oracle.
+    Every tile shape is forced once per case, so each ring and two-stage
+    instantiation runs."""
+    M, N, K = shape
+    p = inputs.make_problem(M, N, K, seed=0xDEE9 + M + N, e=(118, 136), beta=1.0, c_sigma=1.0)
+    p["alpha"], p["beta"] = 0.5, 2.0
+    ref, mag, _ = oracle_ref(p)
+    for tile in range(4):
+        monkeypatch.setenv("MXGEMM_FORCE_TILE", str(tile))
+        for packed in (False, True):
+            for s in ((1, 2, 4) if tile == 0 else (1, 4)):
+                say("case pipelines", shape, "tile", tile, "packed", packed, "split", s)
+                monkeypatch.setenv("MXGEMM_TILE_PIPELINE", "deep")
+                d_deep = gemm_gpu(p, split_k=s, b_packed=packed)
+                monkeypatch.setenv("MXGEMM_TILE_PIPELINE", "two-stage")
+                d_two = gemm_gpu(p, split_k=s, b_packed=packed)
+                monkeypatch.delenv("MXGEMM_TILE_PIPELINE", raising=False)
+                assert_parity(d_deep, ref, mag, "deep %s tile %d packed=%s split=%d" % (shape, tile, packed, s))
+                assert np.array_equal(d_deep, d_two)
