@@ -133,7 +133,14 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     const int rows_a = min(BM, g.M - m0);
     const uint8_t *a_base = g.A + (int64_t)m0 * g.lda_b;
     const uint32_t a_bytes = (uint32_t)(rows_a * g.lda_b);
-    const uint32_t a_lane = (uint32_t)((lane & 15) * g.lda_b + (lane >> 4) * 16);
+    // Row-major operands move in whole 128-byte lines: one load instruction
+    // covers 8 rows x the stage's 128 bytes (lane l: row l/8, 16-byte chunk
+    // (l%8) ^ (l/8) ^ h for the h-th 8-row half of a 16-row group).  The
+    // resulting LDS layout of a 16-row group (2 KiB) puts row r, chunk c at
+    // 16-byte slot (r/8)*64 + (r%8)*8 + (c ^ (r%8) ^ (r/8)): the 16 rows of
+    // one chunk fall in 16 different bank groups, so fragment reads stay
+    // conflict-free.
+    const uint32_t a_lane = (uint32_t)((lane >> 3) * g.lda_b + (((lane & 7) ^ (lane >> 3)) * 16));
     const auto rsa = make_rsrc(g.SA + (int64_t)m0 * g.ldsa, (uint32_t)(rows_a * g.ldsa));
     const uint8_t *b_base;
     uint32_t b_bytes, b_lane, b_rg_stride;
@@ -150,7 +157,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         const int rows_b = min(BN, g.N - n0);
         b_base = g.B + (int64_t)n0 * g.ldb_b;
         b_bytes = (uint32_t)(rows_b * g.ldb_b);
-        b_lane = (uint32_t)((lane & 15) * g.ldb_b + (lane >> 4) * 16);
+        b_lane = (uint32_t)((lane >> 3) * g.ldb_b + (((lane & 7) ^ (lane >> 3)) * 16));
         b_rg_stride = (uint32_t)(16 * g.ldb_b);
         rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)(rows_b * g.ldsb));
     }
@@ -166,22 +173,31 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         const uint32_t b_k = BPACK ? (uint32_t)(kb_s >> 2) * 1024 : (uint32_t)kb_s * 16;
         const auto ra = make_rsrc(a_base + a_k, on ? a_bytes - a_k : 0u);
         const auto rb = make_rsrc(b_base + b_k, on ? b_bytes - b_k : 0u);
+        // chunk (K-block of the stage) a row-major lane loads in half h
+        const int kc0 = (lane & 7) ^ (lane >> 3), kc1 = kc0 ^ 1;
 #pragma unroll
         for (int i = 0; i < A_CH / NW; ++i) {
             const int c = i * NW + wave;
-            const int rg = c >> 1, ks = c & 1;
-            uint32_t off = a_lane + (uint32_t)(rg * 16 * g.lda_b + ks * 64);
+            const int rows8 = c * 8, h = c & 1;  // 8-row half h of group c/2
+            uint32_t off = a_lane + (uint32_t)(rows8 * g.lda_b) + (h ? (uint32_t)((kc1 - kc0) * 16) : 0u);
             if constexpr (!SVEC)  // K tail: blocks at or past the chunk end read as zero
-                off = kb_s + ks * 4 + (lane >> 4) < kb_end ? off : kOOB;
+                off = kb_s + (h ? kc1 : kc0) < kb_end ? off : kOOB;
             load16_to_lds(ra, (lds_void *)(dst_a + c * 1024), off);
         }
 #pragma unroll
         for (int i = 0; i < B_CH / NW; ++i) {
             const int c = i * NW + wave;
-            const int rg = c >> 1, ks = c & 1;
-            uint32_t off = b_lane + (uint32_t)rg * b_rg_stride + (uint32_t)(ks * (BPACK ? 1024 : 64));
-            if constexpr (!SVEC)
-                off = kb_s + ks * 4 + (lane >> 4) < kb_end ? off : kOOB;
+            uint32_t off;
+            if constexpr (BPACK) {
+                // packed B: 1 KiB instruction operands, contiguous
+                const int rg = c >> 1, ks = c & 1;
+                off = b_lane + (uint32_t)rg * b_rg_stride + (uint32_t)(ks * 1024);
+            } else {
+                const int rows8 = c * 8, h = c & 1;
+                off = b_lane + (uint32_t)(rows8 * g.ldb_b) + (h ? (uint32_t)((kc1 - kc0) * 16) : 0u);
+                if constexpr (!SVEC)
+                    off = kb_s + (h ? kc1 : kc0) < kb_end ? off : kOOB;
+            }
             load16_to_lds(rb, (lds_void *)(dst_b + c * 1024), off);
         }
     };
@@ -233,6 +249,13 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         }
     };
 
+    // LDS byte offset of this lane's 16 bytes of a row-major fragment inside
+    // its 16-row group (row lane%16, K-block lane/16 of step 0; step 1 flips
+    // chunk bit 2)
+    const int fr = lane & 15;
+    const uint32_t rl0 = (uint32_t)(((fr >> 3) * 64 + (fr & 7) * 8 + ((lane >> 4) ^ (fr & 7) ^ (fr >> 3))) * 16);
+    const uint32_t rl1 = rl0 ^ 64u;
+
     // ---- main loop
     // Accumulators get their first value from the first stage's matrix
     // instructions (zero accumulator input), never from a register move, so
@@ -265,12 +288,15 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             v4i af[FM];
+            const uint32_t rl = ks ? rl1 : rl0;
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
-                af[fm] = *reinterpret_cast<const v4i *>(sa_tile + ((wave_m * FM + fm) * 2 + ks) * 1024 + lane * 16);
+                af[fm] = *reinterpret_cast<const v4i *>(sa_tile + (wave_m * FM + fm) * 2048 + rl);
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const v4i bf = *reinterpret_cast<const v4i *>(sb_tile + ((wave_n * FN + fn) * 2 + ks) * 1024 + lane * 16);
+                const uint32_t bo = BPACK ? ((wave_n * FN + fn) * 2 + ks) * 1024 + lane * 16
+                                          : (wave_n * FN + fn) * 2048 + rl;
+                const v4i bf = *reinterpret_cast<const v4i *>(sb_tile + bo);
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm)
                     acc[fn][fm] = mma_sel(ks * 2 + (fn & 1), ks * 2 + (fm & 1), bf, af[fm],

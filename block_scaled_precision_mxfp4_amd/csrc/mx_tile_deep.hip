@@ -142,16 +142,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
     constexpr int SC_I = SA_I + SB_I;
     constexpr int SC_PER_WAVE = (SC_I + NW - 1) / NW;
     constexpr int SA_BYTES = BM * 4, SB_BYTES = BPACK ? BN / 32 * 256 : BN * 4;
-    // L2 prefetch ("touch") of step kt+NS-1+PD while step kt+NS-1 is loaded:
-    // one 4-byte lane per 128-byte line, data dropped into the idle LDS row.
-    // Jobs of 64 lanes: operand rows (half of them per step: a row's 64-byte
-    // run of one step is half a line, the line serves two steps), one job
-    // per scale matrix.
-    constexpr int PD = 8;
-    constexpr int JA = (BM / 2 + 63) / 64, JB = (BN / 2 + 63) / 64;
-    constexpr int JOBS = JA + JB + 2;
-    constexpr int T_PER_WAVE = (JOBS + NW - 1) / NW;
-    constexpr int L = A_CH / NW + B_CH / NW + SC_PER_WAVE + T_PER_WAVE;  // loads per wave per stage
+    constexpr int L = A_CH / NW + B_CH / NW + SC_PER_WAVE;  // loads per wave per stage
     static_assert((NS - 2) * L < 64, "vmcnt range");
 
     // One LDS block; regions at compile-time offsets: [A slots][B slots]
@@ -216,70 +207,6 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
         sb_bytes = (uint32_t)(rows_b * g.ldsb);
     }
 
-    // ---- this wave's L2 touch jobs (fixed over the K loop)
-    int t_kind[T_PER_WAVE], t_qlim[T_PER_WAVE];
-    const uint8_t *t_base[T_PER_WAVE];
-    uint32_t t_bytes[T_PER_WAVE], t_lb0[T_PER_WAVE], t_lb1[T_PER_WAVE], t_qstride[T_PER_WAVE];
-    bool t_ok[T_PER_WAVE];
-#pragma unroll
-    for (int i = 0; i < T_PER_WAVE; ++i) {
-        const int j = i * NW + wave;  // wave-uniform
-        t_kind[i] = 4;
-        t_base[i] = sa_base;
-        t_bytes[i] = 0;
-        t_lb0[i] = t_lb1[i] = 0;
-        t_qlim[i] = 0;
-        t_qstride[i] = 0;
-        t_ok[i] = false;
-        if (j < JA) {
-            const int r = j * 64 + lane;
-            t_kind[i] = 0;
-            t_base[i] = a_base;
-            t_bytes[i] = a_bytes;
-            t_ok[i] = r < BM / 2;
-            t_lb0[i] = (uint32_t)(r * g.lda_b);
-            t_lb1[i] = (uint32_t)((r + BM / 2) * g.lda_b);
-        } else if (j < JA + JB) {
-            const int jb = j - JA;
-            t_base[i] = b_base;
-            t_bytes[i] = b_bytes;
-            if constexpr (BPACK) {
-                const int grp = jb * 8 + (lane >> 3);
-                t_kind[i] = 1;
-                t_ok[i] = grp < BN / 16;
-                t_lb0[i] = t_lb1[i] = (uint32_t)grp * b_rg_stride + (uint32_t)(lane & 7) * 128;
-            } else {
-                const int r = jb * 64 + lane;
-                t_kind[i] = 0;
-                t_ok[i] = r < BN / 2;
-                t_lb0[i] = (uint32_t)(r * g.ldb_b);
-                t_lb1[i] = (uint32_t)((r + BN / 2) * g.ldb_b);
-            }
-        } else if (j == JA + JB) {
-            t_kind[i] = 2;
-            t_base[i] = sa_base;
-            t_bytes[i] = sa_bytes;
-            t_ok[i] = true;
-            t_lb0[i] = t_lb1[i] = (uint32_t)(lane * g.ldsa);
-            t_qlim[i] = BM / 64;
-            t_qstride[i] = (uint32_t)g.ldsa;
-        } else if (j == JA + JB + 1) {
-            t_base[i] = sb_base;
-            t_bytes[i] = sb_bytes;
-            if constexpr (BPACK) {
-                t_kind[i] = 3;
-                t_ok[i] = lane < BN / 16;
-                t_lb0[i] = t_lb1[i] = (uint32_t)((lane >> 1) * g.sn8 * 256 + (lane & 1) * 128);
-            } else {
-                t_kind[i] = 2;
-                t_ok[i] = true;
-                t_lb0[i] = t_lb1[i] = (uint32_t)(lane * g.ldsb);
-                t_qlim[i] = BN / 64;
-                t_qstride[i] = (uint32_t)g.ldsb;
-            }
-        }
-    }
-
     // ---- one stage's loads (exactly L per wave; `on` false: empty ranges)
     auto issue = [&](int kt, bool on, int slot) {
         uint8_t *sa_ = smem + slot * A_STAGE, *sb_ = smem + OFF_B + slot * B_STAGE;
@@ -326,36 +253,6 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
                 // out-of-range direct load still writes zeros to its LDS row
                 load4_to_lds(rsb, (lds_void *)(smem + OFF_IDLE), kOOB);
             }
-        }
-        // L2 touches for step kt+PD
-        const int tt = kt + PD;
-        const int kb_t = kb_begin + tt * 4;
-#pragma unroll
-        for (int i = 0; i < T_PER_WAVE; ++i) {
-            uint32_t sp = 0, lb = t_lb0[i];
-            bool sok = tt < nst;
-            switch (t_kind[i]) {
-            case 0:  // operand rows, half of them per step
-                sp = ((uint32_t)kb_t * 16) & ~127u;
-                lb = (tt & 1) ? t_lb1[i] : t_lb0[i];
-                break;
-            case 1:  // packed B: 8 lines of each 16-row group
-                sp = (uint32_t)(kb_t >> 2) * 1024;
-                break;
-            case 2: {  // row-major scales: a line serves 32 steps; 64 rows per step
-                const int q = (kb_t >> 2) & 31;
-                sp = (uint32_t)(q * 64) * t_qstride[i] + ((uint32_t)kb_t & ~127u);
-                sok = sok && q < t_qlim[i];
-                break;
-            }
-            case 3:  // packed B scales: 2 lines per 32-row group and step pair
-                sp = (uint32_t)(kb_t >> 3) * 256;
-                break;
-            default:
-                sok = false;
-            }
-            const uint32_t off = (t_ok[i] && sok) ? lb + sp : kOOB;
-            load4_to_lds(make_rsrc(t_base[i], t_bytes[i]), (lds_void *)(smem + OFF_IDLE), off);
         }
     };
 
