@@ -73,7 +73,7 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False):
 
     p = inputs.make_workload(name)
     M, N, K, alpha, beta = p["M"], p["N"], p["K"], p["alpha"], p["beta"]
-    packed = p["b_packed"]
+    packed, sa_packed = p["b_packed"], p["sa_packed"]
     info = mx.mxgemm_query(M, N, K, int(packed), split_k)
     ws_bytes = algorithmic_bytes(M, N, K, beta)
     copies = 1
@@ -95,11 +95,16 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False):
             SBp = torch.empty(info["packed_sb_bytes"], dtype=torch.uint8, device="cuda")
             mx.mxgemm_pack_b(Bp, SBp, B, SB, N, K)
             B, SB = Bp, SBp
+        if sa_packed:
+            SAp = torch.empty(info["packed_sa_bytes"], dtype=torch.uint8, device="cuda")
+            mx.mxgemm_pack_scales(SAp, SA, M, K)
+            SA = SAp
         sets.append((D, C, A, B, SA, SB))
     del A0, SA0, B0, SB0, C0
     wsp = torch.zeros(max(info["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
     strides = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32,
-                              b_packed=int(packed), workspace=wsp, workspace_bytes=wsp.numel())
+                              b_packed=int(packed), sa_packed=int(sa_packed), workspace=wsp,
+                              workspace_bytes=wsp.numel())
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
@@ -150,6 +155,7 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False):
     per = gpu_ms / 1e3 / steps
     flops = 2.0 * M * N * K
     r = dict(workload=name, M=M, N=N, K=K, alpha=alpha, beta=beta, b_packed=bool(packed),
+             sa_packed=bool(sa_packed),
              kernel=info["kernel_name"], tile="%dx%d" % (info["tile_m"], info["tile_n"]),
              split_k=info["split_k"], grid=info["grid"], copies=copies, timing=timing,
              us_per_step=per * 1e6, tflops=flops / per / 1e12,
@@ -278,7 +284,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": head["us_per_step"] / 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": vs, "dtype": "mxfp4", "data": "synthetic",
         "config": {"workload": head["workload"], "M": head["M"], "N": head["N"], "K": head["K"],
-                   "b_packed": head["b_packed"], "kernel": head["kernel"], "tile": head["tile"],
+                   "b_packed": head["b_packed"], "sa_packed": head["sa_packed"], "kernel": head["kernel"],
+                   "tile": head["tile"],
                    "split_k": head["split_k"], "timing": head["timing"]},
         "roofline": roof,
         "cpu_baseline": base,

@@ -18,8 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
 
 # C-ABI entry points declared in include/libmxgemm.h
-EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_pack_b", "mxgemm_query",
-           "mxgemm_plan", "mxgemm_release_workspaces")
+EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_pack_b", "mxgemm_pack_scales",
+           "mxgemm_query", "mxgemm_plan", "mxgemm_release_workspaces")
 
 STATUS = {0: "MXGEMM_OK", -1: "MXGEMM_ERR_INVALID_ARG", -2: "MXGEMM_ERR_SHAPE",
           -3: "MXGEMM_ERR_ALIGN", -4: "MXGEMM_ERR_UNSUPPORTED_DEVICE", -5: "MXGEMM_ERR_HIP",
@@ -36,7 +36,7 @@ class MxGemmError(RuntimeError):
 class Strides(ctypes.Structure):
     _fields_ = [("ldd", ctypes.c_int64), ("ldc", ctypes.c_int64), ("lda", ctypes.c_int64),
                 ("ldb", ctypes.c_int64), ("ldsa", ctypes.c_int64), ("ldsb", ctypes.c_int64),
-                ("b_packed", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("b_packed", ctypes.c_int32), ("sa_packed", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -44,7 +44,8 @@ class Info(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
                 ("split_k", ctypes.c_int32), ("grid", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_size_t), ("packed_b_bytes", ctypes.c_size_t),
-                ("packed_sb_bytes", ctypes.c_size_t), ("num_cu", ctypes.c_int32),
+                ("packed_sb_bytes", ctypes.c_size_t), ("packed_sa_bytes", ctypes.c_size_t),
+                ("num_cu", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("kernel_name", ctypes.c_char * 64),
                 ("arch", ctypes.c_char * 32), ("peak_flops", ctypes.c_double),
                 ("clock_hz", ctypes.c_double)]
@@ -74,6 +75,8 @@ def lib():
         L.mxgemm_run.restype = i32
         L.mxgemm_pack_b.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, vp]
         L.mxgemm_pack_b.restype = i32
+        L.mxgemm_pack_scales.argtypes = [vp, vp, i32, i32, i64, vp]
+        L.mxgemm_pack_scales.restype = i32
         L.mxgemm_query.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(Info)]
         L.mxgemm_query.restype = i32
         L.mxgemm_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(Info)]
@@ -113,8 +116,9 @@ def _check(status, where):
         raise MxGemmError(status, where)
 
 
-def make_strides(*, ldd, ldc, lda, ldb, ldsa, ldsb, b_packed=0, workspace=None, workspace_bytes=0):
-    return Strides(ldd, ldc, lda, ldb, ldsa, ldsb, b_packed, 0, _ptr(workspace), workspace_bytes)
+def make_strides(*, ldd, ldc, lda, ldb, ldsa, ldsb, b_packed=0, sa_packed=0, workspace=None,
+                 workspace_bytes=0):
+    return Strides(ldd, ldc, lda, ldb, ldsa, ldsb, b_packed, sa_packed, _ptr(workspace), workspace_bytes)
 
 
 def mxgemm_status_string(status: int) -> str:
@@ -141,6 +145,16 @@ def mxgemm_pack_b(Bp, SBp, B, scaleB, N, K, ldb=None, ldsb=None, stream=None, ch
                              int(ldb), int(ldsb), _stream(stream))
     if check:
         _check(st, "mxgemm_pack_b")
+    return st
+
+
+def mxgemm_pack_scales(Sp, S, rows, K, lds=None, stream=None, check=True):
+    """Shuffle a [rows][K/32] scale matrix into the packed scale layout
+    (scaleA for sa_packed = 1; asynchronous)."""
+    lds = K // 32 if lds is None else lds
+    st = lib().mxgemm_pack_scales(_ptr(Sp), _ptr(S), int(rows), int(K), int(lds), _stream(stream))
+    if check:
+        _check(st, "mxgemm_pack_scales")
     return st
 
 

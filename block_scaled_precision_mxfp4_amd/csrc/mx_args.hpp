@@ -13,7 +13,7 @@ struct GemmArgs {
     const uint16_t *C;    // bf16 [M][ldc], read only when beta != 0
     const uint8_t *A;     // fp4x2 [M][lda_b]
     const uint8_t *B;     // fp4x2 [N][ldb_b], or the packed layout
-    const uint8_t *SA;    // E8M0 [M][ldsa]
+    const uint8_t *SA;    // E8M0 [M][ldsa], or the packed scale layout
     const uint8_t *SB;    // E8M0 [N][ldsb], or the packed layout
     float *ws;            // split-K fp32 partials
     int *counters;        // split-K arrival counters, one per output tile, zero between calls
@@ -40,13 +40,16 @@ typedef void (*LaunchFn)(const GemmArgs &, int grid, hipStream_t);
 struct TileKernel {
     int bm, bn;
     int occupancy;        // workgroups per CU the kernel's LDS allows
-    LaunchFn plain, packed;            // two-stage kernel: any strides
-    LaunchFn deep_plain, deep_packed;  // four-slot ring: dword-aligned scale rows, K % 128 == 0
+    // two-stage kernel (any strides); four-slot ring (dword-aligned scale
+    // rows, K % 128 == 0).  plain: row-major B and scales; packed: packed B
+    // and B scales; packed_sa: packed B, B scales and A scales
+    LaunchFn plain, packed, packed_sa;
+    LaunchFn deep_plain, deep_packed, deep_packed_sa;
     bool prefer_deep;                  // the ring kernel is the faster one for this tile
     const char *name;
 };
 
-template <int BM, int BN, int WM, int WN, bool BPACK>
+template <int BM, int BN, int WM, int WN, bool BPACK, bool SAPACK>
 void launch_tile_deep(const GemmArgs &g, int grid, hipStream_t s);
 // Host-side table of the tiled kernels, in the planner's preference order.
 const TileKernel *tile_kernels(int *count);
@@ -55,12 +58,13 @@ const TileKernel *tile_kernels(int *count);
 // index: (mg - 1) * 3 + nr_index with nr in {1, 2, 4}.
 struct SkinnyKernel {
     int mg, nr;
-    LaunchFn plain, packed;
+    LaunchFn plain, packed, packed_sa;
     const char *name;
 };
 const SkinnyKernel *skinny_kernels(int *count);
 
 void launch_pack_b(uint8_t *Bp, const uint8_t *B, int N, int KB, int64_t ldb_b, hipStream_t s);
+// Scale shuffle of rows x KB scale bytes (either operand's scales).
 void launch_pack_sb(uint32_t *SBp, const uint8_t *SB, int N, int KB, int64_t ldsb, hipStream_t s);
 
 }  // namespace mx

@@ -48,7 +48,7 @@ __device__ __forceinline__ uint32_t load_scale_group(__amdgpu_buffer_rsrc_t r, i
     }
 }
 
-template <int MG, int NR, bool BPACK, bool SVEC>
+template <int MG, int NR, bool BPACK, bool SVEC, bool APACK>
 __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
 {
     constexpr int R = 16 * NR;                      // B rows per workgroup
@@ -75,7 +75,8 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
     const int kb_wend = min(kb_end, w_end * 4);  // K-blocks this wave may touch
 
     const auto ra = make_rsrc(g.A, (uint32_t)(g.M * g.lda_b));
-    const auto rsa = make_rsrc(g.SA, (uint32_t)(g.M * g.ldsa));
+    const auto rsa = APACK ? make_rsrc(g.SA, (uint32_t)((g.M + 31) / 32 * g.sn8 * 256))
+                           : make_rsrc(g.SA, (uint32_t)(g.M * g.ldsa));
     __amdgpu_buffer_rsrc_t rb, rsb;
     int half0 = 0;  // packed scales: which 16-row half of its 32-row group row n0 is
     if constexpr (BPACK) {
@@ -94,7 +95,7 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
     struct Batch {
         v4i b[U][NR], a[U][MG];
         uint32_t sb[BPACK ? U / 2 : G][NR];  // packed: one word per step pair, else per group
-        uint32_t sa[G][MG];
+        uint32_t sa[APACK ? U / 2 : G][MG];
     };
 
     auto load_batch = [&](int ks0, Batch &bt) {
@@ -117,13 +118,27 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             const int kb0 = (ks0 + 4 * gi) * 4;  // first K-block of the group
+            if constexpr (!APACK) {
 #pragma unroll
-            for (int mg = 0; mg < MG; ++mg)
-                bt.sa[gi][mg] = load_scale_group<SVEC>(rsa, g.ldsa, mg * 16 + (lane & 15), kb0, kb_wend, lane);
+                for (int mg = 0; mg < MG; ++mg)
+                    bt.sa[gi][mg] = load_scale_group<SVEC>(rsa, g.ldsa, mg * 16 + (lane & 15), kb0, kb_wend, lane);
+            }
             if constexpr (!BPACK) {
 #pragma unroll
                 for (int nr = 0; nr < NR; ++nr)
                     bt.sb[gi][nr] = load_scale_group<SVEC>(rsb, g.ldsb, nr * 16 + (lane & 15), kb0, kb_wend, lane);
+            }
+        }
+        if constexpr (APACK) {
+#pragma unroll
+            for (int p = 0; p < U / 2; ++p) {
+                const int ks = ks0 + 2 * p;  // even: the word holds steps ks, ks+1 x both row halves
+#pragma unroll
+                for (int mg = 0; mg < MG; ++mg) {
+                    const uint32_t w =
+                        load4(rsa, ks * 4 < kb_wend ? (uint32_t)((((mg >> 1) * g.sn8 + (ks >> 1)) * 64 + lane) * 4) : kOOB);
+                    bt.sa[p][mg] = w >> (8 * (mg & 1));  // this row half's bytes at 0 and 2
+                }
             }
         }
         if constexpr (BPACK) {
@@ -157,8 +172,9 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
                 for (int mg = 0; mg < MG; ++mg) {
                     const int ob = BPACK ? (u & 1) * 2 : (u & 3);
                     const uint32_t sbr = BPACK ? bt.sb[u / 2][nr] : bt.sb[u / 4][nr];
-                    acc[nr][mg] = mma_sel(ob, u & 3, bt.b[u][nr], bt.a[u][mg], acc[nr][mg], (int)sbr,
-                                          (int)bt.sa[u / 4][mg]);
+                    const int oa = APACK ? (u & 1) * 2 : (u & 3);
+                    const uint32_t sar = APACK ? bt.sa[u / 2][mg] : bt.sa[u / 4][mg];
+                    acc[nr][mg] = mma_sel(ob, oa, bt.b[u][nr], bt.a[u][mg], acc[nr][mg], (int)sbr, (int)sar);
                 }
     };
 
@@ -232,18 +248,22 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
     }
 }
 
-template <int MG, int NR, bool BPACK>
+template <int MG, int NR, bool BPACK, bool APACK>
 static void launch_skinny(const GemmArgs &g, int grid, hipStream_t s)
 {
-    // 16-byte scale groups need 16-aligned scale rows and whole 16-block groups
-    if (g.scale16)
-        hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, true>), dim3(grid), dim3(256), 0, s, g);
+    // 16-byte scale groups need 16-aligned scale rows and whole 16-block
+    // groups (with both scale operands packed no row-major group is read)
+    if (APACK)
+        hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, false, APACK>), dim3(grid), dim3(256), 0, s, g);
+    else if (g.scale16)
+        hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, true, false>), dim3(grid), dim3(256), 0, s, g);
     else
-        hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, false>), dim3(grid), dim3(256), 0, s, g);
+        hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, false, false>), dim3(grid), dim3(256), 0, s, g);
 }
 
-#define MX_SKINNY(MG, NR) \
-    {MG, NR, launch_skinny<MG, NR, false>, launch_skinny<MG, NR, true>, "skinny_m" #MG "x16_n" #NR "x16"}
+#define MX_SKINNY(MG, NR)                                                                           \
+    {MG, NR, launch_skinny<MG, NR, false, false>, launch_skinny<MG, NR, true, false>,                 \
+     launch_skinny<MG, NR, true, true>, "skinny_m" #MG "x16_n" #NR "x16"}
 const SkinnyKernel *skinny_kernels(int *count)
 {
     static const SkinnyKernel table[] = {

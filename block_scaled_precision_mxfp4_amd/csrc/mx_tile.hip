@@ -75,7 +75,7 @@ __device__ __forceinline__ uint32_t scale_word(const ScaleRows &s, int d5)
            (((s.r0[1] >> sh) & 0xFFu) << 16) | (((s.r1[1] >> sh) & 0xFFu) << 24);
 }
 
-template <int BM, int BN, int WM, int WN, bool BPACK, bool SVEC>
+template <int BM, int BN, int WM, int WN, bool BPACK, bool SVEC, bool SAPACK>
 __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
 {
     constexpr int NW = WM * WN;                // waves per workgroup
@@ -90,6 +90,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     constexpr int SA_W = BM / 32 * 64, SB_W = BN / 32 * 64;  // scale words per stage
     constexpr int SC_W = SA_W + SB_W + 64;                   // + a scratch row for idle threads
     constexpr int SBP_PER_THREAD = (SB_W + NT - 1) / NT;     // packed-scale words per thread
+    constexpr int SAP_PER_THREAD = (SA_W + NT - 1) / NT;
     static_assert(BM / 2 + BN / 2 <= NT, "one scale row pair per thread");
 
     // The two halves of each double buffer are distinct LDS objects and every
@@ -141,7 +142,13 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     // one chunk fall in 16 different bank groups, so fragment reads stay
     // conflict-free.
     const uint32_t a_lane = (uint32_t)((lane >> 3) * g.lda_b + (((lane & 7) ^ (lane >> 3)) * 16));
-    const auto rsa = make_rsrc(g.SA + (int64_t)m0 * g.ldsa, (uint32_t)(rows_a * g.ldsa));
+    __amdgpu_buffer_rsrc_t rsa;
+    if constexpr (SAPACK) {
+        const int m32 = m0 / 32, grp32 = min(BM / 32, (g.M + 31) / 32 - m32);
+        rsa = make_rsrc(g.SA + (int64_t)m32 * g.sn8 * 256, (uint32_t)(grp32 * g.sn8 * 256));
+    } else {
+        rsa = make_rsrc(g.SA + (int64_t)m0 * g.ldsa, (uint32_t)(rows_a * g.ldsa));
+    }
     const uint8_t *b_base;
     uint32_t b_bytes, b_lane, b_rg_stride;
     __amdgpu_buffer_rsrc_t rsb;
@@ -204,7 +211,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
 
     // scale-row ownership: thread < BM/2 owns A row pair tid; the next BN/2
     // threads own B row pairs (row-major B scales only)
-    const bool own_a = tid < BM / 2;
+    const bool own_a = !SAPACK && tid < BM / 2;
     const int ua = own_a ? tid : 0;
     const bool own_b = !BPACK && tid >= BM / 2 && tid < BM / 2 + BN / 2;
     const int ub = own_b ? tid - BM / 2 : 0;
@@ -213,10 +220,23 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     const int wb = own_b ? SA_W + (ub >> 4) * 64 + (ub & 15) : SA_W + SB_W + lane;
 
     ScaleRows sa_rows, sb_rows;
-    uint32_t sbp[SBP_PER_THREAD];
+    uint32_t sbp[SBP_PER_THREAD], sap[SAP_PER_THREAD];
     auto issue_scales = [&](int kt, bool on) {
         const int kb_s = kb_begin + kt * 8;
-        sa_rows = load_scale_rows<SVEC>(rsa, g.ldsa, (ua >> 4) * 32 + (ua & 15), kb_s, kb_end, on && own_a);
+        if constexpr (SAPACK) {
+            // packed words are already the LDS words: word q of the stage is
+            // word q & 63 of 32-row group q / 64's chunk for this 8-block step
+#pragma unroll
+            for (int i = 0; i < SAP_PER_THREAD; ++i) {
+                const int q = i * NT + tid;
+                const uint32_t off = on && q < SA_W
+                                         ? (uint32_t)((((q >> 6) * g.sn8 + (kb_s >> 3)) * 64 + (q & 63)) * 4)
+                                         : kOOB;
+                sap[i] = load4(rsa, off);
+            }
+        } else {
+            sa_rows = load_scale_rows<SVEC>(rsa, g.ldsa, (ua >> 4) * 32 + (ua & 15), kb_s, kb_end, on && own_a);
+        }
         if constexpr (BPACK) {
 #pragma unroll
             for (int i = 0; i < SBP_PER_THREAD; ++i) {
@@ -233,9 +253,17 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     auto commit_scales = [&](auto bufc) {
         constexpr int BUF = decltype(bufc)::value;
         uint32_t *dsc = BUF ? s_sc1 : s_sc0;
+        if constexpr (SAPACK) {
 #pragma unroll
-        for (int d5 = 0; d5 < 4; ++d5)
-            dsc[wa + (own_a ? 16 * d5 : 0)] = scale_word(sa_rows, d5);
+            for (int i = 0; i < SAP_PER_THREAD; ++i) {
+                const int q = i * NT + tid;
+                dsc[q < SA_W ? q : SA_W + SB_W + lane] = sap[i];
+            }
+        } else {
+#pragma unroll
+            for (int d5 = 0; d5 < 4; ++d5)
+                dsc[wa + (own_a ? 16 * d5 : 0)] = scale_word(sa_rows, d5);
+        }
         if constexpr (BPACK) {
 #pragma unroll
             for (int i = 0; i < SBP_PER_THREAD; ++i) {
@@ -364,27 +392,33 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         }
 }
 
-template <int BM, int BN, int WM, int WN, bool BPACK>
+template <int BM, int BN, int WM, int WN, bool BPACK, bool SAPACK>
 static void launch_tile(const GemmArgs &g, int grid, hipStream_t s)
 {
-    if (g.sa_fast && (BPACK || g.sb_fast))
-            hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, true>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
+    // SVEC: whole 8-block stages and 8-byte scale-row loads (packed scales
+    // need only the former)
+    const bool sa_ok = SAPACK ? g.KB % 8 == 0 : g.sa_fast != 0;
+    if (sa_ok && (BPACK ? g.KB % 8 == 0 : g.sb_fast != 0))
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, true, SAPACK>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
     else
-        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, false>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, false, SAPACK>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
 }
+
+#define MX_TILE(BM, BN, WM, WN, OCC, DEEP)                                                              \
+    {BM, BN, OCC, launch_tile<BM, BN, WM, WN, false, false>, launch_tile<BM, BN, WM, WN, true, false>,   \
+     launch_tile<BM, BN, WM, WN, true, true>, launch_tile_deep<BM, BN, WM, WN, false, false>,           \
+     launch_tile_deep<BM, BN, WM, WN, true, false>, launch_tile_deep<BM, BN, WM, WN, true, true>, DEEP, \
+     "tile_" #BM "x" #BN}
 
 const TileKernel *tile_kernels(int *count)
 {
     static const TileKernel table[] = {
-        {256, 256, 1, launch_tile<256, 256, 2, 4, false>, launch_tile<256, 256, 2, 4, true>,
-         launch_tile_deep<256, 256, 2, 4, false>, launch_tile_deep<256, 256, 2, 4, true>, false, "tile_256x256"},
-        {256, 128, 1, launch_tile<256, 128, 2, 2, false>, launch_tile<256, 128, 2, 2, true>,
-         launch_tile_deep<256, 128, 2, 2, false>, launch_tile_deep<256, 128, 2, 2, true>, true, "tile_256x128"},
-        {128, 128, 2, launch_tile<128, 128, 2, 2, false>, launch_tile<128, 128, 2, 2, true>,
-         launch_tile_deep<128, 128, 2, 2, false>, launch_tile_deep<128, 128, 2, 2, true>, false, "tile_128x128"},
-        {64, 64, 4, launch_tile<64, 64, 2, 2, false>, launch_tile<64, 64, 2, 2, true>,
-         launch_tile_deep<64, 64, 2, 2, false>, launch_tile_deep<64, 64, 2, 2, true>, true, "tile_64x64"},
+        MX_TILE(256, 256, 2, 4, 1, false),
+        MX_TILE(256, 128, 2, 2, 1, false),
+        MX_TILE(128, 128, 2, 2, 2, false),
+        MX_TILE(64, 64, 2, 2, 4, true),
     };
+#undef MX_TILE
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;
 }

@@ -123,7 +123,7 @@ __device__ __forceinline__ void load4_to_lds(__amdgpu_buffer_rsrc_t r, lds_void 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, off, 0, 0, 0);
 }
 
-template <int BM, int BN, int WM, int WN, bool BPACK>
+template <int BM, int BN, int WM, int WN, bool BPACK, bool SAPACK>
 __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
 {
     constexpr int NS = 4;                      // stage buffers
@@ -136,12 +136,12 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
     static_assert(A_CH % NW == 0 && B_CH % NW == 0, "chunks split evenly over waves");
     constexpr int A_STAGE = BM * 64, B_STAGE = BN * 64;  // operand bytes per stage
     // scale loads per stage (64 lanes x 4 bytes each)
-    constexpr int SA_I = BM / 64;                     // row-major A: one word per row
+    constexpr int SA_I = SAPACK ? BM / 32 : BM / 64;  // row-major A: one word per row
     constexpr int SB_I = BPACK ? BN / 32 : BN / 64;   // packed: one 256-byte chunk per 32 rows
     static_assert(BM % 64 == 0 && (BPACK ? BN % 32 == 0 : BN % 64 == 0), "whole scale loads");
     constexpr int SC_I = SA_I + SB_I;
     constexpr int SC_PER_WAVE = (SC_I + NW - 1) / NW;
-    constexpr int SA_BYTES = BM * 4, SB_BYTES = BPACK ? BN / 32 * 256 : BN * 4;
+    constexpr int SA_BYTES = SAPACK ? BM / 32 * 256 : BM * 4, SB_BYTES = BPACK ? BN / 32 * 256 : BN * 4;
     constexpr int L = A_CH / NW + B_CH / NW + SC_PER_WAVE;  // loads per wave per stage
     static_assert((NS - 2) * L < 64, "vmcnt range");
 
@@ -184,8 +184,16 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
     const uint8_t *a_base = g.A + (int64_t)m0 * g.lda_b;
     const uint32_t a_bytes = (uint32_t)(rows_a * g.lda_b);
     const uint32_t a_lane = (uint32_t)((lane & 15) * g.lda_b + (lane >> 4) * 16);
-    const uint8_t *sa_base = g.SA + (int64_t)m0 * g.ldsa;
-    const uint32_t sa_bytes = (uint32_t)(rows_a * g.ldsa);
+    const uint8_t *sa_base;
+    uint32_t sa_bytes;
+    if constexpr (SAPACK) {
+        const int m32 = m0 / 32, grp32 = min(BM / 32, (g.M + 31) / 32 - m32);
+        sa_base = g.SA + (int64_t)m32 * g.sn8 * 256;
+        sa_bytes = (uint32_t)(grp32 * g.sn8 * 256);
+    } else {
+        sa_base = g.SA + (int64_t)m0 * g.ldsa;
+        sa_bytes = (uint32_t)(rows_a * g.ldsa);
+    }
     const uint8_t *b_base, *sb_base;
     uint32_t b_bytes, b_lane, b_rg_stride, sb_bytes;
     if constexpr (BPACK) {
@@ -227,7 +235,8 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
             load16_to_lds(rb, (lds_void *)(sb_ + rg * 1024), b_lane + (uint32_t)rg * b_rg_stride);
         }
         // scale loads, round-robin over the waves; slots past SC_I are idle
-        const auto rsa = make_rsrc(sa_base + kb_s, on ? sa_bytes - kb_s : 0u);
+        const uint32_t sa_k = SAPACK ? (uint32_t)(kb_s >> 3) * 256 : (uint32_t)kb_s;
+        const auto rsa = make_rsrc(sa_base + sa_k, on ? sa_bytes - sa_k : 0u);
         uint32_t sb_k;
         if constexpr (BPACK)
             sb_k = (uint32_t)(kb_s >> 3) * 256;  // 8-block group of this step
@@ -239,7 +248,8 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
             const int c = i * NW + wave;  // wave-uniform
             if (c < SA_I) {
                 const int row = c * 64 + lane;
-                load4_to_lds(rsa, (lds_void *)(ssa + c * 256), (uint32_t)(row * g.ldsa));
+                const uint32_t off = SAPACK ? (uint32_t)((c * g.sn8 * 64 + lane) * 4) : (uint32_t)(row * g.ldsa);
+                load4_to_lds(rsa, (lds_void *)(ssa + c * 256), off);
             } else if (c < SC_I) {
                 const int cb = c - SA_I;
                 uint32_t off;
@@ -261,7 +271,9 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
     const uint32_t lds0 = lds_addr(smem);
     const uint32_t base_a = lds0 + (uint32_t)(wave_m * FM * 1024 + lane * 16);
     const uint32_t base_b = lds0 + (uint32_t)(OFF_B + wave_n * FN * 1024 + lane * 16);
-    const uint32_t base_sa = lds0 + (uint32_t)(OFF_SA + (wave_m * TM + (lane & 15)) * 4 + (lane >> 4));
+    const uint32_t base_sa =
+        SAPACK ? lds0 + (uint32_t)(OFF_SA + wave_m * (TM / 32) * 256 + lane * 4)
+               : lds0 + (uint32_t)(OFF_SA + (wave_m * TM + (lane & 15)) * 4 + (lane >> 4));
     uint32_t base_sb;
     if constexpr (BPACK)
         base_sb = lds0 + (uint32_t)(OFF_SB + wave_n * (TN / 32) * 256 + lane * 4);
@@ -281,12 +293,20 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
         // two row halves: shifted so that this step's halves are bytes 0, 1
         // (chunks start on even steps, so the step parity is kt's)
         constexpr int NSB = BPACK ? FN / 2 : FN;
-        uint32_t sav[FM], sbv[NSB];
+        constexpr int NSA = SAPACK ? FM / 2 : FM;
+        uint32_t sav[NSA], sbv[NSB];
         v4i af[FM], bfr[FN];
-        static_for<FM>([&](auto i) {
-            constexpr int fm = decltype(i)::value;
-            sav[fm] = lds_read1<fm * 64>(rsa_);
-        });
+        if constexpr (SAPACK) {
+            static_for<FM / 2>([&](auto i) {
+                constexpr int p = decltype(i)::value;
+                sav[p] = lds_read4<p * 256>(rsa_);
+            });
+        } else {
+            static_for<FM>([&](auto i) {
+                constexpr int fm = decltype(i)::value;
+                sav[fm] = lds_read1<fm * 64>(rsa_);
+            });
+        }
         if constexpr (BPACK) {
             static_for<FN / 2>([&](auto i) {
                 constexpr int p = decltype(i)::value;
@@ -315,14 +335,21 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
             for (int p = 0; p < FN / 2; ++p)
                 sbv[p] >>= sh;
         }
+        if constexpr (SAPACK) {
+            const int sh = (kt & 1) * 16;
+#pragma unroll
+            for (int p = 0; p < FM / 2; ++p)
+                sav[p] >>= sh;
+        }
         static_for<FM>([&](auto i) {
             constexpr int fm = decltype(i)::value;
             lds_wait_n<FM - 1 - fm>(af[fm]);
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
                 const int ob = BPACK ? (fn & 1) : 0;
-                acc[fn][fm] = mma_sel(ob, 0, bfr[fn], af[fm], FIRST ? v4f{0.f, 0.f, 0.f, 0.f} : acc[fn][fm],
-                                      (int)sbv[BPACK ? fn / 2 : fn], (int)sav[fm]);
+                constexpr int oa = SAPACK ? (fm & 1) : 0;
+                acc[fn][fm] = mma_sel(ob, oa, bfr[fn], af[fm], FIRST ? v4f{0.f, 0.f, 0.f, 0.f} : acc[fn][fm],
+                                      (int)sbv[BPACK ? fn / 2 : fn], (int)sav[SAPACK ? fm / 2 : fm]);
             }
         });
     };
@@ -383,19 +410,20 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
         }
 }
 
-template <int BM, int BN, int WM, int WN, bool BPACK>
+template <int BM, int BN, int WM, int WN, bool BPACK, bool SAPACK>
 void launch_tile_deep(const GemmArgs &g, int grid, hipStream_t s)
 {
-    hipLaunchKernelGGL((mx_tile_deep_kernel<BM, BN, WM, WN, BPACK>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
+    hipLaunchKernelGGL((mx_tile_deep_kernel<BM, BN, WM, WN, BPACK, SAPACK>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
 }
 
-template void launch_tile_deep<256, 256, 2, 4, false>(const GemmArgs &, int, hipStream_t);
-template void launch_tile_deep<256, 256, 2, 4, true>(const GemmArgs &, int, hipStream_t);
-template void launch_tile_deep<256, 128, 2, 2, false>(const GemmArgs &, int, hipStream_t);
-template void launch_tile_deep<256, 128, 2, 2, true>(const GemmArgs &, int, hipStream_t);
-template void launch_tile_deep<128, 128, 2, 2, false>(const GemmArgs &, int, hipStream_t);
-template void launch_tile_deep<128, 128, 2, 2, true>(const GemmArgs &, int, hipStream_t);
-template void launch_tile_deep<64, 64, 2, 2, false>(const GemmArgs &, int, hipStream_t);
-template void launch_tile_deep<64, 64, 2, 2, true>(const GemmArgs &, int, hipStream_t);
+#define MX_DEEP(BM, BN, WM, WN)                                                                   \
+    template void launch_tile_deep<BM, BN, WM, WN, false, false>(const GemmArgs &, int, hipStream_t); \
+    template void launch_tile_deep<BM, BN, WM, WN, true, false>(const GemmArgs &, int, hipStream_t);  \
+    template void launch_tile_deep<BM, BN, WM, WN, true, true>(const GemmArgs &, int, hipStream_t);
+MX_DEEP(256, 256, 2, 4)
+MX_DEEP(256, 128, 2, 2)
+MX_DEEP(128, 128, 2, 2)
+MX_DEEP(64, 64, 2, 2)
+#undef MX_DEEP
 
 }  // namespace mx

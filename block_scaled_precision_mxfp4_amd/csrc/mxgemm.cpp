@@ -324,6 +324,7 @@ mxgemm_status mxgemm_plan(int M, int N, int K, int b_packed, int split_k, int nu
     out->workspace_bytes = p.ws_bytes;
     out->packed_b_bytes = packed_b_bytes(N, K);
     out->packed_sb_bytes = packed_sb_bytes(N, K);
+    out->packed_sa_bytes = packed_sb_bytes(M, K);
     out->num_cu = num_cu;
     std::snprintf(out->kernel_name, sizeof out->kernel_name, "%s", p.name);
     return MXGEMM_OK;
@@ -366,7 +367,8 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     mxgemm_strides s;
     if (strides) {
         s = *strides;
-        if (s.reserved != 0 || (s.b_packed != 0 && s.b_packed != 1))
+        if ((s.b_packed != 0 && s.b_packed != 1) || (s.sa_packed != 0 && s.sa_packed != 1) ||
+            (s.sa_packed && !s.b_packed))
             return MXGEMM_ERR_INVALID_ARG;
     } else {
         std::memset(&s, 0, sizeof s);
@@ -375,7 +377,7 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
         s.ldsa = s.ldsb = K / 32;
     }
     const int KB = K / 32;
-    if (s.ldd < N || s.lda < K || s.ldsa < KB || (beta != 0.0f && s.ldc < N))
+    if (s.ldd < N || s.lda < K || (!s.sa_packed && s.ldsa < KB) || (beta != 0.0f && s.ldc < N))
         return MXGEMM_ERR_SHAPE;
     if (!s.b_packed && (s.ldb < K || s.ldsb < KB))
         return MXGEMM_ERR_SHAPE;
@@ -383,7 +385,7 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
         return MXGEMM_ERR_ALIGN;
     if (!aligned(A, 16) || !aligned(B, 16) || (s.lda / 2) % 16 || (!s.b_packed && (s.ldb / 2) % 16))
         return MXGEMM_ERR_ALIGN;
-    if (s.b_packed && !aligned(scaleB, 4))
+    if ((s.b_packed && !aligned(scaleB, 4)) || (s.sa_packed && !aligned(scaleA, 4)))
         return MXGEMM_ERR_ALIGN;
     if (!aligned(D, 2) || (C && beta != 0.0f && !aligned(C, 2)))
         return MXGEMM_ERR_ALIGN;
@@ -450,7 +452,7 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
         const mx::TileKernel &k = mx::tile_kernels(&n)[p.index];
         // the four-slot ring kernel moves scales as 4-byte words and whole
         // 128-K steps; otherwise the two-stage kernel handles any layout
-        const bool deep_ok = KB % 4 == 0 && aligned(scaleA, 4) && s.ldsa % 4 == 0 &&
+        const bool deep_ok = KB % 4 == 0 && (s.sa_packed || (aligned(scaleA, 4) && s.ldsa % 4 == 0)) &&
                              (s.b_packed || (aligned(scaleB, 4) && s.ldsb % 4 == 0));
         bool deep = deep_ok && k.prefer_deep;
         if (const char *e = std::getenv("MXGEMM_TILE_PIPELINE")) {  // "deep" or "two-stage"
@@ -460,13 +462,13 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
                 deep = deep_ok;
         }
         if (deep)
-            (s.b_packed ? k.deep_packed : k.deep_plain)(g, (int)p.grid, stream);
+            (s.sa_packed ? k.deep_packed_sa : s.b_packed ? k.deep_packed : k.deep_plain)(g, (int)p.grid, stream);
         else
-            (s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
+            (s.sa_packed ? k.packed_sa : s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
     } else {
         int n = 0;
         const mx::SkinnyKernel &k = mx::skinny_kernels(&n)[p.index];
-        (s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
+        (s.sa_packed ? k.packed_sa : s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
     }
     if (hipGetLastError() != hipSuccess)
         return MXGEMM_ERR_HIP;
@@ -491,6 +493,27 @@ mxgemm_status mxgemm_pack_b(void *Bp, void *SBp, const void *B, const void *scal
         return st;
     mx::launch_pack_b((uint8_t *)Bp, (const uint8_t *)B, N, K / 32, ldb / 2, stream);
     mx::launch_pack_sb((uint32_t *)SBp, (const uint8_t *)scaleB, N, K / 32, ldsb, stream);
+    if (hipGetLastError() != hipSuccess)
+        return MXGEMM_ERR_HIP;
+    return MXGEMM_OK;
+}
+
+mxgemm_status mxgemm_pack_scales(void *Sp, const void *S, int rows, int K, int64_t lds, hipStream_t stream)
+{
+    if (!Sp || !S)
+        return MXGEMM_ERR_INVALID_ARG;
+    mxgemm_status st = check_shape(rows, 1, K);
+    if (st != MXGEMM_OK)
+        return st;
+    if (lds < K / 32)
+        return MXGEMM_ERR_SHAPE;
+    if (!aligned(Sp, 4))
+        return MXGEMM_ERR_ALIGN;
+    DeviceInfo *d = nullptr;
+    st = device_info(&d);
+    if (st != MXGEMM_OK)
+        return st;
+    mx::launch_pack_sb((uint32_t *)Sp, (const uint8_t *)S, rows, K / 32, lds, stream);
     if (hipGetLastError() != hipSuccess)
         return MXGEMM_ERR_HIP;
     return MXGEMM_OK;

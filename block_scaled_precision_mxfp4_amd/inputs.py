@@ -113,18 +113,19 @@ def gaussian_bf16(seed: int, rows: int, cols: int, sigma: float) -> np.ndarray:
 
 # The five workloads.  Sizes, code and exponent distributions, alpha, beta
 # and C follow the statement of each case; `b_packed` marks the case that is
-# run on the pre-shuffled B layout.
+# run on the pre-shuffled B layout and `sa_packed` the one whose A scales are
+# shuffled too (the operand set of the pages' pre-shuffled kernels).
 WORKLOADS = {
     "tiny_128x256x512": dict(index=0, M=128, N=256, K=512, dist="uniform", e=(123, 131),
-                             alpha=1.0, beta=0.0, c_sigma=None, b_packed=False),
+                             alpha=1.0, beta=0.0, c_sigma=None, b_packed=False, sa_packed=False),
     "mid_512x1024x2048": dict(index=1, M=512, N=1024, K=2048, dist="uniform", e=(123, 131),
-                              alpha=1.0, beta=1.0, c_sigma=1.0, b_packed=False),
+                              alpha=1.0, beta=1.0, c_sigma=1.0, b_packed=False, sa_packed=False),
     "gemv_1x8192x8192": dict(index=2, M=1, N=8192, K=8192, dist="uniform", e=(120, 134),
-                             alpha=0.5, beta=0.0, c_sigma=None, b_packed=False),
+                             alpha=0.5, beta=0.0, c_sigma=None, b_packed=False, sa_packed=False),
     "square_8192": dict(index=3, M=8192, N=8192, K=8192, dist="uniform", e=(123, 131),
-                        alpha=1.0, beta=0.0, c_sigma=None, b_packed=True),
+                        alpha=1.0, beta=0.0, c_sigma=None, b_packed=True, sa_packed=True),
     "skinny_64x7168x16384": dict(index=4, M=64, N=7168, K=16384, dist="half_zero", e=(110, 140),
-                                 alpha=1.0, beta=1.0, c_sigma=2.0, b_packed=False),
+                                 alpha=1.0, beta=1.0, c_sigma=2.0, b_packed=False, sa_packed=False),
 }
 
 
@@ -151,4 +152,5 @@ def make_workload(name: str) -> dict:
                      e=w["e"], alpha=w["alpha"], beta=w["beta"], c_sigma=w["c_sigma"])
     p["name"] = name
     p["b_packed"] = w["b_packed"]
+    p["sa_packed"] = w["sa_packed"]
     return p

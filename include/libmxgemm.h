@@ -65,6 +65,11 @@ const char *mxgemm_status_string(mxgemm_status status);
  * dense rows: ldd = ldc = N, lda = ldb = K, ldsa = ldsb = K/32, b_packed = 0,
  * library-owned workspace.
  *
+ * The fully packed form (b_packed = sa_packed = 1: pre-shuffled B, shuffled
+ * scaleA and scaleB, row-major A) is the operand set of the asm_f4gemm
+ * README's pre-shuffled kernels ("Data layouts") and the fastest one: the
+ * kernels read every shuffled scale word with contiguous loads.
+ *
  * Units follow the asm_f4gemm README ("Kernel ABI", kernarg notes): A and B
  * strides count fp4 ELEMENTS (twice the byte pitch) and must be even; scale
  * strides count bytes; C and D strides count bf16 elements.  ldc and ldd are
@@ -78,7 +83,8 @@ typedef struct mxgemm_strides {
     int64_t ldsa;     /* bytes between rows of scaleA, >= K/32 */
     int64_t ldsb;     /* bytes between rows of scaleB, >= K/32 (ignored if b_packed) */
     int32_t b_packed; /* 0: B, scaleB row-major as above; 1: outputs of mxgemm_pack_b */
-    int32_t reserved; /* must be 0 */
+    int32_t sa_packed; /* 0: scaleA row-major as above; 1: output of mxgemm_pack_scales
+                          for the M rows of A (ldsa ignored; needs b_packed = 1) */
     void *workspace;  /* optional device buffer for split-K partials; NULL = library-owned */
     size_t workspace_bytes;
 } mxgemm_strides;
@@ -151,6 +157,18 @@ mxgemm_status mxgemm_pack_b(void *Bp, void *SBp, const void *B, const void *scal
                             int N, int K, int64_t ldb, int64_t ldsb,
                             hipStream_t stream);
 
+/*
+ * Shuffle a [rows][K/32] E8M0 scale matrix (row pitch lds bytes) into the
+ * layout of the asm_f4gemm README's "A_scale / B_scale" part of "Data
+ * layouts" -- the same transform mxgemm_pack_b applies to scaleB -- for use
+ * as scaleA with sa_packed = 1 (rows = M).  Sp is a caller buffer of
+ * ceil(rows/32)*32 * ceil(K/256)*8 bytes (mxgemm_info.packed_sa_bytes for
+ * rows = M), 4-byte aligned, not overlapping S; padding bytes are 0x7F.
+ * Shape rules as mxgemm_run with rows in place of M.
+ */
+mxgemm_status mxgemm_pack_scales(void *Sp, const void *S, int rows, int K, int64_t lds,
+                                 hipStream_t stream);
+
 /* ---- plan / query ------------------------------------------------------------- */
 
 typedef struct mxgemm_info {
@@ -161,6 +179,7 @@ typedef struct mxgemm_info {
     size_t workspace_bytes;  /* split-K fp32 partials workspace needed (0 if split_k == 1) */
     size_t packed_b_bytes;   /* size of mxgemm_pack_b's Bp for this N, K */
     size_t packed_sb_bytes;  /* size of mxgemm_pack_b's SBp for this N, K */
+    size_t packed_sa_bytes;  /* size of mxgemm_pack_scales' output for the M rows of scaleA */
     int32_t num_cu;          /* compute units the plan assumed */
     int32_t reserved;
     char kernel_name[64];

@@ -36,9 +36,11 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def gemm_gpu(p: dict, split_k: int = -1, b_packed: bool = False, D=None, stream=None):
+def gemm_gpu(p: dict, split_k: int = -1, b_packed: bool = False, D=None, stream=None, sa_packed: bool = False):
     """Run D = bf16(alpha A B^T + beta C) on the GPU for problem p (dense
-    strides).  Returns the bf16 bits of D as numpy uint16 [M, N]."""
+    strides; b_packed: B and its scales pre-shuffled by mxgemm_pack_b;
+    sa_packed: A's scales too, by mxgemm_pack_scales).  Returns the bf16
+    bits of D as numpy uint16 [M, N]."""
     M, N, K = p["M"], p["N"], p["K"]
     A, B, SA, SB = dev_u8(p["A"]), dev_u8(p["B"]), dev_u8(p["SA"]), dev_u8(p["SB"])
     C = dev_bf16(p["C"]) if p.get("C") is not None else None
@@ -51,7 +53,12 @@ def gemm_gpu(p: dict, split_k: int = -1, b_packed: bool = False, D=None, stream=
         SBp = torch.empty(info["packed_sb_bytes"], dtype=torch.uint8, device="cuda")
         mx.mxgemm_pack_b(Bp, SBp, B, SB, N, K)
         B, SB = Bp, SBp
-        strides = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32, b_packed=1)
+        if sa_packed:
+            SAp = torch.empty(info["packed_sa_bytes"], dtype=torch.uint8, device="cuda")
+            mx.mxgemm_pack_scales(SAp, SA, M, K)
+            SA = SAp
+        strides = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32, b_packed=1,
+                                  sa_packed=int(sa_packed))
     mx.mxgemm_run(D, C if p["beta"] != 0.0 else None, A, B, SA, SB, p["alpha"], p["beta"], M, N, K,
                   strides=strides, split_k=split_k, stream=stream)
     torch.cuda.synchronize()

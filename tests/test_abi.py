@@ -82,8 +82,13 @@ def test_run_stride_validation():
     assert _run(strides=st(lda=528)) == -3      # 264-byte pitch: not a multiple of 16
     assert _run(strides=st(ldb=528)) == -3
     s = st()
-    s.reserved = 1
+    s.sa_packed = 2
     assert _run(strides=s) == -1
+    s = st()
+    s.sa_packed = 1  # packed A scales come with packed B only
+    assert _run(strides=s) == -1
+    # packed A scales: ldsa is ignored, scaleA must be 4-byte aligned
+    assert _run(strides=st(ldsa=0, ldb=0, ldsb=0, b_packed=1, sa_packed=1), scaleA=0x4002) == -3
     s = st()
     s.b_packed = 2
     assert _run(strides=s) == -1
@@ -97,6 +102,14 @@ def test_pack_validation_before_any_hip_call():
     assert f(Bp=None) == -1 and f(SBp=None) == -1 and f(B=None) == -1 and f(scaleB=None) == -1
     assert f(N=0) == -2 and f(K=40) == -2 and f(ldb=128) == -2 and f(ldsb=4) == -2
     assert f(Bp=0x1008) == -3 and f(SBp=0x2002) == -3 and f(B=0x3008) == -3 and f(ldb=272) == -3
+
+
+def test_pack_scales_validation_before_any_hip_call():
+    f = lambda **kw: mx.mxgemm_pack_scales(**dict(dict(Sp=0x1000, S=0x2000, rows=64, K=256, stream=0), **kw),
+                                           check=False)
+    assert f(Sp=None) == -1 and f(S=None) == -1
+    assert f(rows=0) == -2 and f(K=40) == -2 and f(lds=4) == -2
+    assert f(Sp=0x1002) == -3
 
 
 def test_query_and_plan_argument_errors():

@@ -1,4 +1,4 @@
-"""mxgemm_pack_b on the GPU against the byte permutations the asm_f4gemm
+"""mxgemm_pack_b and mxgemm_pack_scales on the GPU against the byte permutations the asm_f4gemm
 README prints ("Data layouts": the 16x16 tile-transposed B shuffle and the
 scale shuffle), written here with numpy reshapes exactly as stated there,
 on padded inputs (N to 16 / 32 rows, K to 128 elements / 8 scale blocks;
@@ -61,3 +61,18 @@ def test_pack_honours_row_strides():
     torch.cuda.synchronize()
     assert np.array_equal(Bp.cpu().numpy(), page_b_shuffle(p["B"], N, K))
     assert np.array_equal(SBp.cpu().numpy(), page_scale_shuffle(p["SB"], N, K // 32))
+
+
+@pytest.mark.parametrize("rows,K,lds_extra", [(1, 32, 0), (64, 4096, 0), (257, 1056, 5), (8192, 8192, 0)])
+def test_pack_scales_matches_page_formula(rows, K, lds_extra):
+    """mxgemm_pack_scales (A scales for sa_packed = 1) is the same scale
+    shuffle, for any row count and row pitch."""
+    p = inputs.make_problem(rows, 1, K, seed=0x9AE + rows)
+    lds = K // 32 + lds_extra
+    Ss = np.full((rows, lds), 0xFF, dtype=np.uint8)
+    Ss[:, : K // 32] = p["SA"]
+    info = mx.mxgemm_plan(rows, 1, K, 1, -1, 256)
+    SAp = torch.full((info["packed_sa_bytes"],), 0xEE, dtype=torch.uint8, device="cuda")
+    mx.mxgemm_pack_scales(SAp, dev_u8(Ss), rows, K, lds=lds)
+    torch.cuda.synchronize()
+    assert np.array_equal(SAp.cpu().numpy(), page_scale_shuffle(p["SA"], rows, K // 32))

@@ -46,8 +46,8 @@ def _sample_rows_cols(M, N, seed, n=24):
 def test_workload_parity(name):
     p = inputs.make_workload(name)
     M, N, K = p["M"], p["N"], p["K"]
-    say("case", name, "M N K", M, N, K, "packed", p["b_packed"], "seed", hex(p["seed"]))
-    d = gemm_gpu(p, split_k=-1, b_packed=p["b_packed"])
+    say("case", name, "M N K", M, N, K, "packed", p["b_packed"], p["sa_packed"], "seed", hex(p["seed"]))
+    d = gemm_gpu(p, split_k=-1, b_packed=p["b_packed"], sa_packed=p["sa_packed"])
     if M * N * K <= 8 * 2 ** 30:
         ref, mag, _ = oracle_ref(p)
         rel = assert_parity(d, ref, mag, name)
@@ -91,6 +91,8 @@ def test_packed_b_matches_plain_b(shape):
     d_plain = gemm_gpu(p, split_k=1)
     d_packed = gemm_gpu(p, split_k=1, b_packed=True)
     assert np.array_equal(d_plain, d_packed)
+    d_full = gemm_gpu(p, split_k=1, b_packed=True, sa_packed=True)
+    assert np.array_equal(d_plain, d_full)
     ref, mag, _ = oracle_ref(p)
     assert_parity(d_packed, ref, mag, "packed")
 
@@ -109,6 +111,9 @@ def test_split_counters_survive_plan_changes():
         assert_parity(d, ref, mag, "sequence %s" % ((M, N, K, s),))
 
 
+# (B and its scales packed, A scales packed)
+PACK_MODES = [(False, False), (True, False), (True, True)]
+
 EDGE_SHAPES = [
     (1, 1, 32), (1, 17, 96), (2, 5, 64), (15, 31, 160), (16, 16, 128), (17, 33, 288),
     (63, 100, 4128), (64, 4096, 2048), (65, 257, 544), (127, 129, 1056), (129, 130, 288),
@@ -122,10 +127,10 @@ def test_edge_shapes(shape):
     p = inputs.make_problem(M, N, K, seed=0xED6E + M * 7 + N, e=(118, 136), beta=1.0, c_sigma=1.0)
     p["alpha"], p["beta"] = -1.25, 0.5
     ref, mag, _ = oracle_ref(p)
-    for packed in (False, True):
-        say("case edge", shape, "packed", packed)
-        d = gemm_gpu(p, b_packed=packed)
-        assert_parity(d, ref, mag, "edge %s packed=%s" % (shape, packed))
+    for packed, sa_packed in PACK_MODES:
+        say("case edge", shape, "packed", packed, sa_packed)
+        d = gemm_gpu(p, b_packed=packed, sa_packed=sa_packed)
+        assert_parity(d, ref, mag, "edge %s packed=%s,%s" % (shape, packed, sa_packed))
 
 
 def test_identity_gives_A():
@@ -229,13 +234,14 @@ def test_tile_pipelines_agree(shape, monkeypatch):
     ref, mag, _ = oracle_ref(p)
     for tile in range(4):
         monkeypatch.setenv("MXGEMM_FORCE_TILE", str(tile))
-        for packed in (False, True):
+        for packed, sa_packed in PACK_MODES:
             for s in ((1, 2, 4) if tile == 0 else (1, 4)):
-                say("case pipelines", shape, "tile", tile, "packed", packed, "split", s)
+                say("case pipelines", shape, "tile", tile, "packed", packed, sa_packed, "split", s)
                 monkeypatch.setenv("MXGEMM_TILE_PIPELINE", "deep")
-                d_deep = gemm_gpu(p, split_k=s, b_packed=packed)
+                d_deep = gemm_gpu(p, split_k=s, b_packed=packed, sa_packed=sa_packed)
                 monkeypatch.setenv("MXGEMM_TILE_PIPELINE", "two-stage")
-                d_two = gemm_gpu(p, split_k=s, b_packed=packed)
+                d_two = gemm_gpu(p, split_k=s, b_packed=packed, sa_packed=sa_packed)
                 monkeypatch.delenv("MXGEMM_TILE_PIPELINE", raising=False)
-                assert_parity(d_deep, ref, mag, "deep %s tile %d packed=%s split=%d" % (shape, tile, packed, s))
+                assert_parity(d_deep, ref, mag, "deep %s tile %d packed=%s,%s split=%d"
+                              % (shape, tile, packed, sa_packed, s))
                 assert np.array_equal(d_deep, d_two)
