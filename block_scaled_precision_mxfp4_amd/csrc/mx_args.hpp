@@ -31,6 +31,7 @@ struct GemmArgs {
     int sa_fast, sb_fast; // scale rows allow aligned 8-byte loads (tiled kernel)
     int scale16;          // both scale operands allow aligned 16-byte row groups (skinny kernel)
     int d_vec, c_vec;     // 8-byte D stores / C loads allowed
+    int d_stage;          // beta == 0, D 16-byte aligned, ldd % 8 == 0: LDS-staged epilogue
     int group_m;          // tile-order grouping along M
 };
 

@@ -126,6 +126,53 @@ struct Epilogue {
     int c_vec;  // C rows and base allow 8-byte loads
 };
 
+// Epilogue for beta == 0 through a private LDS region of the wave
+// (16*FM x 16*FN bf16, 16-byte chunks of a row XOR-swizzled by the row
+// index): the fragments are rounded and written to LDS in their own layout,
+// then read back row-wise and written to D with 16-byte stores, each
+// instruction covering whole 16*FN-column row segments (full 128-byte lines
+// for FN = 4) instead of 32-byte pieces of 16 rows.  Same values as
+// store_quad: one rounding of alpha*acc per element.  Needs D 16-byte
+// aligned and ldd a multiple of 8; the wave must own `lds` exclusively.
+template <int FM, int FN>
+__device__ __forceinline__ void store_tile_staged(const Epilogue &ep, int m_base, int n_base,
+                                                  const v4f (&acc)[FN][FM], uint8_t *lds)
+{
+    constexpr int RB = FN * 32;       // bytes per row of the wave tile
+    constexpr int CH = RB / 16;       // 16-byte chunks per row (power of two)
+    constexpr int RPI = 64 / CH;      // rows per copy-out instruction
+    static_assert(CH == 2 || CH == 4 || CH == 8, "row chunking");
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int r = fm * 16 + (lane & 15);
+            const int j = fn * 2 + (lane >> 5);
+            v2u o;
+            o[0] = bf16_rne(ep.alpha * acc[fn][fm][0]) | (bf16_rne(ep.alpha * acc[fn][fm][1]) << 16);
+            o[1] = bf16_rne(ep.alpha * acc[fn][fm][2]) | (bf16_rne(ep.alpha * acc[fn][fm][3]) << 16);
+            *reinterpret_cast<v2u *>(lds + r * RB + ((j ^ (r & (CH - 1))) * 16) + ((lane >> 4) & 1) * 8) = o;
+        }
+#pragma unroll
+    for (int i = 0; i < FM * 16 / RPI; ++i) {
+        const int r = i * RPI + lane / CH, c = lane & (CH - 1);
+        const v4i v = *reinterpret_cast<const v4i *>(lds + r * RB + ((c ^ (r & (CH - 1))) * 16));
+        const int m = m_base + r, n = n_base + c * 8;
+        if (m >= ep.M || n >= ep.N)
+            continue;
+        uint16_t *drow = ep.D + (int64_t)m * ep.ldd + n;
+        if (n + 7 < ep.N) {
+            *reinterpret_cast<v4i *>(drow) = v;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (n + e < ep.N)
+                    drow[e] = (uint16_t)(((uint32_t)v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        }
+    }
+}
+
 // Writes D[m][n..n+3] = bf16(alpha*acc[g] + beta*C[m][n+g]) for the
 // elements inside the matrix.  One rounding per element.
 __device__ __forceinline__ void store_quad(const Epilogue &ep, int m, int n, v4f acc)

@@ -362,6 +362,25 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     const int mb = m0 + wave_m * TM + (lane & 15);
     const int nb = n0 + wave_n * TN + 4 * (lane >> 4);
     if (g.split == 1) {
+        if (g.d_stage) {
+            // every wave has passed the last stage's barrier (after waiting
+            // for its loads): the operand buffers are free; each wave takes
+            // a private TM x TN bf16 region
+            constexpr int REG = TM * TN * 2;
+            constexpr int RPA = A_STAGE / REG, RPB = B_STAGE / REG;
+            static_assert(NW <= 2 * RPA + 2 * RPB, "staging regions fit the operand buffers");
+            uint8_t *buf;
+            if (wave < RPA)
+                buf = s_a0 + wave * REG;
+            else if (wave < 2 * RPA)
+                buf = s_a1 + (wave - RPA) * REG;
+            else if (wave < 2 * RPA + RPB)
+                buf = s_b0 + (wave - 2 * RPA) * REG;
+            else
+                buf = s_b1 + (wave - 2 * RPA - RPB) * REG;
+            store_tile_staged<FM, FN>(ep, m0 + wave_m * TM, n0 + wave_n * TN, acc, buf);
+            return;
+        }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
 #pragma unroll

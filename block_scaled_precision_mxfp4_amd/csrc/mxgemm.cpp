@@ -432,6 +432,7 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
                 (s.b_packed || (aligned(scaleB, 16) && s.ldsb % 16 == 0));
     g.d_vec = aligned(D, 8) && s.ldd % 4 == 0;
     g.c_vec = C && aligned(C, 8) && s.ldc % 4 == 0;
+    g.d_stage = beta == 0.0f && aligned(D, 16) && s.ldd % 8 == 0;
     g.group_m = 4;
 
     if (p.split > 1) {
