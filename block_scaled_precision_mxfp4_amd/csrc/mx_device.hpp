@@ -47,6 +47,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                              kRsrcWord3);
 }
 
+// make_rsrc for values the compiler cannot prove wave-uniform (e.g. after an
+// integer division, which is computed in vector registers): without the
+// explicit read-first-lane every buffer access through the descriptor
+// becomes a loop over the distinct descriptors of the lanes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_u(const void *base, uint32_t bytes)
+{
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    return make_rsrc((const void *)(uintptr_t)(((uint64_t)hi << 32) | lo), n);
+}
+
 __device__ __forceinline__ v4i load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);

@@ -19,38 +19,56 @@
 
 namespace mx {
 
-// Scale bytes of 4 consecutive 128-K steps for one lane, packed into one
-// register: byte u is the scale of step u, so op_sel = u picks it.  The lane's
+// Scale bytes of 4 consecutive 128-K steps for one lane.  The lane's
 // K-block within a step is lane/16; a row's 16 scale bytes for the 4 steps
-// are contiguous.  SVEC: one aligned 16-byte load per row (pitch and K-block
-// count multiples of 16, so a group is entirely inside or outside the chunk);
-// otherwise byte loads, blocks at or past kb_end reading as zero.
+// are contiguous.  The load and the packing into a register are separate
+// steps: the packing (byte u = scale of step u, so op_sel = u picks it) runs
+// only when the multiplies need the word, so waiting for the scale load never
+// holds up the operand loads issued after it.  SVEC: one aligned 16-byte
+// load per row (pitch and K-block count multiples of 16, so a group is
+// entirely inside or outside the chunk); otherwise byte loads, blocks at or
+// past kb_end reading as zero.
 template <bool SVEC>
-__device__ __forceinline__ uint32_t load_scale_group(__amdgpu_buffer_rsrc_t r, int64_t ld, int row, int kb0,
-                                                     int kb_end, int lane)
+__device__ __forceinline__ v4i load_scale_raw(__amdgpu_buffer_rsrc_t r, int64_t ld, int row, int kb0, int kb_end,
+                                              int lane)
 {
-    const int j = lane >> 4;
     if constexpr (SVEC) {
-        const v4i w = load16(r, kb0 < kb_end ? (uint32_t)(row * ld + kb0) : kOOB);
-        uint32_t out = 0;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            out |= (((uint32_t)w[u] >> (8 * j)) & 0xFFu) << (8 * u);
-        return out;
+        return load16(r, kb0 < kb_end ? (uint32_t)(row * ld + kb0) : kOOB);
     } else {
-        uint32_t out = 0;
+        const int j = lane >> 4;
+        v4i w;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int kb = kb0 + 4 * u + j;
-            out |= load1(r, kb < kb_end ? (uint32_t)(row * ld + kb) : kOOB) << (8 * u);
+            w[u] = (int)load1(r, kb < kb_end ? (uint32_t)(row * ld + kb) : kOOB);
         }
-        return out;
+        return w;
     }
 }
 
-template <int MG, int NR, bool BPACK, bool SVEC, bool APACK>
+template <bool SVEC>
+__device__ __forceinline__ uint32_t scale_group_word(v4i w, int lane)
+{
+    const int j = lane >> 4;
+    uint32_t out = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t b = SVEC ? (((uint32_t)w[u] >> (8 * j)) & 0xFFu) : ((uint32_t)w[u] & 0xFFu);
+        out |= b << (8 * u);
+    }
+    return out;
+}
+
+// A1: A is a single row (M == 1, row-major scales).  Each wave then loads
+// the row's K-blocks of a whole batch with one instruction (lane l: K-block
+// l of the batch, with its scale byte) instead of one mostly-empty fragment
+// load per step, and forms each step's operand with cross-lane permutes:
+// operand lane l takes K-block 4u + l/16 of step u.  Operand lanes of rows
+// 1..15 then carry row 0's values too; their result rows are never stored.
+template <int MG, int NR, bool BPACK, bool SVEC, bool APACK, bool A1>
 __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
 {
+    static_assert(!A1 || (MG == 1 && !APACK), "single-row A: one row group, row-major scales");
     constexpr int R = 16 * NR;                      // B rows per workgroup
     constexpr int NF = NR * MG;                     // 16x16 result blocks per workgroup
     constexpr int U = (NR + MG) <= 3 ? 8 : 4;       // 128-K steps per batch (two batches in flight)
@@ -74,28 +92,34 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
     const int w_end = min(ks_end, w_begin + q);
     const int kb_wend = min(kb_end, w_end * 4);  // K-blocks this wave may touch
 
-    const auto ra = make_rsrc(g.A, (uint32_t)(g.M * g.lda_b));
-    const auto rsa = APACK ? make_rsrc(g.SA, (uint32_t)((g.M + 31) / 32 * g.sn8 * 256))
-                           : make_rsrc(g.SA, (uint32_t)(g.M * g.ldsa));
+    const auto ra = make_rsrc_u(g.A, (uint32_t)(g.M * g.lda_b));
+    const auto rsa = APACK ? make_rsrc_u(g.SA, (uint32_t)((g.M + 31) / 32 * g.sn8 * 256))
+                           : make_rsrc_u(g.SA, (uint32_t)(g.M * g.ldsa));
     __amdgpu_buffer_rsrc_t rb, rsb;
     int half0 = 0;  // packed scales: which 16-row half of its 32-row group row n0 is
     if constexpr (BPACK) {
         const int n16 = n0 / 16, g16 = max(0, min(NR, (g.N + 15) / 16 - n16));
-        rb = make_rsrc(g.B + (int64_t)n16 * g.ks_total * 1024, (uint32_t)(g16 * g.ks_total * 1024));
+        rb = make_rsrc_u(g.B + (int64_t)n16 * g.ks_total * 1024, (uint32_t)(g16 * g.ks_total * 1024));
         const int n32 = n0 / 32;
         const int g32 = max(0, min((n0 + R + 31) / 32 - n32, (g.N + 31) / 32 - n32));
-        rsb = make_rsrc(g.SB + (int64_t)n32 * g.sn8 * 256, (uint32_t)(g32 * g.sn8 * 256));
+        rsb = make_rsrc_u(g.SB + (int64_t)n32 * g.sn8 * 256, (uint32_t)(g32 * g.sn8 * 256));
         half0 = n16 & 1;
     } else {
         const int rows = max(0, min(R, g.N - n0));
-        rb = make_rsrc(g.B + (int64_t)n0 * g.ldb_b, (uint32_t)(rows * g.ldb_b));
-        rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)(rows * g.ldsb));
+        rb = make_rsrc_u(g.B + (int64_t)n0 * g.ldb_b, (uint32_t)(rows * g.ldb_b));
+        rsb = make_rsrc_u(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)(rows * g.ldsb));
     }
 
     struct Batch {
-        v4i b[U][NR], a[U][MG];
-        uint32_t sb[BPACK ? U / 2 : G][NR];  // packed: one word per step pair, else per group
-        uint32_t sa[APACK ? U / 2 : G][MG];
+        v4i b[U][NR], a[A1 ? 1 : U][MG];
+        // scales as loaded: packed, one word per step pair (both row halves);
+        // row-major, one raw 16-byte group per 4 steps
+        uint32_t sbp[BPACK ? U / 2 : 1][NR];
+        v4i sbr[BPACK ? 1 : G][NR];
+        uint32_t sap[APACK ? U / 2 : 1][MG];
+        v4i sar[APACK || A1 ? 1 : G][MG];
+        v4i aw;        // A1: K-block kb0 + lane of row 0
+        uint32_t saw;  // A1: its scale byte
     };
 
     auto load_batch = [&](int ks0, Batch &bt) {
@@ -111,22 +135,30 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
                 else
                     bt.b[u][nr] = load16(rb, ok ? (uint32_t)((nr * 16 + (lane & 15)) * g.ldb_b + kb * 16) : kOOB);
             }
+            if constexpr (!A1) {
 #pragma unroll
-            for (int mg = 0; mg < MG; ++mg)
-                bt.a[u][mg] = load16(ra, ok ? (uint32_t)((mg * 16 + (lane & 15)) * g.lda_b + kb * 16) : kOOB);
+                for (int mg = 0; mg < MG; ++mg)
+                    bt.a[u][mg] = load16(ra, ok ? (uint32_t)((mg * 16 + (lane & 15)) * g.lda_b + kb * 16) : kOOB);
+            }
+        }
+        if constexpr (A1) {
+            const int kbl = ks0 * 4 + lane;
+            const bool okl = lane < 4 * U && kbl < kb_wend;
+            bt.aw = load16(ra, okl ? (uint32_t)(kbl * 16) : kOOB);
+            bt.saw = load1(rsa, okl ? (uint32_t)kbl : kOOB);
         }
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             const int kb0 = (ks0 + 4 * gi) * 4;  // first K-block of the group
-            if constexpr (!APACK) {
+            if constexpr (!APACK && !A1) {
 #pragma unroll
                 for (int mg = 0; mg < MG; ++mg)
-                    bt.sa[gi][mg] = load_scale_group<SVEC>(rsa, g.ldsa, mg * 16 + (lane & 15), kb0, kb_wend, lane);
+                    bt.sar[gi][mg] = load_scale_raw<SVEC>(rsa, g.ldsa, mg * 16 + (lane & 15), kb0, kb_wend, lane);
             }
             if constexpr (!BPACK) {
 #pragma unroll
                 for (int nr = 0; nr < NR; ++nr)
-                    bt.sb[gi][nr] = load_scale_group<SVEC>(rsb, g.ldsb, nr * 16 + (lane & 15), kb0, kb_wend, lane);
+                    bt.sbr[gi][nr] = load_scale_raw<SVEC>(rsb, g.ldsb, nr * 16 + (lane & 15), kb0, kb_wend, lane);
             }
         }
         if constexpr (APACK) {
@@ -137,7 +169,7 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
                 for (int mg = 0; mg < MG; ++mg) {
                     const uint32_t w =
                         load4(rsa, ks * 4 < kb_wend ? (uint32_t)((((mg >> 1) * g.sn8 + (ks >> 1)) * 64 + lane) * 4) : kOOB);
-                    bt.sa[p][mg] = w >> (8 * (mg & 1));  // this row half's bytes at 0 and 2
+                    bt.sap[p][mg] = w;
                 }
             }
         }
@@ -147,10 +179,10 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
                 const int ks = ks0 + 2 * p;  // even: the word holds steps ks, ks+1 x both row halves
 #pragma unroll
                 for (int nr = 0; nr < NR; ++nr) {
-                    const int grp = (half0 + nr) >> 1, half = (half0 + nr) & 1;
+                    const int grp = (half0 + nr) >> 1;
                     const uint32_t w =
                         load4(rsb, ks * 4 < kb_wend ? (uint32_t)(((grp * g.sn8 + (ks >> 1)) * 64 + lane) * 4) : kOOB);
-                    bt.sb[p][nr] = w >> (8 * half);  // this row half's bytes at 0 and 2
+                    bt.sbp[p][nr] = w;
                 }
             }
         }
@@ -165,27 +197,47 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
 
     auto compute = [&](const Batch &bt) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
+            v4i a1;
+            uint32_t sa1 = 0;
+            if constexpr (A1) {
+                const int src = (4 * u + (lane >> 4)) * 4;  // byte address of the source lane
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a1[i] = __builtin_amdgcn_ds_bpermute(src, bt.aw[i]);
+                sa1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)bt.saw) & 0xFFu;
+            }
 #pragma unroll
             for (int nr = 0; nr < NR; ++nr)
 #pragma unroll
                 for (int mg = 0; mg < MG; ++mg) {
+                    // packed words: this row half's bytes shifted to 0 and 2
                     const int ob = BPACK ? (u & 1) * 2 : (u & 3);
-                    const uint32_t sbr = BPACK ? bt.sb[u / 2][nr] : bt.sb[u / 4][nr];
-                    const int oa = APACK ? (u & 1) * 2 : (u & 3);
-                    const uint32_t sar = APACK ? bt.sa[u / 2][mg] : bt.sa[u / 4][mg];
-                    acc[nr][mg] = mma_sel(ob, oa, bt.b[u][nr], bt.a[u][mg], acc[nr][mg], (int)sbr, (int)sar);
+                    const uint32_t sbr = BPACK ? bt.sbp[u / 2][nr] >> (8 * ((half0 + nr) & 1))
+                                               : scale_group_word<SVEC>(bt.sbr[u / 4][nr], lane);
+                    const int oa = A1 ? 0 : APACK ? (u & 1) * 2 : (u & 3);
+                    const uint32_t sar = A1      ? sa1
+                                         : APACK ? bt.sap[u / 2][mg] >> (8 * (mg & 1))
+                                                 : scale_group_word<SVEC>(bt.sar[u / 4][mg], lane);
+                    acc[nr][mg] = mma_sel(ob, oa, bt.b[u][nr], A1 ? a1 : bt.a[u][mg], acc[nr][mg], (int)sbr, (int)sar);
                 }
+        }
     };
 
     // two batches in flight: issue the next before multiplying the current
+    // (scheduling barriers keep each batch's loads ahead of the multiplies
+    // of the previous one; left alone the scheduler sinks them below)
     Batch cur, nxt;
     load_batch(w_begin, cur);
     for (int ks0 = w_begin; ks0 < w_end; ks0 += 2 * U) {
         load_batch(ks0 + U, nxt);
+        __builtin_amdgcn_sched_barrier(0);
         compute(cur);
+        __builtin_amdgcn_sched_barrier(0);
         load_batch(ks0 + 2 * U, cur);
+        __builtin_amdgcn_sched_barrier(0);
         compute(nxt);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- the four waves' sums, added in wave order; wave w then owns blocks f = w, w+4, ...
@@ -224,7 +276,7 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
     }
     // fp32 partials of this chunk: [tile][z][block][lane] float4s
     constexpr uint32_t PART = NF * 64 * 16;  // bytes per workgroup partial
-    const auto rws = make_rsrc(g.ws + (size_t)t * g.split * (PART / 4), (uint32_t)(g.split * PART));
+    const auto rws = make_rsrc_u(g.ws + (size_t)t * g.split * (PART / 4), (uint32_t)(g.split * PART));
 #pragma unroll
     for (int i = 0; i < FPW; ++i) {
         const int f = i * 4 + wave;
@@ -253,12 +305,23 @@ static void launch_skinny(const GemmArgs &g, int grid, hipStream_t s)
 {
     // 16-byte scale groups need 16-aligned scale rows and whole 16-block
     // groups (with both scale operands packed no row-major group is read)
-    if (APACK)
-        hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, false, APACK>), dim3(grid), dim3(256), 0, s, g);
-    else if (g.scale16)
-        hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, true, false>), dim3(grid), dim3(256), 0, s, g);
-    else
-        hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, false, false>), dim3(grid), dim3(256), 0, s, g);
+    if constexpr (APACK) {
+        hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, false, true, false>), dim3(grid), dim3(256), 0, s, g);
+    } else {
+        if constexpr (MG == 1) {
+            if (g.M == 1) {
+                if (g.scale16 || BPACK)  // row-major B scales (if any) in 16-byte groups
+                    hipLaunchKernelGGL((mx_skinny_kernel<1, NR, BPACK, true, false, true>), dim3(grid), dim3(256), 0, s, g);
+                else
+                    hipLaunchKernelGGL((mx_skinny_kernel<1, NR, BPACK, false, false, true>), dim3(grid), dim3(256), 0, s, g);
+                return;
+            }
+        }
+        if (g.scale16)
+            hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, true, false, false>), dim3(grid), dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, false, false, false>), dim3(grid), dim3(256), 0, s, g);
+    }
 }
 
 #define MX_SKINNY(MG, NR)                                                                           \

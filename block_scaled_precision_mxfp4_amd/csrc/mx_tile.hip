@@ -390,7 +390,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     }
     // fp32 partial tile of this K chunk: [tile][z][wave][fn][fm][lane] float4s
     constexpr uint32_t PART = BM * BN * 4;  // bytes per partial tile
-    const auto rws = make_rsrc(g.ws + (size_t)t * g.split * (BM * BN), (uint32_t)(g.split * PART));
+    const auto rws = make_rsrc_u(g.ws + (size_t)t * g.split * (BM * BN), (uint32_t)(g.split * PART));
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll

@@ -301,7 +301,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
         return;
     }
     constexpr uint32_t PART = BM * BN * 4;
-    const auto rws = make_rsrc(g.ws + (size_t)t * g.split * (BM * BN), (uint32_t)(g.split * PART));
+    const auto rws = make_rsrc_u(g.ws + (size_t)t * g.split * (BM * BN), (uint32_t)(g.split * PART));
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
