@@ -78,7 +78,10 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    const int lg = xcd_remap(blockIdx.x, gridDim.x);
+    // no XCD regrouping here: workgroups share no B, and spreading each XCD's
+    // streams over the whole matrix (consecutive workgroups on different
+    // XCDs) measured faster than giving each XCD one contiguous part
+    const int lg = blockIdx.x;
     const int z = lg / g.tiles_n;
     const int t = lg - z * g.tiles_n;
     const int n0 = t * R;  // first row of B (column of D) of this workgroup
