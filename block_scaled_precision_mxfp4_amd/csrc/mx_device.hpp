@@ -176,7 +176,9 @@ __device__ __forceinline__ void store_tile_staged(const Epilogue &ep, int m_base
             continue;
         uint16_t *drow = ep.D + (int64_t)m * ep.ldd + n;
         if (n + 7 < ep.N) {
-            *reinterpret_cast<v4i *>(drow) = v;
+            // D is written once and not read back here: streaming stores keep
+            // it from displacing operand lines in L2
+            __builtin_nontemporal_store(v, reinterpret_cast<v4i *>(drow));
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)

@@ -16,6 +16,7 @@
 // last workgroup to arrive, in the same launch.
 #include "mx_args.hpp"
 #include "mx_device.hpp"
+#include "mx_pipe.hpp"
 
 namespace mx {
 
@@ -74,6 +75,16 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
     constexpr int U = (NR + MG) <= 3 ? 8 : 4;       // 128-K steps per batch (two batches in flight)
     constexpr int G = U / 4;                        // scale groups (4 steps) per batch
     __shared__ v4f s_red[4][NF][64];
+    // Row-major B with a single-row A: B goes through a wave-private LDS
+    // buffer per batch so that every load instruction covers whole 128-byte
+    // lines (a row's U*64 bytes of the batch, RPI rows per instruction) instead of
+    // 64-byte halves of 16 rows; 16-byte chunk c of row r sits at slot
+    // c ^ (r % 16), so a fragment's 16 rows hit 16 different bank groups.
+    constexpr bool BST = A1 && !BPACK;
+    constexpr int CPR = U * 4;  // 16-byte chunks per row per batch
+    constexpr int BST_BYTES = BST ? NR * 16 * CPR * 16 : 16;
+    __shared__ __attribute__((aligned(1024))) uint8_t s_bst0[4][BST_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_bst1[4][BST_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -125,7 +136,19 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
         uint32_t saw;  // A1: its scale byte
     };
 
-    auto load_batch = [&](int ks0, Batch &bt) {
+    auto load_batch = [&](int ks0, Batch &bt, auto bufc) {
+        if constexpr (BST) {
+            uint8_t *dst = decltype(bufc)::value ? s_bst1[wave] : s_bst0[wave];
+            constexpr int RPI = 64 / CPR;  // rows per 1 KiB instruction
+            const int rl = lane / CPR, sl = lane % CPR;
+#pragma unroll
+            for (int i = 0; i < NR * 16 / RPI; ++i) {
+                const int row = i * RPI + rl;
+                const int kbc = ks0 * 4 + (sl ^ (row & 15));  // the chunk this slot holds
+                load16_to_lds(rb, (lds_void *)(dst + i * 1024),
+                              kbc < kb_wend ? (uint32_t)(row * g.ldb_b + kbc * 16) : kOOB);
+            }
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int ks = ks0 + u;
@@ -133,7 +156,9 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
             const bool ok = kb < kb_wend;
 #pragma unroll
             for (int nr = 0; nr < NR; ++nr) {
-                if constexpr (BPACK)
+                if constexpr (BST)
+                    ;  // staged above
+                else if constexpr (BPACK)
                     bt.b[u][nr] = load16(rb, ok ? (uint32_t)(((nr * g.ks_total + ks) * 64 + lane) * 16) : kOOB);
                 else
                     bt.b[u][nr] = load16(rb, ok ? (uint32_t)((nr * 16 + (lane & 15)) * g.ldb_b + kb * 16) : kOOB);
@@ -198,7 +223,28 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
         for (int mg = 0; mg < MG; ++mg)
             acc[nr][mg] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const Batch &bt) {
+    // vector-memory instructions of one load_batch (all lanes issue all of
+    // them): staged B, the single A row and its scales, row-major B scales
+    constexpr int LN = NR * U + 2 + G * NR * (SVEC ? 1 : 4);
+    static_assert(!BST || LN < 64, "vmcnt range");
+    auto compute = [&](const Batch &bt, auto bufc) {
+        v4i bst[BST ? U : 1][NR];
+        if constexpr (BST) {
+            // this batch's staging loads have landed (the next batch's LN
+            // loads may still be in flight); then all fragment reads at once
+            wait_vmcnt<LN>();
+            const uint32_t base = lds_addr(decltype(bufc)::value ? s_bst1[wave] : s_bst0[wave]) +
+                                  (uint32_t)((lane & 15) * CPR * 16);
+            static_for<U>([&](auto ui) {
+                constexpr int u = decltype(ui)::value;
+                const uint32_t a = base + (uint32_t)((((u * 4) + (lane >> 4)) ^ (lane & 15)) * 16);
+                static_for<NR>([&](auto ni) {
+                    constexpr int nr = decltype(ni)::value;
+                    bst[u][nr] = lds_read16<nr * 16 * CPR * 16>(a);
+                });
+            });
+            lds_wait_n<0>(bst);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             v4i a1;
@@ -222,7 +268,8 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
                     const uint32_t sar = A1      ? sa1
                                          : APACK ? bt.sap[u / 2][mg] >> (8 * (mg & 1))
                                                  : scale_group_word<SVEC>(bt.sar[u / 4][mg], lane);
-                    acc[nr][mg] = mma_sel(ob, oa, bt.b[u][nr], A1 ? a1 : bt.a[u][mg], acc[nr][mg], (int)sbr, (int)sar);
+                    acc[nr][mg] = mma_sel(ob, oa, BST ? bst[BST ? u : 0][nr] : bt.b[u][nr], A1 ? a1 : bt.a[u][mg],
+                                          acc[nr][mg], (int)sbr, (int)sar);
                 }
         }
     };
@@ -230,16 +277,18 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
     // two batches in flight: issue the next before multiplying the current
     // (scheduling barriers keep each batch's loads ahead of the multiplies
     // of the previous one; left alone the scheduler sinks them below)
+    using Buf0 = std::integral_constant<int, 0>;
+    using Buf1 = std::integral_constant<int, 1>;
     Batch cur, nxt;
-    load_batch(w_begin, cur);
+    load_batch(w_begin, cur, Buf0{});
     for (int ks0 = w_begin; ks0 < w_end; ks0 += 2 * U) {
-        load_batch(ks0 + U, nxt);
+        load_batch(ks0 + U, nxt, Buf1{});
         __builtin_amdgcn_sched_barrier(0);
-        compute(cur);
+        compute(cur, Buf0{});
         __builtin_amdgcn_sched_barrier(0);
-        load_batch(ks0 + 2 * U, cur);
+        load_batch(ks0 + 2 * U, cur, Buf0{});
         __builtin_amdgcn_sched_barrier(0);
-        compute(nxt);
+        compute(nxt, Buf1{});
         __builtin_amdgcn_sched_barrier(0);
     }
 
