@@ -32,6 +32,8 @@ struct GemmArgs {
     int scale16;          // both scale operands allow aligned 16-byte row groups (skinny kernel)
     int d_vec, c_vec;     // 8-byte D stores / C loads allowed
     int d_stage;          // beta == 0, D 16-byte aligned, ldd % 8 == 0: LDS-staged epilogue
+    int sa_packed;        // scaleA in the packed scale layout
+    int sa16, sb16;       // row-major scale rows in 16-byte aligned groups of 16 K-blocks
     int group_m;          // tile-order grouping along M
 };
 
@@ -63,6 +65,16 @@ struct SkinnyKernel {
     const char *name;
 };
 const SkinnyKernel *skinny_kernels(int *count);
+
+// Skinny kernel for 16 < M <= 64 with the waves splitting B's rows and A
+// staged once per workgroup in LDS: mg 16-row groups of A, nrw 16-row groups
+// of B per wave, u 128-K steps per batch, ns ring slots.  index: mg - 2.
+struct RowsKernel {
+    int mg, nrw, u, ns;
+    LaunchFn plain, packed;
+    const char *name;
+};
+const RowsKernel *rows_kernels(int *count);
 
 void launch_pack_b(uint8_t *Bp, const uint8_t *B, int N, int KB, int64_t ldb_b, hipStream_t s);
 // Scale shuffle of rows x KB scale bytes (either operand's scales).

@@ -128,6 +128,46 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h)
     return __uint_as_float(h << 16);
 }
 
+// Scale bytes of 4 consecutive 128-K steps for one lane.  The lane's
+// K-block within a step is lane/16; a row's 16 scale bytes for the 4 steps
+// are contiguous.  The load and the packing into a register are separate
+// steps: the packing (byte u = scale of step u, so op_sel = u picks it) runs
+// only when the multiplies need the word, so waiting for the scale load never
+// holds up the operand loads issued after it.  SVEC: one aligned 16-byte
+// load per row (pitch and K-block count multiples of 16, so a group is
+// entirely inside or outside the chunk); otherwise byte loads, blocks at or
+// past kb_end reading as zero.
+template <bool SVEC>
+__device__ __forceinline__ v4i load_scale_raw(__amdgpu_buffer_rsrc_t r, int64_t ld, int row, int kb0, int kb_end,
+                                              int lane)
+{
+    if constexpr (SVEC) {
+        return load16(r, kb0 < kb_end ? (uint32_t)(row * ld + kb0) : kOOB);
+    } else {
+        const int j = lane >> 4;
+        v4i w;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int kb = kb0 + 4 * u + j;
+            w[u] = (int)load1(r, kb < kb_end ? (uint32_t)(row * ld + kb) : kOOB);
+        }
+        return w;
+    }
+}
+
+template <bool SVEC>
+__device__ __forceinline__ uint32_t scale_group_word(v4i w, int lane)
+{
+    const int j = lane >> 4;
+    uint32_t out = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t b = SVEC ? (((uint32_t)w[u] >> (8 * j)) & 0xFFu) : ((uint32_t)w[u] & 0xFFu);
+        out |= b << (8 * u);
+    }
+    return out;
+}
+
 // Epilogue parameters shared by all kernels.
 struct Epilogue {
     uint16_t *D;

@@ -1,4 +1,4 @@
-// Skinny MXFP4 GEMM for M <= 64 (decode / GEMV shapes) on gfx950.
+// Skinny MXFP4 GEMM for M <= 16 (decode / GEMV shapes) on gfx950.
 //
 // Here the whole cost is reading B once from HBM, so the kernel streams B
 // straight from memory into registers (16 bytes per lane, one instruction
@@ -6,7 +6,10 @@
 // keeps the tiny A in the L2.  A workgroup owns 16*NR rows of B (= columns
 // of D) and one K chunk; its four waves take consecutive quarters of that
 // chunk and add their accumulators through LDS in a fixed order.  The
-// accumulators of a wave cover all M <= 16*MG rows of D.  The scaled FP4
+// accumulators of a wave cover all M <= 16*MG rows of D (the table holds
+// MG = 1: for 16 < M <= 64 every wave would re-read all of A for its
+// quarter of K, and the rows kernel, which shares A through LDS, is
+// faster).  The scaled FP4
 // instruction does the arithmetic: rows of A past M are zero lanes
 // (out-of-range loads return zero without memory traffic), which costs
 // nothing here because the matrix unit is far from busy at HBM speed.
@@ -19,46 +22,6 @@
 #include "mx_pipe.hpp"
 
 namespace mx {
-
-// Scale bytes of 4 consecutive 128-K steps for one lane.  The lane's
-// K-block within a step is lane/16; a row's 16 scale bytes for the 4 steps
-// are contiguous.  The load and the packing into a register are separate
-// steps: the packing (byte u = scale of step u, so op_sel = u picks it) runs
-// only when the multiplies need the word, so waiting for the scale load never
-// holds up the operand loads issued after it.  SVEC: one aligned 16-byte
-// load per row (pitch and K-block count multiples of 16, so a group is
-// entirely inside or outside the chunk); otherwise byte loads, blocks at or
-// past kb_end reading as zero.
-template <bool SVEC>
-__device__ __forceinline__ v4i load_scale_raw(__amdgpu_buffer_rsrc_t r, int64_t ld, int row, int kb0, int kb_end,
-                                              int lane)
-{
-    if constexpr (SVEC) {
-        return load16(r, kb0 < kb_end ? (uint32_t)(row * ld + kb0) : kOOB);
-    } else {
-        const int j = lane >> 4;
-        v4i w;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int kb = kb0 + 4 * u + j;
-            w[u] = (int)load1(r, kb < kb_end ? (uint32_t)(row * ld + kb) : kOOB);
-        }
-        return w;
-    }
-}
-
-template <bool SVEC>
-__device__ __forceinline__ uint32_t scale_group_word(v4i w, int lane)
-{
-    const int j = lane >> 4;
-    uint32_t out = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const uint32_t b = SVEC ? (((uint32_t)w[u] >> (8 * j)) & 0xFFu) : ((uint32_t)w[u] & 0xFFu);
-        out |= b << (8 * u);
-    }
-    return out;
-}
 
 // A1: A is a single row (M == 1, row-major scales).  Each wave then loads
 // the row's K-blocks of a whole batch with one instruction (lane l: K-block
@@ -383,9 +346,6 @@ const SkinnyKernel *skinny_kernels(int *count)
 {
     static const SkinnyKernel table[] = {
         MX_SKINNY(1, 1), MX_SKINNY(1, 2), MX_SKINNY(1, 4),
-        MX_SKINNY(2, 1), MX_SKINNY(2, 2), MX_SKINNY(2, 4),
-        MX_SKINNY(3, 1), MX_SKINNY(3, 2), MX_SKINNY(3, 4),
-        MX_SKINNY(4, 1), MX_SKINNY(4, 2), MX_SKINNY(4, 4),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

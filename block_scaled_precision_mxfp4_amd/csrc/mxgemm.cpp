@@ -6,8 +6,9 @@
 // for each tile shape and prefer fewer, larger-tile rounds, iterating
 // candidates in a fixed order so the choice is reproducible), extended with
 // a per-tile cost so that tiles of different sizes and the split-K
-// reduction can be compared, and with the skinny streaming kernel for
-// M <= 64.
+// reduction can be compared, and with the skinny streaming kernels for
+// M <= 16 (waves split K) and 16 < M <= 64 (waves split the rows of B and
+// share A through LDS).
 #include "libmxgemm.h"
 
 #include <hip/hip_runtime.h>
@@ -31,7 +32,7 @@ constexpr int kMaxDevices = 64;
 constexpr int kSplits[] = {1, 2, 4, 8, 16};
 
 struct Plan {
-    int family = 0;  // 0 tiled, 1 skinny
+    int family = 0;  // 0 tiled, 1 skinny (M <= 16), 2 skinny rows (16 < M <= 64)
     int index = 0;   // index into the kernel table of the family
     int bm = 0, bn = 0;
     int split = 1;
@@ -81,19 +82,62 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
 
     auto consider_split = [&](int s) { return split_req <= 0 || s == split_req; };
 
-    int n_tile = 0, n_skinny = 0;
+    int n_tile = 0, n_skinny = 0, n_rows = 0;  // table sizes (the planner indexes them directly)
     const mx::TileKernel *tile = mx::tile_kernels(&n_tile);
     const mx::SkinnyKernel *skinny = mx::skinny_kernels(&n_skinny);
-    if (M <= 64) {
-        // Skinny kernel: a workgroup owns 16*nr rows of B and one K chunk.
-        // nr grows with M so that A (re-read from L2 per row block) stays
-        // below the B bytes streamed from HBM.  Splitting K costs every
-        // split workgroup a serialized tail (partial write-back, counter,
-        // read-back), so the split is the smallest that gives most CUs a
-        // workgroup (measured on MI355X: 1x8192x8192 fastest unsplit,
-        // 64x7168x16384 with nr 4 fastest at split 2).
+    const mx::RowsKernel *rows = mx::rows_kernels(&n_rows);
+    if (M > 16 && M <= 64) {
+        // Rows kernel: the four waves of a workgroup own 4 x 16 rows of B
+        // and share one K chunk, with A staged once per workgroup.  The split
+        // is the smallest that gives most CUs a workgroup while every chunk
+        // keeps at least two batches (measured on MI355X: 64x7168x16384
+        // fastest at split 2, where a third of the time is the partial-sum
+        // tail and a larger split costs more than it gains).
         const int mg = cdiv(M, 16);
-        int nr = mg == 1 ? 1 : (mg == 2 ? 2 : 4);
+        const int idx = mg - 2;
+        const int u_blocks = 4 * rows[idx].u;  // K-blocks per batch
+        const int rows_wg = 64 * rows[idx].nrw;
+        const int tiles = cdiv(N, rows_wg);
+        int chosen = -1;
+        for (int s : kSplits) {
+            if (!consider_split(s))
+                continue;
+            auto [per, eff] = split_chunks(KB, s, 16);
+            if (split_req <= 0) {
+                if (s > 1 && (eff < s || per < 2 * u_blocks))
+                    break;
+                chosen = s;
+                if ((int64_t)tiles * eff * 5 >= 4LL * num_cu)
+                    break;
+            } else {
+                chosen = s;
+            }
+        }
+        if (chosen < 0)
+            chosen = 1;
+        auto [per, eff] = split_chunks(KB, chosen, 16);
+        best.family = 2;
+        best.index = idx;
+        best.bm = mg * 16;
+        best.bn = rows_wg;
+        best.split = eff;
+        best.kb_per_split = per;
+        best.tiles_m = 1;
+        best.tiles_n = tiles;
+        best.grid = (int64_t)tiles * eff;
+        best.name = rows[idx].name;
+        const size_t part = (size_t)rows_wg * mg * 16 * 4;
+        best.counter_bytes = best.split > 1 ? (size_t)tiles * 4 : 0;
+        best.ws_bytes = best.split > 1 ? (size_t)tiles * best.split * part : 0;
+        return best;
+    }
+    if (M <= 16) {
+        // Skinny kernel: a workgroup owns 16*nr rows of B and one K chunk.
+        // Splitting K costs every split workgroup a serialized tail (partial
+        // write-back, counter, read-back), so the split is the smallest that
+        // gives most CUs a workgroup (measured on MI355X: 1x8192x8192
+        // fastest with nr 1, unsplit).
+        int nr = 1;
         if (const char *e = std::getenv("MXGEMM_FORCE_NR"))
             nr = std::atoi(e) >= 4 ? 4 : (std::atoi(e) >= 2 ? 2 : 1);
         const int nri = nr == 1 ? 0 : (nr == 2 ? 1 : 2);
@@ -118,8 +162,8 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
             chosen = 1;
         auto [per, eff] = split_chunks(KB, chosen, 16);
         best.family = 1;
-        best.index = (mg - 1) * 3 + nri;
-        best.bm = mg * 16;
+        best.index = nri;
+        best.bm = 16;
         best.bn = rows_wg;
         best.split = eff;
         best.kb_per_split = per;
@@ -127,7 +171,7 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
         best.tiles_n = tiles;
         best.grid = (int64_t)tiles * eff;
         best.name = skinny[best.index].name;
-        const size_t part = (size_t)rows_wg * mg * 16 * 4;
+        const size_t part = (size_t)rows_wg * 16 * 4;
         best.counter_bytes = best.split > 1 ? (size_t)tiles * 4 : 0;
         best.ws_bytes = best.split > 1 ? (size_t)tiles * best.split * part : 0;
         return best;
@@ -433,6 +477,9 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     g.d_vec = aligned(D, 8) && s.ldd % 4 == 0;
     g.c_vec = C && aligned(C, 8) && s.ldc % 4 == 0;
     g.d_stage = beta == 0.0f && aligned(D, 16) && s.ldd % 8 == 0;
+    g.sa_packed = s.sa_packed;
+    g.sa16 = !s.sa_packed && aligned(scaleA, 16) && s.ldsa % 16 == 0 && KB % 16 == 0;
+    g.sb16 = !s.b_packed && aligned(scaleB, 16) && s.ldsb % 16 == 0 && KB % 16 == 0;
     g.group_m = 4;
 
     if (p.split > 1) {
@@ -466,10 +513,14 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
             (s.sa_packed ? k.deep_packed_sa : s.b_packed ? k.deep_packed : k.deep_plain)(g, (int)p.grid, stream);
         else
             (s.sa_packed ? k.packed_sa : s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
-    } else {
+    } else if (p.family == 1) {
         int n = 0;
         const mx::SkinnyKernel &k = mx::skinny_kernels(&n)[p.index];
         (s.sa_packed ? k.packed_sa : s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
+    } else {
+        int n = 0;
+        const mx::RowsKernel &k = mx::rows_kernels(&n)[p.index];
+        (s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
     }
     if (hipGetLastError() != hipSuccess)
         return MXGEMM_ERR_HIP;

@@ -100,7 +100,7 @@ typedef struct mxgemm_strides {
  *          chunks whose fp32 partial sums are added in a fixed order (the
  *          result is bitwise reproducible run to run).  Other values:
  *          MXGEMM_ERR_INVALID_ARG.  Chunks are whole units of 256 K (tiled
- *          kernel, M > 64) or 512 K (skinny kernel, M <= 64); a split that
+ *          kernel, M > 64) or 512 K (skinny kernels, M <= 64); a split that
  *          needs smaller chunks is reduced to the number of such units
  *          (mxgemm_query reports the split used).
  *
@@ -172,7 +172,9 @@ mxgemm_status mxgemm_pack_scales(void *Sp, const void *S, int rows, int K, int64
 /* ---- plan / query ------------------------------------------------------------- */
 
 typedef struct mxgemm_info {
-    int32_t kernel;          /* kernel family: 0 = tiled (LDS), 1 = skinny (M <= 64, streams B) */
+    int32_t kernel;          /* kernel family: 0 = tiled (LDS, M > 64); 1 = skinny (M <= 16,
+                                streams B); 2 = skinny rows (16 < M <= 64, streams B, A
+                                shared through LDS) */
     int32_t tile_m, tile_n;  /* output tile per workgroup */
     int32_t split_k;         /* K chunks the plan uses */
     int64_t grid;            /* workgroups launched */

@@ -134,9 +134,12 @@ def test_plan_for_workloads(name):
     for b_packed in (0, 1):
         p = mx.mxgemm_plan(M, N, K, b_packed, -1, 256)
         assert p["split_k"] in (1, 2, 4, 8, 16)
-        if M <= 64:
+        if M <= 16:
             assert p["kernel"] == 1 and p["kernel_name"].startswith("skinny")
             assert p["tile_m"] >= M
+        elif M <= 64:
+            assert p["kernel"] == 2 and p["kernel_name"].startswith("rows")
+            assert p["tile_m"] >= M and p["tile_n"] in (64, 128)
         else:
             assert p["kernel"] == 0 and p["kernel_name"].startswith("tile")
         tiles = cdiv(M, p["tile_m"]) * cdiv(N, p["tile_n"]) if M > 64 else cdiv(N, p["tile_n"])

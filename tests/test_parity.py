@@ -245,3 +245,28 @@ def test_tile_pipelines_agree(shape, monkeypatch):
                 assert_parity(d_deep, ref, mag, "deep %s tile %d packed=%s,%s split=%d"
                               % (shape, tile, packed, sa_packed, s))
                 assert np.array_equal(d_deep, d_two)
+
+
+ROWS_CASES = [(17, 200, 2048), (40, 1000, 1056), (64, 333, 4096), (50, 4096, 8192), (33, 64, 512)]
+
+
+@pytest.mark.parametrize("shape", ROWS_CASES, ids=lambda s: "%dx%dx%d" % s)
+def test_rows_kernel_variants(shape):
+    """16 < M <= 64 (the rows kernel): every operand packing, unsplit and
+    split K, with ragged M, N and chunks that end inside a batch.  K = 1056
+    leaves a K-block count that is not a multiple of 16, so the A scales take
+    the per-wave load path; the other cases stage them through LDS."""
+    M, N, K = shape
+    p = inputs.make_problem(M, N, K, seed=0x2055 + M + N, dist="half_zero", e=(112, 140),
+                            beta=1.0, c_sigma=1.0)
+    p["alpha"], p["beta"] = 1.5, -0.75
+    ref, mag, _ = oracle_ref(p)
+    assert mx.mxgemm_plan(M, N, K, 0, 1, 256)["kernel_name"].startswith("rows_m%dx16" % -(-M // 16))
+    for packed, sa_packed in PACK_MODES:
+        outs = []
+        for s in (1, 2, 4):
+            say("case rows", shape, "packed", packed, sa_packed, "split", s)
+            d = gemm_gpu(p, split_k=s, b_packed=packed, sa_packed=sa_packed)
+            assert_parity(d, ref, mag, "rows %s packed=%s,%s split=%d" % (shape, packed, sa_packed, s))
+            outs.append(d)
+        assert np.array_equal(gemm_gpu(p, split_k=4, b_packed=packed, sa_packed=sa_packed), outs[2])
