@@ -114,14 +114,20 @@ __device__ __forceinline__ v4f mma_sel(int ob, int oa, v4i b, v4i a, v4f c, int 
 }
 
 // fp32 -> bf16, round to nearest, ties to even; NaN stays NaN (quiet).
-__device__ __forceinline__ uint32_t bf16_rne(float f)
+// Two floats to two bf16 (round to nearest even) packed low/high: one
+// v_cvt_pk_bf16_f32, which rounds with the wave's mode (nearest even, fp32
+// denormals preserved -- the kernel descriptor's defaults) and returns a
+// quiet NaN for a NaN input.  A software rounding (add 0x7FFF + lsb, NaN
+// test) compiled to a divergent branch per value.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return (u >> 16) | 0x40u;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    typedef float v2f_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+    const v2f_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2bf_t));
 }
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) { return bf16x2_rne(f, f) & 0xFFFFu; }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h)
 {
@@ -203,8 +209,8 @@ __device__ __forceinline__ void store_tile_staged(const Epilogue &ep, int m_base
             const int r = fm * 16 + (lane & 15);
             const int j = fn * 2 + (lane >> 5);
             v2u o;
-            o[0] = bf16_rne(ep.alpha * acc[fn][fm][0]) | (bf16_rne(ep.alpha * acc[fn][fm][1]) << 16);
-            o[1] = bf16_rne(ep.alpha * acc[fn][fm][2]) | (bf16_rne(ep.alpha * acc[fn][fm][3]) << 16);
+            o[0] = bf16x2_rne(ep.alpha * acc[fn][fm][0], ep.alpha * acc[fn][fm][1]);
+            o[1] = bf16x2_rne(ep.alpha * acc[fn][fm][2], ep.alpha * acc[fn][fm][3]);
             *reinterpret_cast<v2u *>(lds + r * RB + ((j ^ (r & (CH - 1))) * 16) + ((lane >> 4) & 1) * 8) = o;
         }
 #pragma unroll
@@ -257,8 +263,8 @@ __device__ __forceinline__ void store_quad(const Epilogue &ep, int m, int n, v4f
     uint16_t *drow = ep.D + (int64_t)m * ep.ldd + n;
     if (full && ep.d_vec) {
         v2u o;
-        o[0] = bf16_rne(r[0]) | (bf16_rne(r[1]) << 16);
-        o[1] = bf16_rne(r[2]) | (bf16_rne(r[3]) << 16);
+        o[0] = bf16x2_rne(r[0], r[1]);
+        o[1] = bf16x2_rne(r[2], r[3]);
         *reinterpret_cast<v2u *>(drow) = o;
     } else {
 #pragma unroll
