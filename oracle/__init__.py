@@ -66,6 +66,8 @@ def _load():
                 ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_double),
                 ctypes.POINTER(ctypes.c_uint16)]
             lib.oracle_dot_exact_parts.restype = ctypes.c_int
+            lib.oracle_quantize_mxfp4.argtypes = [u8p, i64, i64, i64, u8p, i64, u8p, i64]
+            lib.oracle_quantize_mxfp4.restype = None
             _lib = lib
     return _lib
 
@@ -198,3 +200,19 @@ def dot_exact(A, SA, B, SB, K, i, j, *, lda=None, ldb=None, ldsa=None, ldsb=None
         raise ValueError("exact mode unavailable (code %d)" % rc)
     mant = (hi.value << 64) | lo.value
     return mant, e.value, d.value, int(h.value)
+
+
+def quantize_mxfp4(X, K=None, *, ldx=None):
+    """bf16 [M, ldx] (uint16 bit patterns) -> (A [M, K/2] uint8 fp4x2,
+    S [M, K/32] uint8 E8M0), by the conversion rule in mxfp4_oracle.c
+    (readings Q1-Q4 there)."""
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    M = X.shape[0]
+    ldx = X.shape[1] if ldx is None else ldx
+    K = ldx if K is None else K
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    A = np.zeros((M, K // 2), dtype=np.uint8)
+    S = np.zeros((M, K // 32), dtype=np.uint8)
+    _load().oracle_quantize_mxfp4(_ptr(X), M, K, ldx, _ptr(A), K, _ptr(S), K // 32)
+    return A, S

@@ -325,3 +325,89 @@ int oracle_dot_exact_parts(int64_t K,
     *as_bf16 = oracle_bf16_rne_exact(m, e);
     return 0;
 }
+
+/* ---- activation quantizer: bf16 -> MXFP4 ----------------------------------- */
+
+/*
+ * The pages define the two formats a quantizer produces (E2M1 codes and E8M0
+ * scales, "Data layouts") but not how real-valued input is mapped onto them.
+ * This follows the conversion rule of the OCP Microscaling Formats (MX) v1.0
+ * specification, section 6.3 "Conversion of a vector of scalars to MX".
+ * Readings (each also listed in the design doc):
+ *   Q1 the scale exponent of a 32-block is X = floor(log2(max_i |v_i|)) - 2,
+ *      2 being the largest E2M1 exponent (6 = 1.5 * 2^2), clamped to the E8M0
+ *      range [-127, 127]; the scale code is X + 127.
+ *   Q2 element i is v_i / 2^X rounded to the nearest E2M1 value, ties to the
+ *      encoding whose mantissa bit is 0, magnitudes that round beyond 6 give 6;
+ *      the sign is kept, so a negative value that rounds to zero is code 0x8.
+ *   Q3 a block holding a NaN or an infinity gets scale 0xFF (NaN) and codes 0.
+ *   Q4 an all-zero block gets the clamped exponent of Q1 (-127, code 0x00) and
+ *      codes 0.
+ * All arithmetic is exact in fp64 (bf16 inputs, power-of-two scaling).
+ */
+
+/* Q2: nearest E2M1 magnitude code by direct search over the eight values. */
+static unsigned e2m1_nearest_code(double m)
+{
+    unsigned best = 0;
+    double best_d = fabs(m - E2M1_MAGNITUDE[0]);
+    for (unsigned c = 1; c < 8; ++c) {
+        double d = fabs(m - E2M1_MAGNITUDE[c]);
+        if (d < best_d || (d == best_d && (c & 1u) == 0u)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return best; /* beyond 6 the nearest value is 6 (code 7): saturation */
+}
+
+/*
+ * X is [M][ldx] bf16 (row-major); A receives [M][lda/2] bytes (lda in fp4
+ * elements, element k of a row in the low nibble of byte k/2 when k is even),
+ * S receives [M][lds] scale bytes.  K % 32 == 0.  Only the first K elements
+ * of each row, the first K/2 bytes of each A row and the first K/32 bytes of
+ * each S row are touched.
+ */
+void oracle_quantize_mxfp4(const uint16_t *X, int64_t M, int64_t K, int64_t ldx,
+                           uint8_t *A, int64_t lda, uint8_t *S, int64_t lds)
+{
+    for (int64_t r = 0; r < M; ++r) {
+        for (int64_t kb = 0; kb < K / 32; ++kb) {
+            double v[32];
+            double amax = 0.0;
+            int special = 0;
+            for (int i = 0; i < 32; ++i) {
+                v[i] = oracle_bf16_to_double(X[r * ldx + kb * 32 + i]);
+                if (isnan(v[i]) || isinf(v[i]))
+                    special = 1;
+                else if (fabs(v[i]) > amax)
+                    amax = fabs(v[i]);
+            }
+            uint8_t *arow = A + r * (lda / 2) + kb * 16;
+            if (special) { /* Q3 */
+                S[r * lds + kb] = 0xFFu;
+                memset(arow, 0, 16);
+                continue;
+            }
+            int x = -127; /* Q4 for an all-zero block */
+            if (amax > 0.0) {
+                int e;
+                (void)frexp(amax, &e); /* amax = f * 2^e, f in [0.5, 1) */
+                x = (e - 1) - 2;       /* Q1 */
+                if (x < -127)
+                    x = -127;
+                if (x > 127)
+                    x = 127;
+            }
+            S[r * lds + kb] = (uint8_t)(x + 127);
+            for (int i = 0; i < 32; i += 2) {
+                unsigned c[2];
+                for (int h = 0; h < 2; ++h) {
+                    double s = ldexp(v[i + h], -x); /* exact */
+                    c[h] = e2m1_nearest_code(fabs(s)) | (signbit(s) ? 8u : 0u);
+                }
+                arow[i / 2] = (uint8_t)(c[0] | (c[1] << 4));
+            }
+        }
+    }
+}
