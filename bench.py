@@ -171,6 +171,71 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False):
     return r
 
 
+QUANT_SHAPE = (8192, 8192)  # the bf16 activation of the square workload's A
+
+
+def quant_bytes(M, K):
+    """Algorithmic bytes of one quantizer call: bf16 in, fp4x2 codes and one
+    scale byte per 32 elements out."""
+    return 2 * M * K + M * K // 2 + M * K // 32
+
+
+def time_quantize(steps, warmup, eager=False):
+    """mxgemm_quantize on QUANT_SHAPE, HIP-graph replay over rotated inputs."""
+    import torch
+
+    import block_scaled_precision_mxfp4_amd as mx
+
+    M, K = QUANT_SHAPE
+    nbytes = quant_bytes(M, K)
+    copies = max(1, math.ceil(2.5 * LLC_BYTES / nbytes))
+    g = torch.Generator(device="cuda").manual_seed(0x5EED)
+    sets = []
+    for _ in range(copies):
+        X = (torch.randn((M, K), device="cuda", generator=g) *
+             torch.exp2(torch.randint(-20, 20, (M, 1), device="cuda", generator=g).float())).to(torch.bfloat16)
+        A = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+        S = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda")
+        sets.append((A, S, X))
+    stream = torch.cuda.Stream()
+    launch = lambda i: mx.mxgemm_quantize(*sets[i % copies], M, K, stream=stream.cuda_stream)
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            launch(i)
+    torch.cuda.synchronize()
+    graph, timing = None, "eager"
+    if not eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                launch(i)
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        timing = "hipgraph"
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(steps):
+                launch(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = e0.elapsed_time(e1) / 1e3 / steps
+    gbs = nbytes / per / 1e9
+    del sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log("%-24s %-22s          %9.2f us  %8.1f GB/s  (%s, %d copies)" % (
+        "quantize_%dx%d" % (M, K), "mx_quant_kernel", per * 1e6, gbs, timing, copies))
+    return {"workload": "quantize_%dx%d" % (M, K), "value": gbs, "unit": "GB/s",
+            "us_per_step": per * 1e6, "algorithmic_bytes": nbytes, "copies": copies, "timing": timing,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
+
+
 def cpu_baseline(name, target_s=12.0):
     """The oracle, as it stands, on a bounded sample of the workload's outputs."""
     import numpy as np
@@ -215,6 +280,8 @@ def main():
     ap.add_argument("--only", action="store_true", help="time only --workload (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (counter runs)")
+    ap.add_argument("--quantize-only", action="store_true",
+                    help="time only the bf16 -> MXFP4 quantizer (profiling runs)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 5 times (counter scaling)")
     args = ap.parse_args()
@@ -244,6 +311,9 @@ def main():
         print(json.dumps({"calib_copy_bytes": args.calib_copy, "copies": 5}), flush=True)
         return
     mx.lib()
+    if args.quantize_only:
+        print(json.dumps(time_quantize(args.steps, args.warmup, eager=args.eager)), flush=True)
+        return
 
     head = time_workload(args.workload, args.steps, args.warmup, split_k=args.split_k, eager=args.eager)
     others = []
@@ -261,6 +331,8 @@ def main():
               "roofline": {"bound": "hbm", "achieved": gemv["gbs"], "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": gemv["gbs"] / PEAK_HBM_GBS,
                            "traffic": measured_traffic(gemv["workload"])}}
+
+    quant = None if args.only else time_quantize(args.steps, args.warmup, eager=args.eager)
 
     base = None
     if not args.no_cpu_baseline:
@@ -290,6 +362,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": base,
         "m1": m1,
+        "quantize": quant,
         "device": {"arch": head["arch"], "num_cu": head["num_cu"], "clock_hz": head["clock_hz"],
                    "derived_peak_tflops": head["peak_flops_device"] / 1e12},
         "workloads": [{k: o[k] for k in ("workload", "kernel", "tile", "split_k", "us_per_step",

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
 
 # C-ABI entry points declared in include/libmxgemm.h
-EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_pack_b", "mxgemm_pack_scales",
+EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_pack_b", "mxgemm_pack_scales", "mxgemm_quantize",
            "mxgemm_query", "mxgemm_plan", "mxgemm_release_workspaces")
 
 STATUS = {0: "MXGEMM_OK", -1: "MXGEMM_ERR_INVALID_ARG", -2: "MXGEMM_ERR_SHAPE",
@@ -77,6 +77,8 @@ def lib():
         L.mxgemm_pack_b.restype = i32
         L.mxgemm_pack_scales.argtypes = [vp, vp, i32, i32, i64, vp]
         L.mxgemm_pack_scales.restype = i32
+        L.mxgemm_quantize.argtypes = [vp, vp, vp, i32, i32, i64, i64, i64, vp]
+        L.mxgemm_quantize.restype = i32
         L.mxgemm_query.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(Info)]
         L.mxgemm_query.restype = i32
         L.mxgemm_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(Info)]
@@ -155,6 +157,19 @@ def mxgemm_pack_scales(Sp, S, rows, K, lds=None, stream=None, check=True):
     st = lib().mxgemm_pack_scales(_ptr(Sp), _ptr(S), int(rows), int(K), int(lds), _stream(stream))
     if check:
         _check(st, "mxgemm_pack_scales")
+    return st
+
+
+def mxgemm_quantize(A, SA, X, M, K, ldx=None, lda=None, ldsa=None, stream=None, check=True):
+    """bf16 X [M][ldx] -> packed E2M1 A [M][lda/2] bytes and E8M0 scales
+    SA [M][ldsa] (asynchronous; strides default to dense rows)."""
+    ldx = K if ldx is None else ldx
+    lda = K if lda is None else lda
+    ldsa = K // 32 if ldsa is None else ldsa
+    st = lib().mxgemm_quantize(_ptr(A), _ptr(SA), _ptr(X), int(M), int(K), int(ldx), int(lda),
+                               int(ldsa), _stream(stream))
+    if check:
+        _check(st, "mxgemm_quantize")
     return st
 
 

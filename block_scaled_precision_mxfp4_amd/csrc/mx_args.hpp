@@ -77,6 +77,18 @@ struct RowsKernel {
 const RowsKernel *rows_kernels(int *count);
 
 void launch_pack_b(uint8_t *Bp, const uint8_t *B, int N, int KB, int64_t ldb_b, hipStream_t s);
+
+// bf16 -> MXFP4 quantizer: X [M][ldx] bf16 -> A [M][lda_b] bytes, S [M][lds].
+struct QuantArgs {
+    const uint16_t *X;
+    uint8_t *A;
+    uint8_t *S;
+    int M, K;
+    int64_t ldx, lda_b, lds;
+    int64_t blocks;  // M * K / 32
+};
+int64_t quant_grid(int64_t blocks);  // workgroups launch_quant needs
+void launch_quant(const QuantArgs &q, int64_t grid, hipStream_t s);
 // Scale shuffle of rows x KB scale bytes (either operand's scales).
 void launch_pack_sb(uint32_t *SBp, const uint8_t *SB, int N, int KB, int64_t ldsb, hipStream_t s);
 

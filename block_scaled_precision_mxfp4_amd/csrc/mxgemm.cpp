@@ -571,6 +571,43 @@ mxgemm_status mxgemm_pack_scales(void *Sp, const void *S, int rows, int K, int64
     return MXGEMM_OK;
 }
 
+mxgemm_status mxgemm_quantize(void *A, void *scaleA, const void *X, int M, int K, int64_t ldx,
+                              int64_t lda, int64_t ldsa, hipStream_t stream)
+{
+    if (!A || !scaleA || !X)
+        return MXGEMM_ERR_INVALID_ARG;
+    mxgemm_status st = check_shape(M, 1, K);
+    if (st != MXGEMM_OK)
+        return st;
+    if (ldx < K || lda < K || ldsa < K / 32)
+        return MXGEMM_ERR_SHAPE;
+    // 16-byte loads of 8 bf16 per lane; A as mxgemm_run requires it
+    if (lda % 2 || !aligned(X, 16) || ldx % 8 || !aligned(A, 16) || (lda / 2) % 16)
+        return MXGEMM_ERR_ALIGN;
+    const int64_t blocks = (int64_t)M * (K / 32);
+    const int64_t grid = mx::quant_grid(blocks);
+    if (grid > 0x7FFFFFFF)
+        return MXGEMM_ERR_SHAPE;
+    DeviceInfo *d = nullptr;
+    st = device_info(&d);
+    if (st != MXGEMM_OK)
+        return st;
+    mx::QuantArgs q;
+    q.X = (const uint16_t *)X;
+    q.A = (uint8_t *)A;
+    q.S = (uint8_t *)scaleA;
+    q.M = M;
+    q.K = K;
+    q.ldx = ldx;
+    q.lda_b = lda / 2;
+    q.lds = ldsa;
+    q.blocks = blocks;
+    mx::launch_quant(q, grid, stream);
+    if (hipGetLastError() != hipSuccess)
+        return MXGEMM_ERR_HIP;
+    return MXGEMM_OK;
+}
+
 mxgemm_status mxgemm_release_workspaces(void)
 {
     std::lock_guard<std::mutex> lock(g_mutex);

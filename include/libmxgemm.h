@@ -169,6 +169,37 @@ mxgemm_status mxgemm_pack_b(void *Bp, void *SBp, const void *B, const void *scal
 mxgemm_status mxgemm_pack_scales(void *Sp, const void *S, int rows, int K, int64_t lds,
                                  hipStream_t stream);
 
+/* ---- activation quantizer -------------------------------------------------------- */
+
+/*
+ * Quantize a bf16 matrix X [M][ldx] (row-major, ldx in bf16 elements) to the
+ * operand format of A: packed E2M1 codes A [M][lda/2] bytes (lda in fp4
+ * elements, element 2i in the low nibble of byte i) and E8M0 scales
+ * scaleA [M][ldsa] bytes, one per 32 consecutive K elements ([F4] "Data
+ * layouts").  The outputs can be passed to mxgemm_run as A and scaleA.
+ *
+ * The pages fix the encodings but not how a scale is chosen for real input;
+ * the conversion follows the OCP Microscaling Formats v1.0 specification,
+ * section 6.3: per 32-block, scale = 2^X with X = floor(log2 max|x|) - 2
+ * clamped to [-127, 127]; each element is x / 2^X rounded to the nearest
+ * E2M1 value (ties to the even mantissa), magnitudes beyond 6 saturate to 6,
+ * the sign is kept (a negative value rounding to zero gives code 0x8).  A
+ * block holding a NaN or an infinity gets scale 0xFF and codes 0; an all-zero
+ * block gets scale 0x00 and codes 0.  The result is exact (deterministic and
+ * independent of launch shape): every decision is taken on exactly scaled
+ * values.
+ *
+ * Shapes: M >= 1; K >= 32, K % 32 == 0, K <= 2^24; ldx >= K, lda >= K,
+ * ldsa >= K/32 (else MXGEMM_ERR_SHAPE).  Alignment (else MXGEMM_ERR_ALIGN):
+ * X 16-byte aligned with ldx % 8 == 0; A 16-byte aligned with lda even and
+ * lda/2 a multiple of 16 (the rule mxgemm_run applies to A); scaleA any.
+ * X must not overlap A or scaleA.  Only the first K elements of each X row
+ * are read and only the first K/2 bytes of each A row and K/32 bytes of each
+ * scaleA row are written.  Asynchronous on `stream`; allocates nothing.
+ */
+mxgemm_status mxgemm_quantize(void *A, void *scaleA, const void *X, int M, int K,
+                              int64_t ldx, int64_t lda, int64_t ldsa, hipStream_t stream);
+
 /* ---- plan / query ------------------------------------------------------------- */
 
 typedef struct mxgemm_info {

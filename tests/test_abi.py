@@ -112,6 +112,18 @@ def test_pack_scales_validation_before_any_hip_call():
     assert f(Sp=0x1002) == -3
 
 
+def test_quantize_validation_before_any_hip_call():
+    f = lambda **kw: mx.mxgemm_quantize(**dict(dict(A=0x1000, SA=0x2000, X=0x3000, M=64, K=256, stream=0),
+                                              **kw), check=False)
+    assert f(A=None) == -1 and f(SA=None) == -1 and f(X=None) == -1
+    assert f(M=0) == -2 and f(K=40) == -2 and f(K=0) == -2 and f(ldx=128) == -2 and f(lda=128) == -2
+    assert f(ldsa=4) == -2
+    # X rows in whole 16-byte chunks, A as mxgemm_run requires it
+    assert f(X=0x3008) == -3 and f(ldx=260) == -3 and f(A=0x1008) == -3 and f(lda=257) == -3
+    assert f(lda=272) == -3
+    assert f(SA=0x2001, ldsa=9) != -3  # scales need no alignment (no device here: -4 or -5)
+
+
 def test_query_and_plan_argument_errors():
     info = mx.Info()
     L = mx.lib()

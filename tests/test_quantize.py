@@ -1,0 +1,126 @@
+"""GPU parity of mxgemm_quantize (bf16 -> MXFP4) against the CPU oracle.
+
+Codes and scales are integers decided on exactly scaled values on both
+sides, so the comparison is bit-exact: every byte of A and of the scales.
+Inputs are seeded bf16 matrices with a wide exponent range per row,
+special values (NaN, +-inf, -0, zero blocks), exact rounding ties, padded
+strides, and the 8192 x 8192 activation of the square workload (sampled
+rows).  The last test quantizes activations and feeds them to mxgemm_run,
+the decode path the quantizer exists for.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import block_scaled_precision_mxfp4_amd as mx
+import oracle
+from block_scaled_precision_mxfp4_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from mxgpu import assert_parity, gemm_gpu, oracle_ref  # noqa: E402
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bf16_matrix(rng, M, K, spread=30.0, specials=True):
+    """Gaussian rows times 2^u, u uniform in [-spread, spread] per row, as
+    bf16 bit patterns (truncated), with special values mixed in."""
+    x = rng.standard_normal((M, K)) * np.exp2(rng.uniform(-spread, spread, (M, 1)))
+    X = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    if specials:
+        flat = X.reshape(-1)
+        n = flat.size
+        for val, frac in ((0x7FC0, 0.001), (0x7F80, 0.0005), (0xFF80, 0.0005), (0x8000, 0.01)):
+            idx = rng.integers(0, n, max(1, int(n * frac)))
+            flat[idx] = val
+        # whole zero blocks and blocks of exact ties (block max 6, ties at X = 0)
+        for r in range(0, M, 3):
+            kb = int(rng.integers(0, K // 32))
+            X[r, kb * 32:(kb + 1) * 32] = 0
+        ties = np.array([6.0, 0.25, -0.75, 1.25, -1.75, 2.5, -3.5, 5.0] * 4, dtype=np.float32)
+        for r in range(1, M, 4):
+            kb = int(rng.integers(0, K // 32))
+            X[r, kb * 32:(kb + 1) * 32] = (ties.view(np.uint32) >> 16).astype(np.uint16)
+        # bf16 subnormals (+-), alone (scale 2^-127) and under a normal block
+        # maximum, and blocks whose maximum sits at the bottom of the normal range
+        for r in range(2, M, 5):
+            kb = int(rng.integers(0, K // 32))
+            blk = rng.integers(1, 0x80, 32).astype(np.uint16) | np.where(rng.random(32) < 0.5, 0x8000, 0)
+            if r % 2:
+                blk[int(rng.integers(0, 32))] = rng.choice([0x0080, 0x0100, 0x0180, 0x3F80])
+            X[r, kb * 32:(kb + 1) * 32] = blk.astype(np.uint16)
+    return X
+
+
+def quantize_gpu(X, M, K, ldx=None, lda=None, ldsa=None, fill=0xAB):
+    ldx = K if ldx is None else ldx
+    lda = K if lda is None else lda
+    ldsa = K // 32 if ldsa is None else ldsa
+    Xd = torch.from_numpy(np.ascontiguousarray(X).view(np.int16)).cuda()
+    A = torch.full((M, lda // 2), fill, dtype=torch.uint8, device="cuda")
+    S = torch.full((M, ldsa), fill, dtype=torch.uint8, device="cuda")
+    mx.mxgemm_quantize(A, S, Xd, M, K, ldx=ldx, lda=lda, ldsa=ldsa)
+    torch.cuda.synchronize()
+    return A.cpu().numpy(), S.cpu().numpy()
+
+
+@pytest.mark.parametrize("shape", [(1, 32), (1, 8192), (37, 416), (64, 16384), (129, 96)],
+                         ids=lambda s: "%dx%d" % s)
+def test_quantize_matches_oracle_bitexact(shape):
+    M, K = shape
+    rng = np.random.default_rng(0x9A + M * 7 + K)
+    X = bf16_matrix(rng, M, K)
+    say("case quantize", shape)
+    A, S = quantize_gpu(X, M, K)
+    Ar, Sr = oracle.quantize_mxfp4(X)
+    assert np.array_equal(S, Sr), "scales differ in %d places" % int((S != Sr).sum())
+    assert np.array_equal(A, Ar), "codes differ in %d bytes" % int((A != Ar).sum())
+
+
+def test_quantize_strided_leaves_padding():
+    M, K = 23, 288
+    ldx, lda, ldsa = K + 24, K + 64, K // 32 + 5
+    rng = np.random.default_rng(0x51DE)
+    X = bf16_matrix(rng, M, K)
+    Xp = np.full((M, ldx), 0x7FC0, dtype=np.uint16)  # NaN padding must not be read
+    Xp[:, :K] = X
+    say("case quantize strided")
+    A, S = quantize_gpu(Xp, M, K, ldx=ldx, lda=lda, ldsa=ldsa)
+    Ar, Sr = oracle.quantize_mxfp4(X)
+    assert np.array_equal(A[:, :K // 2], Ar) and np.array_equal(S[:, :K // 32], Sr)
+    assert (A[:, K // 2:] == 0xAB).all() and (S[:, K // 32:] == 0xAB).all()
+
+
+def test_quantize_square_activation_sampled_rows():
+    """The 8192 x 8192 bf16 activation of the square workload's A, quantized
+    on the GPU in one launch; 48 rows (first, last, random) checked."""
+    M = K = 8192
+    rng = np.random.default_rng(0x8192)
+    X = bf16_matrix(rng, M, K, spread=8.0)
+    say("case quantize 8192x8192")
+    A, S = quantize_gpu(X, M, K)
+    rows = sorted(set([0, 1, M - 1] + list(rng.integers(0, M, 45))))
+    Ar, Sr = oracle.quantize_mxfp4(X[rows])
+    assert np.array_equal(S[rows], Sr) and np.array_equal(A[rows], Ar)
+
+
+@pytest.mark.parametrize("M", [1, 40])
+def test_quantized_activations_feed_the_gemm(M):
+    """Quantize bf16 activations on the GPU, multiply with MXFP4 weights:
+    the result matches the oracle GEMM over the oracle's quantization."""
+    N, K = 1000, 2048
+    rng = np.random.default_rng(0xDEC0 + M)
+    X = bf16_matrix(rng, M, K, spread=4.0, specials=False)
+    p = inputs.make_problem(M, N, K, seed=0xDEC1 + M, beta=0.0)
+    A, S = quantize_gpu(X, M, K)
+    p["A"], p["SA"] = oracle.quantize_mxfp4(X)
+    assert np.array_equal(A, p["A"]) and np.array_equal(S, p["SA"])
+    say("case quantize -> gemm", M)
+    d = gemm_gpu(p, split_k=-1)
+    ref, mag, _ = oracle_ref(p)
+    assert_parity(d, ref, mag, "quantized A, M=%d" % M)
