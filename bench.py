@@ -233,7 +233,8 @@ def time_quantize(steps, warmup, eager=False):
     return {"workload": "quantize_%dx%d" % (M, K), "value": gbs, "unit": "GB/s",
             "us_per_step": per * 1e6, "algorithmic_bytes": nbytes, "copies": copies, "timing": timing,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": gbs / PEAK_HBM_GBS, "traffic": None}}
+                         "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": measured_traffic("quantize_%dx%d" % (M, K))}}
 
 
 def cpu_baseline(name, target_s=12.0):
