@@ -72,6 +72,11 @@ constexpr double kMatrixFraction = 0.4;
 constexpr double kCuLoadRate = 65e9;
 constexpr double kSplitChunkCost = 2e-6;
 constexpr double kHbm = 5.0e12;
+// The skinny kernels split K only into chunks of at least 64 scale blocks
+// (2048 K): a sweep of splits 1..16 over 20 shapes with M <= 64 on MI355X
+// found every shorter chunk slower than the next smaller split (the
+// partial-sum tail outweighs the extra parallelism).
+constexpr int kMinSkinnyChunk = 64;
 constexpr double kCuL2 = 64.0 * 2.4e9;
 
 Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
@@ -97,7 +102,6 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
         // tail and a larger split costs more than it gains).
         const int mg = cdiv(M, 16);
         const int idx = mg - 2;
-        const int u_blocks = 4 * rows[idx].u;  // K-blocks per batch
         const int rows_wg = 64 * rows[idx].nrw;
         const int tiles = cdiv(N, rows_wg);
         int chosen = -1;
@@ -106,7 +110,7 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
                 continue;
             auto [per, eff] = split_chunks(KB, s, 16);
             if (split_req <= 0) {
-                if (s > 1 && (eff < s || per < 2 * u_blocks))
+                if (s > 1 && (eff < s || per < kMinSkinnyChunk))
                     break;
                 chosen = s;
                 if ((int64_t)tiles * eff * 5 >= 4LL * num_cu)
@@ -151,8 +155,8 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
                 continue;
             auto [per, eff] = split_chunks(KB, s, 16);
             if (split_req <= 0) {
-                if (s > 1 && (eff < s || per < 32))
-                    break;  // chunks would collapse or leave waves idle
+                if (s > 1 && (eff < s || per < kMinSkinnyChunk))
+                    break;  // chunks would collapse or be too short for their tail
                 chosen = s;
                 if ((int64_t)tiles * eff * 5 >= 4LL * num_cu)
                     break;
