@@ -87,6 +87,21 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, lds_void
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, 0, 0, 0);
 }
 
+// Cache policy of operands that are read once per call (the B stream of the
+// skinny kernels): the non-temporal hint (nt) asks the caches not to keep
+// the lines.
+constexpr int kStream = 2;
+
+__device__ __forceinline__ void load16_to_lds_stream(__amdgpu_buffer_rsrc_t r, lds_void *lds, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, 0, 0, kStream);
+}
+
+__device__ __forceinline__ v4i load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream);
+}
+
 // acc += (B fragment, scaled) x (A fragment, scaled) over 128 K.
 template <int OPSEL_B, int OPSEL_A>
 __device__ __forceinline__ v4f mfma_fp4(v4i bfrag, v4i afrag, v4f acc, int sb, int sa)

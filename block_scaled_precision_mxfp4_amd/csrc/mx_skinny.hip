@@ -99,7 +99,7 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
         uint32_t saw;  // A1: its scale byte
     };
 
-    auto load_batch = [&](int ks0, Batch &bt, auto bufc) {
+    auto load_batch = [&](int ks0, Batch &bt, auto bufc) __attribute__((always_inline)) {
         if constexpr (BST) {
             uint8_t *dst = decltype(bufc)::value ? s_bst1[wave] : s_bst0[wave];
             constexpr int RPI = 64 / CPR;  // rows per 1 KiB instruction
@@ -108,7 +108,7 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
             for (int i = 0; i < NR * 16 / RPI; ++i) {
                 const int row = i * RPI + rl;
                 const int kbc = ks0 * 4 + (sl ^ (row & 15));  // the chunk this slot holds
-                load16_to_lds(rb, (lds_void *)(dst + i * 1024),
+                load16_to_lds_stream(rb, (lds_void *)(dst + i * 1024),
                               kbc < kb_wend ? (uint32_t)(row * g.ldb_b + kbc * 16) : kOOB);
             }
         }
@@ -122,9 +122,9 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
                 if constexpr (BST)
                     ;  // staged above
                 else if constexpr (BPACK)
-                    bt.b[u][nr] = load16(rb, ok ? (uint32_t)(((nr * g.ks_total + ks) * 64 + lane) * 16) : kOOB);
+                    bt.b[u][nr] = load16_stream(rb, ok ? (uint32_t)(((nr * g.ks_total + ks) * 64 + lane) * 16) : kOOB);
                 else
-                    bt.b[u][nr] = load16(rb, ok ? (uint32_t)((nr * 16 + (lane & 15)) * g.ldb_b + kb * 16) : kOOB);
+                    bt.b[u][nr] = load16_stream(rb, ok ? (uint32_t)((nr * 16 + (lane & 15)) * g.ldb_b + kb * 16) : kOOB);
             }
             if constexpr (!A1) {
 #pragma unroll
@@ -190,12 +190,16 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
     // them): staged B, the single A row and its scales, row-major B scales
     constexpr int LN = NR * U + 2 + G * NR * (SVEC ? 1 : 4);
     static_assert(!BST || LN < 64, "vmcnt range");
-    auto compute = [&](const Batch &bt, auto bufc) {
+    auto compute = [&](const Batch &bt, auto bufc, auto lastc) __attribute__((always_inline)) {
         v4i bst[BST ? U : 1][NR];
         if constexpr (BST) {
             // this batch's staging loads have landed (the next batch's LN
-            // loads may still be in flight); then all fragment reads at once
-            wait_vmcnt<LN>();
+            // loads may still be in flight, unless this is the last batch);
+            // then all fragment reads at once
+            if constexpr (decltype(lastc)::value)
+                wait_vmcnt<0>();
+            else
+                wait_vmcnt<LN>();
             const uint32_t base = lds_addr(decltype(bufc)::value ? s_bst1[wave] : s_bst0[wave]) +
                                   (uint32_t)((lane & 15) * CPR * 16);
             static_for<U>([&](auto ui) {
@@ -239,21 +243,34 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
 
     // two batches in flight: issue the next before multiplying the current
     // (scheduling barriers keep each batch's loads ahead of the multiplies
-    // of the previous one; left alone the scheduler sinks them below)
+    // of the previous one; left alone the scheduler sinks them below).  The
+    // last pair of batches is peeled so that no batch past the wave's range
+    // is issued: such a batch loads nothing, but its instructions still
+    // queue on the load path ahead of the last multiplies (at M = 1 the
+    // peel took the 1 x 8192 x 8192 GEMV from 9.5 to 8.9 us).  A wave with
+    // an empty range multiplies two batches of zeros, which adds +0.
     using Buf0 = std::integral_constant<int, 0>;
     using Buf1 = std::integral_constant<int, 1>;
+    using More = std::false_type;
+    using Last = std::true_type;
     Batch cur, nxt;
     load_batch(w_begin, cur, Buf0{});
-    for (int ks0 = w_begin; ks0 < w_end; ks0 += 2 * U) {
+    int ks0 = w_begin;
+    for (; ks0 + 2 * U < w_end; ks0 += 2 * U) {
         load_batch(ks0 + U, nxt, Buf1{});
         __builtin_amdgcn_sched_barrier(0);
-        compute(cur, Buf0{});
+        compute(cur, Buf0{}, More{});
         __builtin_amdgcn_sched_barrier(0);
         load_batch(ks0 + 2 * U, cur, Buf0{});
         __builtin_amdgcn_sched_barrier(0);
-        compute(nxt, Buf1{});
+        compute(nxt, Buf1{}, More{});
         __builtin_amdgcn_sched_barrier(0);
     }
+    load_batch(ks0 + U, nxt, Buf1{});
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, Buf0{}, More{});
+    __builtin_amdgcn_sched_barrier(0);
+    compute(nxt, Buf1{}, Last{});
 
     // ---- the four waves' sums, added in wave order; wave w then owns blocks f = w, w+4, ...
 #pragma unroll

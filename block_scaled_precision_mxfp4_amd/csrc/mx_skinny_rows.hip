@@ -140,9 +140,9 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
 #pragma unroll
             for (int nr = 0; nr < NRW; ++nr) {
                 if constexpr (BPACK)
-                    r.b[u][nr] = load16(rb, ok ? (uint32_t)(((nr * g.ks_total + ks) * 64 + lane) * 16) : kOOB);
+                    r.b[u][nr] = load16_stream(rb, ok ? (uint32_t)(((nr * g.ks_total + ks) * 64 + lane) * 16) : kOOB);
                 else
-                    r.b[u][nr] = load16(rb, ok ? (uint32_t)((nr * 16 + (lane & 15)) * g.ldb_b + kb * 16) : kOOB);
+                    r.b[u][nr] = load16_stream(rb, ok ? (uint32_t)((nr * 16 + (lane & 15)) * g.ldb_b + kb * 16) : kOOB);
             }
         }
         if constexpr (BPACK) {
