@@ -57,7 +57,7 @@ def _load():
             lib.oracle_fp4_code.argtypes = [u8p, i64, i64, i64]
             lib.oracle_fp4_code.restype = ctypes.c_uint
             lib.oracle_mxgemm.argtypes = [i64, u8p, i64, u8p, i64, u8p, i64, u8p, i64,
-                                          u8p, i64, f64, f64, u8p, i64, u8p, i64,
+                                          u8p, i64, ctypes.c_int, f64, f64, u8p, i64, u8p, i64,
                                           u8p, u8p, u8p]
             lib.oracle_mxgemm.restype = ctypes.c_int
             lib.oracle_dot_exact_parts.argtypes = [
@@ -102,7 +102,7 @@ def mxgemm(A, SA, B, SB, K, alpha=1.0, beta=0.0, C=None, *, lda=None, ldb=None,
     """Reference block of D for rows x cols.
 
     A: uint8 [M, lda/2], SA: uint8 [M, ldsa], B: uint8 [N, ldb/2],
-    SB: uint8 [N, ldsb], C: uint16 (bf16 bits) [M, ldc] or None.
+    SB: uint8 [N, ldsb], C: uint16 (bf16 bits) or float32 [M, ldc], or None.
     Returns (ref fp64, mag fp64, dref uint16) of shape [len(rows), len(cols)].
     """
     lib = _load()
@@ -115,10 +115,12 @@ def mxgemm(A, SA, B, SB, K, alpha=1.0, beta=0.0, C=None, *, lda=None, ldb=None,
     ldb = B.shape[1] * 2 if ldb is None else ldb
     ldsa = SA.shape[1] if ldsa is None else ldsa
     ldsb = SB.shape[1] if ldsb is None else ldsb
+    c_f32 = 0
     if beta != 0.0:
         if C is None:
             raise ValueError("beta != 0 needs C")
-        C = np.ascontiguousarray(C, dtype=np.uint16)
+        c_f32 = int(np.asarray(C).dtype == np.float32)
+        C = np.ascontiguousarray(C, dtype=np.float32 if c_f32 else np.uint16)
         ldc = C.shape[1] if ldc is None else ldc
     else:
         ldc = 0 if ldc is None else ldc
@@ -149,7 +151,7 @@ def mxgemm(A, SA, B, SB, K, alpha=1.0, beta=0.0, C=None, *, lda=None, ldb=None,
         m_ = np.zeros((nr, c1 - c0), dtype=np.float64)
         d_ = np.zeros((nr, c1 - c0), dtype=np.uint16)
         rc = lib.oracle_mxgemm(K, _ptr(A), lda, _ptr(SA), ldsa, _ptr(B), ldb, _ptr(SB), ldsb,
-                               _ptr(C) if beta != 0.0 else None, ldc, float(alpha), float(beta),
+                               _ptr(C) if beta != 0.0 else None, ldc, c_f32, float(alpha), float(beta),
                                _ptr(rows), nr, _ptr(cs), c1 - c0,
                                _ptr(r_), _ptr(m_), _ptr(d_))
         if rc != 0:

@@ -129,14 +129,16 @@ uint16_t oracle_bf16_rne(double x)
  *
  * with i = rows[ri], j = cols[cj]; the sum runs over k = 0..K-1 ascending.
  * A is [M][lda/2] bytes, B is [N][ldb/2] bytes (both row-major, K-major),
- * SA is [M][ldsa] bytes, SB is [N][ldsb] bytes, C is [M][ldc] bf16.
+ * SA is [M][ldsa] bytes, SB is [N][ldsb] bytes, C is [M][ldc] bf16, or
+ * float32 when c_f32 != 0 (the f32 bias of the asm_f4gemm README's
+ * "C / bias" note; either way its value enters exactly, in fp64).
  * C is read only when beta != 0.  Any of mag/dref may be NULL.
  * Returns 0, or -1 when scratch memory cannot be allocated.
  */
 int oracle_mxgemm(int64_t K,
                   const uint8_t *A, int64_t lda, const uint8_t *SA, int64_t ldsa,
                   const uint8_t *B, int64_t ldb, const uint8_t *SB, int64_t ldsb,
-                  const uint16_t *C, int64_t ldc, double alpha, double beta,
+                  const void *C, int64_t ldc, int c_f32, double alpha, double beta,
                   const int64_t *rows, int64_t nrows,
                   const int64_t *cols, int64_t ncols,
                   double *ref, double *mag, uint16_t *dref)
@@ -169,8 +171,11 @@ int oracle_mxgemm(int64_t K,
                 m += fabs(p);
             }
             double r = alpha * acc;
-            if (beta != 0.0)
-                r += beta * oracle_bf16_to_double(C[rows[ri] * ldc + cols[cj]]);
+            if (beta != 0.0) {
+                const int64_t ci = rows[ri] * ldc + cols[cj];
+                r += beta * (c_f32 ? (double)((const float *)C)[ci]
+                                   : oracle_bf16_to_double(((const uint16_t *)C)[ci]));
+            }
             int64_t o = ri * ncols + cj;
             ref[o] = r;
             if (mag)

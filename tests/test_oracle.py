@@ -317,6 +317,35 @@ def test_zero_A_gives_bf16_of_beta_C():
     assert np.array_equal(d, expect.astype(np.uint16))
 
 
+def test_f32_C_enters_exactly():
+    """An f32 C (the bias type the asm_f4gemm README's "C / bias" note
+    names) enters at its full f32 value: with A = 0 the reference is
+    beta * C exactly, including values bf16 cannot hold, and the stored D
+    is that value rounded once to bf16."""
+    M, N, K = 8, 16, 64
+    p = small_problem(M, N, K, seed=24)
+    p["A"][:] = 0
+    rng = np.random.default_rng(25)
+    Cf = (rng.standard_normal((M, N)) * 3.0).astype(np.float32)
+    Cf[0, 0] = np.float32(1.0 + 2.0 ** -20)  # not a bf16 value
+    p["C"], p["beta"] = Cf, -0.5
+    r, _, d = _gemm(p)
+    assert np.array_equal(r, -0.5 * Cf.astype(np.float64))
+    assert r[0, 0] == -0.5 * (1.0 + 2.0 ** -20)
+    expect = np.vectorize(lambda v: rne_bf16_fraction(Fraction(float(v))))(r)
+    assert np.array_equal(d, expect.astype(np.uint16))
+
+
+def test_f32_C_holding_bf16_values_matches_bf16_C():
+    M, N, K = 16, 24, 256
+    p = small_problem(M, N, K, seed=26, beta=1.0, c_sigma=1.0)
+    p["beta"] = 0.625
+    r16, m16, d16 = _gemm(p)
+    p["C"] = np.vectorize(oracle.bf16_to_float)(p["C"]).astype(np.float32)
+    r32, m32, d32 = _gemm(p)
+    assert np.array_equal(r16, r32) and np.array_equal(m16, m32) and np.array_equal(d16, d32)
+
+
 def test_beta_zero_ignores_C():
     M, N, K = 4, 8, 64
     p = small_problem(M, N, K, seed=23)
