@@ -37,7 +37,12 @@ class Strides(ctypes.Structure):
     _fields_ = [("ldd", ctypes.c_int64), ("ldc", ctypes.c_int64), ("lda", ctypes.c_int64),
                 ("ldb", ctypes.c_int64), ("ldsa", ctypes.c_int64), ("ldsb", ctypes.c_int64),
                 ("b_packed", ctypes.c_int32), ("sa_packed", ctypes.c_int32),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("c_f32", ctypes.c_int32), ("split_mode", ctypes.c_int32)]
+
+
+SPLIT_FP32 = 0         # MXGEMM_SPLIT_FP32
+SPLIT_BF16_ATOMIC = 1  # MXGEMM_SPLIT_BF16_ATOMIC
 
 
 class Info(ctypes.Structure):
@@ -119,8 +124,9 @@ def _check(status, where):
 
 
 def make_strides(*, ldd, ldc, lda, ldb, ldsa, ldsb, b_packed=0, sa_packed=0, workspace=None,
-                 workspace_bytes=0):
-    return Strides(ldd, ldc, lda, ldb, ldsa, ldsb, b_packed, sa_packed, _ptr(workspace), workspace_bytes)
+                 workspace_bytes=0, c_f32=0, split_mode=SPLIT_FP32):
+    return Strides(ldd, ldc, lda, ldb, ldsa, ldsb, b_packed, sa_packed, _ptr(workspace), workspace_bytes,
+                   c_f32, split_mode)
 
 
 def mxgemm_status_string(status: int) -> str:

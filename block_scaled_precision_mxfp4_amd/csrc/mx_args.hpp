@@ -10,7 +10,7 @@ namespace mx {
 
 struct GemmArgs {
     uint16_t *D;          // bf16 [M][ldd]
-    const uint16_t *C;    // bf16 [M][ldc], read only when beta != 0
+    const void *C;        // bf16 or f32 (c_f32) [M][ldc], read only when beta != 0
     const uint8_t *A;     // fp4x2 [M][lda_b]
     const uint8_t *B;     // fp4x2 [N][ldb_b], or the packed layout
     const uint8_t *SA;    // E8M0 [M][ldsa], or the packed scale layout
@@ -35,6 +35,8 @@ struct GemmArgs {
     int sa_packed;        // scaleA in the packed scale layout
     int sa16, sb16;       // row-major scale rows in 16-byte aligned groups of 16 K-blocks
     int group_m;          // tile-order grouping along M
+    int c_f32;            // C holds float32 elements
+    int split_atomic;     // split > 1: chunks add bf16(alpha * partial) into D with bf16 atomics
 };
 
 typedef void (*LaunchFn)(const GemmArgs &, int grid, hipStream_t);
@@ -91,5 +93,8 @@ int64_t quant_grid(int64_t blocks);  // workgroups launch_quant needs
 void launch_quant(const QuantArgs &q, int64_t grid, hipStream_t s);
 // Scale shuffle of rows x KB scale bytes (either operand's scales).
 void launch_pack_sb(uint32_t *SBp, const uint8_t *SB, int N, int KB, int64_t ldsb, hipStream_t s);
+// bf16-atomic split-K: D = bf16(beta * C) (0 when beta == 0) before the
+// chunks add into it
+void launch_d_init(const GemmArgs &g, hipStream_t s);
 
 }  // namespace mx

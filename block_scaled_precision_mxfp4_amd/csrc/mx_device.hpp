@@ -192,12 +192,13 @@ __device__ __forceinline__ uint32_t scale_group_word(v4i w, int lane)
 // Epilogue parameters shared by all kernels.
 struct Epilogue {
     uint16_t *D;
-    const uint16_t *C;
+    const void *C;  // bf16, or float32 when c_f32
     float alpha, beta;
     int M, N;
     int64_t ldd, ldc;
     int d_vec;  // D rows and base allow 8-byte stores of 4 consecutive n
-    int c_vec;  // C rows and base allow 8-byte loads
+    int c_vec;  // C rows and base allow one vector load of 4 consecutive n
+    int c_f32;
 };
 
 // Epilogue for beta == 0 through a private LDS region of the wave
@@ -260,8 +261,21 @@ __device__ __forceinline__ void store_quad(const Epilogue &ep, int m, int n, v4f
     for (int g = 0; g < 4; ++g)
         r[g] = ep.alpha * acc[g];
     const bool full = n + 3 < ep.N;
-    if (ep.beta != 0.0f) {
-        const uint16_t *crow = ep.C + (int64_t)m * ep.ldc + n;
+    if (ep.beta != 0.0f && ep.c_f32) {
+        const float *crow = reinterpret_cast<const float *>(ep.C) + (int64_t)m * ep.ldc + n;
+        if (full && ep.c_vec) {
+            const v4f c4 = *reinterpret_cast<const v4f *>(crow);
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                r[g] = fmaf(ep.beta, c4[g], r[g]);
+        } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                if (n + g < ep.N)
+                    r[g] = fmaf(ep.beta, crow[g], r[g]);
+        }
+    } else if (ep.beta != 0.0f) {
+        const uint16_t *crow = reinterpret_cast<const uint16_t *>(ep.C) + (int64_t)m * ep.ldc + n;
         if (full && ep.c_vec) {
             v2u c2 = *reinterpret_cast<const v2u *>(crow);
             r[0] = fmaf(ep.beta, bf16_to_f32(c2[0] & 0xFFFFu), r[0]);
@@ -286,6 +300,26 @@ __device__ __forceinline__ void store_quad(const Epilogue &ep, int m, int n, v4f
         for (int g = 0; g < 4; ++g)
             if (n + g < ep.N)
                 drow[g] = (uint16_t)bf16_rne(r[g]);
+    }
+}
+
+// bf16-atomic split-K: this chunk's alpha * acc, rounded to bf16, added into
+// D with packed bf16 atomic adds (two columns per instruction).  Needs D
+// 4-byte aligned and ldd, N even, so a pair never leaves its row; n is a
+// multiple of 4.
+__device__ __forceinline__ void atomic_add_quad(const Epilogue &ep, int m, int n, v4f acc)
+{
+    if (m >= ep.M || n >= ep.N)
+        return;
+    typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+    uint16_t *drow = ep.D + (int64_t)m * ep.ldd + n;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (n + 2 * h < ep.N) {
+            const uint32_t w = bf16x2_rne(ep.alpha * acc[2 * h], ep.alpha * acc[2 * h + 1]);
+            __builtin_amdgcn_global_atomic_fadd_v2bf16(reinterpret_cast<v2bf_t *>(drow + 2 * h),
+                                                       __builtin_bit_cast(v2bf_t, w));
+        }
     }
 }
 

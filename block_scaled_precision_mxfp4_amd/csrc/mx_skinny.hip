@@ -280,7 +280,7 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
             s_red[wave][nr * MG + mg][lane] = acc[nr][mg];
     __syncthreads();
 
-    Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec};
+    Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec, g.c_f32};
     constexpr int FPW = (NF + 3) / 4;  // blocks per wave
     v4f sum[FPW];
 #pragma unroll

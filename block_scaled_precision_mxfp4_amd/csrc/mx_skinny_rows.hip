@@ -267,7 +267,7 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
     wait_vmcnt<0>();  // loads issued past the chunk (they write zeros into free slots)
 
     // ---- epilogue: each wave owns its columns
-    Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec};
+    Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec, g.c_f32};
     const int mb = lane & 15, nb4 = n0 + 4 * (lane >> 4);
     if (g.split == 1) {
 #pragma unroll

@@ -394,7 +394,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     }
 
     // ---- epilogue
-    Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec};
+    Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec, g.c_f32};
     const int mb = m0 + wave_m * TM + (lane & 15);
     const int nb = n0 + wave_n * TN + 4 * (lane >> 4);
     if (g.split == 1) {
@@ -424,6 +424,15 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
                 store_quad(ep, mb + fm * 16, nb + fn * 16, acc[fn][fm]);
         return;
     }
+    if (g.split_atomic) {
+        // bf16-atomic reduction (opt-in): D already holds bf16(beta * C)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                atomic_add_quad(ep, mb + fm * 16, nb + fn * 16, acc[fn][fm]);
+        return;
+    }
     // fp32 partial tile of this K chunk: [tile][z][wave][fn][fm][lane] float4s
     constexpr uint32_t PART = BM * BN * 4;  // bytes per partial tile
     const auto rws = make_rsrc_u(g.ws + (size_t)t * g.split * (BM * BN), (uint32_t)(g.split * PART));
@@ -445,6 +454,37 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
                 sum += load16_coherent(rws, zz * PART + idx);
             store_quad(ep, mb + fm * 16, nb + fn * 16, sum);
         }
+}
+
+// D = bf16(beta * C), or +0 when beta == 0: the starting value the
+// bf16-atomic split-K reduction adds its chunks onto.  One thread per pair
+// of columns (ldd and N are even there).
+__global__ void __launch_bounds__(256) mx_d_init_kernel(GemmArgs g)
+{
+    const int64_t pairs = (int64_t)g.M * (g.N / 2);
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= pairs)
+        return;
+    const int m = (int)(i / (g.N / 2)), n = (int)(i - (int64_t)m * (g.N / 2)) * 2;
+    float v0 = 0.0f, v1 = 0.0f;
+    if (g.beta != 0.0f) {
+        if (g.c_f32) {
+            const float *c = reinterpret_cast<const float *>(g.C) + (int64_t)m * g.ldc + n;
+            v0 = g.beta * c[0];
+            v1 = g.beta * c[1];
+        } else {
+            const uint16_t *c = reinterpret_cast<const uint16_t *>(g.C) + (int64_t)m * g.ldc + n;
+            v0 = g.beta * bf16_to_f32(c[0]);
+            v1 = g.beta * bf16_to_f32(c[1]);
+        }
+    }
+    *reinterpret_cast<uint32_t *>(g.D + (int64_t)m * g.ldd + n) = bf16x2_rne(v0, v1);
+}
+
+void launch_d_init(const GemmArgs &g, hipStream_t s)
+{
+    const int64_t pairs = (int64_t)g.M * (g.N / 2);
+    hipLaunchKernelGGL(mx_d_init_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s, g);
 }
 
 template <int BM, int BN, int WM, int WN, bool BPACK, bool SAPACK>

@@ -280,7 +280,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
     wait_vmcnt<0>();  // idle loads of the last stages
 
     // ---- epilogue (as in mx_tile_kernel)
-    Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec};
+    Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec, g.c_f32};
     const int mb = m0 + wave_m * TM + (lane & 15);
     const int nb = n0 + wave_n * TN + 4 * (lane >> 4);
     if (g.split == 1) {

@@ -79,7 +79,7 @@ constexpr double kHbm = 5.0e12;
 constexpr int kMinSkinnyChunk = 64;
 constexpr double kCuL2 = 64.0 * 2.4e9;
 
-Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
+Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool tiled_only = false)
 {
     const int KB = K / 32;
     if (num_cu <= 0)
@@ -93,7 +93,7 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
     const mx::TileKernel *tile = mx::tile_kernels(&n_tile);
     const mx::SkinnyKernel *skinny = mx::skinny_kernels(&n_skinny);
     const mx::RowsKernel *rows = mx::rows_kernels(&n_rows);
-    if (M > 16 && M <= 64) {
+    if (M > 16 && M <= 64 && !tiled_only) {
         // Rows kernel: the four waves of a workgroup own 4 x 16 rows of B
         // and share one K chunk, with A staged once per workgroup.  The split
         // is the smallest that gives most CUs a workgroup while every chunk
@@ -137,7 +137,7 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu)
         best.ws_bytes = best.split > 1 ? (size_t)tiles * best.split * part : 0;
         return best;
     }
-    if (M <= 16) {
+    if (M <= 16 && !tiled_only) {
         // Skinny kernel: a workgroup owns 16*nr rows of B and one K chunk.
         // Splitting K costs every split workgroup a serialized tail (partial
         // write-back, counter, read-back), so the split is the smallest that
@@ -418,7 +418,8 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     if (strides) {
         s = *strides;
         if ((s.b_packed != 0 && s.b_packed != 1) || (s.sa_packed != 0 && s.sa_packed != 1) ||
-            (s.sa_packed && !s.b_packed))
+            (s.sa_packed && !s.b_packed) || (s.c_f32 != 0 && s.c_f32 != 1) ||
+            (s.split_mode != MXGEMM_SPLIT_FP32 && s.split_mode != MXGEMM_SPLIT_BF16_ATOMIC))
             return MXGEMM_ERR_INVALID_ARG;
     } else {
         std::memset(&s, 0, sizeof s);
@@ -437,7 +438,10 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
         return MXGEMM_ERR_ALIGN;
     if ((s.b_packed && !aligned(scaleB, 4)) || (s.sa_packed && !aligned(scaleA, 4)))
         return MXGEMM_ERR_ALIGN;
-    if (!aligned(D, 2) || (C && beta != 0.0f && !aligned(C, 2)))
+    if (!aligned(D, 2) || (C && beta != 0.0f && !aligned(C, s.c_f32 ? 4 : 2)))
+        return MXGEMM_ERR_ALIGN;
+    const bool atomic = s.split_mode == MXGEMM_SPLIT_BF16_ATOMIC;
+    if (atomic && (!aligned(D, 4) || s.ldd % 2 || N % 2))
         return MXGEMM_ERR_ALIGN;
     // byte offsets inside a tile must stay below 2^31
     if ((int64_t)256 * (s.lda / 2) >= ((int64_t)1 << 31) || (!s.b_packed && (int64_t)256 * (s.ldb / 2) >= ((int64_t)1 << 31)))
@@ -448,12 +452,12 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     st = device_info(&d);
     if (st != MXGEMM_OK)
         return st;
-    Plan p = plan_for(M, N, K, s.b_packed, split_k, d->num_cu);
+    Plan p = plan_for(M, N, K, s.b_packed, split_k, d->num_cu, atomic);
 
     GemmArgs g;
     std::memset(&g, 0, sizeof g);
     g.D = (uint16_t *)D;
-    g.C = (const uint16_t *)C;
+    g.C = C;
     g.A = (const uint8_t *)A;
     g.B = (const uint8_t *)B;
     g.SA = (const uint8_t *)scaleA;
@@ -481,14 +485,20 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     g.scale16 = aligned(scaleA, 16) && s.ldsa % 16 == 0 && KB % 16 == 0 &&
                 (s.b_packed || (aligned(scaleB, 16) && s.ldsb % 16 == 0));
     g.d_vec = aligned(D, 8) && s.ldd % 4 == 0;
-    g.c_vec = C && aligned(C, 8) && s.ldc % 4 == 0;
+    g.c_vec = C && aligned(C, s.c_f32 ? 16 : 8) && s.ldc % 4 == 0;
+    g.c_f32 = s.c_f32;
     g.d_stage = beta == 0.0f && aligned(D, 16) && s.ldd % 8 == 0;
     g.sa_packed = s.sa_packed;
     g.sa16 = !s.sa_packed && aligned(scaleA, 16) && s.ldsa % 16 == 0 && KB % 16 == 0;
     g.sb16 = !s.b_packed && aligned(scaleB, 16) && s.ldsb % 16 == 0 && KB % 16 == 0;
     g.group_m = 4;
 
-    if (p.split > 1) {
+    if (p.split > 1 && atomic) {
+        // chunks add into D, set first to bf16(beta * C); no workspace
+        if ((int64_t)M * (N / 2) / 256 >= 0x7FFFFFFF)
+            return MXGEMM_ERR_SHAPE;
+        g.split_atomic = 1;
+    } else if (p.split > 1) {
         void *counters = nullptr, *partials = nullptr;
         if (s.workspace && s.workspace_bytes < p.ws_bytes)
             return MXGEMM_ERR_WORKSPACE;
@@ -501,6 +511,8 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
 
     if (p.grid > 0x7FFFFFFF)
         return MXGEMM_ERR_SHAPE;
+    if (g.split_atomic)
+        mx::launch_d_init(g, stream);
     if (p.family == 0) {
         int n = 0;
         const mx::TileKernel &k = mx::tile_kernels(&n)[p.index];
@@ -508,12 +520,12 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
         // 128-K steps; otherwise the two-stage kernel handles any layout
         const bool deep_ok = KB % 4 == 0 && (s.sa_packed || (aligned(scaleA, 4) && s.ldsa % 4 == 0)) &&
                              (s.b_packed || (aligned(scaleB, 4) && s.ldsb % 4 == 0));
-        bool deep = deep_ok && k.prefer_deep;
+        bool deep = deep_ok && k.prefer_deep && !g.split_atomic;  // the two-stage kernel implements the atomic mode
         if (const char *e = std::getenv("MXGEMM_TILE_PIPELINE")) {  // "deep" or "two-stage"
             if (std::strcmp(e, "two-stage") == 0)
                 deep = false;
             else if (std::strcmp(e, "deep") == 0)
-                deep = deep_ok;
+                deep = deep_ok && !g.split_atomic;
         }
         if (deep)
             (s.sa_packed ? k.deep_packed_sa : s.b_packed ? k.deep_packed : k.deep_plain)(g, (int)p.grid, stream);

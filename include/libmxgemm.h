@@ -72,12 +72,34 @@ const char *mxgemm_status_string(mxgemm_status status);
  *
  * Units follow the asm_f4gemm README ("Kernel ABI", kernarg notes): A and B
  * strides count fp4 ELEMENTS (twice the byte pitch) and must be even; scale
- * strides count bytes; C and D strides count bf16 elements.  ldc and ldd are
- * honoured separately, so D may alias C (in place) when ldc == ldd.
+ * strides count bytes; C and D strides count elements of their type.  ldc
+ * and ldd are honoured separately, so D may alias C (in place) when ldc ==
+ * ldd and C is bf16.
+ *
+ * The two option fields at the end default to 0 (a zeroed struct):
+ *   c_f32      C is float32 instead of bf16.  The README's "C / bias" note
+ *              says aiter documents its bias operand as f32; with c_f32 = 1
+ *              the epilogue reads that type (D stays bf16; one rounding of
+ *              alpha*acc + beta*C, computed in fp32).
+ *   split_mode MXGEMM_SPLIT_FP32: split-K partials are fp32 sums added in a
+ *              fixed order (deterministic; the default).
+ *              MXGEMM_SPLIT_BF16_ATOMIC: each K chunk adds bf16(alpha *
+ *              partial) into D with packed bf16 atomic adds, onto D first
+ *              set to bf16(beta * C), the reduction the README's kernels use
+ *              ("Verification": split-K accumulates in bf16).  Offered only
+ *              to measure that reduction's error against the fp32 one: the
+ *              result is rounded once per chunk and its bits depend on the
+ *              order the chunks arrive in.  It runs on the tiled kernel
+ *              (the skinny kernels are never chosen), needs D 4-byte
+ *              aligned, ldd and N even (else MXGEMM_ERR_ALIGN), and D must
+ *              not alias C.  With split 1 it is the ordinary path.
  */
+#define MXGEMM_SPLIT_FP32        0
+#define MXGEMM_SPLIT_BF16_ATOMIC 1
+
 typedef struct mxgemm_strides {
     int64_t ldd;      /* bf16 elements between rows of D, >= N */
-    int64_t ldc;      /* bf16 elements between rows of C, >= N (ignored if beta == 0) */
+    int64_t ldc;      /* elements between rows of C, >= N (ignored if beta == 0) */
     int64_t lda;      /* fp4 elements between rows of A, >= K, even */
     int64_t ldb;      /* fp4 elements between rows of B, >= K, even (ignored if b_packed) */
     int64_t ldsa;     /* bytes between rows of scaleA, >= K/32 */
@@ -87,6 +109,8 @@ typedef struct mxgemm_strides {
                           for the M rows of A (ldsa ignored; needs b_packed = 1) */
     void *workspace;  /* optional device buffer for split-K partials; NULL = library-owned */
     size_t workspace_bytes;
+    int32_t c_f32;      /* 0: C is bf16; 1: C is float32 */
+    int32_t split_mode; /* MXGEMM_SPLIT_FP32 or MXGEMM_SPLIT_BF16_ATOMIC */
 } mxgemm_strides;
 
 /* ---- the GEMM ------------------------------------------------------------- */
@@ -111,7 +135,7 @@ typedef struct mxgemm_strides {
  *
  * Alignment: A and B base addresses 16-byte aligned and lda/2, ldb/2 (the
  * byte pitches) multiples of 16.  Scales, C and D need only natural
- * alignment (C and D: 2 bytes).
+ * alignment (D and a bf16 C: 2 bytes; an f32 C: 4 bytes).
  *
  * Split-K (split_k > 1, chosen or forced) keeps fp32 partial sums in a
  * workspace of mxgemm_query(...).workspace_bytes.  With strides->workspace

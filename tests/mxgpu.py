@@ -36,17 +36,27 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def gemm_gpu(p: dict, split_k: int = -1, b_packed: bool = False, D=None, stream=None, sa_packed: bool = False):
+def gemm_gpu(p: dict, split_k: int = -1, b_packed: bool = False, D=None, stream=None, sa_packed: bool = False,
+             split_mode: int = 0):
     """Run D = bf16(alpha A B^T + beta C) on the GPU for problem p (dense
     strides; b_packed: B and its scales pre-shuffled by mxgemm_pack_b;
-    sa_packed: A's scales too, by mxgemm_pack_scales).  Returns the bf16
-    bits of D as numpy uint16 [M, N]."""
+    sa_packed: A's scales too, by mxgemm_pack_scales; a float32 p["C"] is
+    passed as an f32 C).  Returns the bf16 bits of D as numpy uint16 [M, N]."""
     M, N, K = p["M"], p["N"], p["K"]
     A, B, SA, SB = dev_u8(p["A"]), dev_u8(p["B"]), dev_u8(p["SA"]), dev_u8(p["SB"])
-    C = dev_bf16(p["C"]) if p.get("C") is not None else None
+    c_f32 = p.get("C") is not None and p["C"].dtype == np.float32
+    if p.get("C") is None:
+        C = None
+    elif c_f32:
+        C = torch.from_numpy(np.ascontiguousarray(p["C"])).cuda()
+    else:
+        C = dev_bf16(p["C"])
     if D is None:
         D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     strides = None
+    if c_f32 or split_mode:
+        strides = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32,
+                                  c_f32=int(c_f32), split_mode=split_mode)
     if b_packed:
         info = mx.mxgemm_plan(M, N, K, 1, -1, 256)
         Bp = torch.empty(info["packed_b_bytes"], dtype=torch.uint8, device="cuda")
@@ -58,7 +68,7 @@ def gemm_gpu(p: dict, split_k: int = -1, b_packed: bool = False, D=None, stream=
             mx.mxgemm_pack_scales(SAp, SA, M, K)
             SA = SAp
         strides = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32, b_packed=1,
-                                  sa_packed=int(sa_packed))
+                                  sa_packed=int(sa_packed), c_f32=int(c_f32), split_mode=split_mode)
     mx.mxgemm_run(D, C if p["beta"] != 0.0 else None, A, B, SA, SB, p["alpha"], p["beta"], M, N, K,
                   strides=strides, split_k=split_k, stream=stream)
     torch.cuda.synchronize()

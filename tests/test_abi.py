@@ -94,6 +94,47 @@ def test_run_stride_validation():
     assert _run(strides=s) == -1
     # packed B: B strides are ignored, but scaleB must be 4-byte aligned
     assert _run(strides=st(ldb=0, ldsb=0, b_packed=1), scaleB=0x5002) == -3
+    # option fields: 0 or 1 only
+    assert _run(strides=st(c_f32=2)) == -1
+    assert _run(strides=st(split_mode=2)) == -1
+    assert _run(strides=st(split_mode=-1)) == -1
+    # an f32 C needs 4-byte alignment (a bf16 C: 2)
+    assert _run(strides=st(c_f32=1), beta=1.0, C=0x6002) == -3
+    # bf16-atomic split-K: D 4-byte aligned, ldd and N even
+    assert _run(strides=st(split_mode=1), D=0x1002) == -3
+    assert _run(strides=st(split_mode=1, ldd=257)) == -3
+    assert _run(strides=st(split_mode=1), N=255) == -3
+
+
+def test_struct_layouts_match_the_header():
+    """The binding's ctypes structs have the C header's size and field
+    offsets (compiled with the host C compiler)."""
+    import shutil
+    import subprocess
+    import tempfile
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = {"mxgemm_strides": mx.Strides, "mxgemm_info": mx.Info}
+    lines = []
+    for cname, cls in fields.items():
+        lines.append('printf("%%zu\\n", sizeof(%s));' % cname)
+        for f, _ in cls._fields_:
+            lines.append('printf("%%zu\\n", offsetof(%s, %s));' % (cname, f))
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"libmxgemm.h\"\nint main(void){%s return 0;}\n" % " ".join(lines)
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "l.c"), os.path.join(d, "l")
+        open(c, "w").write(src)
+        r = subprocess.run([cc, "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I" + os.path.dirname(HEADER),
+                            c, "-o", exe], capture_output=True, text=True)
+        if r.returncode != 0:
+            pytest.skip("header does not compile here: " + r.stderr[:200])
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+    want = []
+    for cname, cls in fields.items():
+        want.append(ctypes.sizeof(cls))
+        want += [getattr(cls, f).offset for f, _ in cls._fields_]
+    assert got == want
 
 
 def test_pack_validation_before_any_hip_call():
