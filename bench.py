@@ -14,7 +14,10 @@ workloads in a list.  Steps are launched from a HIP graph (captured once,
 replayed) so that kernel-launch overhead of the Python caller does not show
 up as GPU idle time; every kernel in the graph is a real mxgemm_run launch.
 For HBM-bound workloads the inputs rotate over enough copies that each
-step's operands are not resident in the last-level cache.
+step's operands are not resident in the last-level cache.  Before each
+workload's timed replay the GPU runs 500 ms of untimed launches of the same
+workload (--soak-ms), so that the timing sees the clock the chip settles at
+under sustained load rather than its first-launch transient.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.
 """
@@ -64,7 +67,7 @@ def algorithmic_bytes(M, N, K, beta):
     return b
 
 
-def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False):
+def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soak_ms=0.0):
     import numpy as np
     import torch
 
@@ -118,6 +121,17 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False):
         for i in range(warmup):
             launch(i)
     torch.cuda.synchronize()
+    if soak_ms > 0:
+        # untimed load until the clocks have settled (the chip lowers its
+        # clock under sustained matrix load): sustained, not burst, speed
+        t_end = time.perf_counter() + soak_ms / 1e3
+        i = 0
+        while time.perf_counter() < t_end:
+            with torch.cuda.stream(stream):
+                for _ in range(64):
+                    launch(i)
+                    i += 1
+            stream.synchronize()
 
     timing = "hipgraph"
     graph = None
@@ -281,6 +295,9 @@ def main():
     ap.add_argument("--only", action="store_true", help="time only --workload (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (counter runs)")
+    ap.add_argument("--soak-ms", type=float, default=500.0,
+                    help="untimed load before each workload's timing, so that the clocks have "
+                         "settled (0: time right after the warmup launches)")
     ap.add_argument("--quantize-only", action="store_true",
                     help="time only the bf16 -> MXFP4 quantizer (profiling runs)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="BYTES",
@@ -316,12 +333,14 @@ def main():
         print(json.dumps(time_quantize(args.steps, args.warmup, eager=args.eager)), flush=True)
         return
 
-    head = time_workload(args.workload, args.steps, args.warmup, split_k=args.split_k, eager=args.eager)
+    head = time_workload(args.workload, args.steps, args.warmup, split_k=args.split_k, eager=args.eager,
+                         soak_ms=args.soak_ms)
     others = []
     if not args.only:
         for name in inputs.WORKLOADS:
             if name != args.workload:
-                others.append(time_workload(name, args.steps, args.warmup, eager=args.eager))
+                others.append(time_workload(name, args.steps, args.warmup, eager=args.eager,
+                                            soak_ms=args.soak_ms))
     gemv = next((o for o in [head] + others if o["M"] == 1), None)
 
     m1 = None
