@@ -82,6 +82,35 @@ def fp4_codes_packed(seed: int, rows: int, K: int, dist: str = "uniform") -> np.
     raise ValueError("unknown code distribution %r" % dist)
 
 
+# A formats besides FP4 (the library's ids): element width in bits
+FORMAT_BITS = {0: 4, 1: 8, 2: 8, 3: 6, 4: 6}
+
+
+def wide_codes(seed: int, rows: int, K: int, fmt: int) -> np.ndarray:
+    """A matrix of format fmt (1 FP8 E4M3, 2 BF8 E5M2, 3 FP6 E2M3, 4 FP6
+    E3M2) as row-major bytes [rows, K * w / 8]: a little-endian bit stream
+    of w-bit codes per row (element k at bits k*w .. k*w+w-1).  Codes are
+    uniform over the format's finite values: E4M3 leaves out its two NaN
+    codes (exponent and mantissa all ones), E5M2 its eight infinity and NaN
+    codes (exponent all ones); the FP6 formats have none."""
+    n = rows * K
+    h = _u32(seed, n).astype(np.uint64)
+    if fmt in (3, 4):
+        codes = (h >> np.uint64(26)).astype(np.uint32).reshape(rows, K // 4, 4)  # 6 bits
+        v = codes[..., 0] | (codes[..., 1] << 6) | (codes[..., 2] << 12) | (codes[..., 3] << 18)
+        out = np.empty((rows, K // 4, 3), dtype=np.uint8)
+        out[..., 0], out[..., 1], out[..., 2] = v & 0xFF, (v >> 8) & 0xFF, (v >> 16) & 0xFF
+        return out.reshape(rows, K * 3 // 4)
+    if fmt == 1:
+        finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    elif fmt == 2:
+        finite = np.array([c for c in range(256) if (c & 0x7C) != 0x7C], dtype=np.uint8)
+    else:
+        raise ValueError("unknown A format %r" % fmt)
+    idx = (h * np.uint64(len(finite))) >> np.uint64(32)
+    return finite[idx.astype(np.int64)].reshape(rows, K)
+
+
 def e8m0_scales(seed: int, rows: int, K: int, lo: int, hi: int) -> np.ndarray:
     """E8M0 bytes [rows, K/32], exponents uniform over lo..hi inclusive."""
     n = rows * (K // 32)
@@ -131,11 +160,15 @@ WORKLOADS = {
 
 def make_problem(M: int, N: int, K: int, *, seed: int, dist: str = "uniform",
                  e=(123, 131), alpha: float = 1.0, beta: float = 0.0,
-                 c_sigma: float | None = None) -> dict:
-    """Dense (unpadded) operands for one GEMM problem."""
+                 c_sigma: float | None = None, a_fmt: int = 0) -> dict:
+    """Dense (unpadded) operands for one GEMM problem (A in format a_fmt:
+    0 FP4, else see wide_codes; B is always FP4)."""
     lo, hi = e
-    p = dict(M=M, N=N, K=K, alpha=float(alpha), beta=float(beta), seed=seed)
-    p["A"] = fp4_codes_packed(_stream(seed, "A"), M, K, dist)
+    p = dict(M=M, N=N, K=K, alpha=float(alpha), beta=float(beta), seed=seed, a_fmt=a_fmt)
+    if a_fmt == 0:
+        p["A"] = fp4_codes_packed(_stream(seed, "A"), M, K, dist)
+    else:
+        p["A"] = wide_codes(_stream(seed, "A"), M, K, a_fmt)
     p["B"] = fp4_codes_packed(_stream(seed, "B"), N, K, dist)
     p["SA"] = e8m0_scales(_stream(seed, "SA"), M, K, lo, hi)
     p["SB"] = e8m0_scales(_stream(seed, "SB"), N, K, lo, hi)

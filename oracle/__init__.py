@@ -56,7 +56,13 @@ def _load():
             lib.oracle_bf16_to_double.restype = f64
             lib.oracle_fp4_code.argtypes = [u8p, i64, i64, i64]
             lib.oracle_fp4_code.restype = ctypes.c_uint
-            lib.oracle_mxgemm.argtypes = [i64, u8p, i64, u8p, i64, u8p, i64, u8p, i64,
+            lib.oracle_decode.argtypes = [ctypes.c_int, ctypes.c_uint]
+            lib.oracle_decode.restype = f64
+            lib.oracle_format_bits.argtypes = [ctypes.c_int]
+            lib.oracle_format_bits.restype = ctypes.c_int
+            lib.oracle_elem_code.argtypes = [u8p, i64, ctypes.c_int, i64, i64]
+            lib.oracle_elem_code.restype = ctypes.c_uint
+            lib.oracle_mxgemm.argtypes = [i64, ctypes.c_int, u8p, i64, u8p, i64, u8p, i64, u8p, i64,
                                           u8p, i64, ctypes.c_int, f64, f64, u8p, i64, u8p, i64,
                                           u8p, u8p, u8p]
             lib.oracle_mxgemm.restype = ctypes.c_int
@@ -97,11 +103,29 @@ def fp4_code(X: np.ndarray, ld: int, r: int, k: int) -> int:
     return int(_load().oracle_fp4_code(_ptr(X), ld, r, k))
 
 
+# A formats (the library's ids): FP4 E2M1, FP8 E4M3, BF8 E5M2, FP6 E2M3, FP6 E3M2
+FMT_FP4, FMT_E4M3, FMT_E5M2, FMT_E2M3, FMT_E3M2 = 0, 1, 2, 3, 4
+
+
+def decode(fmt: int, code: int) -> float:
+    return float(_load().oracle_decode(int(fmt), int(code)))
+
+
+def format_bits(fmt: int) -> int:
+    return int(_load().oracle_format_bits(int(fmt)))
+
+
+def elem_code(X: np.ndarray, ld_bytes: int, bits: int, r: int, k: int) -> int:
+    X = np.ascontiguousarray(X, dtype=np.uint8)
+    return int(_load().oracle_elem_code(_ptr(X), int(ld_bytes), int(bits), int(r), int(k)))
+
+
 def mxgemm(A, SA, B, SB, K, alpha=1.0, beta=0.0, C=None, *, lda=None, ldb=None,
-           ldsa=None, ldsb=None, ldc=None, rows=None, cols=None, threads=None):
+           ldsa=None, ldsb=None, ldc=None, rows=None, cols=None, threads=None, a_fmt=FMT_FP4):
     """Reference block of D for rows x cols.
 
-    A: uint8 [M, lda/2], SA: uint8 [M, ldsa], B: uint8 [N, ldb/2],
+    A: uint8 [M, lda * w / 8] for A's format (w = 4, 8 or 6 bits; lda counts
+    elements), SA: uint8 [M, ldsa], B: uint8 [N, ldb/2] (FP4),
     SB: uint8 [N, ldsb], C: uint16 (bf16 bits) or float32 [M, ldc], or None.
     Returns (ref fp64, mag fp64, dref uint16) of shape [len(rows), len(cols)].
     """
@@ -111,7 +135,7 @@ def mxgemm(A, SA, B, SB, K, alpha=1.0, beta=0.0, C=None, *, lda=None, ldb=None,
     SA = np.ascontiguousarray(SA, dtype=np.uint8)
     SB = np.ascontiguousarray(SB, dtype=np.uint8)
     M, N = A.shape[0], B.shape[0]
-    lda = A.shape[1] * 2 if lda is None else lda
+    lda = A.shape[1] * 8 // format_bits(a_fmt) if lda is None else lda
     ldb = B.shape[1] * 2 if ldb is None else ldb
     ldsa = SA.shape[1] if ldsa is None else ldsa
     ldsb = SB.shape[1] if ldsb is None else ldsb
@@ -150,7 +174,7 @@ def mxgemm(A, SA, B, SB, K, alpha=1.0, beta=0.0, C=None, *, lda=None, ldb=None,
         r_ = np.zeros((nr, c1 - c0), dtype=np.float64)
         m_ = np.zeros((nr, c1 - c0), dtype=np.float64)
         d_ = np.zeros((nr, c1 - c0), dtype=np.uint16)
-        rc = lib.oracle_mxgemm(K, _ptr(A), lda, _ptr(SA), ldsa, _ptr(B), ldb, _ptr(SB), ldsb,
+        rc = lib.oracle_mxgemm(K, int(a_fmt), _ptr(A), lda, _ptr(SA), ldsa, _ptr(B), ldb, _ptr(SB), ldsb,
                                _ptr(C) if beta != 0.0 else None, ldc, c_f32, float(alpha), float(beta),
                                _ptr(rows), nr, _ptr(cs), c1 - c0,
                                _ptr(r_), _ptr(m_), _ptr(d_))

@@ -76,6 +76,81 @@ double oracle_mx_element(const uint8_t *X, int64_t ld, const uint8_t *SX,
            oracle_e8m0(SX[r * lds + k / 32]);
 }
 
+/* ---- wider A formats ----------------------------------------------------- */
+
+/*
+ * "CDNA4 dense MFMA builtins", section "Mixed-precision with scaling": the
+ * scaled matrix instructions take FP8 (E4M3), BF8 (E5M2), FP6 (E2M3),
+ * FP6 (E3M2) and FP4 (E2M1) inputs, 8, 8, 6, 6 and 4 bits per element,
+ * selected per operand.  The pages give the names and widths only; the
+ * element encodings are those of the OCP Microscaling Formats v1.0
+ * specification (section 5.3): sign in the top bit, then the exponent
+ * field, then the mantissa field; exponent field 0 is subnormal
+ * (0.m x 2^(1 - bias)); E4M3 has no infinities and NaN only at
+ * exponent 1111 with mantissa 111; E5M2 is IEEE-like (exponent 11111:
+ * infinity with mantissa 0, else NaN); the FP6 formats have no special
+ * codes.
+ *
+ * Format ids here (the library's, not the instructions' codes):
+ *   0 FP4 E2M1, 1 FP8 E4M3, 2 BF8 E5M2, 3 FP6 E2M3, 4 FP6 E3M2.
+ *
+ * Reading (the pages do not say how rows of these formats are laid out in
+ * memory): a row of A is a little-endian bit stream of w-bit fields,
+ * element k at bits [k*w, k*w + w).  For FP4 this is the low-nibble-first
+ * byte order of "Data layouts"; for FP8 element k is byte k; for FP6 one
+ * 32-element block is 24 bytes.
+ */
+int oracle_format_bits(int fmt)
+{
+    static const int bits[5] = {4, 8, 8, 6, 6};
+    return (fmt >= 0 && fmt < 5) ? bits[fmt] : 0;
+}
+
+double oracle_decode(int fmt, unsigned code)
+{
+    if (fmt == 0)
+        return oracle_e2m1(code & 0xFu);
+    /* exponent bits, mantissa bits, bias */
+    static const int EB[5] = {2, 4, 5, 2, 3}, MB[5] = {1, 3, 2, 3, 2}, BIAS[5] = {1, 7, 15, 1, 3};
+    if (fmt < 1 || fmt > 4)
+        return NAN;
+    const int eb = EB[fmt], mb = MB[fmt], bias = BIAS[fmt];
+    const unsigned s = (code >> (eb + mb)) & 1u;
+    const unsigned e = (code >> mb) & ((1u << eb) - 1u);
+    const unsigned m = code & ((1u << mb) - 1u);
+    double v;
+    if (fmt == 1 && e == 15u && m == 7u)
+        return NAN;
+    if (fmt == 2 && e == 31u)
+        v = m == 0u ? INFINITY : NAN;
+    else if (e == 0u)
+        v = ldexp((double)m, 1 - bias - mb);
+    else
+        v = ldexp((double)((1u << mb) + m), (int)e - bias - mb);
+    return s ? -v : v;
+}
+
+/* Code of element k of row r: bits [k*w, k*w + w) of the row's bytes,
+ * little-endian; rows are ld_bytes apart. */
+unsigned oracle_elem_code(const uint8_t *X, int64_t ld_bytes, int w, int64_t r, int64_t k)
+{
+    const int64_t bit = k * w;
+    const uint8_t *p = X + r * ld_bytes + bit / 8;
+    const int sh = (int)(bit % 8);
+    unsigned v = p[0];
+    if (sh + w > 8)
+        v |= (unsigned)p[1] << 8;
+    return (v >> sh) & ((1u << w) - 1u);
+}
+
+/* Dequantized element of a row of format fmt (rows ld_bytes apart). */
+double oracle_mx_element_fmt(const uint8_t *X, int64_t ld_bytes, int fmt, const uint8_t *SX,
+                             int64_t lds, int64_t r, int64_t k)
+{
+    return oracle_decode(fmt, oracle_elem_code(X, ld_bytes, oracle_format_bits(fmt), r, k)) *
+           oracle_e8m0(SX[r * lds + k / 32]);
+}
+
 /* ---- bf16 --------------------------------------------------------------- */
 
 double oracle_bf16_to_double(uint16_t h)
@@ -128,14 +203,16 @@ uint16_t oracle_bf16_rne(double x)
  *   dref[...]        = bf16_rne(ref)
  *
  * with i = rows[ri], j = cols[cj]; the sum runs over k = 0..K-1 ascending.
- * A is [M][lda/2] bytes, B is [N][ldb/2] bytes (both row-major, K-major),
+ * A is [M][lda/2] bytes, B is [N][ldb/2] bytes (both row-major, K-major;
+ * with a_fmt != 0 A holds that format and its rows are lda * w / 8 bytes
+ * apart, w its element width),
  * SA is [M][ldsa] bytes, SB is [N][ldsb] bytes, C is [M][ldc] bf16, or
  * float32 when c_f32 != 0 (the f32 bias of the asm_f4gemm README's
  * "C / bias" note; either way its value enters exactly, in fp64).
  * C is read only when beta != 0.  Any of mag/dref may be NULL.
  * Returns 0, or -1 when scratch memory cannot be allocated.
  */
-int oracle_mxgemm(int64_t K,
+int oracle_mxgemm(int64_t K, int a_fmt,
                   const uint8_t *A, int64_t lda, const uint8_t *SA, int64_t ldsa,
                   const uint8_t *B, int64_t ldb, const uint8_t *SB, int64_t ldsb,
                   const void *C, int64_t ldc, int c_f32, double alpha, double beta,
@@ -153,9 +230,11 @@ int oracle_mxgemm(int64_t K,
         return -1;
     }
     /* Dequantize the rows of A and of B that the requested block needs. */
+    const int64_t lda_bytes = lda * oracle_format_bits(a_fmt) / 8;
     for (int64_t ri = 0; ri < nrows; ++ri)
         for (int64_t k = 0; k < K; ++k)
-            a[ri * K + k] = oracle_mx_element(A, lda, SA, ldsa, rows[ri], k);
+            a[ri * K + k] = a_fmt == 0 ? oracle_mx_element(A, lda, SA, ldsa, rows[ri], k)
+                                       : oracle_mx_element_fmt(A, lda_bytes, a_fmt, SA, ldsa, rows[ri], k);
     for (int64_t cj = 0; cj < ncols; ++cj)
         for (int64_t k = 0; k < K; ++k)
             b[cj * K + k] = oracle_mx_element(B, ldb, SB, ldsb, cols[cj], k);
