@@ -128,6 +128,39 @@ __device__ __forceinline__ v4f mma_sel(int ob, int oa, v4i b, v4i a, v4f c, int 
     return c;
 }
 
+// A operand of a wider format (FP8 E4M3 / BF8 E5M2: 8 dwords; FP6 E2M3 /
+// E3M2: the low 6 dwords), B FP4: the hardware format code of A (the
+// instruction's "blgp", since B is the instruction's first source) selects
+// the element type ("CDNA4 dense MFMA builtins", "Mixed-precision with
+// scaling": codes 0 FP8, 1 BF8, 2 FP6 E2M3, 3 FP6 E3M2, 4 FP4).
+template <int FMT_A, int OPSEL_B, int OPSEL_A>
+__device__ __forceinline__ v4f mfma_fp4_wide(v4i bfrag, v8i afrag, v4f acc, int sb, int sa)
+{
+    v8i b = {bfrag[0], bfrag[1], bfrag[2], bfrag[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, afrag, acc, kFmtFp4, FMT_A, OPSEL_B, sb,
+                                                           OPSEL_A, sa);
+}
+
+template <int FMT_A>
+__device__ __forceinline__ v4f mma_sel_wide(int ob, int oa, v4i b, v8i a, v4f c, int sb, int sa)
+{
+#define MX_CASE(OB, OA) \
+    case OB * 4 + OA: return mfma_fp4_wide<FMT_A, OB, OA>(b, a, c, sb, sa);
+    switch (ob * 4 + oa) {
+        MX_CASE(0, 0) MX_CASE(0, 1) MX_CASE(0, 2) MX_CASE(0, 3)
+        MX_CASE(1, 0) MX_CASE(1, 1) MX_CASE(1, 2) MX_CASE(1, 3)
+        MX_CASE(2, 0) MX_CASE(2, 1) MX_CASE(2, 2) MX_CASE(2, 3)
+        MX_CASE(3, 0) MX_CASE(3, 1) MX_CASE(3, 2) MX_CASE(3, 3)
+    }
+#undef MX_CASE
+    return c;
+}
+
+// A formats, the library's ids (mxgemm_strides.a_format): element width and
+// the matrix instruction's format code
+constexpr int kFmtBits[5] = {4, 8, 8, 6, 6};
+constexpr int kFmtHw[5] = {4, 0, 1, 2, 3};
+
 // fp32 -> bf16, round to nearest, ties to even; NaN stays NaN (quiet).
 // Two floats to two bf16 (round to nearest even) packed low/high: one
 // v_cvt_pk_bf16_f32, which rounds with the wave's mode (nearest even, fp32

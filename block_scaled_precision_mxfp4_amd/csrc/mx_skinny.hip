@@ -21,6 +21,8 @@
 #include "mx_device.hpp"
 #include "mx_pipe.hpp"
 
+#include <type_traits>
+
 namespace mx {
 
 // A1: A is a single row (M == 1, row-major scales).  Each wave then loads
@@ -29,10 +31,42 @@ namespace mx {
 // load per step, and forms each step's operand with cross-lane permutes:
 // operand lane l takes K-block 4u + l/16 of step u.  Operand lanes of rows
 // 1..15 then carry row 0's values too; their result rows are never stored.
-template <int MG, int NR, bool BPACK, bool SVEC, bool APACK, bool A1>
+// AFMT: A's format (0 FP4; 1 FP8 E4M3, 2 BF8 E5M2, 3 FP6 E2M3, 4 FP6 E3M2;
+// B is FP4).  A lane's operand is 32 elements of its row, 16, 32 or 24
+// bytes held as 4, 8 or 6 dwords.  For the 4- and 6-bit formats they are
+// K-block g = lane/16 of the 128-K step.  For the 8-bit formats the
+// instruction reads the 32 bytes as two runs of 16 elements, K 16g..16g+15
+// and 64+16g..64+16g+15 of the step (found with an identity-B probe on
+// MI355X; the scales still go by 32-element block, lane g holding block
+// g's), so the lane loads those two 16-byte pieces.
+template <int MG, int NR, bool BPACK, bool SVEC, bool APACK, bool A1, int AFMT = 0>
 __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
 {
     static_assert(!A1 || (MG == 1 && !APACK), "single-row A: one row group, row-major scales");
+    constexpr int AW = kFmtBits[AFMT];  // dwords of a lane's A operand (= element bits)
+    constexpr int AKB = 4 * AW;         // bytes of one A K-block
+    constexpr bool A8 = AW == 8;        // 8-bit A: two 16-element runs per lane
+    using a_t = typename std::conditional<AFMT == 0, v4i, v8i>::type;
+    // A1 with 8-bit A holds one 16-byte chunk per lane, else one K-block
+    using aw_t = typename std::conditional<A8, v4i, a_t>::type;
+    static_assert(!(A1 && A8) || (NR + MG) <= 3, "single-row 8-bit A: 8 steps per batch, one chunk per lane");
+    // one lane's K-block of A at byte offset off (out-of-range offsets read zeros)
+    auto load_a = [](__amdgpu_buffer_rsrc_t r, uint32_t off) __attribute__((always_inline)) {
+        if constexpr (AFMT == 0) {
+            return load16(r, off);
+        } else {
+            const v4i lo = load16(r, off);
+            v8i a = {lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+            if constexpr (AW == 8) {
+                const v4i hi = load16(r, off == kOOB ? kOOB : off + 16);
+                a[4] = hi[0], a[5] = hi[1], a[6] = hi[2], a[7] = hi[3];
+            } else {
+                const v2u hi = load8(r, off == kOOB ? kOOB : off + 16);
+                a[4] = (int)hi[0], a[5] = (int)hi[1];
+            }
+            return a;
+        }
+    };
     constexpr int R = 16 * NR;                      // B rows per workgroup
     constexpr int NF = NR * MG;                     // 16x16 result blocks per workgroup
     constexpr int U = (NR + MG) <= 3 ? 8 : 4;       // 128-K steps per batch (two batches in flight)
@@ -88,14 +122,15 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
     }
 
     struct Batch {
-        v4i b[U][NR], a[A1 ? 1 : U][MG];
+        v4i b[U][NR];
+        a_t a[A1 ? 1 : U][MG];
         // scales as loaded: packed, one word per step pair (both row halves);
         // row-major, one raw 16-byte group per 4 steps
         uint32_t sbp[BPACK ? U / 2 : 1][NR];
         v4i sbr[BPACK ? 1 : G][NR];
         uint32_t sap[APACK ? U / 2 : 1][MG];
         v4i sar[APACK || A1 ? 1 : G][MG];
-        v4i aw;        // A1: K-block kb0 + lane of row 0
+        aw_t aw;       // A1: K-block kb0 + lane (8-bit A: 16-byte chunk lane) of row 0
         uint32_t saw;  // A1: its scale byte
     };
 
@@ -126,16 +161,32 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
                 else
                     bt.b[u][nr] = load16_stream(rb, ok ? (uint32_t)((nr * 16 + (lane & 15)) * g.ldb_b + kb * 16) : kOOB);
             }
-            if constexpr (!A1) {
+            if constexpr (!A1 && A8) {
+                // bytes 16g..16g+15 (K-block 2*ks0.. first pair) and 64+16g.. of the step
+                const int gq = lane >> 4;
+                const bool ok_lo = ks * 4 + (gq >> 1) < kb_wend, ok_hi = ks * 4 + 2 + (gq >> 1) < kb_wend;
+#pragma unroll
+                for (int mg = 0; mg < MG; ++mg) {
+                    const uint32_t base = (uint32_t)((mg * 16 + (lane & 15)) * g.lda_b + ks * 128 + gq * 16);
+                    const v4i lo = load16(ra, ok_lo ? base : kOOB), hi = load16(ra, ok_hi ? base + 64 : kOOB);
+                    bt.a[u][mg] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+            } else if constexpr (!A1) {
 #pragma unroll
                 for (int mg = 0; mg < MG; ++mg)
-                    bt.a[u][mg] = load16(ra, ok ? (uint32_t)((mg * 16 + (lane & 15)) * g.lda_b + kb * 16) : kOOB);
+                    bt.a[u][mg] = load_a(ra, ok ? (uint32_t)((mg * 16 + (lane & 15)) * g.lda_b + kb * AKB) : kOOB);
             }
         }
         if constexpr (A1) {
             const int kbl = ks0 * 4 + lane;
             const bool okl = lane < 4 * U && kbl < kb_wend;
-            bt.aw = load16(ra, okl ? (uint32_t)(kbl * 16) : kOOB);
+            if constexpr (A8) {
+                // 16-byte chunk `lane` of the batch (K-block kb0 + lane/2)
+                const bool okc = ks0 * 4 + (lane >> 1) < kb_wend;
+                bt.aw = load16(ra, okc ? (uint32_t)(ks0 * 128 + lane * 16) : kOOB);
+            } else {
+                bt.aw = load_a(ra, okl ? (uint32_t)(kbl * AKB) : kOOB);
+            }
             bt.saw = load1(rsa, okl ? (uint32_t)kbl : kOOB);
         }
 #pragma unroll
@@ -188,7 +239,7 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
 
     // vector-memory instructions of one load_batch (all lanes issue all of
     // them): staged B, the single A row and its scales, row-major B scales
-    constexpr int LN = NR * U + 2 + G * NR * (SVEC ? 1 : 4);
+    constexpr int LN = NR * U + (AW == 6 ? 3 : 2) + G * NR * (SVEC ? 1 : 4);
     static_assert(!BST || LN < 64, "vmcnt range");
     auto compute = [&](const Batch &bt, auto bufc, auto lastc) __attribute__((always_inline)) {
         v4i bst[BST ? U : 1][NR];
@@ -214,13 +265,24 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            v4i a1;
+            a_t a1 = {};
             uint32_t sa1 = 0;
+            if constexpr (A1 && A8) {
+                // chunks 8u + g and 8u + 4 + g of the batch
+                const int lo = (8 * u + (lane >> 4)) * 4, hi = lo + 16;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a1[i] = __builtin_amdgcn_ds_bpermute(lo, bt.aw[i]);
+                    a1[4 + i] = __builtin_amdgcn_ds_bpermute(hi, bt.aw[i]);
+                }
+            }
             if constexpr (A1) {
                 const int src = (4 * u + (lane >> 4)) * 4;  // byte address of the source lane
+                if constexpr (!A8) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a1[i] = __builtin_amdgcn_ds_bpermute(src, bt.aw[i]);
+                    for (int i = 0; i < AW; ++i)
+                        a1[i] = __builtin_amdgcn_ds_bpermute(src, bt.aw[i]);
+                }
                 sa1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)bt.saw) & 0xFFu;
             }
 #pragma unroll
@@ -235,8 +297,12 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
                     const uint32_t sar = A1      ? sa1
                                          : APACK ? bt.sap[u / 2][mg] >> (8 * (mg & 1))
                                                  : scale_group_word<SVEC>(bt.sar[u / 4][mg], lane);
-                    acc[nr][mg] = mma_sel(ob, oa, BST ? bst[BST ? u : 0][nr] : bt.b[u][nr], A1 ? a1 : bt.a[u][mg],
-                                          acc[nr][mg], (int)sbr, (int)sar);
+                    const v4i bf = BST ? bst[BST ? u : 0][nr] : bt.b[u][nr];
+                    if constexpr (AFMT == 0)
+                        acc[nr][mg] = mma_sel(ob, oa, bf, A1 ? a1 : bt.a[u][mg], acc[nr][mg], (int)sbr, (int)sar);
+                    else
+                        acc[nr][mg] = mma_sel_wide<kFmtHw[AFMT]>(ob, oa, bf, A1 ? a1 : bt.a[u][mg], acc[nr][mg],
+                                                                 (int)sbr, (int)sar);
                 }
         }
     };
@@ -353,6 +419,38 @@ static void launch_skinny(const GemmArgs &g, int grid, hipStream_t s)
             hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, true, false, false>), dim3(grid), dim3(256), 0, s, g);
         else
             hipLaunchKernelGGL((mx_skinny_kernel<MG, NR, BPACK, false, false, false>), dim3(grid), dim3(256), 0, s, g);
+    }
+}
+
+// Wider A formats: one row group (M <= 16 per launch), row-major A scales.
+template <int AFMT, bool BPACK>
+static void launch_skinny_fmt(const GemmArgs &g, int grid, hipStream_t s)
+{
+    if (g.M == 1) {
+        if (g.scale16 || BPACK)
+            hipLaunchKernelGGL((mx_skinny_kernel<1, 1, BPACK, true, false, true, AFMT>), dim3(grid), dim3(256), 0, s, g);
+        else
+            hipLaunchKernelGGL((mx_skinny_kernel<1, 1, BPACK, false, false, true, AFMT>), dim3(grid), dim3(256), 0, s, g);
+        return;
+    }
+    if (g.scale16)
+        hipLaunchKernelGGL((mx_skinny_kernel<1, 1, BPACK, true, false, false, AFMT>), dim3(grid), dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((mx_skinny_kernel<1, 1, BPACK, false, false, false, AFMT>), dim3(grid), dim3(256), 0, s, g);
+}
+
+void launch_skinny_wide(int a_fmt, bool b_packed, const GemmArgs &g, int grid, hipStream_t s)
+{
+    switch (a_fmt * 2 + (b_packed ? 1 : 0)) {
+    case 2: launch_skinny_fmt<1, false>(g, grid, s); break;
+    case 3: launch_skinny_fmt<1, true>(g, grid, s); break;
+    case 4: launch_skinny_fmt<2, false>(g, grid, s); break;
+    case 5: launch_skinny_fmt<2, true>(g, grid, s); break;
+    case 6: launch_skinny_fmt<3, false>(g, grid, s); break;
+    case 7: launch_skinny_fmt<3, true>(g, grid, s); break;
+    case 8: launch_skinny_fmt<4, false>(g, grid, s); break;
+    case 9: launch_skinny_fmt<4, true>(g, grid, s); break;
+    default: break;
     }
 }
 

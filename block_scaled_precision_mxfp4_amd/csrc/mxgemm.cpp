@@ -79,7 +79,8 @@ constexpr double kHbm = 5.0e12;
 constexpr int kMinSkinnyChunk = 64;
 constexpr double kCuL2 = 64.0 * 2.4e9;
 
-Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool tiled_only = false)
+Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool tiled_only = false,
+              int force_nr = 0)
 {
     const int KB = K / 32;
     if (num_cu <= 0)
@@ -146,6 +147,8 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool
         int nr = 1;
         if (const char *e = std::getenv("MXGEMM_FORCE_NR"))
             nr = std::atoi(e) >= 4 ? 4 : (std::atoi(e) >= 2 ? 2 : 1);
+        if (force_nr > 0)
+            nr = force_nr;
         const int nri = nr == 1 ? 0 : (nr == 2 ? 1 : 2);
         const int rows_wg = 16 * nr;
         const int tiles = cdiv(N, rows_wg);
@@ -419,7 +422,10 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
         s = *strides;
         if ((s.b_packed != 0 && s.b_packed != 1) || (s.sa_packed != 0 && s.sa_packed != 1) ||
             (s.sa_packed && !s.b_packed) || (s.c_f32 != 0 && s.c_f32 != 1) ||
-            (s.split_mode != MXGEMM_SPLIT_FP32 && s.split_mode != MXGEMM_SPLIT_BF16_ATOMIC))
+            (s.split_mode != MXGEMM_SPLIT_FP32 && s.split_mode != MXGEMM_SPLIT_BF16_ATOMIC) ||
+            s.a_format < MXGEMM_FMT_FP4 || s.a_format > MXGEMM_FMT_FP6_E3M2 || s.reserved != 0)
+            return MXGEMM_ERR_INVALID_ARG;
+        if (s.a_format != MXGEMM_FMT_FP4 && (s.sa_packed || s.split_mode != MXGEMM_SPLIT_FP32))
             return MXGEMM_ERR_INVALID_ARG;
     } else {
         std::memset(&s, 0, sizeof s);
@@ -432,9 +438,15 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
         return MXGEMM_ERR_SHAPE;
     if (!s.b_packed && (s.ldb < K || s.ldsb < KB))
         return MXGEMM_ERR_SHAPE;
-    if (s.lda % 2 || (!s.b_packed && s.ldb % 2))
+    // A's byte pitch: lda elements of its format (FP4: 4 bits, FP8: 8, FP6: 6)
+    static const int kBits[5] = {4, 8, 8, 6, 6};
+    const int a_bits = kBits[s.a_format];
+    if ((s.lda * a_bits) % 8 || (!s.b_packed && s.ldb % 2))
         return MXGEMM_ERR_ALIGN;
-    if (!aligned(A, 16) || !aligned(B, 16) || (s.lda / 2) % 16 || (!s.b_packed && (s.ldb / 2) % 16))
+    const int64_t lda_bytes = s.lda * a_bits / 8;
+    // (an FP6 row of K elements is 24 * K/32 bytes: its loads need 8-byte rows)
+    if (!aligned(A, 16) || !aligned(B, 16) || lda_bytes % (a_bits == 6 ? 8 : 16) ||
+        (!s.b_packed && (s.ldb / 2) % 16))
         return MXGEMM_ERR_ALIGN;
     if ((s.b_packed && !aligned(scaleB, 4)) || (s.sa_packed && !aligned(scaleA, 4)))
         return MXGEMM_ERR_ALIGN;
@@ -444,7 +456,7 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     if (atomic && (!aligned(D, 4) || s.ldd % 2 || N % 2))
         return MXGEMM_ERR_ALIGN;
     // byte offsets inside a tile must stay below 2^31
-    if ((int64_t)256 * (s.lda / 2) >= ((int64_t)1 << 31) || (!s.b_packed && (int64_t)256 * (s.ldb / 2) >= ((int64_t)1 << 31)))
+    if ((int64_t)256 * lda_bytes >= ((int64_t)1 << 31) || (!s.b_packed && (int64_t)256 * (s.ldb / 2) >= ((int64_t)1 << 31)))
         return MXGEMM_ERR_SHAPE;
 
     // ---- device and plan
@@ -452,7 +464,11 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     st = device_info(&d);
     if (st != MXGEMM_OK)
         return st;
-    Plan p = plan_for(M, N, K, s.b_packed, split_k, d->num_cu, atomic);
+    // A in a wider format: the skinny kernel (one 16-row group, nr 1), one
+    // launch per 16 rows of A
+    const bool wide = s.a_format != MXGEMM_FMT_FP4;
+    Plan p = wide ? plan_for(std::min(M, 16), N, K, s.b_packed, split_k, d->num_cu, false, 1)
+                  : plan_for(M, N, K, s.b_packed, split_k, d->num_cu, atomic);
 
     GemmArgs g;
     std::memset(&g, 0, sizeof g);
@@ -468,7 +484,7 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     g.N = N;
     g.K = K;
     g.KB = KB;
-    g.lda_b = s.lda / 2;
+    g.lda_b = lda_bytes;
     g.ldb_b = s.ldb / 2;
     g.ldsa = s.ldsa;
     g.ldsb = s.ldsb;
@@ -513,7 +529,20 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
         return MXGEMM_ERR_SHAPE;
     if (g.split_atomic)
         mx::launch_d_init(g, stream);
-    if (p.family == 0) {
+    if (wide) {
+        // stream-ordered launches over 16-row blocks of A, C and D; the split
+        // counters return to zero at the end of each
+        for (int m0 = 0; m0 < M; m0 += 16) {
+            GemmArgs gb = g;
+            gb.M = std::min(16, M - m0);
+            gb.A = g.A + (int64_t)m0 * g.lda_b;
+            gb.SA = g.SA + (int64_t)m0 * g.ldsa;
+            gb.D = g.D + (int64_t)m0 * g.ldd;
+            if (g.C)
+                gb.C = (const uint8_t *)g.C + (int64_t)m0 * g.ldc * (g.c_f32 ? 4 : 2);
+            mx::launch_skinny_wide(s.a_format, s.b_packed != 0, gb, (int)p.grid, stream);
+        }
+    } else if (p.family == 0) {
         int n = 0;
         const mx::TileKernel &k = mx::tile_kernels(&n)[p.index];
         // the four-slot ring kernel moves scales as 4-byte words and whole

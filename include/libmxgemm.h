@@ -76,7 +76,22 @@ const char *mxgemm_status_string(mxgemm_status status);
  * and ldd are honoured separately, so D may alias C (in place) when ldc ==
  * ldd and C is bf16.
  *
- * The two option fields at the end default to 0 (a zeroed struct):
+ * The option fields at the end default to 0 (a zeroed struct):
+ *   a_format   A's element format, MXGEMM_FMT_*: FP4 E2M1 (the default),
+ *              FP8 E4M3, BF8 E5M2, FP6 E2M3 or FP6 E3M2 -- the inputs of the
+ *              scaled matrix instructions ("CDNA4 dense MFMA builtins",
+ *              "Mixed-precision with scaling"; encodings per the OCP MX
+ *              v1.0 specification).  B stays FP4.  A row is a little-endian
+ *              bit stream of the format's w-bit codes (element k at bits
+ *              k*w .. k*w+w-1; for FP4 the low-nibble-first bytes), one E8M0
+ *              scale per 32 elements as for FP4.  lda counts elements of
+ *              A's format; the byte pitch lda*w/8 must be a whole multiple of
+ *              16 (of 8 for the FP6 formats, whose dense rows are 24 bytes
+ *              per 32 elements).  A wider format runs on the skinny kernel,
+ *              one launch per
+ *              16 rows of A (at M = 1 the speed of the FP4 case; for large M
+ *              B is read once per 16 rows).  It needs sa_packed = 0 and
+ *              split_mode = MXGEMM_SPLIT_FP32 (else MXGEMM_ERR_INVALID_ARG).
  *   c_f32      C is float32 instead of bf16.  The README's "C / bias" note
  *              says aiter documents its bias operand as f32; with c_f32 = 1
  *              the epilogue reads that type (D stays bf16; one rounding of
@@ -97,10 +112,16 @@ const char *mxgemm_status_string(mxgemm_status status);
 #define MXGEMM_SPLIT_FP32        0
 #define MXGEMM_SPLIT_BF16_ATOMIC 1
 
+#define MXGEMM_FMT_FP4      0  /* E2M1, 4 bits */
+#define MXGEMM_FMT_FP8_E4M3 1  /* 8 bits */
+#define MXGEMM_FMT_FP8_E5M2 2  /* 8 bits */
+#define MXGEMM_FMT_FP6_E2M3 3  /* 6 bits */
+#define MXGEMM_FMT_FP6_E3M2 4  /* 6 bits */
+
 typedef struct mxgemm_strides {
     int64_t ldd;      /* bf16 elements between rows of D, >= N */
     int64_t ldc;      /* elements between rows of C, >= N (ignored if beta == 0) */
-    int64_t lda;      /* fp4 elements between rows of A, >= K, even */
+    int64_t lda;      /* elements between rows of A (fp4 unless a_format says otherwise), >= K */
     int64_t ldb;      /* fp4 elements between rows of B, >= K, even (ignored if b_packed) */
     int64_t ldsa;     /* bytes between rows of scaleA, >= K/32 */
     int64_t ldsb;     /* bytes between rows of scaleB, >= K/32 (ignored if b_packed) */
@@ -111,6 +132,8 @@ typedef struct mxgemm_strides {
     size_t workspace_bytes;
     int32_t c_f32;      /* 0: C is bf16; 1: C is float32 */
     int32_t split_mode; /* MXGEMM_SPLIT_FP32 or MXGEMM_SPLIT_BF16_ATOMIC */
+    int32_t a_format;   /* MXGEMM_FMT_* */
+    int32_t reserved;   /* 0 */
 } mxgemm_strides;
 
 /* ---- the GEMM ------------------------------------------------------------- */

@@ -54,9 +54,10 @@ def gemm_gpu(p: dict, split_k: int = -1, b_packed: bool = False, D=None, stream=
     if D is None:
         D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     strides = None
-    if c_f32 or split_mode:
+    a_fmt = int(p.get("a_fmt", 0))
+    if c_f32 or split_mode or a_fmt:
         strides = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32,
-                                  c_f32=int(c_f32), split_mode=split_mode)
+                                  c_f32=int(c_f32), split_mode=split_mode, a_format=a_fmt)
     if b_packed:
         info = mx.mxgemm_plan(M, N, K, 1, -1, 256)
         Bp = torch.empty(info["packed_b_bytes"], dtype=torch.uint8, device="cuda")
@@ -68,7 +69,8 @@ def gemm_gpu(p: dict, split_k: int = -1, b_packed: bool = False, D=None, stream=
             mx.mxgemm_pack_scales(SAp, SA, M, K)
             SA = SAp
         strides = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32, b_packed=1,
-                                  sa_packed=int(sa_packed), c_f32=int(c_f32), split_mode=split_mode)
+                                  sa_packed=int(sa_packed), c_f32=int(c_f32), split_mode=split_mode,
+                                  a_format=a_fmt)
     mx.mxgemm_run(D, C if p["beta"] != 0.0 else None, A, B, SA, SB, p["alpha"], p["beta"], M, N, K,
                   strides=strides, split_k=split_k, stream=stream)
     torch.cuda.synchronize()
@@ -77,7 +79,7 @@ def gemm_gpu(p: dict, split_k: int = -1, b_packed: bool = False, D=None, stream=
 
 def oracle_ref(p: dict, rows=None, cols=None):
     return oracle.mxgemm(p["A"], p["SA"], p["B"], p["SB"], p["K"], p["alpha"], p["beta"],
-                         p.get("C"), rows=rows, cols=cols)
+                         p.get("C"), rows=rows, cols=cols, a_fmt=int(p.get("a_fmt", 0)))
 
 
 def compare(d_bits: np.ndarray, ref: np.ndarray, mag: np.ndarray):

@@ -100,6 +100,19 @@ def test_run_stride_validation():
     assert _run(strides=st(split_mode=-1)) == -1
     # an f32 C needs 4-byte alignment (a bf16 C: 2)
     assert _run(strides=st(c_f32=1), beta=1.0, C=0x6002) == -3
+    # A formats: 0..4; wider formats need row-major A scales and the fp32 split;
+    # the reserved field must be 0; A's byte pitch lda * w / 8 a multiple of 16
+    assert _run(strides=st(a_format=5)) == -1
+    assert _run(strides=st(a_format=-1)) == -1
+    s = st(a_format=1)
+    s.reserved = 1
+    assert _run(strides=s) == -1
+    assert _run(strides=st(a_format=1, ldsa=0, ldb=0, ldsb=0, b_packed=1, sa_packed=1)) == -1
+    assert _run(strides=st(a_format=2, split_mode=1)) == -1
+    assert _run(strides=st(a_format=1, lda=520)) == -3   # 520-byte pitch
+    assert _run(strides=st(a_format=3, lda=516)) == -3   # 387-byte pitch
+    assert _run(strides=st(a_format=4, lda=528)) == -3   # 396 bytes: not a multiple of 8
+    assert _run(strides=st(a_format=4, lda=510)) == -2   # lda < K
     # bf16-atomic split-K: D 4-byte aligned, ldd and N even
     assert _run(strides=st(split_mode=1), D=0x1002) == -3
     assert _run(strides=st(split_mode=1, ldd=257)) == -3

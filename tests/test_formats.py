@@ -1,0 +1,85 @@
+"""GPU parity of mixed-format GEMMs, through the C-ABI: A in FP8 E4M3,
+BF8 E5M2, FP6 E2M3 or FP6 E3M2 (the other inputs of the scaled matrix
+instructions, "CDNA4 dense MFMA builtins", "Mixed-precision with scaling"),
+B in FP4, against the oracle's exact fp64 reference with the per-element
+tolerance of the FP4 tests.
+
+Cases cover the single-row path (M = 1), one 16-row block, several blocks
+with a ragged last one, K tails, ragged N, forced split-K, packed B, and C
+in bf16 and f32; the 1 x 8192 x 8192 decode shape is checked on sampled
+columns.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import block_scaled_precision_mxfp4_amd as mx
+from block_scaled_precision_mxfp4_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from mxgpu import assert_parity, gemm_gpu, oracle_ref  # noqa: E402
+
+FORMATS = [mx.FMT_FP8_E4M3, mx.FMT_FP8_E5M2, mx.FMT_FP6_E2M3, mx.FMT_FP6_E3M2]
+NAMES = {1: "e4m3", 2: "e5m2", 3: "e2m3", 4: "e3m2"}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# (M, N, K, split, b_packed, C): C None, "bf16" or "f32"
+CASES = [
+    (1, 1000, 2048, 1, False, None),
+    (1, 777, 1056, -1, False, "bf16"),
+    (5, 512, 4096, 4, False, None),
+    (16, 300, 512, 1, True, "f32"),
+    (17, 640, 2048, 2, False, "bf16"),
+    (40, 333, 1024, 1, True, None),
+    (70, 256, 4096, 8, False, "f32"),
+]
+
+
+def problem(case, fmt, seed):
+    M, N, K, split, packed, c = case
+    e = (120, 134) if fmt in (3, 4) else (110, 130)  # keep FP8 products inside fp32's range
+    p = inputs.make_problem(M, N, K, seed=seed, e=e, beta=0.0 if c is None else 1.0,
+                            c_sigma=None if c is None else 2.0, a_fmt=fmt)
+    if c == "f32":
+        rng = np.random.default_rng(seed)
+        p["C"] = (rng.standard_normal((M, N)) * 2.0).astype(np.float32)
+    if c is not None:
+        p["beta"] = -0.75
+    p["alpha"] = 0.5
+    return p
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=lambda f: NAMES[f])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "%dx%dx%d_s%d%s%s" % (
+    c[0], c[1], c[2], c[3], "_packed" if c[4] else "", "_" + c[5] if c[5] else ""))
+def test_mixed_format_matches_oracle(case, fmt):
+    M, N, K, split, packed, c = case
+    p = problem(case, fmt, seed=0xF0F0 + 97 * fmt + M * 7 + N)
+    say("case", NAMES[fmt], case)
+    d = gemm_gpu(p, split_k=split, b_packed=packed)
+    ref, mag, _ = oracle_ref(p)
+    assert_parity(d, ref, mag, "%s %s" % (NAMES[fmt], case))
+
+
+@pytest.mark.parametrize("fmt", FORMATS, ids=lambda f: NAMES[f])
+def test_decode_shape_sampled(fmt):
+    """1 x 8192 x 8192, the decode shape of the M = 1 workload, with A in
+    the wider format; 256 sampled columns against the oracle."""
+    M = 1
+    N = K = 8192
+    p = inputs.make_problem(M, N, K, seed=0xDEC + fmt, e=(120, 134) if fmt in (3, 4) else (115, 128),
+                            a_fmt=fmt)
+    p["alpha"] = 0.5
+    say("case decode", NAMES[fmt])
+    d = gemm_gpu(p)
+    cols = np.sort(np.random.default_rng(fmt).choice(N, 256, replace=False))
+    ref, mag, _ = oracle_ref(p, cols=cols)
+    assert_parity(d[:, cols], ref, mag, "decode %s" % NAMES[fmt])
+
