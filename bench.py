@@ -60,14 +60,14 @@ def measured_traffic(workload):
     return None if w is None else w["traffic_bytes"]
 
 
-def algorithmic_bytes(M, N, K, beta):
-    b = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + 2 * M * N
+def algorithmic_bytes(M, N, K, beta, a_bits=4):
+    b = M * K * a_bits // 8 + M * K // 32 + N * K // 2 + N * K // 32 + 2 * M * N
     if beta != 0.0:
         b += 2 * M * N
     return b
 
 
-def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soak_ms=0.0):
+def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soak_ms=0.0, a_fmt=0):
     import numpy as np
     import torch
 
@@ -77,8 +77,12 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soa
     p = inputs.make_workload(name)
     M, N, K, alpha, beta = p["M"], p["N"], p["K"], p["alpha"], p["beta"]
     packed, sa_packed = p["b_packed"], p["sa_packed"]
-    info = mx.mxgemm_query(M, N, K, int(packed), split_k)
-    ws_bytes = algorithmic_bytes(M, N, K, beta)
+    a_bits = mx.FORMAT_BITS[a_fmt]
+    if a_fmt:  # the same workload with A in a wider format (row-major A scales)
+        p["A"] = inputs.wide_codes(inputs.SEED_BASE + 0x100 + a_fmt, M, K, a_fmt)
+        sa_packed = False
+    info = mx.mxgemm_query(min(M, 16) if a_fmt else M, N, K, int(packed), split_k)
+    ws_bytes = algorithmic_bytes(M, N, K, beta, a_bits)
     copies = 1
     if rotate and ws_bytes < 2 * LLC_BYTES:
         copies = min(64, math.ceil(2.5 * LLC_BYTES / ws_bytes))
@@ -107,7 +111,7 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soa
     wsp = torch.zeros(max(info["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
     strides = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32,
                               b_packed=int(packed), sa_packed=int(sa_packed), workspace=wsp,
-                              workspace_bytes=wsp.numel())
+                              workspace_bytes=wsp.numel(), a_format=a_fmt)
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
@@ -168,22 +172,28 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soa
     gpu_ms = e0.elapsed_time(e1)
     per = gpu_ms / 1e3 / steps
     flops = 2.0 * M * N * K
-    r = dict(workload=name, M=M, N=N, K=K, alpha=alpha, beta=beta, b_packed=bool(packed),
+    r = dict(workload=name, a_format=a_fmt, M=M, N=N, K=K, alpha=alpha, beta=beta, b_packed=bool(packed),
              sa_packed=bool(sa_packed),
              kernel=info["kernel_name"], tile="%dx%d" % (info["tile_m"], info["tile_n"]),
              split_k=info["split_k"], grid=info["grid"], copies=copies, timing=timing,
              us_per_step=per * 1e6, tflops=flops / per / 1e12,
-             gbs=algorithmic_bytes(M, N, K, beta) / per / 1e9,
-             algorithmic_bytes=algorithmic_bytes(M, N, K, beta), wall_s=wall, gpu_ms=gpu_ms,
+             gbs=algorithmic_bytes(M, N, K, beta, a_bits) / per / 1e9,
+             algorithmic_bytes=algorithmic_bytes(M, N, K, beta, a_bits), wall_s=wall, gpu_ms=gpu_ms,
              peak_flops_device=info["peak_flops"], clock_hz=info["clock_hz"], num_cu=info["num_cu"],
              arch=info["arch"])
     del sets, wsp
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     log("%-24s %-22s split %2d  %9.2f us  %8.1f TFLOP/s  %8.1f GB/s  (%s, %d copies)" % (
-        name, r["kernel"], r["split_k"], r["us_per_step"], r["tflops"], r["gbs"], timing, copies))
+        name + ("" if not a_fmt else " A:" + FORMAT_NAMES[a_fmt]), r["kernel"], r["split_k"], r["us_per_step"],
+        r["tflops"], r["gbs"], timing, copies))
     return r
 
+
+FORMAT_NAMES = {0: "fp4", 1: "fp8_e4m3", 2: "fp8_e5m2", 3: "fp6_e2m3", 4: "fp6_e3m2"}
+# mixed-format lines: (workload, A format) -- decode and a small batch with
+# FP8 and FP6 activations against FP4 weights
+MIXED = [("gemv_1x8192x8192", 1), ("gemv_1x8192x8192", 3), ("skinny_64x7168x16384", 1)]
 
 QUANT_SHAPE = (8192, 8192)  # the bf16 activation of the square workload's A
 
@@ -354,6 +364,16 @@ def main():
 
     quant = None if args.only else time_quantize(args.steps, args.warmup, eager=args.eager)
 
+    mixed = []
+    if not args.only:
+        for name, fmt in MIXED:
+            r = time_workload(name, args.steps, args.warmup, eager=args.eager, soak_ms=args.soak_ms, a_fmt=fmt)
+            mixed.append({"workload": name, "a_format": FORMAT_NAMES[fmt], "us_per_step": r["us_per_step"],
+                          "value": r["gbs"], "unit": "GB/s", "tflops": r["tflops"],
+                          "algorithmic_bytes": r["algorithmic_bytes"], "kernel": r["kernel"],
+                          "roofline": {"bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS,
+                                       "unit": "GB/s", "frac": r["gbs"] / PEAK_HBM_GBS, "traffic": None}})
+
     base = None
     if not args.no_cpu_baseline:
         base = cpu_baseline(args.workload)
@@ -382,6 +402,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": base,
         "m1": m1,
+        "mixed": mixed,
         "quantize": quant,
         "device": {"arch": head["arch"], "num_cu": head["num_cu"], "clock_hz": head["clock_hz"],
                    "derived_peak_tflops": head["peak_flops_device"] / 1e12},
