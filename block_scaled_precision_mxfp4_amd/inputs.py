@@ -140,6 +140,17 @@ def gaussian_bf16(seed: int, rows: int, cols: int, sigma: float) -> np.ndarray:
     return f32_to_bf16_bits(z.astype(np.float32)).reshape(rows, cols)
 
 
+def gaussian_f16(seed: int, rows: int, cols: int, sigma: float) -> np.ndarray:
+    """fp16 bit patterns [rows, cols] of N(0, sigma^2) draws (Box-Muller,
+    rounded to nearest by numpy's float16 conversion)."""
+    n = rows * cols
+    w = splitmix64(seed, 2 * n)
+    u1 = ((w[0::2] >> np.uint64(11)).astype(np.float64) + 1.0) * 2.0 ** -53
+    u2 = (w[1::2] >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
+    z = np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2) * sigma
+    return z.astype(np.float16).view(np.uint16).reshape(rows, cols)
+
+
 # The five workloads.  Sizes, code and exponent distributions, alpha, beta
 # and C follow the statement of each case; `b_packed` marks the case that is
 # run on the pre-shuffled B layout and `sa_packed` the one whose A scales are

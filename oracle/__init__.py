@@ -56,6 +56,10 @@ def _load():
             lib.oracle_bf16_to_double.restype = f64
             lib.oracle_fp4_code.argtypes = [u8p, i64, i64, i64]
             lib.oracle_fp4_code.restype = ctypes.c_uint
+            lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
+            lib.oracle_f16_to_double.restype = f64
+            lib.oracle_f16_gemm.argtypes = [i64, u8p, i64, u8p, i64, u8p, i64, u8p, i64, u8p, u8p]
+            lib.oracle_f16_gemm.restype = ctypes.c_int
             lib.oracle_decode.argtypes = [ctypes.c_int, ctypes.c_uint]
             lib.oracle_decode.restype = f64
             lib.oracle_format_bits.argtypes = [ctypes.c_int]
@@ -105,6 +109,47 @@ def fp4_code(X: np.ndarray, ld: int, r: int, k: int) -> int:
 
 # A formats (the library's ids): FP4 E2M1, FP8 E4M3, BF8 E5M2, FP6 E2M3, FP6 E3M2
 FMT_FP4, FMT_E4M3, FMT_E5M2, FMT_E2M3, FMT_E3M2 = 0, 1, 2, 3, 4
+
+
+def f16_to_float(h: int) -> float:
+    return float(_load().oracle_f16_to_double(int(h)))
+
+
+def f16_gemm(A, B, K, *, lda=None, ldb=None, rows=None, cols=None, threads=None):
+    """Reference C = A B for fp16 bit patterns A [M, lda], B [K, ldb]
+    (row-major, B K-major); returns (ref fp64, mag fp64) for rows x cols."""
+    lib = _load()
+    A = np.ascontiguousarray(A, dtype=np.uint16)
+    B = np.ascontiguousarray(B, dtype=np.uint16)
+    M, N = A.shape[0], B.shape[1]
+    lda = A.shape[1] if lda is None else lda
+    ldb = B.shape[1] if ldb is None else ldb
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.arange(N, dtype=np.int64) if cols is None else np.ascontiguousarray(cols, dtype=np.int64)
+    nr, nc = len(rows), len(cols)
+    ref = np.zeros((nr, nc), dtype=np.float64)
+    mag = np.zeros((nr, nc), dtype=np.float64)
+    if nr == 0 or nc == 0:
+        return ref, mag
+    threads = max(1, min(threads or min(16, os.cpu_count() or 1), nr))
+    bounds = np.linspace(0, nr, threads + 1).astype(np.int64)
+
+    def work(t):
+        r0, r1 = int(bounds[t]), int(bounds[t + 1])
+        if r1 <= r0:
+            return
+        rs = np.ascontiguousarray(rows[r0:r1])
+        r_ = np.zeros((r1 - r0, nc), dtype=np.float64)
+        m_ = np.zeros((r1 - r0, nc), dtype=np.float64)
+        lib.oracle_f16_gemm(K, _ptr(A), lda, _ptr(B), ldb, _ptr(rs), r1 - r0, _ptr(cols), nc, _ptr(r_), _ptr(m_))
+        ref[r0:r1], mag[r0:r1] = r_, m_
+
+    ths = [threading.Thread(target=work, args=(t,)) for t in range(threads)]
+    for th in ths:
+        th.start()
+    for th in ths:
+        th.join()
+    return ref, mag
 
 
 def decode(fmt: int, code: int) -> float:

@@ -268,6 +268,49 @@ int oracle_mxgemm(int64_t K, int a_fmt,
     return 0;
 }
 
+/* ---- FP16 GEMM ------------------------------------------------------------ */
+
+/*
+ * "CDNA4 MFMA transpose load builtins", "FP16 GEMM example": C = A * B with
+ * A [M][K] fp16 row-major, B [K][N] fp16 row-major and fp32 C.  The
+ * reference is the exact sum of the fp16 products in fp64, k ascending.
+ * fp16 is IEEE binary16: sign, 5 exponent bits (bias 15), 10 fraction bits;
+ * exponent 0 subnormal, 31 infinity or NaN.
+ */
+double oracle_f16_to_double(uint16_t h)
+{
+    const int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -24);
+    else
+        v = ldexp((double)(1024 + m), e - 25);
+    return s ? -v : v;
+}
+
+/* ref/mag for the sub-block rows[] x cols[]; lda, ldb in elements */
+int oracle_f16_gemm(int64_t K, const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                    const int64_t *rows, int64_t nrows, const int64_t *cols, int64_t ncols,
+                    double *ref, double *mag)
+{
+    for (int64_t ri = 0; ri < nrows; ++ri)
+        for (int64_t cj = 0; cj < ncols; ++cj) {
+            double acc = 0.0, m = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double p = oracle_f16_to_double(A[rows[ri] * lda + k]) *
+                                 oracle_f16_to_double(B[k * ldb + cols[cj]]);
+                acc += p;
+                m += fabs(p);
+            }
+            ref[ri * ncols + cj] = acc;
+            if (mag)
+                mag[ri * ncols + cj] = m;
+        }
+    return 0;
+}
+
 /* ---- exact mode ------------------------------------------------------------ */
 
 /*
