@@ -190,6 +190,58 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soa
     return r
 
 
+PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+
+
+def time_f16(steps, warmup, soak_ms=0.0, M=8192, N=8192, K=8192):
+    """mxgemm_f16_run (fp32 C = fp16 A x K-major fp16 B) on one 8192^3
+    problem, HIP-graph replay (operands stay in HBM and the last-level
+    cache between steps, as for the square MXFP4 workload)."""
+    import torch
+
+    import block_scaled_precision_mxfp4_amd as mx
+
+    g = torch.Generator(device="cuda").manual_seed(0xF16)
+    A = torch.randn((M, K), device="cuda", generator=g).to(torch.float16)
+    B = torch.randn((K, N), device="cuda", generator=g).to(torch.float16)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def launch():
+        mx.mxgemm_f16_run(C, A, B, M, N, K, stream=stream.cuda_stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            launch()
+    torch.cuda.synchronize()
+    if soak_ms > 0:
+        t_end = time.perf_counter() + soak_ms / 1e3
+        while time.perf_counter() < t_end:
+            with torch.cuda.stream(stream):
+                for _ in range(16):
+                    launch()
+            stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(steps):
+            launch()
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = e0.elapsed_time(e1) / 1e3 / steps
+    tflops = 2.0 * M * N * K / per / 1e12
+    log("%-24s %-22s           %9.2f us  %8.1f TFLOP/s  (hipgraph)" % ("f16_8192", "mx_f16_kernel", per * 1e6, tflops))
+    return {"workload": "f16_%dx%dx%d" % (M, N, K), "us_per_step": per * 1e6, "value": tflops, "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tflops / PEAK_F16_TFLOPS, "traffic": None}}
+
+
 FORMAT_NAMES = {0: "fp4", 1: "fp8_e4m3", 2: "fp8_e5m2", 3: "fp6_e2m3", 4: "fp6_e3m2"}
 # mixed-format lines: (workload, A format) -- decode and a small batch with
 # FP8 and FP6 activations against FP4 weights
@@ -364,6 +416,8 @@ def main():
 
     quant = None if args.only else time_quantize(args.steps, args.warmup, eager=args.eager)
 
+    f16 = None if args.only else time_f16(args.steps, args.warmup, soak_ms=args.soak_ms)
+
     mixed = []
     if not args.only:
         for name, fmt in MIXED:
@@ -403,6 +457,7 @@ def main():
         "cpu_baseline": base,
         "m1": m1,
         "mixed": mixed,
+        "f16": f16,
         "quantize": quant,
         "device": {"arch": head["arch"], "num_cu": head["num_cu"], "clock_hz": head["clock_hz"],
                    "derived_peak_tflops": head["peak_flops_device"] / 1e12},

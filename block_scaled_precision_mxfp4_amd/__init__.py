@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
 
 # C-ABI entry points declared in include/libmxgemm.h
 EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_pack_b", "mxgemm_pack_scales", "mxgemm_quantize",
-           "mxgemm_query", "mxgemm_plan", "mxgemm_release_workspaces")
+           "mxgemm_f16_run", "mxgemm_query", "mxgemm_plan", "mxgemm_release_workspaces")
 
 STATUS = {0: "MXGEMM_OK", -1: "MXGEMM_ERR_INVALID_ARG", -2: "MXGEMM_ERR_SHAPE",
           -3: "MXGEMM_ERR_ALIGN", -4: "MXGEMM_ERR_UNSUPPORTED_DEVICE", -5: "MXGEMM_ERR_HIP",
@@ -88,6 +88,8 @@ def lib():
         L.mxgemm_pack_scales.restype = i32
         L.mxgemm_quantize.argtypes = [vp, vp, vp, i32, i32, i64, i64, i64, vp]
         L.mxgemm_quantize.restype = i32
+        L.mxgemm_f16_run.argtypes = [vp, vp, vp, i32, i32, i32, i64, i64, i64, vp]
+        L.mxgemm_f16_run.restype = i32
         L.mxgemm_query.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(Info)]
         L.mxgemm_query.restype = i32
         L.mxgemm_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(Info)]
@@ -180,6 +182,19 @@ def mxgemm_quantize(A, SA, X, M, K, ldx=None, lda=None, ldsa=None, stream=None, 
                                int(ldsa), _stream(stream))
     if check:
         _check(st, "mxgemm_quantize")
+    return st
+
+
+def mxgemm_f16_run(C, A, B, M, N, K, lda=None, ldb=None, ldc=None, stream=None, check=True):
+    """fp32 C [M][ldc] = fp16 A [M][lda] x fp16 B [K][ldb] (asynchronous;
+    strides in elements, default dense)."""
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    st = lib().mxgemm_f16_run(_ptr(C), _ptr(A), _ptr(B), int(M), int(N), int(K), int(lda), int(ldb), int(ldc),
+                              _stream(stream))
+    if check:
+        _check(st, "mxgemm_f16_run")
     return st
 
 

@@ -96,6 +96,18 @@ int64_t quant_grid(int64_t blocks);  // workgroups launch_quant needs
 void launch_quant(const QuantArgs &q, int64_t grid, hipStream_t s);
 // Scale shuffle of rows x KB scale bytes (either operand's scales).
 void launch_pack_sb(uint32_t *SBp, const uint8_t *SB, int N, int KB, int64_t ldsb, hipStream_t s);
+// FP16 GEMM (transposed LDS reads of a K-major B): C = A x B, fp32 out
+struct F16Args {
+    const uint8_t *A;  // fp16 [M][lda_b bytes]
+    const uint8_t *B;  // fp16 [K][ldb_b bytes]
+    float *C;          // fp32 [M][ldc]
+    int M, N, K;
+    int64_t lda_b, ldb_b, ldc;
+    int tiles_m, tiles_n;
+};
+int64_t f16_grid(int M, int N);
+void launch_f16(const F16Args &a, int64_t grid, hipStream_t s);
+
 // bf16-atomic split-K: D = bf16(beta * C) (0 when beta == 0) before the
 // chunks add into it
 void launch_d_init(const GemmArgs &g, hipStream_t s);

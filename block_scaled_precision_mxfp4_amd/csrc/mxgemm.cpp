@@ -618,6 +618,43 @@ mxgemm_status mxgemm_pack_scales(void *Sp, const void *S, int rows, int K, int64
     return MXGEMM_OK;
 }
 
+mxgemm_status mxgemm_f16_run(void *C, const void *A, const void *B, int M, int N, int K, int64_t lda,
+                             int64_t ldb, int64_t ldc, hipStream_t stream)
+{
+    if (!C || !A || !B)
+        return MXGEMM_ERR_INVALID_ARG;
+    if (M < 1 || N < 1 || K < 1 || K % 8 || N % 8 || lda < K || ldb < N || ldc < N)
+        return MXGEMM_ERR_SHAPE;
+    if ((int64_t)256 * lda * 2 >= ((int64_t)1 << 31) || (int64_t)K * ldb * 2 >= ((int64_t)1 << 31))
+        return MXGEMM_ERR_SHAPE;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 4) || lda % 8 || ldb % 8)
+        return MXGEMM_ERR_ALIGN;
+    DeviceInfo *d = nullptr;
+    mxgemm_status st = device_info(&d);
+    if (st != MXGEMM_OK)
+        return st;
+    mx::F16Args a;
+    std::memset(&a, 0, sizeof a);
+    a.A = (const uint8_t *)A;
+    a.B = (const uint8_t *)B;
+    a.C = (float *)C;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.lda_b = lda * 2;
+    a.ldb_b = ldb * 2;
+    a.ldc = ldc;
+    a.tiles_m = cdiv(M, 256);
+    a.tiles_n = cdiv(N, 256);
+    const int64_t grid = mx::f16_grid(M, N);
+    if (grid > 0x7FFFFFFF)
+        return MXGEMM_ERR_SHAPE;
+    mx::launch_f16(a, grid, stream);
+    if (hipGetLastError() != hipSuccess)
+        return MXGEMM_ERR_HIP;
+    return MXGEMM_OK;
+}
+
 mxgemm_status mxgemm_quantize(void *A, void *scaleA, const void *X, int M, int K, int64_t ldx,
                               int64_t lda, int64_t ldsa, hipStream_t stream)
 {

@@ -247,6 +247,26 @@ mxgemm_status mxgemm_pack_scales(void *Sp, const void *S, int rows, int K, int64
 mxgemm_status mxgemm_quantize(void *A, void *scaleA, const void *X, int M, int K,
                               int64_t ldx, int64_t lda, int64_t ldsa, hipStream_t stream);
 
+/* ---- FP16 GEMM with transposed LDS reads ---------------------------------- */
+
+/*
+ * C = A * B with A [M, K] fp16 row-major, B [K, N] fp16 row-major (K-major:
+ * row k holds the N columns of that k) and C [M, N] fp32: the FP16 GEMM of
+ * "CDNA4 MFMA transpose load builtins" ("FP16 GEMM example"), whose B
+ * fragments are read from LDS with ds_read_tr16_b64 (a hardware 16-bit
+ * transpose) because B is stored K-major.  Products are exact in fp32 and
+ * accumulate in fp32 inside the v_mfma_f32_16x16x32_f16 instructions.
+ *
+ * Strides count elements: lda >= K, ldb >= N, ldc >= N.  Shapes: M, N, K
+ * >= 1, K and N multiples of 8 (whole 16-byte chunks of the rows of A and
+ * B), 256 * lda * 2 and K * ldb * 2 below 2^31 bytes.  A, B base 16-byte
+ * aligned, lda and ldb multiples of 8; C 4-byte aligned.  Errors:
+ * MXGEMM_ERR_INVALID_ARG (NULL pointer), MXGEMM_ERR_SHAPE, MXGEMM_ERR_ALIGN,
+ * all before any HIP call.  Asynchronous on `stream`; allocates nothing.
+ */
+mxgemm_status mxgemm_f16_run(void *C, const void *A, const void *B, int M, int N, int K,
+                             int64_t lda, int64_t ldb, int64_t ldc, hipStream_t stream);
+
 /* ---- plan / query ------------------------------------------------------------- */
 
 typedef struct mxgemm_info {

@@ -166,6 +166,14 @@ def test_pack_scales_validation_before_any_hip_call():
     assert f(Sp=0x1002) == -3
 
 
+def test_f16_validation_before_any_hip_call():
+    f = lambda **kw: mx.mxgemm_f16_run(**dict(dict(C=0x1000, A=0x2000, B=0x3000, M=64, N=64, K=64,
+                                                   lda=None, ldb=None, ldc=None, stream=0), **kw), check=False)
+    assert f(C=None) == -1 and f(A=None) == -1 and f(B=None) == -1
+    assert f(M=0) == -2 and f(K=60) == -2 and f(N=60) == -2 and f(lda=32) == -2 and f(ldc=60) == -2
+    assert f(A=0x2008) == -3 and f(C=0x1002) == -3 and f(lda=72 + 4) == -3 and f(ldb=68) == -3
+
+
 def test_quantize_validation_before_any_hip_call():
     f = lambda **kw: mx.mxgemm_quantize(**dict(dict(A=0x1000, SA=0x2000, X=0x3000, M=64, K=256, stream=0),
                                               **kw), check=False)
