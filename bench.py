@@ -81,7 +81,13 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soa
     if a_fmt:  # the same workload with A in a wider format (row-major A scales)
         p["A"] = inputs.wide_codes(inputs.SEED_BASE + 0x100 + a_fmt, M, K, a_fmt)
         sa_packed = False
-    info = mx.mxgemm_query(min(M, 16) if a_fmt else M, N, K, int(packed), split_k)
+    if a_fmt:
+        info = mx.mxgemm_query_ex(M, N, K, mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32,
+                                                          b_packed=int(packed), a_format=a_fmt), split_k)
+        info["packed_b_bytes"] = mx.mxgemm_query(M, N, K, int(packed), split_k)["packed_b_bytes"]
+        info["packed_sb_bytes"] = mx.mxgemm_query(M, N, K, int(packed), split_k)["packed_sb_bytes"]
+    else:
+        info = mx.mxgemm_query(M, N, K, int(packed), split_k)
     ws_bytes = algorithmic_bytes(M, N, K, beta, a_bits)
     copies = 1
     if rotate and ws_bytes < 2 * LLC_BYTES:

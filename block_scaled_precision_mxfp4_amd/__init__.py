@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
 
 # C-ABI entry points declared in include/libmxgemm.h
 EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_pack_b", "mxgemm_pack_scales", "mxgemm_quantize",
-           "mxgemm_f16_run", "mxgemm_query", "mxgemm_plan", "mxgemm_release_workspaces")
+           "mxgemm_f16_run", "mxgemm_query", "mxgemm_plan", "mxgemm_query_ex", "mxgemm_plan_ex",
+           "mxgemm_release_workspaces")
 
 STATUS = {0: "MXGEMM_OK", -1: "MXGEMM_ERR_INVALID_ARG", -2: "MXGEMM_ERR_SHAPE",
           -3: "MXGEMM_ERR_ALIGN", -4: "MXGEMM_ERR_UNSUPPORTED_DEVICE", -5: "MXGEMM_ERR_HIP",
@@ -94,6 +95,10 @@ def lib():
         L.mxgemm_query.restype = i32
         L.mxgemm_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(Info)]
         L.mxgemm_plan.restype = i32
+        L.mxgemm_query_ex.argtypes = [i32, i32, i32, ctypes.POINTER(Strides), i32, ctypes.POINTER(Info)]
+        L.mxgemm_query_ex.restype = i32
+        L.mxgemm_plan_ex.argtypes = [i32, i32, i32, ctypes.POINTER(Strides), i32, i32, ctypes.POINTER(Info)]
+        L.mxgemm_plan_ex.restype = i32
         L.mxgemm_release_workspaces.argtypes = []
         L.mxgemm_release_workspaces.restype = i32
         _lib = L
@@ -202,6 +207,23 @@ def mxgemm_query(M, N, K, b_packed=0, split_k=-1) -> dict:
     info = Info()
     _check(lib().mxgemm_query(int(M), int(N), int(K), int(b_packed), int(split_k),
                               ctypes.byref(info)), "mxgemm_query")
+    return info.as_dict()
+
+
+def mxgemm_query_ex(M, N, K, strides=None, split_k=-1) -> dict:
+    """mxgemm_query for the path mxgemm_run takes with these strides/options."""
+    info = Info()
+    sp = ctypes.byref(strides) if strides is not None else None
+    _check(lib().mxgemm_query_ex(int(M), int(N), int(K), sp, int(split_k), ctypes.byref(info)), "mxgemm_query_ex")
+    return info.as_dict()
+
+
+def mxgemm_plan_ex(M, N, K, strides=None, split_k=-1, num_cu=256) -> dict:
+    """mxgemm_plan for the path mxgemm_run takes with these strides/options."""
+    info = Info()
+    sp = ctypes.byref(strides) if strides is not None else None
+    _check(lib().mxgemm_plan_ex(int(M), int(N), int(K), sp, int(split_k), int(num_cu), ctypes.byref(info)),
+           "mxgemm_plan_ex")
     return info.as_dict()
 
 

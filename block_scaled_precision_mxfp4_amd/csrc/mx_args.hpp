@@ -59,6 +59,16 @@ void launch_tile_deep(const GemmArgs &g, int grid, hipStream_t s);
 // Host-side table of the tiled kernels, in the planner's preference order.
 const TileKernel *tile_kernels(int *count);
 
+// Tiled kernel with 8-bit A (FP8 E4M3, BF8 E5M2; B FP4, row-major A scales):
+// launchers indexed by a_format - 1
+struct TileKernelA8 {
+    int bm, bn;
+    int occupancy;
+    LaunchFn plain[2], packed[2];
+    const char *name;
+};
+const TileKernelA8 *tile_kernels_a8(int *count);
+
 // Skinny kernel (M <= 64, B streamed from memory into registers).
 // index: (mg - 1) * 3 + nr_index with nr in {1, 2, 4}.
 struct SkinnyKernel {

@@ -75,18 +75,25 @@ __device__ __forceinline__ uint32_t scale_word(const ScaleRows &s, int d5)
            (((s.r0[1] >> sh) & 0xFFu) << 16) | (((s.r1[1] >> sh) & 0xFFu) << 24);
 }
 
-template <int BM, int BN, int WM, int WN, bool BPACK, bool SVEC, bool SAPACK>
+// AFMT: A's format (0 FP4; 1 FP8 E4M3 or 2 BF8 E5M2; B is FP4).  An 8-bit
+// A row holds 256 bytes per 256-K stage: the stage is two FP4-shaped A
+// tiles, one per 128-K step (rows of 128 bytes, the same swizzle), and a
+// lane's operand for step ks is chunks g and g+4 of that step's tile -- the
+// two 16-element runs K 16g.. and 64+16g.. the 8-bit instruction reads.
+template <int BM, int BN, int WM, int WN, bool BPACK, bool SVEC, bool SAPACK, int AFMT = 0>
 __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
 {
+    static_assert(AFMT == 0 || ((AFMT == 1 || AFMT == 2) && !SAPACK), "8-bit A with row-major A scales");
+    constexpr int AREG = AFMT == 0 ? 1 : 2;  // FP4-shaped A tiles per stage
     constexpr int NW = WM * WN;                // waves per workgroup
     constexpr int NT = 64 * NW;                // threads per workgroup
     constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
     constexpr int FM = TM / 16, FN = TN / 16;  // 16-row fragments per wave
     static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(FM % 2 == 0 && FN % 2 == 0, "scale words cover 32-row groups");
-    constexpr int A_CH = BM / 8, B_CH = BN / 8;  // 1 KiB chunks per stage
+    constexpr int A_CH = BM / 8 * AREG, B_CH = BN / 8;  // 1 KiB chunks per stage
     static_assert(A_CH % NW == 0 && B_CH % NW == 0, "chunks split evenly over waves");
-    constexpr int A_STAGE = BM * 128, B_STAGE = BN * 128;    // bytes per stage
+    constexpr int A_STAGE = BM * 128 * AREG, B_STAGE = BN * 128;  // bytes per stage
     constexpr int SA_W = BM / 32 * 64, SB_W = BN / 32 * 64;  // scale words per stage
     constexpr int SC_W = SA_W + SB_W + 64;                   // + a scratch row for idle threads
     constexpr int SBP_PER_THREAD = (SB_W + NT - 1) / NT;     // packed-scale words per thread
@@ -176,7 +183,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         uint8_t *dst_b = BUF ? s_b1 : s_b0;
         const int kb_s = kb_begin + kt * 8;
         // K offset of the stage: bytes along a row (row-major) or 1 KiB steps (packed)
-        const uint32_t a_k = (uint32_t)kb_s * 16;
+        const uint32_t a_k = (uint32_t)kb_s * 16 * AREG;
         const uint32_t b_k = BPACK ? (uint32_t)(kb_s >> 2) * 1024 : (uint32_t)kb_s * 16;
         const auto ra = make_rsrc(a_base + a_k, on ? a_bytes - a_k : 0u);
         const auto rb = make_rsrc(b_base + b_k, on ? b_bytes - b_k : 0u);
@@ -185,10 +192,15 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
 #pragma unroll
         for (int i = 0; i < A_CH / NW; ++i) {
             const int c = i * NW + wave;
-            const int rows8 = c * 8, h = c & 1;  // 8-row half h of group c/2
+            const int reg = AREG == 1 ? 0 : c / (BM / 8), cc = AREG == 1 ? c : c % (BM / 8);  // A tile, chunk
+            const int rows8 = cc * 8, h = cc & 1;            // 8-row half h of group cc/2
             uint32_t off = a_lane + (uint32_t)(rows8 * g.lda_b) + (h ? (uint32_t)((kc1 - kc0) * 16) : 0u);
-            if constexpr (!SVEC)  // K tail: blocks at or past the chunk end read as zero
-                off = kb_s + (h ? kc1 : kc0) < kb_end ? off : kOOB;
+            if constexpr (AREG > 1)
+                off += (uint32_t)(reg * 128);
+            if constexpr (!SVEC) {  // K tail: blocks at or past the chunk end read as zero
+                const int kc = h ? kc1 : kc0;
+                off = kb_s + (AREG == 1 ? kc : 4 * reg + kc / 2) < kb_end ? off : kOOB;
+            }
             load16_to_lds(ra, (lds_void *)(dst_a + c * 1024), off);
         }
 #pragma unroll
@@ -327,11 +339,20 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
             sbw[p] = ssc[SA_W + (wave_n * (FN / 2) + p) * 64 + lane];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            v4i af[FM];
+            using a_t = typename std::conditional<AFMT == 0, v4i, v8i>::type;
+            a_t af[FM];
             const uint32_t rl = ks ? rl1 : rl0;
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-                af[fm] = *reinterpret_cast<const v4i *>(sa_tile + (wave_m * FM + fm) * 2048 + rl);
+            for (int fm = 0; fm < FM; ++fm) {
+                if constexpr (AFMT == 0) {
+                    af[fm] = *reinterpret_cast<const v4i *>(sa_tile + (wave_m * FM + fm) * 2048 + rl);
+                } else {
+                    const uint8_t *t = sa_tile + ks * (BM * 128) + (wave_m * FM + fm) * 2048;
+                    const v4i lo = *reinterpret_cast<const v4i *>(t + rl0);
+                    const v4i hi = *reinterpret_cast<const v4i *>(t + rl1);
+                    af[fm] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+            }
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
                 if constexpr (LOADS_AT > 0) {
@@ -342,10 +363,17 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
                                           : (wave_n * FN + fn) * 2048 + rl;
                 const v4i bf = *reinterpret_cast<const v4i *>(sb_tile + bo);
 #pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-                    acc[fn][fm] = mma_sel(ks * 2 + (fn & 1), ks * 2 + (fm & 1), bf, af[fm],
-                                          FIRST && ks == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : acc[fn][fm],
-                                          (int)sbw[fn >> 1], (int)saw[fm >> 1]);
+                for (int fm = 0; fm < FM; ++fm) {
+                    if constexpr (AFMT == 0)
+                        acc[fn][fm] = mma_sel(ks * 2 + (fn & 1), ks * 2 + (fm & 1), bf, af[fm],
+                                              FIRST && ks == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : acc[fn][fm],
+                                              (int)sbw[fn >> 1], (int)saw[fm >> 1]);
+                    else
+                        acc[fn][fm] = mma_sel_wide<kFmtHw[AFMT]>(
+                            ks * 2 + (fn & 1), ks * 2 + (fm & 1), bf, af[fm],
+                            FIRST && ks == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : acc[fn][fm], (int)sbw[fn >> 1],
+                            (int)saw[fm >> 1]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -498,6 +526,33 @@ static void launch_tile(const GemmArgs &g, int grid, hipStream_t s)
     else
         hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, false, SAPACK>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
 }
+
+// 8-bit A (FP8 E4M3 / BF8 E5M2), row-major A scales
+template <int BM, int BN, int WM, int WN, bool BPACK, int AFMT>
+static void launch_tile_a8(const GemmArgs &g, int grid, hipStream_t s)
+{
+    if (g.sa_fast && (BPACK ? g.KB % 8 == 0 : g.sb_fast != 0))
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, true, false, AFMT>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
+    else
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, false, false, AFMT>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
+}
+
+#define MX_TILE_A8(BM, BN, WM, WN, OCC)                                                                    \
+    {BM, BN, OCC,                                                                                          \
+     {launch_tile_a8<BM, BN, WM, WN, false, 1>, launch_tile_a8<BM, BN, WM, WN, false, 2>},                 \
+     {launch_tile_a8<BM, BN, WM, WN, true, 1>, launch_tile_a8<BM, BN, WM, WN, true, 2>}, "tile_a8_" #BM "x" #BN}
+
+const TileKernelA8 *tile_kernels_a8(int *count)
+{
+    static const TileKernelA8 table[] = {
+        MX_TILE_A8(128, 256, 2, 4, 1),
+        MX_TILE_A8(128, 128, 2, 2, 1),
+        MX_TILE_A8(64, 64, 2, 2, 3),
+    };
+    *count = (int)(sizeof(table) / sizeof(table[0]));
+    return table;
+}
+#undef MX_TILE_A8
 
 #define MX_TILE(BM, BN, WM, WN, OCC, DEEP)                                                              \
     {BM, BN, OCC, launch_tile<BM, BN, WM, WN, false, false>, launch_tile<BM, BN, WM, WN, true, false>,   \

@@ -232,6 +232,70 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool
     return best;
 }
 
+// Tiled plan for 8-bit A (family 3): the cost model of the FP4 tiles with
+// the matrix time doubled (the 8-bit scaled instruction runs at half the
+// FP4 rate, "CDNA4 dense MFMA builtins", "Instruction throughput") and A's
+// bytes doubled.
+Plan plan_a8(int M, int N, int K, int split_req, int num_cu)
+{
+    const int KB = K / 32;
+    if (num_cu <= 0)
+        num_cu = 256;
+    int n = 0;
+    const mx::TileKernelA8 *tile = mx::tile_kernels_a8(&n);
+    Plan best;
+    double best_t = 1e300;
+    for (int k = 0; k < n; ++k) {
+        const mx::TileKernelA8 &tk = tile[k];
+        const int tm = cdiv(M, tk.bm), tn = cdiv(N, tk.bn);
+        const int64_t tiles = (int64_t)tm * tn;
+        for (int s : kSplits) {
+            if (split_req > 0 && s != split_req)
+                continue;
+            auto [per, eff] = split_chunks(KB, s, 8);
+            if (split_req <= 0 && s > 1 && eff < s)
+                continue;
+            const int64_t wgs = tiles * eff;
+            const double rounds = (double)((wgs + (int64_t)num_cu * tk.occupancy - 1) / ((int64_t)num_cu * tk.occupancy));
+            const double t_math = 2.0 * 2.0 * tk.bm * tk.bn * 256.0 * tk.occupancy / (kCuFlops * kMatrixFraction);
+            const double t_load = (double)(2 * tk.bm + tk.bn) * 128.0 * tk.occupancy / kCuLoadRate;
+            double t = rounds * (per / 8) * std::max(t_math, t_load);
+            if (eff > 1)
+                t += kSplitChunkCost * eff + (double)tiles * eff * tk.bm * tk.bn * 4 * 2 / kHbm +
+                     (double)eff * tk.bm * tk.bn * 4 / kCuL2;
+            if (t < best_t * 0.97 || (split_req > 0 && t < best_t)) {
+                best_t = t;
+                best.family = 3;
+                best.index = k;
+                best.bm = tk.bm;
+                best.bn = tk.bn;
+                best.split = eff;
+                best.kb_per_split = per;
+                best.tiles_m = tm;
+                best.tiles_n = tn;
+                best.grid = wgs;
+                best.name = tk.name;
+            }
+        }
+    }
+    const int64_t tiles = (int64_t)best.tiles_m * best.tiles_n;
+    best.counter_bytes = best.split > 1 ? (size_t)tiles * 4 : 0;
+    best.ws_bytes = best.split > 1 ? (size_t)tiles * best.split * best.bm * best.bn * 4 : 0;
+    return best;
+}
+
+// The plan mxgemm_run follows for these options: FP4 A by the cost model
+// (the tiled kernel only in the bf16-atomic mode); 8-bit A with M > 16 on
+// the 8-bit tiles; any other wider A on the skinny kernel per 16 rows.
+Plan plan_run(int M, int N, int K, const mxgemm_strides &s, int split_k, int num_cu)
+{
+    if (s.a_format == MXGEMM_FMT_FP4)
+        return plan_for(M, N, K, s.b_packed, split_k, num_cu, s.split_mode == MXGEMM_SPLIT_BF16_ATOMIC);
+    if ((s.a_format == MXGEMM_FMT_FP8_E4M3 || s.a_format == MXGEMM_FMT_FP8_E5M2) && M > 16)
+        return plan_a8(M, N, K, split_k, num_cu);
+    return plan_for(std::min(M, 16), N, K, s.b_packed, split_k, num_cu, false, 1);
+}
+
 size_t packed_b_bytes(int N, int K) { return (size_t)cdiv(N, 16) * 16 * (size_t)cdiv(K / 32, 4) * 64; }
 size_t packed_sb_bytes(int N, int K) { return (size_t)cdiv(N, 32) * 32 * (size_t)cdiv(K / 32, 8) * 8; }
 
@@ -360,14 +424,8 @@ const char *mxgemm_status_string(mxgemm_status s)
     }
 }
 
-mxgemm_status mxgemm_plan(int M, int N, int K, int b_packed, int split_k, int num_cu, mxgemm_info *out)
+static void fill_info(const Plan &p, int M, int N, int K, int num_cu, mxgemm_info *out)
 {
-    if (!out || !valid_split(split_k) || (b_packed != 0 && b_packed != 1) || num_cu < 1)
-        return MXGEMM_ERR_INVALID_ARG;
-    mxgemm_status st = check_shape(M, N, K);
-    if (st != MXGEMM_OK)
-        return st;
-    Plan p = plan_for(M, N, K, b_packed, split_k, num_cu);
     std::memset(out, 0, sizeof *out);
     out->kernel = p.family;
     out->tile_m = p.bm;
@@ -380,6 +438,58 @@ mxgemm_status mxgemm_plan(int M, int N, int K, int b_packed, int split_k, int nu
     out->packed_sa_bytes = packed_sb_bytes(M, K);
     out->num_cu = num_cu;
     std::snprintf(out->kernel_name, sizeof out->kernel_name, "%s", p.name);
+}
+
+mxgemm_status mxgemm_plan(int M, int N, int K, int b_packed, int split_k, int num_cu, mxgemm_info *out)
+{
+    if (!out || !valid_split(split_k) || (b_packed != 0 && b_packed != 1) || num_cu < 1)
+        return MXGEMM_ERR_INVALID_ARG;
+    mxgemm_status st = check_shape(M, N, K);
+    if (st != MXGEMM_OK)
+        return st;
+    fill_info(plan_for(M, N, K, b_packed, split_k, num_cu), M, N, K, num_cu, out);
+    return MXGEMM_OK;
+}
+
+static bool valid_options(const mxgemm_strides &s)
+{
+    return (s.b_packed == 0 || s.b_packed == 1) && (s.sa_packed == 0 || s.sa_packed == 1) &&
+           (!s.sa_packed || s.b_packed) && (s.c_f32 == 0 || s.c_f32 == 1) &&
+           (s.split_mode == MXGEMM_SPLIT_FP32 || s.split_mode == MXGEMM_SPLIT_BF16_ATOMIC) &&
+           s.a_format >= MXGEMM_FMT_FP4 && s.a_format <= MXGEMM_FMT_FP6_E3M2 && s.reserved == 0 &&
+           (s.a_format == MXGEMM_FMT_FP4 || (!s.sa_packed && s.split_mode == MXGEMM_SPLIT_FP32));
+}
+
+mxgemm_status mxgemm_plan_ex(int M, int N, int K, const mxgemm_strides *strides, int split_k, int num_cu,
+                             mxgemm_info *out)
+{
+    mxgemm_strides s;
+    std::memset(&s, 0, sizeof s);
+    if (strides)
+        s = *strides;
+    if (!out || !valid_split(split_k) || num_cu < 1 || !valid_options(s))
+        return MXGEMM_ERR_INVALID_ARG;
+    mxgemm_status st = check_shape(M, N, K);
+    if (st != MXGEMM_OK)
+        return st;
+    fill_info(plan_run(M, N, K, s, split_k, num_cu), M, N, K, num_cu, out);
+    return MXGEMM_OK;
+}
+
+mxgemm_status mxgemm_query_ex(int M, int N, int K, const mxgemm_strides *strides, int split_k, mxgemm_info *out)
+{
+    DeviceInfo *d = nullptr;
+    if (!out)
+        return MXGEMM_ERR_INVALID_ARG;
+    mxgemm_status st = device_info(&d);
+    if (st != MXGEMM_OK)
+        return st;
+    st = mxgemm_plan_ex(M, N, K, strides, split_k, d->num_cu, out);
+    if (st != MXGEMM_OK)
+        return st;
+    std::snprintf(out->arch, sizeof out->arch, "%s", d->arch);
+    out->clock_hz = d->clock_hz;
+    out->peak_flops = 65536.0 / 16.0 * 4.0 * d->num_cu * d->clock_hz;
     return MXGEMM_OK;
 }
 
@@ -464,11 +574,10 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     st = device_info(&d);
     if (st != MXGEMM_OK)
         return st;
-    // A in a wider format: the skinny kernel (one 16-row group, nr 1), one
-    // launch per 16 rows of A
-    const bool wide = s.a_format != MXGEMM_FMT_FP4;
-    Plan p = wide ? plan_for(std::min(M, 16), N, K, s.b_packed, split_k, d->num_cu, false, 1)
-                  : plan_for(M, N, K, s.b_packed, split_k, d->num_cu, atomic);
+    Plan p = plan_run(M, N, K, s, split_k, d->num_cu);
+    // a wider A not on the 8-bit tiles: the skinny kernel (one 16-row
+    // group, nr 1), one launch per 16 rows of A
+    const bool wide = s.a_format != MXGEMM_FMT_FP4 && p.family != 3;
 
     GemmArgs g;
     std::memset(&g, 0, sizeof g);
@@ -542,6 +651,10 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
                 gb.C = (const uint8_t *)g.C + (int64_t)m0 * g.ldc * (g.c_f32 ? 4 : 2);
             mx::launch_skinny_wide(s.a_format, s.b_packed != 0, gb, (int)p.grid, stream);
         }
+    } else if (p.family == 3) {
+        int n = 0;
+        const mx::TileKernelA8 &k = mx::tile_kernels_a8(&n)[p.index];
+        (s.b_packed ? k.packed : k.plain)[s.a_format - 1](g, (int)p.grid, stream);
     } else if (p.family == 0) {
         int n = 0;
         const mx::TileKernel &k = mx::tile_kernels(&n)[p.index];

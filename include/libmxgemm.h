@@ -87,11 +87,13 @@ const char *mxgemm_status_string(mxgemm_status status);
  *              scale per 32 elements as for FP4.  lda counts elements of
  *              A's format; the byte pitch lda*w/8 must be a whole multiple of
  *              16 (of 8 for the FP6 formats, whose dense rows are 24 bytes
- *              per 32 elements).  A wider format runs on the skinny kernel,
- *              one launch per
- *              16 rows of A (at M = 1 the speed of the FP4 case; for large M
- *              B is read once per 16 rows).  It needs sa_packed = 0 and
- *              split_mode = MXGEMM_SPLIT_FP32 (else MXGEMM_ERR_INVALID_ARG).
+ *              per 32 elements).  Kernels: for M <= 16 the skinny kernel
+ *              (the speed of the FP4 case); for M > 16 the 8-bit formats
+ *              run on the tiled kernel with 8-bit A tiles, the FP6 formats
+ *              on the skinny kernel once per 16 rows of A (B is then read
+ *              once per 16 rows).  Needs sa_packed = 0 and split_mode =
+ *              MXGEMM_SPLIT_FP32 (else MXGEMM_ERR_INVALID_ARG); size a caller
+ *              workspace with mxgemm_query_ex.
  *   c_f32      C is float32 instead of bf16.  The README's "C / bias" note
  *              says aiter documents its bias operand as f32; with c_f32 = 1
  *              the epilogue reads that type (D stays bf16; one rounding of
@@ -303,6 +305,18 @@ mxgemm_status mxgemm_query(int M, int N, int K, int b_packed, int split_k,
  */
 mxgemm_status mxgemm_plan(int M, int N, int K, int b_packed, int split_k, int num_cu,
                           mxgemm_info *out);
+
+/* mxgemm_plan / mxgemm_query for the exact path mxgemm_run takes with these
+ * strides and options (a_format, split_mode, b_packed; NULL = defaults):
+ * with a wider A format or the bf16-atomic split the kernel and the
+ * workspace differ from the FP4 plan, and a caller workspace must be sized
+ * from this call.  kernel = 3 is the tiled kernel with 8-bit A.  Same
+ * errors as mxgemm_plan / mxgemm_query, plus MXGEMM_ERR_INVALID_ARG for
+ * option values mxgemm_run rejects. */
+mxgemm_status mxgemm_plan_ex(int M, int N, int K, const mxgemm_strides *strides, int split_k, int num_cu,
+                             mxgemm_info *out);
+mxgemm_status mxgemm_query_ex(int M, int N, int K, const mxgemm_strides *strides, int split_k,
+                              mxgemm_info *out);
 
 /* Free the library-owned split-K workspaces (after synchronizing their
  * streams).  Later calls allocate again. */

@@ -83,3 +83,38 @@ def test_decode_shape_sampled(fmt):
     ref, mag, _ = oracle_ref(p, cols=cols)
     assert_parity(d[:, cols], ref, mag, "decode %s" % NAMES[fmt])
 
+
+
+# 8-bit A with M > 16 runs on the tiled kernel with 8-bit A tiles
+CASES_A8 = [
+    (300, 520, 1056, -1, False, "bf16"),  # K tail (blocks past a stage's end)
+    (512, 1024, 2048, 1, True, None),     # packed B
+    (256, 768, 4096, 4, False, "f32"),    # forced split, f32 C
+    (129, 96, 512, 1, False, None),       # ragged M and N
+]
+
+
+@pytest.mark.parametrize("fmt", [mx.FMT_FP8_E4M3, mx.FMT_FP8_E5M2], ids=lambda f: NAMES[f])
+@pytest.mark.parametrize("case", CASES_A8, ids=lambda c: "%dx%dx%d_s%d%s%s" % (
+    c[0], c[1], c[2], c[3], "_packed" if c[4] else "", "_" + c[5] if c[5] else ""))
+def test_fp8_tiled_matches_oracle(case, fmt):
+    M, N, K, split, packed, c = case
+    st = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32, b_packed=int(packed), a_format=fmt)
+    assert mx.mxgemm_plan_ex(M, N, K, st, split, 256)["kernel"] == 3
+    p = problem(case, fmt, seed=0xA8A8 + 31 * fmt + M + N)
+    say("case tiled", NAMES[fmt], case)
+    d = gemm_gpu(p, split_k=split, b_packed=packed)
+    ref, mag, _ = oracle_ref(p)
+    assert_parity(d, ref, mag, "tiled %s %s" % (NAMES[fmt], case))
+
+
+def test_fp8_tiled_large_sampled():
+    M, N, K = 2048, 2048, 4096
+    fmt = mx.FMT_FP8_E4M3
+    p = inputs.make_problem(M, N, K, seed=0xA8A9, e=(115, 128), a_fmt=fmt)
+    say("case tiled 2048x2048x4096")
+    d = gemm_gpu(p, b_packed=True)
+    rng = np.random.default_rng(8)
+    rows = np.sort(rng.choice(M, 24, replace=False))
+    ref, mag, _ = oracle_ref(p, rows=rows)
+    assert_parity(d[rows], ref, mag, "tiled 2048x2048x4096")
