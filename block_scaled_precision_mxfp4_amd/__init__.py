@@ -56,12 +56,12 @@ class Info(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t), ("packed_b_bytes", ctypes.c_size_t),
                 ("packed_sb_bytes", ctypes.c_size_t), ("packed_sa_bytes", ctypes.c_size_t),
                 ("num_cu", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("kernel_name", ctypes.c_char * 64),
+                ("persist_grid", ctypes.c_int32), ("kernel_name", ctypes.c_char * 64),
                 ("arch", ctypes.c_char * 32), ("peak_flops", ctypes.c_double),
                 ("clock_hz", ctypes.c_double)]
 
     def as_dict(self):
-        d = {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        d = {f: getattr(self, f) for f, _ in self._fields_}
         d["kernel_name"] = self.kernel_name.decode()
         d["arch"] = self.arch.decode()
         return d

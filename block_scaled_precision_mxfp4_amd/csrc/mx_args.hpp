@@ -37,6 +37,7 @@ struct GemmArgs {
     int group_m;          // tile-order grouping along M
     int c_f32;            // C holds float32 elements
     int split_atomic;     // split > 1: chunks add bf16(alpha * partial) into D with bf16 atomics
+    int persist_grid;     // > 0: the 256x256 tiled kernel runs persistent with this many workgroups
 };
 
 typedef void (*LaunchFn)(const GemmArgs &, int grid, hipStream_t);

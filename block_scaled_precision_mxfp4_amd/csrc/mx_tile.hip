@@ -22,6 +22,7 @@
 // the epilogue, so results do not depend on arrival order.
 #include "mx_args.hpp"
 #include "mx_device.hpp"
+#include "mx_pipe.hpp"
 
 #include <type_traits>
 
@@ -75,12 +76,57 @@ __device__ __forceinline__ uint32_t scale_word(const ScaleRows &s, int d5)
            (((s.r0[1] >> sh) & 0xFFu) << 16) | (((s.r1[1] >> sh) & 0xFFu) << 24);
 }
 
+// Whole-tile form of the staged epilogue (every row and column inside D,
+// beta == 0): D[m_base + r][n_base + c] = bf16(alpha * acc), staged through
+// the wave's private LDS region exactly as store_tile_staged does, without
+// the bounds checks.  `lane` comes in through an opaque register so that the
+// persistent kernel recomputes the addresses per tile instead of hoisting
+// them out of its tile loop (where they would be spilled, and every reload
+// would wait for all outstanding memory operations).
+template <int FM, int FN>
+__device__ __forceinline__ void store_whole_tile_staged(uint16_t *D, int64_t ldd, float alpha, int m_base,
+                                                        int n_base, const v4f (&acc)[FN][FM], uint8_t *lds,
+                                                        int lane)
+{
+    constexpr int RB = FN * 32;  // bytes per row of the wave tile
+    constexpr int CH = RB / 16;  // 16-byte chunks per row
+    constexpr int RPI = 64 / CH; // rows per copy-out instruction
+    static_assert(CH == 2 || CH == 4 || CH == 8, "row chunking");
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int r = fm * 16 + (lane & 15);
+            const int j = fn * 2 + (lane >> 5);
+            v2u o;
+            o[0] = bf16x2_rne(alpha * acc[fn][fm][0], alpha * acc[fn][fm][1]);
+            o[1] = bf16x2_rne(alpha * acc[fn][fm][2], alpha * acc[fn][fm][3]);
+            *reinterpret_cast<v2u *>(lds + r * RB + ((j ^ (r & (CH - 1))) * 16) + ((lane >> 4) & 1) * 8) = o;
+        }
+    const int r0 = lane / CH, c = lane & (CH - 1);
+    uint16_t *d0 = D + (int64_t)(m_base + r0) * ldd + n_base + c * 8;
+#pragma unroll
+    for (int i = 0; i < FM * 16 / RPI; ++i) {
+        const int r = i * RPI + r0;
+        const v4i v = *reinterpret_cast<const v4i *>(lds + r * RB + ((c ^ (r & (CH - 1))) * 16));
+        __builtin_nontemporal_store(v, reinterpret_cast<v4i *>(d0 + (int64_t)(i * RPI) * ldd));
+    }
+}
+
 // AFMT: A's format (0 FP4; 1 FP8 E4M3 or 2 BF8 E5M2; B is FP4).  An 8-bit
 // A row holds 256 bytes per 256-K stage: the stage is two FP4-shaped A
 // tiles, one per 128-K step (rows of 128 bytes, the same swizzle), and a
 // lane's operand for step ks is chunks g and g+4 of that step's tile -- the
 // two 16-element runs K 16g.. and 64+16g.. the 8-bit instruction reads.
-template <int BM, int BN, int WM, int WN, bool BPACK, bool SVEC, bool SAPACK, int AFMT = 0>
+// PERSIST: one workgroup per CU walks its tiles in the order the plain grid
+// runs them (hardware id i * grid + blockIdx, through the same XCD remap).
+// After a tile's last stage it issues the next tile's first stage into the
+// free buffer pair, then writes D through the other pair (half a wave tile
+// per pass): the next tile's load latency hides behind the epilogue, and
+// the epilogue's stores drain behind the next tile's first stage.  Needs
+// split 1, the staged epilogue and M, N multiples of the tile (every wave
+// then issues exactly 16 stores after those loads; the host checks).
+template <int BM, int BN, int WM, int WN, bool BPACK, bool SVEC, bool SAPACK, int AFMT = 0, bool PERSIST = false>
 __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
 {
     static_assert(AFMT == 0 || ((AFMT == 1 || AFMT == 2) && !SAPACK), "8-bit A with row-major A scales");
@@ -115,32 +161,17 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS/chunk math scalar
     const int wave_m = wave % WM, wave_n = wave / WM;
 
-    // ---- which tile and K chunk
+    // ---- which tile and K chunk, and the operand sources rebased at the
+    // tile (offsets stay below 2^31).  Per stage the base advances by the
+    // stage's K offset and the range shrinks by the same amount, so a lane's
+    // offset inside a stage is its fixed lane part plus a wave-uniform chunk
+    // part.  A stage that must not load gets an empty range: every load
+    // returns zero without traffic.
     const int tiles = g.tiles_m * g.tiles_n;
-    const int lg = xcd_remap(blockIdx.x, gridDim.x);
-    const int z = lg / tiles;
-    const int t = lg - z * tiles;
-    const int per_group = g.group_m * g.tiles_n;
-    const int grp = t / per_group;
-    const int first_m = grp * g.group_m;
-    const int gsz = min(g.tiles_m - first_m, g.group_m);
-    const int within = t - grp * per_group;
-    const int tm = first_m + within % gsz;
-    const int tn = within / gsz;
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    const int kb_begin = z * g.kb_per_split;
-    const int kb_end = min(g.KB, kb_begin + g.kb_per_split);
-    const int nst = (kb_end - kb_begin + 7) >> 3;
-
-    // ---- operand sources, rebased at the tile (offsets stay below 2^31).
-    // Per stage the base advances by the stage's K offset and the range
-    // shrinks by the same amount, so a lane's offset inside a stage is its
-    // fixed lane part plus a wave-uniform chunk part.  A stage that must not
-    // load gets an empty range: every load returns zero without traffic.
-    const int rows_a = min(BM, g.M - m0);
-    const uint8_t *a_base = g.A + (int64_t)m0 * g.lda_b;
-    const uint32_t a_bytes = (uint32_t)(rows_a * g.lda_b);
+    int z, t, m0, n0, kb_begin, kb_end, nst;
+    const uint8_t *a_base, *b_base;
+    uint32_t a_bytes, b_bytes;
+    __amdgpu_buffer_rsrc_t rsa, rsb;
     // Row-major operands move in whole 128-byte lines: one load instruction
     // covers 8 rows x the stage's 128 bytes (lane l: row l/8, 16-byte chunk
     // (l%8) ^ (l/8) ^ h for the h-th 8-row half of a 16-row group).  The
@@ -149,32 +180,56 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     // one chunk fall in 16 different bank groups, so fragment reads stay
     // conflict-free.
     const uint32_t a_lane = (uint32_t)((lane >> 3) * g.lda_b + (((lane & 7) ^ (lane >> 3)) * 16));
-    __amdgpu_buffer_rsrc_t rsa;
-    if constexpr (SAPACK) {
-        const int m32 = m0 / 32, grp32 = min(BM / 32, (g.M + 31) / 32 - m32);
-        rsa = make_rsrc(g.SA + (int64_t)m32 * g.sn8 * 256, (uint32_t)(grp32 * g.sn8 * 256));
-    } else {
-        rsa = make_rsrc(g.SA + (int64_t)m0 * g.ldsa, (uint32_t)(rows_a * g.ldsa));
-    }
-    const uint8_t *b_base;
-    uint32_t b_bytes, b_lane, b_rg_stride;
-    __amdgpu_buffer_rsrc_t rsb;
+    uint32_t b_lane, b_rg_stride;
     if constexpr (BPACK) {
-        const int n16 = n0 / 16, grp16 = min(BN / 16, (g.N + 15) / 16 - n16);
-        b_base = g.B + (int64_t)n16 * g.ks_total * 1024;
-        b_bytes = (uint32_t)(grp16 * g.ks_total * 1024);
         b_lane = (uint32_t)(lane * 16);
         b_rg_stride = (uint32_t)(g.ks_total * 1024);
-        const int n32 = n0 / 32, grp32 = min(BN / 32, (g.N + 31) / 32 - n32);
-        rsb = make_rsrc(g.SB + (int64_t)n32 * g.sn8 * 256, (uint32_t)(grp32 * g.sn8 * 256));
     } else {
-        const int rows_b = min(BN, g.N - n0);
-        b_base = g.B + (int64_t)n0 * g.ldb_b;
-        b_bytes = (uint32_t)(rows_b * g.ldb_b);
         b_lane = (uint32_t)((lane >> 3) * g.ldb_b + (((lane & 7) ^ (lane >> 3)) * 16));
         b_rg_stride = (uint32_t)(16 * g.ldb_b);
-        rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)(rows_b * g.ldsb));
     }
+    auto load_src = [&](int lg) __attribute__((always_inline)) {
+        z = lg / tiles;
+        t = lg - z * tiles;
+        const int per_group = g.group_m * g.tiles_n;
+        const int grp = t / per_group;
+        const int first_m = grp * g.group_m;
+        const int gsz = min(g.tiles_m - first_m, g.group_m);
+        const int within = t - grp * per_group;
+        const int tm = first_m + within % gsz;
+        const int tn = within / gsz;
+        m0 = tm * BM;
+        n0 = tn * BN;
+        kb_begin = z * g.kb_per_split;
+        kb_end = min(g.KB, kb_begin + g.kb_per_split);
+        nst = (kb_end - kb_begin + 7) >> 3;
+        const int rows_a = min(BM, g.M - m0);
+        a_base = g.A + (int64_t)m0 * g.lda_b;
+        a_bytes = (uint32_t)(rows_a * g.lda_b);
+        if constexpr (SAPACK) {
+            const int m32 = m0 / 32, grp32 = min(BM / 32, (g.M + 31) / 32 - m32);
+            rsa = make_rsrc(g.SA + (int64_t)m32 * g.sn8 * 256, (uint32_t)(grp32 * g.sn8 * 256));
+        } else {
+            rsa = make_rsrc(g.SA + (int64_t)m0 * g.ldsa, (uint32_t)(rows_a * g.ldsa));
+        }
+        if constexpr (BPACK) {
+            const int n16 = n0 / 16, grp16 = min(BN / 16, (g.N + 15) / 16 - n16);
+            b_base = g.B + (int64_t)n16 * g.ks_total * 1024;
+            b_bytes = (uint32_t)(grp16 * g.ks_total * 1024);
+            const int n32 = n0 / 32, grp32 = min(BN / 32, (g.N + 31) / 32 - n32);
+            rsb = make_rsrc(g.SB + (int64_t)n32 * g.sn8 * 256, (uint32_t)(grp32 * g.sn8 * 256));
+        } else {
+            const int rows_b = min(BN, g.N - n0);
+            b_base = g.B + (int64_t)n0 * g.ldb_b;
+            b_bytes = (uint32_t)(rows_b * g.ldb_b);
+            rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)(rows_b * g.ldsb));
+        }
+    };
+    // units of work are (tile, K chunk) pairs: the plain grid runs one per
+    // workgroup, the persistent one walks hardware ids blockIdx + i * grid
+    const int units = tiles * g.split;
+    int unit_hw = blockIdx.x;
+    load_src(xcd_remap(unit_hw, PERSIST ? units : (int)gridDim.x));
 
     // ---- stage loaders
     auto issue_operands = [&](int kt, bool on, auto bufc) __attribute__((always_inline)) {
@@ -392,6 +447,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     // so that the loop body has no branch (no join over the accumulators).
     using First = std::true_type;
     using Rest = std::false_type;
+    for (;;) {
     auto run = [&](auto loadsc) __attribute__((always_inline)) {
         stage(0, B0{}, First{}, loadsc);
         int kt = 1;
@@ -419,6 +475,54 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
             run(std::integral_constant<int, 0>{});
     } else {
         run(std::integral_constant<int, -1>{});
+    }
+    if constexpr (PERSIST) {
+        const int ep_m0 = m0, ep_n0 = n0;
+        const int next_hw = unit_hw + (int)gridDim.x;
+        const bool has_next = next_hw < units;
+        if (has_next) {
+            // the next unit's first stage into the free buffer pair
+            // (its last readers passed the barrier ending stage nst - 2)
+            load_src(xcd_remap(next_hw, units));
+            issue_operands(0, true, B0{});
+            issue_scales(0, true);
+        }
+        // staged epilogue in the last stage's A buffer: each wave stages a
+        // quarter of its tile at a time in a private 4 KiB region of s_a1,
+        // 4 stores per quarter.  Naming that one array lets the compiler
+        // tell the staging accesses from the next stage's direct-to-LDS
+        // loads into the other pair, so they do not wait for those loads.
+        int lane_e = lane;
+        asm volatile("" : "+v"(lane_e));
+        constexpr int PARTS = 4;
+        constexpr int QREG = (TM / PARTS) * TN * 2;
+        static_assert(NW * QREG <= A_STAGE && FM % PARTS == 0, "quarter-tile staging fits the A buffer");
+        uint8_t *buf = s_a1 + wave * QREG;
+#pragma unroll
+        for (int part = 0; part < PARTS; ++part) {
+            v4f q[FN][FM / PARTS];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int i = 0; i < FM / PARTS; ++i)
+                    q[fn][i] = acc[fn][part * (FM / PARTS) + i];
+            store_whole_tile_staged<FM / PARTS, FN>(g.D, g.ldd, g.alpha, ep_m0 + wave_m * TM + part * (TM / PARTS),
+                                                    ep_n0 + wave_n * TN, q, buf, lane_e);
+        }
+        if (!has_next)
+            return;
+        // the first-stage loads were issued before this wave's 16 stores:
+        // in-order completion makes them landed at 16 outstanding
+        static_assert(PARTS * (FM / PARTS) * 16 / (64 / (FN * 2)) == 16, "16 stores per wave");
+        wait_vmcnt<16>();
+        commit_scales(B0{});
+        // the stage and its scales are in place, and every wave is done with
+        // its staging region before the next stage is loaded over it
+        __syncthreads();
+        unit_hw = next_hw;
+        continue;
+    }
+    break;
     }
 
     // ---- epilogue
@@ -521,6 +625,13 @@ static void launch_tile(const GemmArgs &g, int grid, hipStream_t s)
     // SVEC: whole 8-block stages and 8-byte scale-row loads (packed scales
     // need only the former)
     const bool sa_ok = SAPACK ? g.KB % 8 == 0 : g.sa_fast != 0;
+    if constexpr (BM == 256 && BN == 256) {
+        if (g.persist_grid > 0 && sa_ok && (BPACK ? g.KB % 8 == 0 : g.sb_fast != 0)) {
+            hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, true, SAPACK, 0, true>), dim3(g.persist_grid),
+                               dim3(64 * WM * WN), 0, s, g);
+            return;
+        }
+    }
     if (sa_ok && (BPACK ? g.KB % 8 == 0 : g.sb_fast != 0))
         hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, true, SAPACK>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
     else

@@ -283,7 +283,10 @@ typedef struct mxgemm_info {
     size_t packed_sb_bytes;  /* size of mxgemm_pack_b's SBp for this N, K */
     size_t packed_sa_bytes;  /* size of mxgemm_pack_scales' output for the M rows of scaleA */
     int32_t num_cu;          /* compute units the plan assumed */
-    int32_t reserved;
+    int32_t persist_grid;    /* > 0: the tiled kernel runs persistent, this many workgroups
+                                (one per CU) walking the `grid` tiles in the same order;
+                                assumes beta == 0 and 16-byte aligned pointers, as the
+                                persistent form needs (else mxgemm_run uses the plain grid) */
     char kernel_name[64];
     char arch[32];           /* device architecture (mxgemm_query only) */
     double peak_flops;       /* dense MXFP4 matrix peak, flop/s, from the device clock and CU count */

@@ -251,3 +251,23 @@ def test_plan_is_deterministic():
     a = [mx.mxgemm_plan(m, n, k, 0, -1, 256) for m, n, k in [(77, 999, 2048), (4096, 4096, 4096)]]
     b = [mx.mxgemm_plan(m, n, k, 0, -1, 256) for m, n, k in [(77, 999, 2048), (4096, 4096, 4096)]]
     assert a == b
+
+
+def test_persistent_form_is_planned_only_where_it_applies(monkeypatch):
+    """The 256 x 256 tiled kernel's persistent form: whole unsplit tiles,
+    an even number of 8-block stages, more tiles than CUs, and a staged
+    epilogue (ldd % 8 == 0)."""
+    st = lambda N, K, ldd=None, pk=1: mx.make_strides(ldd=ldd or N, ldc=N, lda=K, ldb=K, ldsa=K // 32,
+                                                       ldsb=K // 32, b_packed=pk, sa_packed=pk)
+    pg = lambda M, N, K, s, split=-1: mx.mxgemm_plan_ex(M, N, K, s, split, 256)["persist_grid"]
+    assert pg(8192, 8192, 8192, st(8192, 8192)) == 256
+    assert mx.mxgemm_plan(8192, 8192, 8192, 1, -1, 256)["persist_grid"] == 256
+    assert pg(5120, 5120, 512, st(5120, 512, pk=0)) == 256
+    assert pg(8192, 8192, 8192, st(8192, 8192), split=2) == 0      # split K
+    assert pg(8192, 8192, 8448, st(8192, 8448)) == 0               # 264 blocks: odd stage count
+    assert pg(8192, 8200, 8192, st(8200, 8192)) == 0               # ragged N tile
+    assert pg(4096, 4096, 4096, st(4096, 4096)) == 0               # one round of tiles
+    assert pg(8192, 8192, 8192, st(8192, 8192, ldd=8196)) == 0     # unstaged epilogue
+    assert mx.mxgemm_plan_ex(8192, 8192, 8192, st(8192, 8192), -1, 128)["persist_grid"] == 128
+    monkeypatch.setenv("MXGEMM_TILE_PERSIST", "0")
+    assert pg(8192, 8192, 8192, st(8192, 8192)) == 0
