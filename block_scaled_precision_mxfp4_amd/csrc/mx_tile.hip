@@ -118,7 +118,7 @@ __device__ __forceinline__ void store_whole_tile_staged(uint16_t *D, int64_t ldd
 // tiles, one per 128-K step (rows of 128 bytes, the same swizzle), and a
 // lane's operand for step ks is chunks g and g+4 of that step's tile -- the
 // two 16-element runs K 16g.. and 64+16g.. the 8-bit instruction reads.
-// PERSIST: one workgroup per CU walks its tiles in the order the plain grid
+// PERSIST (tiles with one workgroup per CU): one workgroup per CU walks its tiles in the order the plain grid
 // runs them (hardware id i * grid + blockIdx, through the same XCD remap).
 // After a tile's last stage it issues the next tile's first stage into the
 // free buffer pair, then writes D through the other pair (half a wave tile
@@ -487,16 +487,16 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
             issue_operands(0, true, B0{});
             issue_scales(0, true);
         }
-        // staged epilogue in the last stage's A buffer: each wave stages a
-        // quarter of its tile at a time in a private 4 KiB region of s_a1,
-        // 4 stores per quarter.  Naming that one array lets the compiler
-        // tell the staging accesses from the next stage's direct-to-LDS
-        // loads into the other pair, so they do not wait for those loads.
+        // staged epilogue in the last stage's A buffer: each wave stages
+        // 1/PARTS of its tile at a time in a private region of s_a1.  Naming
+        // that one array lets the compiler tell the staging accesses from
+        // the next stage's direct-to-LDS loads into the other pair, so they
+        // do not wait for those loads.
         int lane_e = lane;
         asm volatile("" : "+v"(lane_e));
-        constexpr int PARTS = 4;
+        constexpr int PARTS = NW * TM * TN * 2 <= A_STAGE ? 1 : NW * TM * TN <= A_STAGE ? 2 : 4;
         constexpr int QREG = (TM / PARTS) * TN * 2;
-        static_assert(NW * QREG <= A_STAGE && FM % PARTS == 0, "quarter-tile staging fits the A buffer");
+        static_assert(NW * QREG <= A_STAGE && FM % PARTS == 0, "partial-tile staging fits the A buffer");
         uint8_t *buf = s_a1 + wave * QREG;
 #pragma unroll
         for (int part = 0; part < PARTS; ++part) {
@@ -511,10 +511,11 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         }
         if (!has_next)
             return;
-        // the first-stage loads were issued before this wave's 16 stores:
-        // in-order completion makes them landed at 16 outstanding
-        static_assert(PARTS * (FM / PARTS) * 16 / (64 / (FN * 2)) == 16, "16 stores per wave");
-        wait_vmcnt<16>();
+        // the first-stage loads were issued before this wave's STORES stores
+        // (16-byte stores of 64 / (2 FN) rows each): in-order completion
+        // makes them landed at STORES outstanding
+        constexpr int STORES = FM * 16 / (64 / (FN * 2));
+        wait_vmcnt<STORES>();
         commit_scales(B0{});
         // the stage and its scales are in place, and every wave is done with
         // its staging region before the next stage is loaded over it
@@ -625,7 +626,10 @@ static void launch_tile(const GemmArgs &g, int grid, hipStream_t s)
     // SVEC: whole 8-block stages and 8-byte scale-row loads (packed scales
     // need only the former)
     const bool sa_ok = SAPACK ? g.KB % 8 == 0 : g.sa_fast != 0;
-    if constexpr (BM == 256 && BN == 256) {
+    // persistent form: 256 x 256 with packed B and A scales (its other
+    // layouts spill in the tile loop; the 256 x 128 tile and the 8-bit
+    // 128 x 256 tile measured no faster persistent)
+    if constexpr (BM == 256 && BN == 256 && BPACK && SAPACK) {
         if (g.persist_grid > 0 && sa_ok && (BPACK ? g.KB % 8 == 0 : g.sb_fast != 0)) {
             hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, true, SAPACK, 0, true>), dim3(g.persist_grid),
                                dim3(64 * WM * WN), 0, s, g);

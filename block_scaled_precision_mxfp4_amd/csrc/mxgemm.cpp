@@ -299,12 +299,13 @@ Plan plan_run(int M, int N, int K, const mxgemm_strides &s, int split_k, int num
 size_t packed_b_bytes(int N, int K) { return (size_t)cdiv(N, 16) * 16 * (size_t)cdiv(K / 32, 4) * 64; }
 size_t packed_sb_bytes(int N, int K) { return (size_t)cdiv(N, 32) * 32 * (size_t)cdiv(K / 32, 8) * 8; }
 
-// The 256 x 256 two-stage kernel runs persistent (one workgroup per CU
-// walking its tiles) when every tile is whole and unsplit, the epilogue is
-// staged (d_stage), whole 8-block stages with 8-byte scale loads apply
-// (svec), each tile has an even number of stages and there is more than one
-// round of tiles.  Returns the persistent grid, or 0 for the plain grid.
-int64_t persist_grid(const Plan &p, int M, int N, int K, int num_cu, bool d_stage, bool svec)
+// The two-stage tiled kernel's 256 x 256 tile with packed B and A scales runs
+// persistent (one workgroup per CU walking its tiles) when every tile is
+// whole and unsplit, the epilogue is staged (d_stage), whole 8-block stages
+// with 8-byte scale loads apply (svec), each tile has an even number of
+// stages and there is more than one round of tiles.  Returns the persistent
+// grid, or 0 for the plain grid.
+int64_t persist_grid(const Plan &p, int M, int N, int K, int num_cu, bool d_stage, bool svec, bool sa_packed)
 {
     const char *e = std::getenv("MXGEMM_TILE_PERSIST");  // "0": always the plain grid
     if (e && std::strcmp(e, "0") == 0)
@@ -312,9 +313,10 @@ int64_t persist_grid(const Plan &p, int M, int N, int K, int num_cu, bool d_stag
     const char *pipe = std::getenv("MXGEMM_TILE_PIPELINE");
     if (pipe && std::strcmp(pipe, "deep") == 0)
         return 0;
-    if (p.family != 0 || p.bm != 256 || p.bn != 256 || p.split != 1 || !d_stage || !svec)
+    const bool tile_ok = p.family == 0 && p.bm == 256 && p.bn == 256 && sa_packed;
+    if (!tile_ok || p.split != 1 || !d_stage || !svec)
         return 0;
-    if (M % 256 || N % 256 || (K / 32) % 16 || num_cu % 8 || p.grid <= num_cu)
+    if (M % p.bm || N % p.bn || (K / 32) % 16 || num_cu % 8 || p.grid <= num_cu)
         return 0;
     return num_cu;
 }
@@ -450,7 +452,7 @@ static void fill_info(const Plan &p, int M, int N, int K, int num_cu, const mxge
     // what mxgemm_run launches for beta == 0 and 16-byte aligned pointers
     const int KB = K / 32;
     const bool svec = KB % 8 == 0 && (s.sa_packed || s.ldsa % 8 == 0) && (s.b_packed || s.ldsb % 8 == 0);
-    out->persist_grid = persist_grid(p, M, N, K, num_cu, s.ldd % 8 == 0, svec);
+    out->persist_grid = persist_grid(p, M, N, K, num_cu, s.ldd % 8 == 0, svec, s.sa_packed != 0);
     out->kernel = p.family;
     out->tile_m = p.bm;
     out->tile_n = p.bn;
@@ -707,7 +709,7 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
         if (!deep) {
             const bool svec = (s.sa_packed ? KB % 8 == 0 : g.sa_fast != 0) &&
                               (s.b_packed ? KB % 8 == 0 : g.sb_fast != 0);
-            g.persist_grid = (int)persist_grid(p, M, N, K, d->num_cu, g.d_stage != 0, svec);
+            g.persist_grid = (int)persist_grid(p, M, N, K, d->num_cu, g.d_stage != 0, svec, s.sa_packed != 0);
         }
         if (deep)
             (s.sa_packed ? k.deep_packed_sa : s.b_packed ? k.deep_packed : k.deep_plain)(g, (int)p.grid, stream);

@@ -261,8 +261,10 @@ def test_persistent_form_is_planned_only_where_it_applies(monkeypatch):
                                                        ldsb=K // 32, b_packed=pk, sa_packed=pk)
     pg = lambda M, N, K, s, split=-1: mx.mxgemm_plan_ex(M, N, K, s, split, 256)["persist_grid"]
     assert pg(8192, 8192, 8192, st(8192, 8192)) == 256
-    assert mx.mxgemm_plan(8192, 8192, 8192, 1, -1, 256)["persist_grid"] == 256
-    assert pg(5120, 5120, 512, st(5120, 512, pk=0)) == 256
+    assert mx.mxgemm_plan(8192, 8192, 8192, 1, -1, 256)["persist_grid"] == 0    # row-major A scales
+    assert pg(5120, 5120, 512, st(5120, 512, pk=0)) == 0            # 256 x 256 needs packed B and A scales
+    assert pg(5120, 5120, 512, st(5120, 512)) == 256
+    assert pg(4352, 4352, 1024, st(4352, 1024)) == 0                # 256 x 128 tile: plain grid
     assert pg(8192, 8192, 8192, st(8192, 8192), split=2) == 0      # split K
     assert pg(8192, 8192, 8448, st(8192, 8448)) == 0               # 264 blocks: odd stage count
     assert pg(8192, 8200, 8192, st(8200, 8192)) == 0               # ragged N tile
