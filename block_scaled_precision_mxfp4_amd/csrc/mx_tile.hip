@@ -118,14 +118,16 @@ __device__ __forceinline__ void store_whole_tile_staged(uint16_t *D, int64_t ldd
 // tiles, one per 128-K step (rows of 128 bytes, the same swizzle), and a
 // lane's operand for step ks is chunks g and g+4 of that step's tile -- the
 // two 16-element runs K 16g.. and 64+16g.. the 8-bit instruction reads.
-// PERSIST (tiles with one workgroup per CU): one workgroup per CU walks its tiles in the order the plain grid
-// runs them (hardware id i * grid + blockIdx, through the same XCD remap).
-// After a tile's last stage it issues the next tile's first stage into the
-// free buffer pair, then writes D through the other pair (half a wave tile
-// per pass): the next tile's load latency hides behind the epilogue, and
-// the epilogue's stores drain behind the next tile's first stage.  Needs
-// split 1, the staged epilogue and M, N multiples of the tile (every wave
-// then issues exactly 16 stores after those loads; the host checks).
+// PERSIST (a tile with one workgroup per CU; launched for 256 x 256 with
+// packed B and A scales): one workgroup per CU walks its tiles in the order
+// the plain grid runs them (hardware id blockIdx + i * grid, through the same
+// XCD remap).  After a tile's last stage (which reads buffer 1) it issues the
+// next tile's first stage into buffer 0, then writes D through buffer 1's A
+// half, 1/PARTS of the wave tile per pass: the next tile's load latency
+// hides behind the epilogue, and the epilogue's stores drain behind the next
+// tile's first stage.  Needs split 1, beta == 0 with the staged epilogue, an
+// even stage count and M, N multiples of the tile, so that every wave issues
+// exactly STORES stores after those loads (the host checks).
 template <int BM, int BN, int WM, int WN, bool BPACK, bool SVEC, bool SAPACK, int AFMT = 0, bool PERSIST = false>
 __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
 {
