@@ -354,6 +354,17 @@ def cpu_baseline(name, target_s=12.0):
                 n_rows, n_cols, name, macs, dt)}
 
 
+def split_sweep(name, args):
+    """The workload at every forced split (the heuristic's pick is timed on
+    its own line): us and algorithmic GB/s per split."""
+    out = []
+    for s in (1, 2, 4, 8, 16):
+        r = time_workload(name, args.steps, args.warmup, split_k=s, eager=args.eager,
+                          soak_ms=min(args.soak_ms, 100.0))
+        out.append({"split_k": r["split_k"], "us_per_step": r["us_per_step"], "gbs": r["gbs"]})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -420,6 +431,8 @@ def main():
               "roofline": {"bound": "hbm", "achieved": gemv["gbs"], "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": gemv["gbs"] / PEAK_HBM_GBS,
                            "traffic": measured_traffic(gemv["workload"])}}
+        if not args.only:
+            m1["split_sweep"] = split_sweep(gemv["workload"], args)
 
     quant = None if args.only else time_quantize(args.steps, args.warmup, eager=args.eager)
 
@@ -477,6 +490,9 @@ def main():
         "workloads": [{k: o[k] for k in ("workload", "kernel", "tile", "split_k", "us_per_step",
                                          "tflops", "gbs", "copies", "timing")} for o in [head] + others],
     }
+    skinny = next((o for o in others if o["workload"] == "skinny_64x7168x16384"), None)
+    if skinny is not None:
+        line["skinny_split_sweep"] = split_sweep(skinny["workload"], args)
     print(json.dumps(line), flush=True)
 
 
