@@ -466,13 +466,15 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         // load path takes about 16 cycles each to accept; a wave whose load
         // is not yet accepted cannot issue its next multiply either.  Waves
         // 0-3 therefore prefetch before their first multiply and waves 4-7
-        // after their first 16, so that while one wave of a SIMD waits on
-        // the load path the other one multiplies (8192^3: 5 % faster than
-        // one common issue point, measured on the same MI355X).  The K-tail
+        // before fragment step 3 (after their first 24 multiplies), so that
+        // while one wave of a SIMD waits on the load path the other one
+        // multiplies.  8192^3 on one MI355X: issue points (0, 2) were 5 %
+        // faster than one common point, and (0, 3) 1.5-2 % faster than
+        // (0, 2); (0, 1), (1, 3), (0, 4), (0, 5) and (0, 6) were slower.  The K-tail
         // variant (!SVEC) keeps one issue point: its larger address state
         // spills inside the loop when the loop is instantiated twice.
         if (wave >= 4)
-            run(std::integral_constant<int, 2>{});
+            run(std::integral_constant<int, 3>{});
         else
             run(std::integral_constant<int, 0>{});
     } else {
