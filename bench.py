@@ -251,7 +251,8 @@ def time_f16(steps, warmup, soak_ms=0.0, M=8192, N=8192, K=8192):
 FORMAT_NAMES = {0: "fp4", 1: "fp8_e4m3", 2: "fp8_e5m2", 3: "fp6_e2m3", 4: "fp6_e3m2"}
 # mixed-format lines: (workload, A format) -- decode and a small batch with
 # FP8 and FP6 activations against FP4 weights
-MIXED = [("gemv_1x8192x8192", 1), ("gemv_1x8192x8192", 3), ("skinny_64x7168x16384", 1), ("square_8192", 1)]
+MIXED = [("gemv_1x8192x8192", 1), ("gemv_1x8192x8192", 3), ("skinny_64x7168x16384", 1), ("square_8192", 1),
+         ("skinny_64x7168x16384", 3), ("square_8192", 3)]
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense 8-bit scaled matrix peak (half the FP4 rate)
 
 QUANT_SHAPE = (8192, 8192)  # the bf16 activation of the square workload's A
@@ -442,9 +443,10 @@ def main():
     if not args.only:
         for name, fmt in MIXED:
             r = time_workload(name, args.steps, args.warmup, eager=args.eager, soak_ms=args.soak_ms, a_fmt=fmt)
-            if r["M"] > 64:  # a contraction: the 8-bit matrix peak
-                roof = {"bound": "mfma", "achieved": r["tflops"], "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                        "frac": r["tflops"] / PEAK_FP8_TFLOPS, "traffic": None}
+            if r["M"] > 64:  # a contraction: the matrix peak of A's format (FP6 runs at the FP4 rate)
+                peak = PEAK_FP8_TFLOPS if fmt in (1, 2) else PEAK_MXFP4_TFLOPS
+                roof = {"bound": "mfma", "achieved": r["tflops"], "peak": peak, "unit": "TFLOP/s",
+                        "frac": r["tflops"] / peak, "traffic": None}
                 value, unit = r["tflops"], "TFLOP/s"
             else:
                 roof = {"bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",

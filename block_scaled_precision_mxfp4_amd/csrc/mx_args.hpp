@@ -123,4 +123,8 @@ void launch_f16(const F16Args &a, int64_t grid, hipStream_t s);
 // chunks add into it
 void launch_d_init(const GemmArgs &g, hipStream_t s);
 
+// FP6 A (E2M3 or E3M2, rows of lda_b bytes) -> FP8 A (E4M3 or E5M2 respectively,
+// rows of K bytes) in `out`, exactly; K % 16 == 0, lda_b % 4 == 0
+void launch_fp6_to_fp8(int a_fmt, const uint8_t *A, int64_t lda_b, uint8_t *out, int M, int K, hipStream_t s);
+
 }  // namespace mx

@@ -293,6 +293,11 @@ Plan plan_run(int M, int N, int K, const mxgemm_strides &s, int split_k, int num
         return plan_for(M, N, K, s.b_packed, split_k, num_cu, s.split_mode == MXGEMM_SPLIT_BF16_ATOMIC);
     if ((s.a_format == MXGEMM_FMT_FP8_E4M3 || s.a_format == MXGEMM_FMT_FP8_E5M2) && M > 16)
         return plan_a8(M, N, K, split_k, num_cu);
+    // FP6 with M > 16: A converted exactly to FP8 (rows of K bytes), then the
+    // 8-bit tiles, while a 256-row tile of the converted A stays below 2^31 bytes
+    if ((s.a_format == MXGEMM_FMT_FP6_E2M3 || s.a_format == MXGEMM_FMT_FP6_E3M2) && M > 16 &&
+        (int64_t)256 * K < ((int64_t)1 << 31))
+        return plan_a8(M, N, K, split_k, num_cu);
     return plan_for(std::min(M, 16), N, K, s.b_packed, split_k, num_cu, false, 1);
 }
 
@@ -368,6 +373,7 @@ struct DeviceBuffer {
 };
 struct StreamBuffers {
     DeviceBuffer partials, counters;
+    DeviceBuffer conv;  // FP6 A converted to FP8 (M x K bytes)
 };
 std::map<std::pair<int, hipStream_t>, StreamBuffers> g_ws;
 
@@ -414,6 +420,21 @@ mxgemm_status get_split_buffers(hipStream_t stream, size_t counter_need, size_t 
             return st;
         *partials = w.partials.ptr;
     }
+    return MXGEMM_OK;
+}
+
+// The per-stream buffer for FP6 A converted to FP8.
+mxgemm_status get_conv_buffer(hipStream_t stream, size_t need, void **conv)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return MXGEMM_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    StreamBuffers &w = g_ws[{dev, stream}];
+    mxgemm_status st = grow(w.conv, need, stream, false);
+    if (st != MXGEMM_OK)
+        return st;
+    *conv = w.conv.ptr;
     return MXGEMM_OK;
 }
 
@@ -691,7 +712,19 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     } else if (p.family == 3) {
         int n = 0;
         const mx::TileKernelA8 &k = mx::tile_kernels_a8(&n)[p.index];
-        (s.b_packed ? k.packed : k.plain)[s.a_format - 1](g, (int)p.grid, stream);
+        int fmt8 = s.a_format;
+        if (s.a_format == MXGEMM_FMT_FP6_E2M3 || s.a_format == MXGEMM_FMT_FP6_E3M2) {
+            // exact FP6 -> FP8 copy of A (E2M3 -> E4M3, E3M2 -> E5M2), same scales
+            void *conv = nullptr;
+            st = get_conv_buffer(stream, (size_t)M * (size_t)K, &conv);
+            if (st != MXGEMM_OK)
+                return st;
+            mx::launch_fp6_to_fp8(s.a_format, (const uint8_t *)A, lda_bytes, (uint8_t *)conv, M, K, stream);
+            g.A = (const uint8_t *)conv;
+            g.lda_b = K;
+            fmt8 = s.a_format == MXGEMM_FMT_FP6_E2M3 ? MXGEMM_FMT_FP8_E4M3 : MXGEMM_FMT_FP8_E5M2;
+        }
+        (s.b_packed ? k.packed : k.plain)[fmt8 - 1](g, (int)p.grid, stream);
     } else if (p.family == 0) {
         int n = 0;
         const mx::TileKernel &k = mx::tile_kernels(&n)[p.index];
@@ -856,7 +889,7 @@ mxgemm_status mxgemm_release_workspaces(void)
     for (auto &kv : g_ws) {
         if (hipSetDevice(kv.first.first) != hipSuccess || hipStreamSynchronize(kv.first.second) != hipSuccess)
             st = MXGEMM_ERR_HIP;
-        for (DeviceBuffer *b : {&kv.second.partials, &kv.second.counters})
+        for (DeviceBuffer *b : {&kv.second.partials, &kv.second.counters, &kv.second.conv})
             if (b->ptr && hipFree(b->ptr) != hipSuccess)
                 st = MXGEMM_ERR_HIP;
     }

@@ -118,3 +118,59 @@ def test_fp8_tiled_large_sampled():
     rows = np.sort(rng.choice(M, 24, replace=False))
     ref, mag, _ = oracle_ref(p, rows=rows)
     assert_parity(d[rows], ref, mag, "tiled 2048x2048x4096")
+
+
+# FP6 A with M > 16: A converted exactly to FP8 (E2M3 -> E4M3, E3M2 -> E5M2),
+# then the tiled kernel with 8-bit A tiles
+@pytest.mark.parametrize("fmt", [mx.FMT_FP6_E2M3, mx.FMT_FP6_E3M2], ids=lambda f: NAMES[f])
+def test_fp6_all_codes_through_the_8bit_tiles(fmt):
+    """B = I (FP4 1.0 on the diagonal, unit scales): D is A dequantized, and
+    every FP6 value has at most 4 significant bits, so D must equal the
+    oracle's bf16 result bit for bit.  The 32 rows hold all 64 codes, each
+    row a different rotation, with varied scales."""
+    M, K = 32, 64
+    N = K
+    codes = np.array([[(r + k) % 64 for k in range(K)] for r in range(M)], dtype=np.uint64)
+    A = np.zeros((M, K * 6 // 8), dtype=np.uint8)
+    for r in range(M):
+        acc = 0
+        for k in range(K):
+            acc |= int(codes[r, k]) << (6 * k)
+        A[r] = np.frombuffer(acc.to_bytes(K * 6 // 8, "little"), dtype=np.uint8)
+    rng = np.random.default_rng(fmt)
+    SA = rng.integers(118, 136, (M, K // 32)).astype(np.uint8)
+    B = np.zeros((N, K // 2), dtype=np.uint8)
+    for j in range(N):
+        B[j, j // 2] |= 0x2 << (4 * (j % 2))
+    SB = np.full((N, K // 32), 127, dtype=np.uint8)
+    p = dict(M=M, N=N, K=K, A=A, SA=SA, B=B, SB=SB, alpha=1.0, beta=0.0, C=None, a_fmt=fmt)
+    st = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32, a_format=fmt)
+    assert mx.mxgemm_plan_ex(M, N, K, st, -1, 256)["kernel"] == 3
+    say("case fp6 identity", NAMES[fmt])
+    d = gemm_gpu(p)
+    _, _, dref = oracle_ref(p)
+    same = (d == dref) | (((d | dref) & 0x7FFF) == 0)  # +0 and -0 are equal
+    assert same.all(), "%d of %d elements differ" % (int((~same).sum()), d.size)
+
+
+FP6_TILED = [
+    (300, 520, 1056, -1, False, "bf16"),  # K tail, C
+    (2048, 2048, 4096, 1, True, None),    # packed B, sampled
+]
+
+
+@pytest.mark.parametrize("fmt", [mx.FMT_FP6_E2M3, mx.FMT_FP6_E3M2], ids=lambda f: NAMES[f])
+@pytest.mark.parametrize("case", FP6_TILED, ids=lambda c: "%dx%dx%d" % c[:3])
+def test_fp6_tiled_matches_oracle(case, fmt):
+    M, N, K, split, packed, c = case
+    p = problem(case, fmt, seed=0xF6F6 + 13 * fmt + M)
+    say("case fp6 tiled", NAMES[fmt], case)
+    d = gemm_gpu(p, split_k=split, b_packed=packed)
+    if M * N <= 300 * 520:
+        ref, mag, _ = oracle_ref(p)
+        assert_parity(d, ref, mag, "fp6 tiled %s %s" % (NAMES[fmt], case))
+    else:
+        rng = np.random.default_rng(M + fmt)
+        rows = np.sort(rng.choice(M, 20, replace=False))
+        ref, mag, _ = oracle_ref(p, rows=rows)
+        assert_parity(d[rows], ref, mag, "fp6 tiled %s %s" % (NAMES[fmt], case))
