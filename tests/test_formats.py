@@ -174,3 +174,32 @@ def test_fp6_tiled_matches_oracle(case, fmt):
         rows = np.sort(rng.choice(M, 20, replace=False))
         ref, mag, _ = oracle_ref(p, rows=rows)
         assert_parity(d[rows], ref, mag, "fp6 tiled %s %s" % (NAMES[fmt], case))
+
+
+def test_fp6_conversion_buffers_are_per_stream():
+    """FP6 A with M > 16 is copied to FP8 in a buffer owned per (device,
+    stream).  Two problems of different sizes and formats on two streams,
+    each launched twice with no synchronization in between, must both match
+    the oracle."""
+    from mxgpu import dev_u8, host_bits
+    cases = [(mx.FMT_FP6_E2M3, 96, 512, 2048), (mx.FMT_FP6_E3M2, 200, 384, 1024)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    runs = []
+    for (fmt, M, N, K), s in zip(cases, streams):
+        p = inputs.make_problem(M, N, K, seed=0x5757 + fmt, e=(120, 134), a_fmt=fmt)
+        p["alpha"] = 0.5
+        A, B, SA, SB = dev_u8(p["A"]), dev_u8(p["B"]), dev_u8(p["SA"]), dev_u8(p["SB"])
+        D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        st = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32, a_format=fmt)
+        assert mx.mxgemm_plan_ex(M, N, K, st, -1, 256)["kernel"] == 3
+        runs.append((p, A, B, SA, SB, D, st, s))
+    torch.cuda.synchronize()
+    say("case fp6 two streams")
+    for _ in range(2):
+        for p, A, B, SA, SB, D, st, s in runs:
+            mx.mxgemm_run(D, None, A, B, SA, SB, p["alpha"], 0.0, p["M"], p["N"], p["K"], strides=st,
+                          stream=s.cuda_stream)
+    torch.cuda.synchronize()
+    for p, A, B, SA, SB, D, st, s in runs:
+        ref, mag, _ = oracle_ref(p)
+        assert_parity(host_bits(D), ref, mag, "fp6 stream %d" % p["a_fmt"])
