@@ -264,6 +264,71 @@ def quant_bytes(M, K):
     return 2 * M * K + M * K // 2 + M * K // 32
 
 
+def time_decode(steps, warmup, soak_ms=0.0, N=8192, K=8192):
+    """The decode step 1 x N x K from a bf16 activation: mxgemm_run_bf16a (the
+    quantizer fused into the GEMV's A load, one launch) against
+    mxgemm_quantize followed by mxgemm_run (two launches), each HIP-graph
+    replayed over rotated B copies so that B comes from HBM."""
+    import torch
+
+    import block_scaled_precision_mxfp4_amd as mx
+
+    copies = max(1, math.ceil(2.5 * LLC_BYTES / (N * K // 2 + N * K // 32)))
+    g = torch.Generator(device="cuda").manual_seed(0xDEC)
+    X = torch.randn((1, K), device="cuda", generator=g).to(torch.bfloat16)
+    Bs = [(torch.randint(0, 256, (N, K // 2), device="cuda", dtype=torch.uint8, generator=g),
+           torch.randint(118, 136, (N, K // 32), device="cuda", dtype=torch.uint8, generator=g))
+          for _ in range(copies)]
+    A = torch.empty((1, K // 2), dtype=torch.uint8, device="cuda")
+    SA = torch.empty((1, K // 32), dtype=torch.uint8, device="cuda")
+    D = torch.empty((1, N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.Stream()
+    cs = stream.cuda_stream
+
+    def fused(i):
+        B, SB = Bs[i % copies]
+        mx.mxgemm_run_bf16a(D, None, X, B, SB, 1.0, 0.0, 1, N, K, stream=cs)
+
+    def two_step(i):
+        B, SB = Bs[i % copies]
+        mx.mxgemm_quantize(A, SA, X, 1, K, stream=cs)
+        mx.mxgemm_run(D, None, A, B, SA, SB, 1.0, 0.0, 1, N, K, stream=cs)
+
+    out = {}
+    for name, launch in (("fused", fused), ("quantize_then_gemm", two_step)):
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                launch(i)
+            if soak_ms > 0:
+                t_end = time.time() + soak_ms / 1e3
+                i = 0
+                while time.time() < t_end:
+                    launch(i)
+                    i += 1
+                    if i % 64 == 0:
+                        torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                launch(i)
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) * 1e3 / steps
+        del graph
+    log("%-24s %-22s           %9.2f us  (quantize then GEMM: %.2f us, hipgraph, %d copies)" % (
+        "decode_1x%dx%d" % (N, K), "fused bf16 A", out["fused"], out["quantize_then_gemm"], copies))
+    return {"workload": "decode_1x%dx%d_bf16_activation" % (N, K), "us_per_step": out["fused"],
+            "us_two_launches": out["quantize_then_gemm"], "copies": copies}
+
+
 def time_quantize(steps, warmup, eager=False):
     """mxgemm_quantize on QUANT_SHAPE, HIP-graph replay over rotated inputs."""
     import torch
@@ -436,6 +501,7 @@ def main():
             m1["split_sweep"] = split_sweep(gemv["workload"], args)
 
     quant = None if args.only else time_quantize(args.steps, args.warmup, eager=args.eager)
+    decode = None if args.only or args.eager else time_decode(args.steps, args.warmup, soak_ms=min(args.soak_ms, 200.0))
 
     f16 = None if args.only else time_f16(args.steps, args.warmup, soak_ms=args.soak_ms)
 
@@ -487,6 +553,7 @@ def main():
         "mixed": mixed,
         "f16": f16,
         "quantize": quant,
+        "decode": decode,
         "device": {"arch": head["arch"], "num_cu": head["num_cu"], "clock_hz": head["clock_hz"],
                    "derived_peak_tflops": head["peak_flops_device"] / 1e12},
         "workloads": [{k: o[k] for k in ("workload", "kernel", "tile", "split_k", "us_per_step",

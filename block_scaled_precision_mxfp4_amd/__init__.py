@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
 
 # C-ABI entry points declared in include/libmxgemm.h
-EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_pack_b", "mxgemm_pack_scales", "mxgemm_quantize",
+EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_run_bf16a", "mxgemm_pack_b", "mxgemm_pack_scales", "mxgemm_quantize",
            "mxgemm_f16_run", "mxgemm_query", "mxgemm_plan", "mxgemm_query_ex", "mxgemm_plan_ex",
            "mxgemm_release_workspaces")
 
@@ -83,6 +83,9 @@ def lib():
         L.mxgemm_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, i32, i32, i32,
                                  ctypes.POINTER(Strides), i32, vp]
         L.mxgemm_run.restype = i32
+        L.mxgemm_run_bf16a.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, i32, i32, i32, i64,
+                                       ctypes.POINTER(Strides), i32, vp]
+        L.mxgemm_run_bf16a.restype = i32
         L.mxgemm_pack_b.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, vp]
         L.mxgemm_pack_b.restype = i32
         L.mxgemm_pack_scales.argtypes = [vp, vp, i32, i32, i64, vp]
@@ -174,6 +177,19 @@ def mxgemm_pack_scales(Sp, S, rows, K, lds=None, stream=None, check=True):
     st = lib().mxgemm_pack_scales(_ptr(Sp), _ptr(S), int(rows), int(K), int(lds), _stream(stream))
     if check:
         _check(st, "mxgemm_pack_scales")
+    return st
+
+
+def mxgemm_run_bf16a(D, C, X, B, scaleB, alpha, beta, M, N, K, ldx=None, strides=None, split_k=-1,
+                     stream=None, check=True):
+    """D = bf16(alpha * quantize(X) * B^T + beta * C) on `stream` (asynchronous);
+    X is a bf16 [M, ldx] activation (one fused launch at M = 1)."""
+    sp = ctypes.byref(strides) if strides is not None else None
+    st = lib().mxgemm_run_bf16a(_ptr(D), _ptr(C), _ptr(X), _ptr(B), _ptr(scaleB), float(alpha), float(beta),
+                                int(M), int(N), int(K), int(K if ldx is None else ldx), sp, int(split_k),
+                                _stream(stream))
+    if check:
+        _check(st, "mxgemm_run_bf16a")
     return st
 
 

@@ -81,6 +81,9 @@ const SkinnyKernel *skinny_kernels(int *count);
 // The skinny kernel with one 16-row group (M <= 16) and NR = 1 for A in a
 // wider format (a_fmt 1..4: FP8 E4M3, BF8 E5M2, FP6 E2M3, FP6 E3M2), B FP4.
 void launch_skinny_wide(int a_fmt, bool b_packed, const GemmArgs &g, int grid, hipStream_t s);
+// M == 1 with a bf16 A row quantized to MXFP4 on load (g.A = the row,
+// g.lda_b its byte pitch; g.SA unused); nr = 1, 2 or 4 as planned
+void launch_skinny_bf16a(int nr, bool b_packed, const GemmArgs &g, int grid, hipStream_t s);
 
 // Skinny kernel for 16 < M <= 64 with the waves splitting B's rows and A
 // staged once per workgroup in LDS: mg 16-row groups of A, nrw 16-row groups

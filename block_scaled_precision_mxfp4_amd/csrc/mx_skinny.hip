@@ -19,6 +19,7 @@
 // last workgroup to arrive, in the same launch.
 #include "mx_args.hpp"
 #include "mx_device.hpp"
+#include "mx_quantize.hpp"
 #include "mx_pipe.hpp"
 
 #include <type_traits>
@@ -39,20 +40,27 @@ namespace mx {
 // and 64+16g..64+16g+15 of the step (found with an identity-B probe on
 // MI355X; the scales still go by 32-element block, lane g holding block
 // g's), so the lane loads those two 16-byte pieces.
+// AFMT kBf16A: A is a single bf16 row (g.A, g.lda_b bytes per row), quantized
+// to MXFP4 on load with the activation quantizer's rule; g.SA is not read.
+constexpr int kBf16A = 5;
+
 template <int MG, int NR, bool BPACK, bool SVEC, bool APACK, bool A1, int AFMT = 0>
 __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
 {
     static_assert(!A1 || (MG == 1 && !APACK), "single-row A: one row group, row-major scales");
-    constexpr int AW = kFmtBits[AFMT];  // dwords of a lane's A operand (= element bits)
+    constexpr bool XQ = AFMT == kBf16A;  // bf16 A, quantized on load
+    static_assert(!XQ || A1, "quantize-on-load needs the single-row path");
+    constexpr int AF = XQ ? 0 : AFMT;   // the operand format the instruction sees
+    constexpr int AW = kFmtBits[AF];    // dwords of a lane's A operand (= element bits)
     constexpr int AKB = 4 * AW;         // bytes of one A K-block
     constexpr bool A8 = AW == 8;        // 8-bit A: two 16-element runs per lane
-    using a_t = typename std::conditional<AFMT == 0, v4i, v8i>::type;
+    using a_t = typename std::conditional<AF == 0, v4i, v8i>::type;
     // A1 with 8-bit A holds one 16-byte chunk per lane, else one K-block
     using aw_t = typename std::conditional<A8, v4i, a_t>::type;
     static_assert(!(A1 && A8) || (NR + MG) <= 3, "single-row 8-bit A: 8 steps per batch, one chunk per lane");
     // one lane's K-block of A at byte offset off (out-of-range offsets read zeros)
     auto load_a = [](__amdgpu_buffer_rsrc_t r, uint32_t off) __attribute__((always_inline)) {
-        if constexpr (AFMT == 0) {
+        if constexpr (AF == 0) {
             return load16(r, off);
         } else {
             const v4i lo = load16(r, off);
@@ -132,6 +140,9 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
         v4i sar[APACK || A1 ? 1 : G][MG];
         aw_t aw;       // A1: K-block kb0 + lane (8-bit A: 16-byte chunk lane) of row 0
         uint32_t saw;  // A1: its scale byte
+        // XQ: bf16 quarter-blocks of the batch, U/4 loads of 64 lanes: in load
+        // h, lane l holds elements 8(l%4) .. 8(l%4)+7 of K-block 16h + l/4
+        v4i xq[XQ ? U / 4 : 1];
     };
 
     auto load_batch = [&](int ks0, Batch &bt, auto bufc) __attribute__((always_inline)) {
@@ -177,7 +188,13 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
                     bt.a[u][mg] = load_a(ra, ok ? (uint32_t)((mg * 16 + (lane & 15)) * g.lda_b + kb * AKB) : kOOB);
             }
         }
-        if constexpr (A1) {
+        if constexpr (XQ) {
+#pragma unroll
+            for (int h = 0; h < U / 4; ++h) {
+                const int kbx = ks0 * 4 + 16 * h + (lane >> 2);
+                bt.xq[h] = load16(ra, kbx < kb_wend ? (uint32_t)(kbx * 64 + (lane & 3) * 16) : kOOB);
+            }
+        } else if constexpr (A1) {
             const int kbl = ks0 * 4 + lane;
             const bool okl = lane < 4 * U && kbl < kb_wend;
             if constexpr (A8) {
@@ -239,7 +256,7 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
 
     // vector-memory instructions of one load_batch (all lanes issue all of
     // them): staged B, the single A row and its scales, row-major B scales
-    constexpr int LN = NR * U + (AW == 6 ? 3 : 2) + G * NR * (SVEC ? 1 : 4);
+    constexpr int LN = NR * U + (XQ ? U / 4 : AW == 6 ? 3 : 2) + G * NR * (SVEC ? 1 : 4);
     static_assert(!BST || LN < 64, "vmcnt range");
     auto compute = [&](const Batch &bt, auto bufc, auto lastc) __attribute__((always_inline)) {
         v4i bst[BST ? U : 1][NR];
@@ -263,6 +280,33 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
             });
             lds_wait_n<0>(bst);
         }
+        // the single A row's K-blocks of the batch: lane b < 4U holds block
+        // ks0*4 + b (16 bytes) and its scale byte
+        aw_t aw_use = {};
+        uint32_t saw_use = 0;
+        if constexpr (XQ) {
+            // quantize the quarter-blocks (four lanes per block), then gather
+            // block b's four words and its scale from lanes 4(b%16) .. +3 of
+            // load b/16
+            const int src = (lane & 15) * 16;  // byte address of lane 4(b%16)
+#pragma unroll
+            for (int h = 0; h < U / 4; ++h) {
+                uint32_t word;
+                uint8_t sc;
+                quantize_quarter(bt.xq[h], word, sc);
+                const bool mine = (lane >> 4) == h;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int v = __builtin_amdgcn_ds_bpermute(src + 4 * i, (int)word);
+                    aw_use[i] = mine ? v : aw_use[i];
+                }
+                const int sv = __builtin_amdgcn_ds_bpermute(src, (int)sc);
+                saw_use = mine ? (uint32_t)sv : saw_use;
+            }
+        } else if constexpr (A1) {
+            aw_use = bt.aw;
+            saw_use = bt.saw;
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             a_t a1 = {};
@@ -272,8 +316,8 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
                 const int lo = (8 * u + (lane >> 4)) * 4, hi = lo + 16;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    a1[i] = __builtin_amdgcn_ds_bpermute(lo, bt.aw[i]);
-                    a1[4 + i] = __builtin_amdgcn_ds_bpermute(hi, bt.aw[i]);
+                    a1[i] = __builtin_amdgcn_ds_bpermute(lo, aw_use[i]);
+                    a1[4 + i] = __builtin_amdgcn_ds_bpermute(hi, aw_use[i]);
                 }
             }
             if constexpr (A1) {
@@ -281,9 +325,9 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
                 if constexpr (!A8) {
 #pragma unroll
                     for (int i = 0; i < AW; ++i)
-                        a1[i] = __builtin_amdgcn_ds_bpermute(src, bt.aw[i]);
+                        a1[i] = __builtin_amdgcn_ds_bpermute(src, aw_use[i]);
                 }
-                sa1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)bt.saw) & 0xFFu;
+                sa1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)saw_use) & 0xFFu;
             }
 #pragma unroll
             for (int nr = 0; nr < NR; ++nr)
@@ -298,10 +342,10 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
                                          : APACK ? bt.sap[u / 2][mg] >> (8 * (mg & 1))
                                                  : scale_group_word<SVEC>(bt.sar[u / 4][mg], lane);
                     const v4i bf = BST ? bst[BST ? u : 0][nr] : bt.b[u][nr];
-                    if constexpr (AFMT == 0)
+                    if constexpr (AF == 0)
                         acc[nr][mg] = mma_sel(ob, oa, bf, A1 ? a1 : bt.a[u][mg], acc[nr][mg], (int)sbr, (int)sar);
                     else
-                        acc[nr][mg] = mma_sel_wide<kFmtHw[AFMT]>(ob, oa, bf, A1 ? a1 : bt.a[u][mg], acc[nr][mg],
+                        acc[nr][mg] = mma_sel_wide<kFmtHw[AF]>(ob, oa, bf, A1 ? a1 : bt.a[u][mg], acc[nr][mg],
                                                                  (int)sbr, (int)sar);
                 }
         }
@@ -437,6 +481,27 @@ static void launch_skinny_fmt(const GemmArgs &g, int grid, hipStream_t s)
         hipLaunchKernelGGL((mx_skinny_kernel<1, 1, BPACK, true, false, false, AFMT>), dim3(grid), dim3(256), 0, s, g);
     else
         hipLaunchKernelGGL((mx_skinny_kernel<1, 1, BPACK, false, false, false, AFMT>), dim3(grid), dim3(256), 0, s, g);
+}
+
+template <int NR, bool BPACK>
+static void launch_skinny_bf16a_nr(const GemmArgs &g, int grid, hipStream_t s)
+{
+    if (g.scale16 || BPACK)
+        hipLaunchKernelGGL((mx_skinny_kernel<1, NR, BPACK, true, false, true, kBf16A>), dim3(grid), dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((mx_skinny_kernel<1, NR, BPACK, false, false, true, kBf16A>), dim3(grid), dim3(256), 0, s, g);
+}
+
+void launch_skinny_bf16a(int nr, bool b_packed, const GemmArgs &g, int grid, hipStream_t s)
+{
+    switch ((nr == 1 ? 0 : nr == 2 ? 1 : 2) * 2 + (b_packed ? 1 : 0)) {
+    case 0: launch_skinny_bf16a_nr<1, false>(g, grid, s); break;
+    case 1: launch_skinny_bf16a_nr<1, true>(g, grid, s); break;
+    case 2: launch_skinny_bf16a_nr<2, false>(g, grid, s); break;
+    case 3: launch_skinny_bf16a_nr<2, true>(g, grid, s); break;
+    case 4: launch_skinny_bf16a_nr<4, false>(g, grid, s); break;
+    default: launch_skinny_bf16a_nr<4, true>(g, grid, s); break;
+    }
 }
 
 void launch_skinny_wide(int a_fmt, bool b_packed, const GemmArgs &g, int grid, hipStream_t s)

@@ -573,12 +573,22 @@ mxgemm_status mxgemm_query(int M, int N, int K, int b_packed, int split_k, mxgem
     return MXGEMM_OK;
 }
 
-mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, const void *scaleA,
-                         const void *scaleB, float alpha, float beta, int M, int N, int K,
-                         const mxgemm_strides *strides, int split_k, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// mxgemm_run, and with X != NULL the fused single-row form of
+// mxgemm_run_bf16a: A is the bf16 row X (ldx elements between rows),
+// quantized to MXFP4 on load by the skinny kernel; A and scaleA are unused.
+mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, const void *scaleA,
+                       const void *scaleB, float alpha, float beta, int M, int N, int K,
+                       const mxgemm_strides *strides, int split_k, hipStream_t stream, const void *X,
+                       int64_t ldx)
 {
     // ---- host-only validation (no HIP call before it passes)
-    if (!D || !A || !B || !scaleA || !scaleB || !valid_split(split_k))
+    if (!D || !B || !scaleB || !valid_split(split_k))
+        return MXGEMM_ERR_INVALID_ARG;
+    if (X ? M != 1 : (!A || !scaleA))
         return MXGEMM_ERR_INVALID_ARG;
     if (beta != 0.0f && !C)
         return MXGEMM_ERR_INVALID_ARG;
@@ -602,6 +612,18 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
         s.ldsa = s.ldsb = K / 32;
     }
     const int KB = K / 32;
+    if (X) {
+        // the bf16 row replaces A and its scales
+        if (s.a_format != MXGEMM_FMT_FP4 || s.sa_packed || s.split_mode != MXGEMM_SPLIT_FP32)
+            return MXGEMM_ERR_INVALID_ARG;
+        if (ldx < K)
+            return MXGEMM_ERR_SHAPE;
+        if (!aligned(X, 16) || ldx % 8)
+            return MXGEMM_ERR_ALIGN;
+        A = X;
+        s.lda = 4 * ldx;  // the row's byte pitch (2 * ldx) in fp4 elements
+        s.ldsa = KB;
+    }
     if (s.ldd < N || s.lda < K || (!s.sa_packed && s.ldsa < KB) || (beta != 0.0f && s.ldc < N))
         return MXGEMM_ERR_SHAPE;
     if (!s.b_packed && (s.ldb < K || s.ldsb < KB))
@@ -616,7 +638,7 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     if (!aligned(A, 16) || !aligned(B, 16) || lda_bytes % (a_bits == 6 ? 8 : 16) ||
         (!s.b_packed && (s.ldb / 2) % 16))
         return MXGEMM_ERR_ALIGN;
-    if ((s.b_packed && !aligned(scaleB, 4)) || (s.sa_packed && !aligned(scaleA, 4)))
+    if ((s.b_packed && !aligned(scaleB, 4)) || (!X && s.sa_packed && !aligned(scaleA, 4)))
         return MXGEMM_ERR_ALIGN;
     if (!aligned(D, 2) || (C && beta != 0.0f && !aligned(C, s.c_f32 ? 4 : 2)))
         return MXGEMM_ERR_ALIGN;
@@ -643,7 +665,7 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     g.C = C;
     g.A = (const uint8_t *)A;
     g.B = (const uint8_t *)B;
-    g.SA = (const uint8_t *)scaleA;
+    g.SA = X ? nullptr : (const uint8_t *)scaleA;
     g.SB = (const uint8_t *)scaleB;
     g.alpha = alpha;
     g.beta = beta;
@@ -663,16 +685,16 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     g.tiles_n = p.tiles_n;
     g.ks_total = cdiv(KB, 4);
     g.sn8 = cdiv(KB, 8);
-    g.sa_fast = aligned(scaleA, 8) && s.ldsa % 8 == 0 && KB % 8 == 0;
+    g.sa_fast = !X && aligned(scaleA, 8) && s.ldsa % 8 == 0 && KB % 8 == 0;
     g.sb_fast = !s.b_packed && aligned(scaleB, 8) && s.ldsb % 8 == 0 && KB % 8 == 0;
-    g.scale16 = aligned(scaleA, 16) && s.ldsa % 16 == 0 && KB % 16 == 0 &&
+    g.scale16 = (X || (aligned(scaleA, 16) && s.ldsa % 16 == 0)) && KB % 16 == 0 &&
                 (s.b_packed || (aligned(scaleB, 16) && s.ldsb % 16 == 0));
     g.d_vec = aligned(D, 8) && s.ldd % 4 == 0;
     g.c_vec = C && aligned(C, s.c_f32 ? 16 : 8) && s.ldc % 4 == 0;
     g.c_f32 = s.c_f32;
     g.d_stage = beta == 0.0f && aligned(D, 16) && s.ldd % 8 == 0;
     g.sa_packed = s.sa_packed;
-    g.sa16 = !s.sa_packed && aligned(scaleA, 16) && s.ldsa % 16 == 0 && KB % 16 == 0;
+    g.sa16 = !X && !s.sa_packed && aligned(scaleA, 16) && s.ldsa % 16 == 0 && KB % 16 == 0;
     g.sb16 = !s.b_packed && aligned(scaleB, 16) && s.ldsb % 16 == 0 && KB % 16 == 0;
     g.group_m = 4;
 
@@ -696,7 +718,11 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
         return MXGEMM_ERR_SHAPE;
     if (g.split_atomic)
         mx::launch_d_init(g, stream);
-    if (wide) {
+    if (X) {
+        if (p.family != 1)  // M == 1 with the fp32 split reduction plans the skinny kernel
+            return MXGEMM_ERR_INVALID_ARG;
+        mx::launch_skinny_bf16a(p.bn / 16, s.b_packed != 0, g, (int)p.grid, stream);
+    } else if (wide) {
         // stream-ordered launches over 16-row blocks of A, C and D; the split
         // counters return to zero at the end of each
         for (int m0 = 0; m0 < M; m0 += 16) {
@@ -760,6 +786,54 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
     if (hipGetLastError() != hipSuccess)
         return MXGEMM_ERR_HIP;
     return MXGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, const void *scaleA,
+                         const void *scaleB, float alpha, float beta, int M, int N, int K,
+                         const mxgemm_strides *strides, int split_k, hipStream_t stream)
+{
+    return run_impl(D, C, A, B, scaleA, scaleB, alpha, beta, M, N, K, strides, split_k, stream, nullptr, 0);
+}
+
+mxgemm_status mxgemm_run_bf16a(void *D, const void *C, const void *X, const void *B, const void *scaleB,
+                               float alpha, float beta, int M, int N, int K, int64_t ldx,
+                               const mxgemm_strides *strides, int split_k, hipStream_t stream)
+{
+    if (!X)
+        return MXGEMM_ERR_INVALID_ARG;
+    if (M == 1)
+        return run_impl(D, C, nullptr, B, nullptr, scaleB, alpha, beta, M, N, K, strides, split_k, stream, X, ldx);
+    // M > 1: quantize into a per-stream buffer, then the ordinary call
+    mxgemm_status st = check_shape(M, N, K);
+    if (st != MXGEMM_OK)
+        return st;
+    if (strides && (strides->a_format != MXGEMM_FMT_FP4 || strides->sa_packed))
+        return MXGEMM_ERR_INVALID_ARG;
+    const size_t a_bytes = align_up((size_t)M * (size_t)(K / 2), 256);
+    void *buf = nullptr;
+    st = get_conv_buffer(stream, a_bytes + (size_t)M * (size_t)(K / 32), &buf);
+    if (st != MXGEMM_OK)
+        return st;
+    uint8_t *Aq = (uint8_t *)buf, *SAq = Aq + a_bytes;
+    st = mxgemm_quantize(Aq, SAq, X, M, K, ldx, K, K / 32, stream);
+    if (st != MXGEMM_OK)
+        return st;
+    mxgemm_strides s2;
+    if (strides) {
+        s2 = *strides;
+    } else {
+        std::memset(&s2, 0, sizeof s2);
+        s2.ldd = s2.ldc = N;
+        s2.ldb = K;
+        s2.ldsb = K / 32;
+    }
+    s2.lda = K;
+    s2.ldsa = K / 32;
+    return mxgemm_run(D, C, Aq, B, SAq, scaleB, alpha, beta, M, N, K, &s2, split_k, stream);
 }
 
 mxgemm_status mxgemm_pack_b(void *Bp, void *SBp, const void *B, const void *scaleB, int N, int K, int64_t ldb,

@@ -254,6 +254,28 @@ mxgemm_status mxgemm_pack_scales(void *Sp, const void *S, int rows, int K, int64
 mxgemm_status mxgemm_quantize(void *A, void *scaleA, const void *X, int M, int K,
                               int64_t ldx, int64_t lda, int64_t ldsa, hipStream_t stream);
 
+/*
+ * D = bf16(alpha * Q(X) * B^T + beta * C), where X is a bf16 activation
+ * matrix [M][ldx] (row-major, ldx in bf16 elements, 16-byte aligned rows:
+ * ldx % 8 == 0, X 16-byte aligned, ldx >= K) and Q is mxgemm_quantize's
+ * encoding -- the activation-side quantizer in front of the GEMM.  B,
+ * scaleB, C, D, strides (ldd, ldc, ldb, ldsb, b_packed, c_f32, workspace)
+ * and split_k as for mxgemm_run; strides->lda / ldsa are ignored, and
+ * a_format, sa_packed and split_mode must be 0 (else
+ * MXGEMM_ERR_INVALID_ARG).
+ *   M == 1 (decode): one launch.  The skinny kernel loads the bf16 row and
+ *     quantizes each 32-block in registers with the quantizer's rule, so D
+ *     is bit for bit what mxgemm_quantize followed by mxgemm_run gives.
+ *   M > 1: mxgemm_quantize into a library-owned buffer of
+ *     M*K/2 + M*K/32 bytes per (device, stream) (allocated on first use like
+ *     the split-K buffers, freed by mxgemm_release_workspaces), then
+ *     mxgemm_run on it, both on `stream`.
+ * Asynchronous on `stream`; errors as mxgemm_run.
+ */
+mxgemm_status mxgemm_run_bf16a(void *D, const void *C, const void *X, const void *B, const void *scaleB,
+                               float alpha, float beta, int M, int N, int K, int64_t ldx,
+                               const mxgemm_strides *strides, int split_k, hipStream_t stream);
+
 /* ---- FP16 GEMM with transposed LDS reads ---------------------------------- */
 
 /*

@@ -273,3 +273,22 @@ def test_persistent_form_is_planned_only_where_it_applies(monkeypatch):
     assert mx.mxgemm_plan_ex(8192, 8192, 8192, st(8192, 8192), -1, 128)["persist_grid"] == 128
     monkeypatch.setenv("MXGEMM_TILE_PERSIST", "0")
     assert pg(8192, 8192, 8192, st(8192, 8192)) == 0
+
+
+def test_run_bf16a_validation_before_any_hip_call():
+    def f(**kw):
+        args = dict(D=0x1000, C=None, X=0x2000, B=0x3000, scaleB=0x5000, alpha=1.0, beta=0.0, M=1, N=256,
+                    K=512, ldx=None, strides=None, split_k=-1, stream=0)
+        args.update(kw)
+        return mx.mxgemm_run_bf16a(**args, check=False)
+    st = lambda **kw: mx.make_strides(**dict(dict(ldd=256, ldc=256, lda=512, ldb=512, ldsa=16, ldsb=16), **kw))
+    assert f(X=None) == -1 and f(B=None) == -1 and f(scaleB=None) == -1 and f(D=None) == -1
+    assert f(beta=1.0) == -1 and f(split_k=3) == -1
+    for M in (1, 8):
+        # A's options must stay at their defaults: the row is quantized to FP4 with row-major scales
+        assert f(M=M, strides=st(a_format=mx.FMT_FP8_E4M3)) == -1
+        assert f(M=M, strides=st(b_packed=1, sa_packed=1)) == -1
+        assert f(M=M, K=48) == -2 and f(M=M, N=0) == -2
+    assert f(strides=st(split_mode=mx.SPLIT_BF16_ATOMIC)) == -1
+    assert f(ldx=480) == -2                      # ldx < K
+    assert f(X=0x2008) == -3 and f(ldx=516) == -3  # 16-byte rows of X
