@@ -139,3 +139,18 @@ def test_bf16a_several_rows_matches_quantize_then_gemm(M):
     d = run_fused(p)
     d2 = run_two_step(p)
     assert same_bits(d, d2)
+
+
+@pytest.mark.parametrize("nr", [2, 4])
+def test_fused_decode_wider_row_groups(nr, monkeypatch):
+    """32 and 64 rows of B per workgroup (MXGEMM_FORCE_NR; the planner picks
+    16 at M = 1): the quantize-on-load kernels for those row groups, row-major
+    and packed B, against the two-step path."""
+    monkeypatch.setenv("MXGEMM_FORCE_NR", str(nr))
+    assert mx.mxgemm_plan(1, 1000, 2048, 0, -1, 256)["tile_n"] == 16 * nr
+    for packed in (False, True):
+        p = problem(1, 1000, 2048, seed=0x4E52 + nr, beta=1.0)
+        say("case fused decode nr", nr, "packed", packed)
+        d = run_fused(p, packed)
+        d2 = run_two_step(p, packed)
+        assert same_bits(d, d2)
