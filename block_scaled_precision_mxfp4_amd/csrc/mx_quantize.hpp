@@ -27,10 +27,12 @@ __device__ __forceinline__ void quantize_quarter(v4i x, uint32_t &word, uint8_t 
             amag = max(amag, hb & 0x7FFFu);
         }
     }
-    amag = max(amag, (uint32_t)__shfl_xor((int)amag, 1));
-    amag = max(amag, (uint32_t)__shfl_xor((int)amag, 2));
-    special |= (uint32_t)__shfl_xor((int)special, 1);
-    special |= (uint32_t)__shfl_xor((int)special, 2);
+    // the block's four lanes are one aligned quad: quad permutes (lane ^ 1,
+    // lane ^ 2) exchange within it without going through LDS
+    amag = max(amag, (uint32_t)__builtin_amdgcn_mov_dpp((int)amag, 0xB1, 0xF, 0xF, true));
+    amag = max(amag, (uint32_t)__builtin_amdgcn_mov_dpp((int)amag, 0x4E, 0xF, 0xF, true));
+    special |= (uint32_t)__builtin_amdgcn_mov_dpp((int)special, 0xB1, 0xF, 0xF, true);
+    special |= (uint32_t)__builtin_amdgcn_mov_dpp((int)special, 0x4E, 0xF, 0xF, true);
 
     // floor(log2 amax) from the bf16 fields (subnormal: from the top set
     // mantissa bit), then the scale exponent
