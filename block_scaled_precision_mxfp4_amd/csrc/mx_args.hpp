@@ -96,6 +96,8 @@ struct RowsKernel {
 const RowsKernel *rows_kernels(int *count);
 
 void launch_pack_b(uint8_t *Bp, const uint8_t *B, int N, int KB, int64_t ldb_b, hipStream_t s);
+// p[0 .. words) = 0, on stream s
+void launch_zero_words(uint32_t *p, size_t words, hipStream_t s);
 
 // bf16 -> MXFP4 quantizer: X [M][ldx] bf16 -> A [M][lda_b] bytes, S [M][lds].
 struct QuantArgs {

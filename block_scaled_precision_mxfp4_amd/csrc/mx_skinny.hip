@@ -588,6 +588,19 @@ void launch_pack_b(uint8_t *Bp, const uint8_t *B, int N, int KB, int64_t ldb_b, 
     hipLaunchKernelGGL(mx_pack_b_kernel, dim3((unsigned)blocks), dim3(256), 0, s, Bp, B, N, KB, ldb_b, KS, total);
 }
 
+__global__ void __launch_bounds__(256) mx_zero_words_kernel(uint32_t *p, int64_t words)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < words)
+        p[i] = 0u;
+}
+
+void launch_zero_words(uint32_t *p, size_t words, hipStream_t s)
+{
+    const int64_t blocks = ((int64_t)words + 255) / 256;
+    hipLaunchKernelGGL(mx_zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, (int64_t)words);
+}
+
 void launch_pack_sb(uint32_t *SBp, const uint8_t *SB, int N, int KB, int64_t ldsb, hipStream_t s)
 {
     const int sn8 = (KB + 7) / 8;

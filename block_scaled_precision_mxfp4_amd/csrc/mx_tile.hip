@@ -205,26 +205,28 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         kb_begin = z * g.kb_per_split;
         kb_end = min(g.KB, kb_begin + g.kb_per_split);
         nst = (kb_end - kb_begin + 7) >> 3;
+        // (every range below is under 2^31 bytes: the host rejects strides
+        // and K for which a 256-row tile's would not be)
         const int rows_a = min(BM, g.M - m0);
         a_base = g.A + (int64_t)m0 * g.lda_b;
-        a_bytes = (uint32_t)(rows_a * g.lda_b);
+        a_bytes = (uint32_t)((int64_t)rows_a * g.lda_b);
         if constexpr (SAPACK) {
             const int m32 = m0 / 32, grp32 = min(BM / 32, (g.M + 31) / 32 - m32);
-            rsa = make_rsrc(g.SA + (int64_t)m32 * g.sn8 * 256, (uint32_t)(grp32 * g.sn8 * 256));
+            rsa = make_rsrc(g.SA + (int64_t)m32 * g.sn8 * 256, (uint32_t)((int64_t)grp32 * g.sn8 * 256));
         } else {
-            rsa = make_rsrc(g.SA + (int64_t)m0 * g.ldsa, (uint32_t)(rows_a * g.ldsa));
+            rsa = make_rsrc(g.SA + (int64_t)m0 * g.ldsa, (uint32_t)((int64_t)rows_a * g.ldsa));
         }
         if constexpr (BPACK) {
             const int n16 = n0 / 16, grp16 = min(BN / 16, (g.N + 15) / 16 - n16);
             b_base = g.B + (int64_t)n16 * g.ks_total * 1024;
-            b_bytes = (uint32_t)(grp16 * g.ks_total * 1024);
+            b_bytes = (uint32_t)((int64_t)grp16 * g.ks_total * 1024);
             const int n32 = n0 / 32, grp32 = min(BN / 32, (g.N + 31) / 32 - n32);
-            rsb = make_rsrc(g.SB + (int64_t)n32 * g.sn8 * 256, (uint32_t)(grp32 * g.sn8 * 256));
+            rsb = make_rsrc(g.SB + (int64_t)n32 * g.sn8 * 256, (uint32_t)((int64_t)grp32 * g.sn8 * 256));
         } else {
             const int rows_b = min(BN, g.N - n0);
             b_base = g.B + (int64_t)n0 * g.ldb_b;
-            b_bytes = (uint32_t)(rows_b * g.ldb_b);
-            rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)(rows_b * g.ldsb));
+            b_bytes = (uint32_t)((int64_t)rows_b * g.ldb_b);
+            rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)((int64_t)rows_b * g.ldsb));
         }
     };
     // units of work are (tile, K chunk) pairs: the plain grid runs one per

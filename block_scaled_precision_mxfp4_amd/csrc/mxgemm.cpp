@@ -392,9 +392,16 @@ mxgemm_status grow(DeviceBuffer &b, size_t need, hipStream_t stream, bool zero)
     void *p = nullptr;
     if (hipMalloc(&p, sz) != hipSuccess)
         return MXGEMM_ERR_HIP;
-    if (zero && hipMemset(p, 0, sz) != hipSuccess) {
-        (void)hipFree(p);
-        return MXGEMM_ERR_HIP;
+    if (zero) {
+        // zeroed by a kernel on the caller's stream, so that the zeroing is
+        // ordered before every later launch on that stream that uses the
+        // buffer (a memset on the null stream is not ordered with
+        // non-blocking streams)
+        mx::launch_zero_words((uint32_t *)p, sz / 4, stream);
+        if (hipGetLastError() != hipSuccess) {
+            (void)hipFree(p);
+            return MXGEMM_ERR_HIP;
+        }
     }
     b.ptr = p;
     b.bytes = sz;
@@ -645,8 +652,12 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     const bool atomic = s.split_mode == MXGEMM_SPLIT_BF16_ATOMIC;
     if (atomic && (!aligned(D, 4) || s.ldd % 2 || N % 2))
         return MXGEMM_ERR_ALIGN;
-    // byte offsets inside a tile must stay below 2^31
-    if ((int64_t)256 * lda_bytes >= ((int64_t)1 << 31) || (!s.b_packed && (int64_t)256 * (s.ldb / 2) >= ((int64_t)1 << 31)))
+    // byte offsets and buffer ranges inside a 256-row tile must stay below
+    // 2^31: A and B rows, scale rows, and a 256-row slice of packed B
+    const int64_t k31 = (int64_t)1 << 31;
+    if ((int64_t)256 * lda_bytes >= k31 || (!s.b_packed && (int64_t)256 * (s.ldb / 2) >= k31) ||
+        (!X && !s.sa_packed && (int64_t)256 * s.ldsa >= k31) || (!s.b_packed && (int64_t)256 * s.ldsb >= k31) ||
+        (s.b_packed && (int64_t)16 * cdiv(KB, 4) * 1024 >= k31))
         return MXGEMM_ERR_SHAPE;
 
     // ---- device and plan

@@ -113,6 +113,12 @@ def test_run_stride_validation():
     assert _run(strides=st(a_format=3, lda=516)) == -3   # 387-byte pitch
     assert _run(strides=st(a_format=4, lda=528)) == -3   # 396 bytes: not a multiple of 8
     assert _run(strides=st(a_format=4, lda=510)) == -2   # lda < K
+    # every byte range of a 256-row tile stays below 2^31: scale row pitches
+    assert _run(strides=st(ldsa=1 << 23)) == -2
+    assert _run(strides=st(ldsb=1 << 23)) == -2
+    # (just below the limit validation passes; the call then fails for want
+    # of a device here)
+    assert _run(strides=st(ldsa=(1 << 23) - 1, ldsb=(1 << 23) - 1)) not in (-1, -2, -3)
     # bf16-atomic split-K: D 4-byte aligned, ldd and N even
     assert _run(strides=st(split_mode=1), D=0x1002) == -3
     assert _run(strides=st(split_mode=1, ldd=257)) == -3
