@@ -121,14 +121,36 @@ def test_fused_decode_matches_quantize_then_gemm(case):
 
 
 def test_fused_decode_special_values():
-    """NaN / inf blocks (scale 0xFF), -0, zero blocks, exact ties: the
-    outputs (NaN where a NaN or inf block meets a nonzero product) match the
-    two-step path bit for bit."""
+    """NaN / inf blocks (scale 0xFF), -0, zero blocks, exact ties, bf16
+    subnormal blocks: the fused kernel matches the two-step path bit for
+    bit and the oracle's quantizer and GEMM element by element.  With a NaN
+    or infinity anywhere in the row, every output is NaN (a block of scale
+    0xFF holds codes 0, and 0 x NaN is NaN); the same row with its NaN and
+    infinities replaced by finite values checks the other specials against
+    the oracle's values."""
     for K in (1024, 4096):
         p = problem(1, 512, K, seed=0x5BEC + K, specials=True)
+        say("case fused decode specials K", K)
         d = run_fused(p)
         d2 = run_two_step(p)
         assert same_bits(d, d2)
+        p["A"], p["SA"] = oracle.quantize_mxfp4(p["X"])
+        assert (p["SA"] == 0xFF).any()
+        ref, mag, _ = oracle_ref(p)
+        assert np.isnan(ref).all()
+        assert_parity(d, ref, mag, "fused decode specials K=%d" % K)
+        # finite specials only
+        X = p["X"].copy()
+        nonfinite = (X & 0x7F80) == 0x7F80
+        X[nonfinite] = 0x3F80 | (X[nonfinite] & 0x8000)  # +-1.0
+        p["X"] = X
+        d = run_fused(p)
+        assert same_bits(d, run_two_step(p))
+        p["A"], p["SA"] = oracle.quantize_mxfp4(X)
+        assert not (p["SA"] == 0xFF).any()
+        ref, mag, _ = oracle_ref(p)
+        assert np.isfinite(ref).all()
+        assert_parity(d, ref, mag, "fused decode finite specials K=%d" % K)
 
 
 @pytest.mark.parametrize("M", [2, 16, 40, 300])
