@@ -18,13 +18,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
 
 # C-ABI entry points declared in include/libmxgemm.h
-EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_run_bf16a", "mxgemm_pack_b", "mxgemm_pack_scales", "mxgemm_quantize",
+EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_run_noalloc", "mxgemm_run_bf16a", "mxgemm_pack_b", "mxgemm_pack_scales", "mxgemm_quantize",
            "mxgemm_f16_run", "mxgemm_query", "mxgemm_plan", "mxgemm_query_ex", "mxgemm_plan_ex",
            "mxgemm_release_workspaces")
 
 STATUS = {0: "MXGEMM_OK", -1: "MXGEMM_ERR_INVALID_ARG", -2: "MXGEMM_ERR_SHAPE",
           -3: "MXGEMM_ERR_ALIGN", -4: "MXGEMM_ERR_UNSUPPORTED_DEVICE", -5: "MXGEMM_ERR_HIP",
-          -6: "MXGEMM_ERR_WORKSPACE"}
+          -6: "MXGEMM_ERR_WORKSPACE", -7: "MXGEMM_ERR_SCRATCH"}
 
 
 class MxGemmError(RuntimeError):
@@ -48,6 +48,7 @@ SPLIT_BF16_ATOMIC = 1  # MXGEMM_SPLIT_BF16_ATOMIC
 # MXGEMM_FMT_*: A's element format
 FMT_FP4, FMT_FP8_E4M3, FMT_FP8_E5M2, FMT_FP6_E2M3, FMT_FP6_E3M2 = 0, 1, 2, 3, 4
 FORMAT_BITS = (4, 8, 8, 6, 6)
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MXGEMM_NOALLOC_SCRATCH_BYTES
 
 
 class Info(ctypes.Structure):
@@ -83,6 +84,8 @@ def lib():
         L.mxgemm_run.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, i32, i32, i32,
                                  ctypes.POINTER(Strides), i32, vp]
         L.mxgemm_run.restype = i32
+        L.mxgemm_run_noalloc.argtypes = L.mxgemm_run.argtypes
+        L.mxgemm_run_noalloc.restype = i32
         L.mxgemm_run_bf16a.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, i32, i32, i32, i64,
                                        ctypes.POINTER(Strides), i32, vp]
         L.mxgemm_run_bf16a.restype = i32
@@ -156,6 +159,18 @@ def mxgemm_run(D, C, A, B, scaleA, scaleB, alpha, beta, M, N, K, strides=None, s
                           _stream(stream))
     if check:
         _check(st, "mxgemm_run")
+    return st
+
+
+def mxgemm_run_noalloc(D, C, A, B, scaleA, scaleB, alpha, beta, M, N, K, strides=None, split_k=-1,
+                       stream=None, check=True):
+    """mxgemm_run with the library's buffers in its fixed device scratch (no allocation)."""
+    sp = ctypes.byref(strides) if strides is not None else None
+    st = lib().mxgemm_run_noalloc(_ptr(D), _ptr(C), _ptr(A), _ptr(B), _ptr(scaleA), _ptr(scaleB),
+                                  float(alpha), float(beta), int(M), int(N), int(K), sp, int(split_k),
+                                  _stream(stream))
+    if check:
+        _check(st, "mxgemm_run_noalloc")
     return st
 
 

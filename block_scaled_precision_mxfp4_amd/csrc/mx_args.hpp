@@ -128,6 +128,15 @@ void launch_f16(const F16Args &a, int64_t grid, hipStream_t s);
 // chunks add into it
 void launch_d_init(const GemmArgs &g, hipStream_t s);
 
+// Fixed device scratch of the allocation-free entry point (mx_scratch.hip):
+// kScratchBytes per device; the first kScratchCounterBytes hold split-K
+// arrival counters, the rest partial sums and FP6 A's FP8 copy.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr size_t kScratchCounterBytes = (size_t)64 << 10;
+// This device's scratch address (looked up once per device, with the device
+// current); never the array's host-side name.
+hipError_t scratch_address(void **ptr);
+
 // FP6 A (E2M3 or E3M2, rows of lda_b bytes) -> FP8 A (E4M3 or E5M2 respectively,
 // rows of K bytes) in `out`, exactly; K % 16 == 0, lda_b % 4 == 0
 void launch_fp6_to_fp8(int a_fmt, const uint8_t *A, int64_t lda_b, uint8_t *out, int M, int K, hipStream_t s);

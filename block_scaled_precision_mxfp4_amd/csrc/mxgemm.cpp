@@ -28,6 +28,7 @@ namespace {
 using mx::GemmArgs;
 
 constexpr int kMaxK = 1 << 24;
+static_assert(MXGEMM_NOALLOC_SCRATCH_BYTES == mx::kScratchBytes, "header and library agree on the scratch size");
 constexpr int kMaxDevices = 64;
 constexpr int kSplits[] = {1, 2, 4, 8, 16};
 
@@ -470,6 +471,7 @@ const char *mxgemm_status_string(mxgemm_status s)
     case MXGEMM_ERR_UNSUPPORTED_DEVICE: return "device is not gfx950";
     case MXGEMM_ERR_HIP: return "HIP runtime error";
     case MXGEMM_ERR_WORKSPACE: return "workspace too small";
+    case MXGEMM_ERR_SCRATCH: return "plan needs more than the fixed scratch of mxgemm_run_noalloc";
     default: return "unknown status";
     }
 }
@@ -590,7 +592,7 @@ namespace {
 mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, const void *scaleA,
                        const void *scaleB, float alpha, float beta, int M, int N, int K,
                        const mxgemm_strides *strides, int split_k, hipStream_t stream, const void *X,
-                       int64_t ldx)
+                       int64_t ldx, bool noalloc = false)
 {
     // ---- host-only validation (no HIP call before it passes)
     if (!D || !B || !scaleB || !valid_split(split_k))
@@ -709,6 +711,27 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     g.sb16 = !s.b_packed && aligned(scaleB, 16) && s.ldsb % 16 == 0 && KB % 16 == 0;
     g.group_m = 4;
 
+    // FP6 A on the 8-bit tiles is first copied to FP8 (M x K bytes)
+    const bool fp6_conv = p.family == 3 && (s.a_format == MXGEMM_FMT_FP6_E2M3 || s.a_format == MXGEMM_FMT_FP6_E3M2);
+    const size_t conv_bytes = fp6_conv ? (size_t)M * (size_t)K : 0;
+    // the allocation-free form: counters, partials and the FP6 copy come
+    // from the device's fixed scratch (counters first, then partials, then
+    // the copy); a plan that needs more is refused before any launch
+    uint8_t *scr = nullptr;
+    size_t scr_part = 0;
+    if (noalloc) {
+        const bool fp32_split = p.split > 1 && !atomic;
+        const size_t part = fp32_split && !s.workspace ? align_up(p.ws_bytes, 256) : 0;
+        if ((fp32_split && p.counter_bytes > mx::kScratchCounterBytes) ||
+            part + conv_bytes > mx::kScratchBytes - mx::kScratchCounterBytes)
+            return MXGEMM_ERR_SCRATCH;
+        void *base = nullptr;
+        if (mx::scratch_address(&base) != hipSuccess)
+            return MXGEMM_ERR_HIP;
+        scr = (uint8_t *)base;
+        scr_part = part;
+    }
+
     if (p.split > 1 && atomic) {
         // chunks add into D, set first to bf16(beta * C); no workspace
         if ((int64_t)M * (N / 2) / 256 >= 0x7FFFFFFF)
@@ -718,9 +741,17 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
         void *counters = nullptr, *partials = nullptr;
         if (s.workspace && s.workspace_bytes < p.ws_bytes)
             return MXGEMM_ERR_WORKSPACE;
-        st = get_split_buffers(stream, p.counter_bytes, s.workspace ? 0 : p.ws_bytes, &counters, &partials);
-        if (st != MXGEMM_OK)
-            return st;
+        if (noalloc) {
+            // the scratch keeps the last call's contents: this call's
+            // counters are cleared (by a kernel, ordered on `stream`)
+            counters = scr;
+            partials = scr + mx::kScratchCounterBytes;
+            mx::launch_zero_words((uint32_t *)counters, (p.counter_bytes + 3) / 4, stream);
+        } else {
+            st = get_split_buffers(stream, p.counter_bytes, s.workspace ? 0 : p.ws_bytes, &counters, &partials);
+            if (st != MXGEMM_OK)
+                return st;
+        }
         g.counters = (int *)counters;
         g.ws = (float *)(s.workspace ? s.workspace : partials);
     }
@@ -750,12 +781,16 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
         int n = 0;
         const mx::TileKernelA8 &k = mx::tile_kernels_a8(&n)[p.index];
         int fmt8 = s.a_format;
-        if (s.a_format == MXGEMM_FMT_FP6_E2M3 || s.a_format == MXGEMM_FMT_FP6_E3M2) {
+        if (fp6_conv) {
             // exact FP6 -> FP8 copy of A (E2M3 -> E4M3, E3M2 -> E5M2), same scales
             void *conv = nullptr;
-            st = get_conv_buffer(stream, (size_t)M * (size_t)K, &conv);
-            if (st != MXGEMM_OK)
-                return st;
+            if (noalloc) {
+                conv = scr + mx::kScratchCounterBytes + scr_part;
+            } else {
+                st = get_conv_buffer(stream, conv_bytes, &conv);
+                if (st != MXGEMM_OK)
+                    return st;
+            }
             mx::launch_fp6_to_fp8(s.a_format, (const uint8_t *)A, lda_bytes, (uint8_t *)conv, M, K, stream);
             g.A = (const uint8_t *)conv;
             g.lda_b = K;
@@ -808,6 +843,13 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B, c
                          const mxgemm_strides *strides, int split_k, hipStream_t stream)
 {
     return run_impl(D, C, A, B, scaleA, scaleB, alpha, beta, M, N, K, strides, split_k, stream, nullptr, 0);
+}
+
+mxgemm_status mxgemm_run_noalloc(void *D, const void *C, const void *A, const void *B, const void *scaleA,
+                                 const void *scaleB, float alpha, float beta, int M, int N, int K,
+                                 const mxgemm_strides *strides, int split_k, hipStream_t stream)
+{
+    return run_impl(D, C, A, B, scaleA, scaleB, alpha, beta, M, N, K, strides, split_k, stream, nullptr, 0, true);
 }
 
 mxgemm_status mxgemm_run_bf16a(void *D, const void *C, const void *X, const void *B, const void *scaleB,

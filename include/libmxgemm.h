@@ -54,6 +54,7 @@ typedef int mxgemm_status;
 #define MXGEMM_ERR_UNSUPPORTED_DEVICE -4  /* current device is not gfx950 */
 #define MXGEMM_ERR_HIP                -5  /* a HIP runtime call failed (launch, allocation) */
 #define MXGEMM_ERR_WORKSPACE          -6  /* caller workspace smaller than mxgemm_query's workspace_bytes */
+#define MXGEMM_ERR_SCRATCH            -7  /* mxgemm_run_noalloc: the plan needs more than its fixed scratch */
 
 /* Static string naming a status code (never NULL). */
 const char *mxgemm_status_string(mxgemm_status status);
@@ -183,6 +184,37 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B,
                          float alpha, float beta, int M, int N, int K,
                          const mxgemm_strides *strides, int split_k,
                          hipStream_t stream);
+
+/* ---- allocation-free GEMM ------------------------------------------------------ */
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * mxgemm_run with every library-owned buffer taken from one fixed device
+ * array per GPU of MXGEMM_NOALLOC_SCRATCH_BYTES (32 MiB), which the library
+ * holds from load until the process ends: the split-K arrival counters
+ * (first 64 KiB: 4 bytes per output tile of a split plan), the split-K fp32
+ * partials unless strides->workspace brings them, and the FP8 copy of an FP6
+ * A with M > 16 (M*K bytes).  Same arguments, plans, kernels and results as
+ * mxgemm_run, bit for bit.  Never calls hipMalloc or hipFree (the first call
+ * on a device looks up that device's array once).  A plan that needs more
+ * than the array holds returns MXGEMM_ERR_SCRATCH before any launch;
+ * mxgemm_query_ex gives the plan's workspace_bytes.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents; each call clears the counters it uses (with a kernel on
+ * `stream`) before its GEMM.  Calls that can overlap on one GPU (on
+ * different streams, or from host threads without ordering) race on the
+ * array and must not be issued; calls ordered on one stream are safe.
+ */
+#define MXGEMM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+mxgemm_status mxgemm_run_noalloc(void *D, const void *C, const void *A, const void *B,
+                                 const void *scaleA, const void *scaleB,
+                                 float alpha, float beta, int M, int N, int K,
+                                 const mxgemm_strides *strides, int split_k,
+                                 hipStream_t stream);
 
 /* ---- B pre-shuffle ----------------------------------------------------------- */
 

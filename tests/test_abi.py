@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = mx.mxgemm_status_string(code)
         assert s and s != "unknown status"
     assert mx.mxgemm_status_string(-99) == "unknown status"
