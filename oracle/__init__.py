@@ -66,7 +66,7 @@ def _load():
             lib.oracle_format_bits.restype = ctypes.c_int
             lib.oracle_elem_code.argtypes = [u8p, i64, ctypes.c_int, i64, i64]
             lib.oracle_elem_code.restype = ctypes.c_uint
-            lib.oracle_mxgemm.argtypes = [i64, ctypes.c_int, u8p, i64, u8p, i64, u8p, i64, u8p, i64,
+            lib.oracle_mxgemm.argtypes = [i64, ctypes.c_int, u8p, i64, u8p, i64, u8p, i64, u8p, i64, ctypes.c_int,
                                           u8p, i64, ctypes.c_int, f64, f64, u8p, i64, u8p, i64,
                                           u8p, u8p, u8p]
             lib.oracle_mxgemm.restype = ctypes.c_int
@@ -166,11 +166,13 @@ def elem_code(X: np.ndarray, ld_bytes: int, bits: int, r: int, k: int) -> int:
 
 
 def mxgemm(A, SA, B, SB, K, alpha=1.0, beta=0.0, C=None, *, lda=None, ldb=None,
-           ldsa=None, ldsb=None, ldc=None, rows=None, cols=None, threads=None, a_fmt=FMT_FP4):
+           ldsa=None, ldsb=None, ldc=None, rows=None, cols=None, threads=None, a_fmt=FMT_FP4,
+           b_layout=0):
     """Reference block of D for rows x cols.
 
     A: uint8 [M, lda * w / 8] for A's format (w = 4, 8 or 6 bits; lda counts
-    elements), SA: uint8 [M, ldsa], B: uint8 [N, ldb/2] (FP4),
+    elements), SA: uint8 [M, ldsa], B: uint8 [N, ldb/2] (FP4; with
+    b_layout=1 MN-major: [K, ldb/2], row k holding the N columns' codes),
     SB: uint8 [N, ldsb], C: uint16 (bf16 bits) or float32 [M, ldc], or None.
     Returns (ref fp64, mag fp64, dref uint16) of shape [len(rows), len(cols)].
     """
@@ -179,7 +181,7 @@ def mxgemm(A, SA, B, SB, K, alpha=1.0, beta=0.0, C=None, *, lda=None, ldb=None,
     B = np.ascontiguousarray(B, dtype=np.uint8)
     SA = np.ascontiguousarray(SA, dtype=np.uint8)
     SB = np.ascontiguousarray(SB, dtype=np.uint8)
-    M, N = A.shape[0], B.shape[0]
+    M, N = A.shape[0], (B.shape[0] if b_layout == 0 else SB.shape[0])
     lda = A.shape[1] * 8 // format_bits(a_fmt) if lda is None else lda
     ldb = B.shape[1] * 2 if ldb is None else ldb
     ldsa = SA.shape[1] if ldsa is None else ldsa
@@ -220,6 +222,7 @@ def mxgemm(A, SA, B, SB, K, alpha=1.0, beta=0.0, C=None, *, lda=None, ldb=None,
         m_ = np.zeros((nr, c1 - c0), dtype=np.float64)
         d_ = np.zeros((nr, c1 - c0), dtype=np.uint16)
         rc = lib.oracle_mxgemm(K, int(a_fmt), _ptr(A), lda, _ptr(SA), ldsa, _ptr(B), ldb, _ptr(SB), ldsb,
+                               int(b_layout),
                                _ptr(C) if beta != 0.0 else None, ldc, c_f32, float(alpha), float(beta),
                                _ptr(rows), nr, _ptr(cs), c1 - c0,
                                _ptr(r_), _ptr(m_), _ptr(d_))

@@ -210,11 +210,20 @@ uint16_t oracle_bf16_rne(double x)
  * float32 when c_f32 != 0 (the f32 bias of the asm_f4gemm README's
  * "C / bias" note; either way its value enters exactly, in fp64).
  * C is read only when beta != 0.  Any of mag/dref may be NULL.
+ *
+ * b_layout selects how B's codes are stored ("CDNA4 MFMA transpose load
+ * builtins", opening section: an operand may be kept MN-major, B in
+ * row-major [K][N] order, instead of K-major):
+ *   0  B is [N][ldb/2] bytes, row j holding its K codes (K-major);
+ *   1  B is [K][ldb/2] bytes, row k holding the codes of the N columns at
+ *      that k (MN-major), element j of the row in the low nibble of byte j/2
+ *      when j is even -- the same packing along the row as for K-major rows.
+ * SB is [N][ldsb] (one scale per column j and 32-block of k) either way.
  * Returns 0, or -1 when scratch memory cannot be allocated.
  */
 int oracle_mxgemm(int64_t K, int a_fmt,
                   const uint8_t *A, int64_t lda, const uint8_t *SA, int64_t ldsa,
-                  const uint8_t *B, int64_t ldb, const uint8_t *SB, int64_t ldsb,
+                  const uint8_t *B, int64_t ldb, const uint8_t *SB, int64_t ldsb, int b_layout,
                   const void *C, int64_t ldc, int c_f32, double alpha, double beta,
                   const int64_t *rows, int64_t nrows,
                   const int64_t *cols, int64_t ncols,
@@ -237,7 +246,10 @@ int oracle_mxgemm(int64_t K, int a_fmt,
                                        : oracle_mx_element_fmt(A, lda_bytes, a_fmt, SA, ldsa, rows[ri], k);
     for (int64_t cj = 0; cj < ncols; ++cj)
         for (int64_t k = 0; k < K; ++k)
-            b[cj * K + k] = oracle_mx_element(B, ldb, SB, ldsb, cols[cj], k);
+            b[cj * K + k] = b_layout == 0
+                                ? oracle_mx_element(B, ldb, SB, ldsb, cols[cj], k)
+                                : oracle_e2m1(oracle_fp4_code(B, ldb, k, cols[cj])) *
+                                      oracle_e8m0(SB[cols[cj] * ldsb + k / 32]);
 
     for (int64_t ri = 0; ri < nrows; ++ri) {
         const double *ar = a + ri * K;
