@@ -40,7 +40,7 @@ class Strides(ctypes.Structure):
                 ("b_packed", ctypes.c_int32), ("sa_packed", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("c_f32", ctypes.c_int32), ("split_mode", ctypes.c_int32),
-                ("a_format", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("a_format", ctypes.c_int32), ("b_layout", ctypes.c_int32)]
 
 
 SPLIT_FP32 = 0         # MXGEMM_SPLIT_FP32
@@ -48,6 +48,7 @@ SPLIT_BF16_ATOMIC = 1  # MXGEMM_SPLIT_BF16_ATOMIC
 # MXGEMM_FMT_*: A's element format
 FMT_FP4, FMT_FP8_E4M3, FMT_FP8_E5M2, FMT_FP6_E2M3, FMT_FP6_E3M2 = 0, 1, 2, 3, 4
 FORMAT_BITS = (4, 8, 8, 6, 6)
+B_NK, B_KN = 0, 1  # MXGEMM_B_NK, MXGEMM_B_KN
 NOALLOC_SCRATCH_BYTES = 32 << 20  # MXGEMM_NOALLOC_SCRATCH_BYTES
 
 
@@ -141,9 +142,9 @@ def _check(status, where):
 
 
 def make_strides(*, ldd, ldc, lda, ldb, ldsa, ldsb, b_packed=0, sa_packed=0, workspace=None,
-                 workspace_bytes=0, c_f32=0, split_mode=SPLIT_FP32, a_format=FMT_FP4):
+                 workspace_bytes=0, c_f32=0, split_mode=SPLIT_FP32, a_format=FMT_FP4, b_layout=B_NK):
     return Strides(ldd, ldc, lda, ldb, ldsa, ldsb, b_packed, sa_packed, _ptr(workspace), workspace_bytes,
-                   c_f32, split_mode, a_format, 0)
+                   c_f32, split_mode, a_format, b_layout)
 
 
 def mxgemm_status_string(status: int) -> str:

@@ -51,6 +51,9 @@ struct TileKernel {
     // and B scales; packed_sa: packed B, B scales and A scales
     LaunchFn plain, packed, packed_sa;
     LaunchFn deep_plain, deep_packed, deep_packed_sa;
+    // two-stage kernel with MN-major B codes ([K][N], N contiguous): B
+    // scales row-major; B scales packed; B and A scales packed
+    LaunchFn kn, kn_packed_sb, kn_packed_sa;
     bool prefer_deep;                  // the ring kernel is the faster one for this tile
     const char *name;
 };

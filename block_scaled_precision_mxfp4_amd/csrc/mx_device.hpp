@@ -28,6 +28,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -85,6 +86,15 @@ __device__ __forceinline__ uint32_t load1(__amdgpu_buffer_rsrc_t r, uint32_t off
 __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, lds_void *lds, uint32_t off)
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, 0, 0, 0);
+}
+
+// Transposed 4-bit LDS read ("CDNA4 MFMA transpose load builtins",
+// ds_read_tr4_b64): within each group of 16 lanes, lane q names 8 bytes (16
+// codes, element j in nibble j) and lane j receives code j of every lane q
+// of its group, in nibble q.  p must point into LDS, 8-byte aligned.
+__device__ __forceinline__ v2i lds_tr4(const uint8_t *p)
+{
+    return __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) v2i *)(p));
 }
 
 // Cache policy of operands that are read once per call (the B stream of the

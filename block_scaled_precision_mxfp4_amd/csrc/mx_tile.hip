@@ -128,10 +128,34 @@ __device__ __forceinline__ void store_whole_tile_staged(uint16_t *D, int64_t ldd
 // tile's first stage.  Needs split 1, beta == 0 with the staged epilogue, an
 // even stage count and M, N multiples of the tile, so that every wave issues
 // exactly STORES stores after those loads (the host checks).
-template <int BM, int BN, int WM, int WN, bool BPACK, bool SVEC, bool SAPACK, int AFMT = 0, bool PERSIST = false>
+//
+// BLAY: B's storage.  0: codes [N][K] and scales [N][KB], row-major; 1: both
+// as mxgemm_pack_b writes them; 2: codes MN-major [K][N] (row k holds the N
+// columns at that k), scales row-major; 3: MN-major codes, scales shuffled
+// as mxgemm_pack_b shuffles them.  An MN-major stage is 256 K-rows of BN/2
+// bytes in LDS; a B fragment (16 columns x 128 K) is two transposed reads
+// ("CDNA4 MFMA transpose load builtins", ds_read_tr4_b64: each 16-lane group
+// names 16 K-rows of 8 bytes, i.e. 16 columns, and every lane receives its
+// own column's 16 K values as 8 bytes, row q in nibble q; the table of that
+// page's "Hardware constraints" splits the K positions over the two calls),
+// K-rows 32g .. 32g+15 and 32g+16 .. 32g+31 of the step for lane group g,
+// which is the K-block g the instruction reads from lane group g.
+template <int BM, int BN, int WM, int WN, int BLAY, bool SVEC, bool SAPACK, int AFMT = 0, bool PERSIST = false>
 __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
 {
     static_assert(AFMT == 0 || ((AFMT == 1 || AFMT == 2) && !SAPACK), "8-bit A with row-major A scales");
+    static_assert(BLAY >= 0 && BLAY <= 3 && (AFMT == 0 || BLAY <= 1), "B layouts");
+    constexpr bool BPACK = BLAY == 1;                 // packed codes
+    constexpr bool BKN = BLAY >= 2;                   // MN-major codes
+    constexpr bool SBPACK = BLAY == 1 || BLAY == 3;   // packed B scales
+    static_assert(!SAPACK || SBPACK, "packed A scales come with packed B scales");
+    // MN-major stage geometry: bytes per K-row, 16-byte chunks per K-row,
+    // K-rows per direct-to-LDS instruction and per 256-byte bank window.
+    // Chunk c of K-row r sits at slot c ^ ((r / KN_RPW) % KN_CPR): the 16
+    // K-rows one lane group names in a transposed read then fall on 16
+    // different 8-byte bank positions.
+    constexpr int KN_ROWB = BN / 2, KN_CPR = BN / 32;
+    constexpr int KN_RPI = 1024 / KN_ROWB, KN_RPW = 256 / KN_ROWB;
     constexpr int AREG = AFMT == 0 ? 1 : 2;  // FP4-shaped A tiles per stage
     constexpr int NW = WM * WN;                // waves per workgroup
     constexpr int NT = 64 * NW;                // threads per workgroup
@@ -171,6 +195,14 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     // returns zero without traffic.
     const int tiles = g.tiles_m * g.tiles_n;
     int z, t, m0, n0, kb_begin, kb_end, nst;
+    // MN-major B: this lane's byte offset inside a stage's K-rows for every
+    // load instruction of the wave (instruction c adds c * KN_RPI K-rows),
+    // or an offset past any range (2^31) for chunks beyond column N.  Lane
+    // l fills slot l % KN_CPR of K-row c * KN_RPI + l / KN_CPR, i.e. chunk
+    // slot ^ ((4c + (l / KN_CPR) / KN_RPW) % KN_CPR), and 4c % KN_CPR depends
+    // on c only through c % 2 = wave % 2 (c = i * NW + wave, NW even).
+    uint32_t kn_lane = 0;
+    static_assert(NW % 2 == 0 && KN_RPI == 4 * KN_RPW, "MN-major load geometry");
     const uint8_t *a_base, *b_base;
     uint32_t a_bytes, b_bytes;
     __amdgpu_buffer_rsrc_t rsa, rsb;
@@ -220,12 +252,22 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
             const int n16 = n0 / 16, grp16 = min(BN / 16, (g.N + 15) / 16 - n16);
             b_base = g.B + (int64_t)n16 * g.ks_total * 1024;
             b_bytes = (uint32_t)((int64_t)grp16 * g.ks_total * 1024);
-            const int n32 = n0 / 32, grp32 = min(BN / 32, (g.N + 31) / 32 - n32);
-            rsb = make_rsrc(g.SB + (int64_t)n32 * g.sn8 * 256, (uint32_t)((int64_t)grp32 * g.sn8 * 256));
+        } else if constexpr (BKN) {
+            b_base = g.B;  // each stage rebases at its first K-row
+            b_bytes = 0;
+            const int chunk = (lane % KN_CPR) ^ ((4 * wave + (lane / KN_CPR) / KN_RPW) % KN_CPR);
+            kn_lane = n0 + 32 * chunk < g.N ? (uint32_t)((lane / KN_CPR) * g.ldb_b + n0 / 2 + 16 * chunk)
+                                            : 0x80000000u;
         } else {
             const int rows_b = min(BN, g.N - n0);
             b_base = g.B + (int64_t)n0 * g.ldb_b;
             b_bytes = (uint32_t)((int64_t)rows_b * g.ldb_b);
+        }
+        if constexpr (SBPACK) {
+            const int n32 = n0 / 32, grp32 = min(BN / 32, (g.N + 31) / 32 - n32);
+            rsb = make_rsrc(g.SB + (int64_t)n32 * g.sn8 * 256, (uint32_t)((int64_t)grp32 * g.sn8 * 256));
+        } else {
+            const int rows_b = min(BN, g.N - n0);
             rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)((int64_t)rows_b * g.ldsb));
         }
     };
@@ -245,7 +287,11 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         const uint32_t a_k = (uint32_t)kb_s * 16 * AREG;
         const uint32_t b_k = BPACK ? (uint32_t)(kb_s >> 2) * 1024 : (uint32_t)kb_s * 16;
         const auto ra = make_rsrc(a_base + a_k, on ? a_bytes - a_k : 0u);
-        const auto rb = make_rsrc(b_base + b_k, on ? b_bytes - b_k : 0u);
+        // MN-major: the stage's K-rows kb_s*32 .. up to the chunk end; rows
+        // past it are outside the range and load zeros
+        const auto rb = BKN ? make_rsrc_u(b_base + (int64_t)kb_s * 32 * g.ldb_b,
+                                          on ? (uint32_t)(min(256, (kb_end - kb_s) * 32) * g.ldb_b) : 0u)
+                            : make_rsrc(b_base + b_k, on ? b_bytes - b_k : 0u);
         // chunk (K-block of the stage) a row-major lane loads in half h
         const int kc0 = (lane & 7) ^ (lane >> 3), kc1 = kc0 ^ 1;
 #pragma unroll
@@ -270,6 +316,10 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
                 // packed B: 1 KiB instruction operands, contiguous
                 const int rg = c >> 1, ks = c & 1;
                 off = b_lane + (uint32_t)rg * b_rg_stride + (uint32_t)(ks * 1024);
+            } else if constexpr (BKN) {
+                // MN-major: instruction c fills K-rows c * KN_RPI .. (a range
+                // below 2^31 - 2^31 + this, so past-N lanes stay out of range)
+                off = kn_lane + (uint32_t)(c * KN_RPI) * (uint32_t)g.ldb_b;
             } else {
                 const int rows8 = c * 8, h = c & 1;
                 off = b_lane + (uint32_t)(rows8 * g.ldb_b) + (h ? (uint32_t)((kc1 - kc0) * 16) : 0u);
@@ -284,7 +334,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     // threads own B row pairs (row-major B scales only)
     const bool own_a = !SAPACK && tid < BM / 2;
     const int ua = own_a ? tid : 0;
-    const bool own_b = !BPACK && tid >= BM / 2 && tid < BM / 2 + BN / 2;
+    const bool own_b = !SBPACK && tid >= BM / 2 && tid < BM / 2 + BN / 2;
     const int ub = own_b ? tid - BM / 2 : 0;
     // LDS word index (per d5 add 16*d5) each thread commits its A / B words to
     const int wa = own_a ? (ua >> 4) * 64 + (ua & 15) : SA_W + SB_W + lane;
@@ -308,7 +358,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         } else {
             sa_rows = load_scale_rows<SVEC>(rsa, g.ldsa, (ua >> 4) * 32 + (ua & 15), kb_s, kb_end, on && own_a);
         }
-        if constexpr (BPACK) {
+        if constexpr (SBPACK) {
 #pragma unroll
             for (int i = 0; i < SBP_PER_THREAD; ++i) {
                 const int q = i * NT + tid;
@@ -335,7 +385,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
             for (int d5 = 0; d5 < 4; ++d5)
                 dsc[wa + (own_a ? 16 * d5 : 0)] = scale_word(sa_rows, d5);
         }
-        if constexpr (BPACK) {
+        if constexpr (SBPACK) {
 #pragma unroll
             for (int i = 0; i < SBP_PER_THREAD; ++i) {
                 const int q = i * NT + tid;
@@ -354,6 +404,12 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     const int fr = lane & 15;
     const uint32_t rl0 = (uint32_t)(((fr >> 3) * 64 + (fr & 7) * 8 + ((lane >> 4) ^ (fr & 7) ^ (fr >> 3))) * 16);
     const uint32_t rl1 = rl0 ^ 64u;
+    // MN-major fragment reads: lane (group g, row i) names K-row 32g + i of
+    // the step (call 1; call 2 is 16 K-rows further), whose chunks are
+    // swizzled by h = (i / KN_RPW) % KN_CPR (the same for both calls and
+    // every step: 16, 32 and 128 are multiples of KN_RPW * KN_CPR)
+    const uint32_t kn_row = (uint32_t)((lane >> 4) * 32 + fr) * KN_ROWB;
+    const int kn_h = (fr / KN_RPW) % KN_CPR;
 
     // ---- main loop
     // Accumulators get their first value from the first stage's matrix
@@ -418,9 +474,18 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
                     if (ks * FN + fn == LOADS_AT)
                         prefetch();
                 }
-                const uint32_t bo = BPACK ? ((wave_n * FN + fn) * 2 + ks) * 1024 + lane * 16
-                                          : (wave_n * FN + fn) * 2048 + rl;
-                const v4i bf = *reinterpret_cast<const v4i *>(sb_tile + bo);
+                v4i bf;
+                if constexpr (BKN) {
+                    // 8-byte unit u of the K-row: columns 16u .. 16u+15 of the tile
+                    const int u = wave_n * FN + fn;
+                    const uint8_t *t = sb_tile + ks * 128 * KN_ROWB + kn_row + (((u >> 1) ^ kn_h) * 16) + (u & 1) * 8;
+                    const v2i lo = lds_tr4(t), hi = lds_tr4(t + 16 * KN_ROWB);
+                    bf = v4i{lo[0], lo[1], hi[0], hi[1]};
+                } else {
+                    const uint32_t bo = BPACK ? ((wave_n * FN + fn) * 2 + ks) * 1024 + lane * 16
+                                              : (wave_n * FN + fn) * 2048 + rl;
+                    bf = *reinterpret_cast<const v4i *>(sb_tile + bo);
+                }
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm) {
                     if constexpr (AFMT == 0)
@@ -626,36 +691,39 @@ void launch_d_init(const GemmArgs &g, hipStream_t s)
     hipLaunchKernelGGL(mx_d_init_kernel, dim3((unsigned)((pairs + 255) / 256)), dim3(256), 0, s, g);
 }
 
-template <int BM, int BN, int WM, int WN, bool BPACK, bool SAPACK>
+template <int BM, int BN, int WM, int WN, int BLAY, bool SAPACK>
 static void launch_tile(const GemmArgs &g, int grid, hipStream_t s)
 {
+    constexpr bool SBPACK = BLAY == 1 || BLAY == 3;
     // SVEC: whole 8-block stages and 8-byte scale-row loads (packed scales
     // need only the former)
     const bool sa_ok = SAPACK ? g.KB % 8 == 0 : g.sa_fast != 0;
+    const bool sb_ok = SBPACK ? g.KB % 8 == 0 : g.sb_fast != 0;
     // persistent form: 256 x 256 with packed B and A scales (its other
     // layouts spill in the tile loop; the 256 x 128 tile and the 8-bit
     // 128 x 256 tile measured no faster persistent)
-    if constexpr (BM == 256 && BN == 256 && BPACK && SAPACK) {
-        if (g.persist_grid > 0 && sa_ok && (BPACK ? g.KB % 8 == 0 : g.sb_fast != 0)) {
-            hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, true, SAPACK, 0, true>), dim3(g.persist_grid),
+    if constexpr (BM == 256 && BN == 256 && BLAY == 1 && SAPACK) {
+        if (g.persist_grid > 0 && sa_ok && sb_ok) {
+            hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BLAY, true, SAPACK, 0, true>), dim3(g.persist_grid),
                                dim3(64 * WM * WN), 0, s, g);
             return;
         }
     }
-    if (sa_ok && (BPACK ? g.KB % 8 == 0 : g.sb_fast != 0))
-        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, true, SAPACK>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
+    if (sa_ok && sb_ok)
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BLAY, true, SAPACK>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
     else
-        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, false, SAPACK>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BLAY, false, SAPACK>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
 }
 
 // 8-bit A (FP8 E4M3 / BF8 E5M2), row-major A scales
 template <int BM, int BN, int WM, int WN, bool BPACK, int AFMT>
 static void launch_tile_a8(const GemmArgs &g, int grid, hipStream_t s)
 {
+    constexpr int BLAY = BPACK ? 1 : 0;
     if (g.sa_fast && (BPACK ? g.KB % 8 == 0 : g.sb_fast != 0))
-        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, true, false, AFMT>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BLAY, true, false, AFMT>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
     else
-        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BPACK, false, false, AFMT>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BLAY, false, false, AFMT>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
 }
 
 #define MX_TILE_A8(BM, BN, WM, WN, OCC)                                                                    \
@@ -676,10 +744,11 @@ const TileKernelA8 *tile_kernels_a8(int *count)
 #undef MX_TILE_A8
 
 #define MX_TILE(BM, BN, WM, WN, OCC, DEEP)                                                              \
-    {BM, BN, OCC, launch_tile<BM, BN, WM, WN, false, false>, launch_tile<BM, BN, WM, WN, true, false>,   \
-     launch_tile<BM, BN, WM, WN, true, true>, launch_tile_deep<BM, BN, WM, WN, false, false>,           \
-     launch_tile_deep<BM, BN, WM, WN, true, false>, launch_tile_deep<BM, BN, WM, WN, true, true>, DEEP, \
-     "tile_" #BM "x" #BN}
+    {BM, BN, OCC, launch_tile<BM, BN, WM, WN, 0, false>, launch_tile<BM, BN, WM, WN, 1, false>,         \
+     launch_tile<BM, BN, WM, WN, 1, true>, launch_tile_deep<BM, BN, WM, WN, false, false>,              \
+     launch_tile_deep<BM, BN, WM, WN, true, false>, launch_tile_deep<BM, BN, WM, WN, true, true>,       \
+     launch_tile<BM, BN, WM, WN, 2, false>, launch_tile<BM, BN, WM, WN, 3, false>,                      \
+     launch_tile<BM, BN, WM, WN, 3, true>, DEEP, "tile_" #BM "x" #BN}
 
 const TileKernel *tile_kernels(int *count)
 {

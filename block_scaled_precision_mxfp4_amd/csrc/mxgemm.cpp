@@ -290,8 +290,10 @@ Plan plan_a8(int M, int N, int K, int split_req, int num_cu)
 // the 8-bit tiles; any other wider A on the skinny kernel per 16 rows.
 Plan plan_run(int M, int N, int K, const mxgemm_strides &s, int split_k, int num_cu)
 {
+    // an MN-major B is read through the tiled kernel's transposed LDS loads
     if (s.a_format == MXGEMM_FMT_FP4)
-        return plan_for(M, N, K, s.b_packed, split_k, num_cu, s.split_mode == MXGEMM_SPLIT_BF16_ATOMIC);
+        return plan_for(M, N, K, s.b_packed, split_k, num_cu,
+                        s.split_mode == MXGEMM_SPLIT_BF16_ATOMIC || s.b_layout == MXGEMM_B_KN);
     if ((s.a_format == MXGEMM_FMT_FP8_E4M3 || s.a_format == MXGEMM_FMT_FP8_E5M2) && M > 16)
         return plan_a8(M, N, K, split_k, num_cu);
     // FP6 with M > 16: A converted exactly to FP8 (rows of K bytes), then the
@@ -482,7 +484,8 @@ static void fill_info(const Plan &p, int M, int N, int K, int num_cu, const mxge
     // what mxgemm_run launches for beta == 0 and 16-byte aligned pointers
     const int KB = K / 32;
     const bool svec = KB % 8 == 0 && (s.sa_packed || s.ldsa % 8 == 0) && (s.b_packed || s.ldsb % 8 == 0);
-    out->persist_grid = persist_grid(p, M, N, K, num_cu, s.ldd % 8 == 0, svec, s.sa_packed != 0);
+    out->persist_grid = s.b_layout == MXGEMM_B_KN ? 0 : persist_grid(p, M, N, K, num_cu, s.ldd % 8 == 0, svec,
+                                                                     s.sa_packed != 0);
     out->kernel = p.family;
     out->tile_m = p.bm;
     out->tile_n = p.bn;
@@ -517,7 +520,8 @@ static bool valid_options(const mxgemm_strides &s)
     return (s.b_packed == 0 || s.b_packed == 1) && (s.sa_packed == 0 || s.sa_packed == 1) &&
            (!s.sa_packed || s.b_packed) && (s.c_f32 == 0 || s.c_f32 == 1) &&
            (s.split_mode == MXGEMM_SPLIT_FP32 || s.split_mode == MXGEMM_SPLIT_BF16_ATOMIC) &&
-           s.a_format >= MXGEMM_FMT_FP4 && s.a_format <= MXGEMM_FMT_FP6_E3M2 && s.reserved == 0 &&
+           s.a_format >= MXGEMM_FMT_FP4 && s.a_format <= MXGEMM_FMT_FP6_E3M2 &&
+           (s.b_layout == MXGEMM_B_NK || (s.b_layout == MXGEMM_B_KN && s.a_format == MXGEMM_FMT_FP4)) &&
            (s.a_format == MXGEMM_FMT_FP4 || (!s.sa_packed && s.split_mode == MXGEMM_SPLIT_FP32));
 }
 
@@ -610,7 +614,9 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
         if ((s.b_packed != 0 && s.b_packed != 1) || (s.sa_packed != 0 && s.sa_packed != 1) ||
             (s.sa_packed && !s.b_packed) || (s.c_f32 != 0 && s.c_f32 != 1) ||
             (s.split_mode != MXGEMM_SPLIT_FP32 && s.split_mode != MXGEMM_SPLIT_BF16_ATOMIC) ||
-            s.a_format < MXGEMM_FMT_FP4 || s.a_format > MXGEMM_FMT_FP6_E3M2 || s.reserved != 0)
+            s.a_format < MXGEMM_FMT_FP4 || s.a_format > MXGEMM_FMT_FP6_E3M2 ||
+            (s.b_layout != MXGEMM_B_NK && s.b_layout != MXGEMM_B_KN) ||
+            (s.b_layout == MXGEMM_B_KN && s.a_format != MXGEMM_FMT_FP4))
             return MXGEMM_ERR_INVALID_ARG;
         if (s.a_format != MXGEMM_FMT_FP4 && (s.sa_packed || s.split_mode != MXGEMM_SPLIT_FP32))
             return MXGEMM_ERR_INVALID_ARG;
@@ -623,7 +629,8 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     const int KB = K / 32;
     if (X) {
         // the bf16 row replaces A and its scales
-        if (s.a_format != MXGEMM_FMT_FP4 || s.sa_packed || s.split_mode != MXGEMM_SPLIT_FP32)
+        if (s.a_format != MXGEMM_FMT_FP4 || s.sa_packed || s.split_mode != MXGEMM_SPLIT_FP32 ||
+            s.b_layout != MXGEMM_B_NK)
             return MXGEMM_ERR_INVALID_ARG;
         if (ldx < K)
             return MXGEMM_ERR_SHAPE;
@@ -635,17 +642,21 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     }
     if (s.ldd < N || s.lda < K || (!s.sa_packed && s.ldsa < KB) || (beta != 0.0f && s.ldc < N))
         return MXGEMM_ERR_SHAPE;
-    if (!s.b_packed && (s.ldb < K || s.ldsb < KB))
+    // B's codes as rows: [N][ldb/2] (K-major) or [K][ldb/2] (MN-major, whose
+    // scales may still be packed)
+    const bool b_kn = s.b_layout == MXGEMM_B_KN;
+    const bool b_rows = !s.b_packed || b_kn;
+    if ((b_kn ? s.ldb < N : (!s.b_packed && s.ldb < K)) || (!s.b_packed && s.ldsb < KB))
         return MXGEMM_ERR_SHAPE;
     // A's byte pitch: lda elements of its format (FP4: 4 bits, FP8: 8, FP6: 6)
     static const int kBits[5] = {4, 8, 8, 6, 6};
     const int a_bits = kBits[s.a_format];
-    if ((s.lda * a_bits) % 8 || (!s.b_packed && s.ldb % 2))
+    if ((s.lda * a_bits) % 8 || (b_rows && s.ldb % 2))
         return MXGEMM_ERR_ALIGN;
     const int64_t lda_bytes = s.lda * a_bits / 8;
     // (an FP6 row of K elements is 24 * K/32 bytes: its loads need 8-byte rows)
     if (!aligned(A, 16) || !aligned(B, 16) || lda_bytes % (a_bits == 6 ? 8 : 16) ||
-        (!s.b_packed && (s.ldb / 2) % 16))
+        (b_rows && (s.ldb / 2) % 16))
         return MXGEMM_ERR_ALIGN;
     if ((s.b_packed && !aligned(scaleB, 4)) || (!X && s.sa_packed && !aligned(scaleA, 4)))
         return MXGEMM_ERR_ALIGN;
@@ -657,9 +668,9 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     // byte offsets and buffer ranges inside a 256-row tile must stay below
     // 2^31: A and B rows, scale rows, and a 256-row slice of packed B
     const int64_t k31 = (int64_t)1 << 31;
-    if ((int64_t)256 * lda_bytes >= k31 || (!s.b_packed && (int64_t)256 * (s.ldb / 2) >= k31) ||
+    if ((int64_t)256 * lda_bytes >= k31 || (b_rows && (int64_t)256 * (s.ldb / 2) >= k31) ||
         (!X && !s.sa_packed && (int64_t)256 * s.ldsa >= k31) || (!s.b_packed && (int64_t)256 * s.ldsb >= k31) ||
-        (s.b_packed && (int64_t)16 * cdiv(KB, 4) * 1024 >= k31))
+        (s.b_packed && !b_kn && (int64_t)16 * cdiv(KB, 4) * 1024 >= k31))
         return MXGEMM_ERR_SHAPE;
 
     // ---- device and plan
@@ -804,19 +815,22 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
         // 128-K steps; otherwise the two-stage kernel handles any layout
         const bool deep_ok = KB % 4 == 0 && (s.sa_packed || (aligned(scaleA, 4) && s.ldsa % 4 == 0)) &&
                              (s.b_packed || (aligned(scaleB, 4) && s.ldsb % 4 == 0));
-        bool deep = deep_ok && k.prefer_deep && !g.split_atomic;  // the two-stage kernel implements the atomic mode
+        bool deep = deep_ok && k.prefer_deep && !g.split_atomic && !b_kn;  // the two-stage kernel implements
+                                                                           // the atomic mode and MN-major B
         if (const char *e = std::getenv("MXGEMM_TILE_PIPELINE")) {  // "deep" or "two-stage"
             if (std::strcmp(e, "two-stage") == 0)
                 deep = false;
             else if (std::strcmp(e, "deep") == 0)
-                deep = deep_ok && !g.split_atomic;
+                deep = deep_ok && !g.split_atomic && !b_kn;
         }
-        if (!deep) {
+        if (!deep && !b_kn) {
             const bool svec = (s.sa_packed ? KB % 8 == 0 : g.sa_fast != 0) &&
                               (s.b_packed ? KB % 8 == 0 : g.sb_fast != 0);
             g.persist_grid = (int)persist_grid(p, M, N, K, d->num_cu, g.d_stage != 0, svec, s.sa_packed != 0);
         }
-        if (deep)
+        if (b_kn)
+            (s.sa_packed ? k.kn_packed_sa : s.b_packed ? k.kn_packed_sb : k.kn)(g, (int)p.grid, stream);
+        else if (deep)
             (s.sa_packed ? k.deep_packed_sa : s.b_packed ? k.deep_packed : k.deep_plain)(g, (int)p.grid, stream);
         else
             (s.sa_packed ? k.packed_sa : s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
@@ -858,7 +872,9 @@ mxgemm_status mxgemm_run_bf16a(void *D, const void *C, const void *X, const void
 {
     if (!X)
         return MXGEMM_ERR_INVALID_ARG;
-    if (M == 1)
+    // the fused decode kernel streams a K-major B; an MN-major B goes through
+    // the tiled kernel like M > 1
+    if (M == 1 && !(strides && strides->b_layout == MXGEMM_B_KN))
         return run_impl(D, C, nullptr, B, nullptr, scaleB, alpha, beta, M, N, K, strides, split_k, stream, X, ldx);
     // M > 1: quantize into a per-stream buffer, then the ordinary call
     mxgemm_status st = check_shape(M, N, K);

@@ -111,6 +111,19 @@ def wide_codes(seed: int, rows: int, K: int, fmt: int) -> np.ndarray:
     return finite[idx.astype(np.int64)].reshape(rows, K)
 
 
+def to_mn_major(B: np.ndarray, N: int, K: int, ldb: int, pad: int = 0) -> np.ndarray:
+    """Re-store a K-major packed fp4x2 B [N, K/2] as MN-major [K, ldb/2]
+    bytes: row k holds the codes of columns 0..N-1 at that k (element n in
+    the low nibble of byte n/2 when n is even), columns N..ldb-1 hold the
+    nibble `pad`.  A pure data movement of the codes."""
+    codes = np.empty((N, K), dtype=np.uint8)
+    codes[:, 0::2] = B[:, : K // 2] & 0x0F
+    codes[:, 1::2] = B[:, : K // 2] >> 4
+    kn = np.full((K, ldb), pad & 0xF, dtype=np.uint8)
+    kn[:, :N] = codes.T
+    return (kn[:, 0::2] | (kn[:, 1::2] << 4)).astype(np.uint8)
+
+
 def e8m0_scales(seed: int, rows: int, K: int, lo: int, hi: int) -> np.ndarray:
     """E8M0 bytes [rows, K/32], exponents uniform over lo..hi inclusive."""
     n = rows * (K // 32)

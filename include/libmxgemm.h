@@ -116,9 +116,29 @@ const char *mxgemm_status_string(mxgemm_status status);
  *              (the skinny kernels are never chosen), needs D 4-byte
  *              aligned, ldd and N even (else MXGEMM_ERR_ALIGN), and D must
  *              not alias C.  With split 1 it is the ordinary path.
+ *   b_layout   MXGEMM_B_NK: B as above ([N][ldb/2] rows, or mxgemm_pack_b's
+ *              layout with b_packed = 1).  MXGEMM_B_KN: B's codes are
+ *              stored MN-major, [K][ldb/2] bytes: row k holds the codes of
+ *              the N columns at that k, element n in the low nibble of byte
+ *              n/2 when n is even (a weight kept as W[K][N]).  ldb then
+ *              counts fp4 elements between K-rows: ldb >= N, even, ldb/2 a
+ *              multiple of 16 bytes.  scaleB stays one byte per column and
+ *              32-block of k: [N][ldsb] with b_packed = 0, or
+ *              mxgemm_pack_scales' shuffle of it over the N rows with
+ *              b_packed = 1 (the codes are never pre-shuffled in this
+ *              layout).  The tiled kernel reads such a B from LDS with the
+ *              4-bit transposed loads of "CDNA4 MFMA transpose load
+ *              builtins" (ds_read_tr4_b64, two per 16 x 128 operand, K
+ *              split as that page's "Hardware constraints" table gives),
+ *              for every M.  Needs a_format = MXGEMM_FMT_FP4 (else
+ *              MXGEMM_ERR_INVALID_ARG); mxgemm_run_bf16a then quantizes
+ *              first also at M = 1.
  */
 #define MXGEMM_SPLIT_FP32        0
 #define MXGEMM_SPLIT_BF16_ATOMIC 1
+
+#define MXGEMM_B_NK 0  /* B [N][ldb/2]: row n holds its K codes (K-major) */
+#define MXGEMM_B_KN 1  /* B [K][ldb/2]: row k holds the N columns' codes (MN-major) */
 
 #define MXGEMM_FMT_FP4      0  /* E2M1, 4 bits */
 #define MXGEMM_FMT_FP8_E4M3 1  /* 8 bits */
@@ -130,7 +150,8 @@ typedef struct mxgemm_strides {
     int64_t ldd;      /* bf16 elements between rows of D, >= N */
     int64_t ldc;      /* elements between rows of C, >= N (ignored if beta == 0) */
     int64_t lda;      /* elements between rows of A (fp4 unless a_format says otherwise), >= K */
-    int64_t ldb;      /* fp4 elements between rows of B, >= K, even (ignored if b_packed) */
+    int64_t ldb;      /* fp4 elements between rows of B, >= K (>= N for MXGEMM_B_KN), even
+                         (ignored if b_packed with MXGEMM_B_NK) */
     int64_t ldsa;     /* bytes between rows of scaleA, >= K/32 */
     int64_t ldsb;     /* bytes between rows of scaleB, >= K/32 (ignored if b_packed) */
     int32_t b_packed; /* 0: B, scaleB row-major as above; 1: outputs of mxgemm_pack_b */
@@ -141,7 +162,7 @@ typedef struct mxgemm_strides {
     int32_t c_f32;      /* 0: C is bf16; 1: C is float32 */
     int32_t split_mode; /* MXGEMM_SPLIT_FP32 or MXGEMM_SPLIT_BF16_ATOMIC */
     int32_t a_format;   /* MXGEMM_FMT_* */
-    int32_t reserved;   /* 0 */
+    int32_t b_layout;   /* MXGEMM_B_NK (B's rows hold K) or MXGEMM_B_KN (B's rows hold N) */
 } mxgemm_strides;
 
 /* ---- the GEMM ------------------------------------------------------------- */
@@ -295,10 +316,11 @@ mxgemm_status mxgemm_quantize(void *A, void *scaleA, const void *X, int M, int K
  * and split_k as for mxgemm_run; strides->lda / ldsa are ignored, and
  * a_format, sa_packed and split_mode must be 0 (else
  * MXGEMM_ERR_INVALID_ARG).
- *   M == 1 (decode): one launch.  The skinny kernel loads the bf16 row and
- *     quantizes each 32-block in registers with the quantizer's rule, so D
- *     is bit for bit what mxgemm_quantize followed by mxgemm_run gives.
- *   M > 1: mxgemm_quantize into a library-owned buffer of
+ *   M == 1 (decode), K-major B: one launch.  The skinny kernel loads the
+ *     bf16 row and quantizes each 32-block in registers with the quantizer's
+ *     rule, so D is bit for bit what mxgemm_quantize followed by mxgemm_run
+ *     gives.
+ *   M > 1, or an MN-major B (b_layout = MXGEMM_B_KN): mxgemm_quantize into a library-owned buffer of
  *     M*K/2 + M*K/32 bytes per (device, stream) (allocated on first use like
  *     the split-K buffers, freed by mxgemm_release_workspaces), then
  *     mxgemm_run on it, both on `stream`.

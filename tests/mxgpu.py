@@ -59,7 +59,11 @@ def gemm_gpu(p: dict, split_k: int = -1, b_packed: bool = False, D=None, stream=
     """Run D = bf16(alpha A B^T + beta C) on the GPU for problem p (dense
     strides; b_packed: B and its scales pre-shuffled by mxgemm_pack_b;
     sa_packed: A's scales too, by mxgemm_pack_scales; a float32 p["C"] is
-    passed as an f32 C).  Returns the bf16 bits of D as numpy uint16 [M, N]."""
+    passed as an f32 C).  With p["B_kn"] (MN-major codes [K, ldb/2], ldb =
+    p["ldb_kn"]) B is passed MN-major and b_packed packs only its scales.
+    Returns the bf16 bits of D as numpy uint16 [M, N]."""
+    if p.get("B_kn") is not None:
+        return gemm_gpu_kn(p, split_k, b_packed, sa_packed, D=D, stream=stream, split_mode=split_mode)
     M, N, K = p["M"], p["N"], p["K"]
     A, B, SA, SB = dev_u8(p["A"]), dev_u8(p["B"]), dev_u8(p["SA"]), dev_u8(p["SB"])
     c_f32 = p.get("C") is not None and p["C"].dtype == np.float32
@@ -95,7 +99,39 @@ def gemm_gpu(p: dict, split_k: int = -1, b_packed: bool = False, D=None, stream=
     return host_bits(D)
 
 
+def gemm_gpu_kn(p: dict, split_k=-1, sb_packed=False, sa_packed=False, D=None, stream=None, split_mode=0):
+    """gemm_gpu with B's codes MN-major (p["B_kn"], row pitch p["ldb_kn"]
+    fp4 elements); sb_packed: scaleB shuffled by mxgemm_pack_scales."""
+    M, N, K = p["M"], p["N"], p["K"]
+    A, B, SA, SB = dev_u8(p["A"]), dev_u8(p["B_kn"]), dev_u8(p["SA"]), dev_u8(p["SB"])
+    C = None
+    if p.get("C") is not None:
+        C = torch.from_numpy(np.ascontiguousarray(p["C"])).cuda() if p["C"].dtype == np.float32 else dev_bf16(p["C"])
+    if D is None:
+        D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    info = mx.mxgemm_plan(M, N, K, 1, -1, 256)
+    if sb_packed:
+        SBp = torch.empty(mx.mxgemm_plan(N, N, K, 1, -1, 256)["packed_sa_bytes"], dtype=torch.uint8, device="cuda")
+        mx.mxgemm_pack_scales(SBp, SB, N, K)
+        SB = SBp
+    if sa_packed:
+        SAp = torch.empty(info["packed_sa_bytes"], dtype=torch.uint8, device="cuda")
+        mx.mxgemm_pack_scales(SAp, SA, M, K)
+        SA = SAp
+    c_f32 = p.get("C") is not None and p["C"].dtype == np.float32
+    st = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=p["ldb_kn"], ldsa=K // 32, ldsb=K // 32, b_packed=int(sb_packed),
+                         sa_packed=int(sa_packed), c_f32=int(c_f32), split_mode=split_mode, b_layout=mx.B_KN)
+    mx.mxgemm_run(D, C if p["beta"] != 0.0 else None, A, B, SA, SB, p["alpha"], p["beta"], M, N, K,
+                  strides=st, split_k=split_k, stream=stream)
+    torch.cuda.synchronize()
+    return host_bits(D)
+
+
 def oracle_ref(p: dict, rows=None, cols=None):
+    if p.get("B_kn") is not None:  # the oracle reads the same MN-major bytes
+        return oracle.mxgemm(p["A"], p["SA"], p["B_kn"], p["SB"], p["K"], p["alpha"], p["beta"],
+                             p.get("C"), rows=rows, cols=cols, a_fmt=int(p.get("a_fmt", 0)),
+                             ldb=p["ldb_kn"], b_layout=1)
     return oracle.mxgemm(p["A"], p["SA"], p["B"], p["SB"], p["K"], p["alpha"], p["beta"],
                          p.get("C"), rows=rows, cols=cols, a_fmt=int(p.get("a_fmt", 0)))
 

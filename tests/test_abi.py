@@ -101,12 +101,18 @@ def test_run_stride_validation():
     # an f32 C needs 4-byte alignment (a bf16 C: 2)
     assert _run(strides=st(c_f32=1), beta=1.0, C=0x6002) == -3
     # A formats: 0..4; wider formats need row-major A scales and the fp32 split;
-    # the reserved field must be 0; A's byte pitch lda * w / 8 a multiple of 16
+    # b_layout is 0 or 1 (MN-major B needs FP4 A); A's byte pitch lda * w / 8 a multiple of 16
     assert _run(strides=st(a_format=5)) == -1
     assert _run(strides=st(a_format=-1)) == -1
     s = st(a_format=1)
-    s.reserved = 1
+    s.b_layout = 2
     assert _run(strides=s) == -1
+    assert _run(strides=st(b_layout=1, a_format=1)) == -1
+    # MN-major B: ldb counts the N columns of a K-row (>= N, even, a 16-byte pitch)
+    assert _run(strides=st(b_layout=1, ldb=255)) == -2
+    assert _run(strides=st(b_layout=1, ldb=264)) == -3      # 132-byte pitch
+    assert _run(strides=st(b_layout=1, ldb=256)) not in (-1, -2, -3)
+    assert _run(strides=st(b_layout=1, ldb=1 << 24), K=512) == -2  # 256 K-rows reach 2^31 bytes
     assert _run(strides=st(a_format=1, ldsa=0, ldb=0, ldsb=0, b_packed=1, sa_packed=1)) == -1
     assert _run(strides=st(a_format=2, split_mode=1)) == -1
     assert _run(strides=st(a_format=1, lda=520)) == -3   # 520-byte pitch

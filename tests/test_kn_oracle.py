@@ -31,6 +31,16 @@ def to_kn(B_nk: np.ndarray, N: int, K: int, ldb: int) -> np.ndarray:
     return (kn[:, 0::2] | (kn[:, 1::2] << 4)).astype(np.uint8)
 
 
+def test_input_helper_is_the_same_transpose():
+    """inputs.to_mn_major (used by the GPU tests) moves the codes exactly as
+    the transpose above does."""
+    from block_scaled_precision_mxfp4_amd import inputs
+    p = small_problem(4, 37, 96, seed=9)
+    assert np.array_equal(inputs.to_mn_major(p["B"], 37, 96, 64), to_kn(p["B"], 37, 96, 64))
+    kn = inputs.to_mn_major(p["B"], 37, 96, 64, pad=7)
+    assert (kn[:, 19:] == 0x77).all() and (kn[:, 18] >> 4 == 7).all()
+
+
 def kn_code(B_kn: np.ndarray, k: int, n: int) -> int:
     byte = int(B_kn[k, n // 2])
     return (byte >> 4) if (n & 1) else (byte & 0xF)
