@@ -67,7 +67,8 @@ def algorithmic_bytes(M, N, K, beta, a_bits=4):
     return b
 
 
-def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soak_ms=0.0, a_fmt=0):
+def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soak_ms=0.0, a_fmt=0, b_layout=0,
+                  packed=None):
     import numpy as np
     import torch
 
@@ -76,14 +77,23 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soa
 
     p = inputs.make_workload(name)
     M, N, K, alpha, beta = p["M"], p["N"], p["K"], p["alpha"], p["beta"]
-    packed, sa_packed = p["b_packed"], p["sa_packed"]
+    sa_packed = p["sa_packed"]
+    if packed is None:
+        packed = p["b_packed"]
+    elif packed and not sa_packed and M > 64:
+        sa_packed = True
+    ldb = K
+    if b_layout:  # the same B stored MN-major ([K][N] codes), scales packed as the workload's
+        p["B"] = inputs.to_mn_major(p["B"], N, K, N)
+        ldb = N
     a_bits = mx.FORMAT_BITS[a_fmt]
     if a_fmt:  # the same workload with A in a wider format (row-major A scales)
         p["A"] = inputs.wide_codes(inputs.SEED_BASE + 0x100 + a_fmt, M, K, a_fmt)
         sa_packed = False
-    if a_fmt:
-        info = mx.mxgemm_query_ex(M, N, K, mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32,
-                                                          b_packed=int(packed), a_format=a_fmt), split_k)
+    if a_fmt or b_layout:
+        info = mx.mxgemm_query_ex(M, N, K, mx.make_strides(ldd=N, ldc=N, lda=K, ldb=ldb, ldsa=K // 32, ldsb=K // 32,
+                                                          b_packed=int(packed), sa_packed=int(sa_packed),
+                                                          a_format=a_fmt, b_layout=b_layout), split_k)
         info["packed_b_bytes"] = mx.mxgemm_query(M, N, K, int(packed), split_k)["packed_b_bytes"]
         info["packed_sb_bytes"] = mx.mxgemm_query(M, N, K, int(packed), split_k)["packed_sb_bytes"]
     else:
@@ -103,7 +113,11 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soa
         B, SB = B0.clone(), SB0.clone()
         C = C0.clone() if C0 is not None else None
         D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        if packed:
+        if packed and b_layout:  # MN-major codes stay as they are; only the scales are shuffled
+            SBp = torch.empty(info["packed_sb_bytes"], dtype=torch.uint8, device="cuda")
+            mx.mxgemm_pack_scales(SBp, SB, N, K)
+            SB = SBp
+        elif packed:
             Bp = torch.empty(info["packed_b_bytes"], dtype=torch.uint8, device="cuda")
             SBp = torch.empty(info["packed_sb_bytes"], dtype=torch.uint8, device="cuda")
             mx.mxgemm_pack_b(Bp, SBp, B, SB, N, K)
@@ -115,9 +129,9 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soa
         sets.append((D, C, A, B, SA, SB))
     del A0, SA0, B0, SB0, C0
     wsp = torch.zeros(max(info["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
-    strides = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32,
+    strides = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=ldb, ldsa=K // 32, ldsb=K // 32,
                               b_packed=int(packed), sa_packed=int(sa_packed), workspace=wsp,
-                              workspace_bytes=wsp.numel(), a_format=a_fmt)
+                              workspace_bytes=wsp.numel(), a_format=a_fmt, b_layout=b_layout)
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
@@ -178,7 +192,8 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soa
     gpu_ms = e0.elapsed_time(e1)
     per = gpu_ms / 1e3 / steps
     flops = 2.0 * M * N * K
-    r = dict(workload=name, a_format=a_fmt, M=M, N=N, K=K, alpha=alpha, beta=beta, b_packed=bool(packed),
+    r = dict(workload=name, a_format=a_fmt, b_layout=("kn" if b_layout else "nk"), M=M, N=N, K=K, alpha=alpha,
+             beta=beta, b_packed=bool(packed),
              sa_packed=bool(sa_packed),
              kernel=info["kernel_name"], tile="%dx%d" % (info["tile_m"], info["tile_n"]),
              split_k=info["split_k"], grid=info["grid"], copies=copies, timing=timing,
@@ -191,7 +206,8 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soa
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     log("%-24s %-22s split %2d  %9.2f us  %8.1f TFLOP/s  %8.1f GB/s  (%s, %d copies)" % (
-        name + ("" if not a_fmt else " A:" + FORMAT_NAMES[a_fmt]), r["kernel"], r["split_k"], r["us_per_step"],
+        name + ("" if not a_fmt else " A:" + FORMAT_NAMES[a_fmt]) + (" B:KN" if b_layout else "") +
+        (" packed" if packed and not p["b_packed"] else ""), r["kernel"], r["split_k"], r["us_per_step"],
         r["tflops"], r["gbs"], timing, copies))
     return r
 
@@ -386,8 +402,52 @@ def time_quantize(steps, warmup, eager=False):
                          "traffic": measured_traffic("quantize_%dx%d" % (M, K))}}
 
 
+def time_stream_read(nbytes, steps, warmup):
+    """mxgemm_stream_read of nbytes over rotated copies (as many as the GEMM
+    lines rotate for that byte count), HIP-graph replay: the HBM read rate
+    this chip reaches for a kernel whose minimum traffic is nbytes."""
+    import torch
+
+    import block_scaled_precision_mxfp4_amd as mx
+
+    nbytes = nbytes // 16 * 16
+    copies = max(1, math.ceil(2.5 * LLC_BYTES / nbytes))
+    g = torch.Generator(device="cuda").manual_seed(0x57EA)
+    bufs = [torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g) for _ in range(copies)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    launch = lambda i: mx.mxgemm_stream_read(bufs[i % copies], nbytes, sink, stream=stream.cuda_stream)
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            launch(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(steps):
+            launch(i)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per = e0.elapsed_time(e1) / 1e3 / steps
+    del bufs, graph
+    torch.cuda.empty_cache()
+    gbs = nbytes / per / 1e9
+    log("%-24s %-22s           %9.2f us  %8.1f GB/s  (hipgraph, %d copies)" % (
+        "stream_read_%d" % nbytes, "mx_stream_read_kernel", per * 1e6, gbs, copies))
+    return {"bytes": nbytes, "us_per_step": per * 1e6, "gbs": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS,
+            "copies": copies}
+
+
 def cpu_baseline(name, target_s=12.0):
-    """The oracle, as it stands, on a bounded sample of the workload's outputs."""
+    """The oracle, as it stands, on a bounded sample of the workload's outputs:
+    threaded over the output columns (the machine's CPU share is 16 cores per GPU,
+    whatever the host's own count), and on one thread for a 64-row slice."""
     import numpy as np
 
     import oracle
@@ -415,9 +475,42 @@ def cpu_baseline(name, target_s=12.0):
         else:
             n_rows = min(M, max(n_rows + 1, int(n_rows * grow)))
     macs = n_rows * n_cols * K
+    # one thread: a 64-row slice of the first 64 columns, extrapolated to the
+    # whole workload at the same per-MAC rate
+    rows1 = np.arange(min(M, 64), dtype=np.int64)
+    cols1 = np.arange(min(N, 64), dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.mxgemm(p["A"], p["SA"], p["B"], p["SB"], K, p["alpha"], p["beta"], p["C"],
+                  rows=rows1, cols=cols1, threads=1)
+    dt1 = time.perf_counter() - t0
+    macs1 = len(rows1) * len(cols1) * K
     return {"value": 2.0 * macs / dt / 1e9, "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "%d rows x %d cols of %s (%.3g MACs, fp64) in %.2f s" % (
-                n_rows, n_cols, name, macs, dt)}
+            "nproc": os.cpu_count(),
+            "sample": "%d rows x %d cols of %s (%.3g MACs, fp64) in %.2f s on %d threads" % (
+                n_rows, n_cols, name, macs, dt, threads),
+            "single_thread": {"value": 2.0 * macs1 / dt1 / 1e9, "unit": "GFLOP/s", "cores": 1,
+                              "sample": "%d rows x %d cols of %s (%.3g MACs) in %.2f s" % (
+                                  len(rows1), len(cols1), name, macs1, dt1),
+                              "extrapolated_full_s": dt1 * (M * N * K) / macs1}}
+
+
+def tile_split_sweep(name, args):
+    """The workload on every tile shape (forced) at splits 1, 2 and 4: us per
+    step (checks the planner's pick, timed on its own line)."""
+    import block_scaled_precision_mxfp4_amd as mx
+    out = []
+    n_tiles = 4
+    for tile in range(n_tiles):
+        os.environ["MXGEMM_FORCE_TILE"] = str(tile)
+        try:
+            for s in (1, 2, 4):
+                r = time_workload(name, args.steps, args.warmup, split_k=s, eager=args.eager,
+                                  soak_ms=min(args.soak_ms, 100.0))
+                out.append({"tile": r["tile"], "kernel": r["kernel"], "split_k": r["split_k"],
+                            "us_per_step": r["us_per_step"]})
+        finally:
+            del os.environ["MXGEMM_FORCE_TILE"]
+    return out
 
 
 def split_sweep(name, args):
@@ -439,6 +532,8 @@ def main():
     ap.add_argument("--workload", default="square_8192")
     ap.add_argument("--split-k", type=int, default=-1)
     ap.add_argument("--only", action="store_true", help="time only --workload (profiling runs)")
+    ap.add_argument("--b-layout", choices=("nk", "kn"), default="nk",
+                    help="B of --workload stored K-major (nk, the default) or MN-major (kn, scales packed)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (counter runs)")
     ap.add_argument("--soak-ms", type=float, default=500.0,
@@ -480,7 +575,8 @@ def main():
         return
 
     head = time_workload(args.workload, args.steps, args.warmup, split_k=args.split_k, eager=args.eager,
-                         soak_ms=args.soak_ms)
+                         soak_ms=args.soak_ms, b_layout=int(args.b_layout == "kn"),
+                         packed=True if args.b_layout == "kn" else None)
     others = []
     if not args.only:
         for name in inputs.WORKLOADS:
@@ -499,6 +595,13 @@ def main():
                            "traffic": measured_traffic(gemv["workload"])}}
         if not args.only:
             m1["split_sweep"] = split_sweep(gemv["workload"], args)
+
+    if m1 is not None and not args.eager:
+        # the achievable HBM read rate for the same byte count, rotated the same way
+        st = time_stream_read(gemv["algorithmic_bytes"], args.steps, args.warmup)
+        m1["achievable_gbs"] = st["gbs"]
+        m1["stream_read"] = st
+        m1["frac_of_achievable"] = gemv["gbs"] / st["gbs"]
 
     quant = None if args.only else time_quantize(args.steps, args.warmup, eager=args.eager)
     decode = None if args.only or args.eager else time_decode(args.steps, args.warmup, soak_ms=min(args.soak_ms, 200.0))
@@ -521,6 +624,24 @@ def main():
             mixed.append({"workload": name, "a_format": FORMAT_NAMES[fmt], "us_per_step": r["us_per_step"],
                           "value": value, "unit": unit, "tflops": r["tflops"],
                           "algorithmic_bytes": r["algorithmic_bytes"], "kernel": r["kernel"], "roofline": roof})
+
+    # B stored MN-major ([K][N], read through the transposed LDS loads) on
+    # the square workload, and the skinny workload with a pre-shuffled B
+    layouts = []
+    if not args.only:
+        for name, b_layout, packed in (("square_8192", 1, True), ("skinny_64x7168x16384", 0, True)):
+            r = time_workload(name, args.steps, args.warmup, eager=args.eager, soak_ms=args.soak_ms,
+                              b_layout=b_layout, packed=packed)
+            if r["M"] > 64:
+                roof = {"bound": "mfma", "achieved": r["tflops"], "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s",
+                        "frac": r["tflops"] / PEAK_MXFP4_TFLOPS, "traffic": None}
+            else:
+                roof = {"bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": r["gbs"] / PEAK_HBM_GBS, "traffic": None}
+            layouts.append({"workload": name, "b_layout": r["b_layout"], "b_packed": r["b_packed"],
+                            "sa_packed": r["sa_packed"], "kernel": r["kernel"], "tile": r["tile"],
+                            "split_k": r["split_k"], "us_per_step": r["us_per_step"], "tflops": r["tflops"],
+                            "gbs": r["gbs"], "roofline": roof})
 
     base = None
     if not args.no_cpu_baseline:
@@ -554,6 +675,7 @@ def main():
         "f16": f16,
         "quantize": quant,
         "decode": decode,
+        "b_layouts": layouts,
         "device": {"arch": head["arch"], "num_cu": head["num_cu"], "clock_hz": head["clock_hz"],
                    "derived_peak_tflops": head["peak_flops_device"] / 1e12},
         "workloads": [{k: o[k] for k in ("workload", "kernel", "tile", "split_k", "us_per_step",
@@ -562,6 +684,9 @@ def main():
     skinny = next((o for o in others if o["workload"] == "skinny_64x7168x16384"), None)
     if skinny is not None:
         line["skinny_split_sweep"] = split_sweep(skinny["workload"], args)
+    mid = next((o for o in others if o["workload"] == "mid_512x1024x2048"), None)
+    if mid is not None:
+        line["mid_tile_split_sweep"] = tile_split_sweep(mid["workload"], args)
     print(json.dumps(line), flush=True)
 
 

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
 # C-ABI entry points declared in include/libmxgemm.h
 EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_run_noalloc", "mxgemm_run_bf16a", "mxgemm_pack_b", "mxgemm_pack_scales", "mxgemm_quantize",
            "mxgemm_f16_run", "mxgemm_query", "mxgemm_plan", "mxgemm_query_ex", "mxgemm_plan_ex",
-           "mxgemm_release_workspaces")
+           "mxgemm_stream_read", "mxgemm_release_workspaces")
 
 STATUS = {0: "MXGEMM_OK", -1: "MXGEMM_ERR_INVALID_ARG", -2: "MXGEMM_ERR_SHAPE",
           -3: "MXGEMM_ERR_ALIGN", -4: "MXGEMM_ERR_UNSUPPORTED_DEVICE", -5: "MXGEMM_ERR_HIP",
@@ -106,6 +106,8 @@ def lib():
         L.mxgemm_query_ex.restype = i32
         L.mxgemm_plan_ex.argtypes = [i32, i32, i32, ctypes.POINTER(Strides), i32, i32, ctypes.POINTER(Info)]
         L.mxgemm_plan_ex.restype = i32
+        L.mxgemm_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+        L.mxgemm_stream_read.restype = i32
         L.mxgemm_release_workspaces.argtypes = []
         L.mxgemm_release_workspaces.restype = i32
         _lib = L
@@ -264,6 +266,14 @@ def mxgemm_plan(M, N, K, b_packed=0, split_k=-1, num_cu=256) -> dict:
     _check(lib().mxgemm_plan(int(M), int(N), int(K), int(b_packed), int(split_k), int(num_cu),
                              ctypes.byref(info)), "mxgemm_plan")
     return info.as_dict()
+
+
+def mxgemm_stream_read(src, nbytes, sink, stream=None, check=True):
+    """Streaming read of nbytes at src (the achievable-bandwidth reference)."""
+    st = lib().mxgemm_stream_read(_ptr(src), int(nbytes), _ptr(sink), _stream(stream))
+    if check:
+        _check(st, "mxgemm_stream_read")
+    return st
 
 
 def mxgemm_release_workspaces():

@@ -131,6 +131,11 @@ void launch_f16(const F16Args &a, int64_t grid, hipStream_t s);
 // chunks add into it
 void launch_d_init(const GemmArgs &g, hipStream_t s);
 
+// Streaming read of `bytes` (a multiple of 16, below 2^31) from src; sink
+// receives at most one word
+int64_t stream_read_grid(size_t bytes);
+void launch_stream_read(const uint8_t *src, size_t bytes, uint32_t *sink, hipStream_t s);
+
 // Fixed device scratch of the allocation-free entry point (mx_scratch.hip):
 // kScratchBytes per device; the first kScratchCounterBytes hold split-K
 // arrival counters, the rest partial sums and FP6 A's FP8 copy.

@@ -1023,6 +1023,24 @@ mxgemm_status mxgemm_quantize(void *A, void *scaleA, const void *X, int M, int K
     return MXGEMM_OK;
 }
 
+mxgemm_status mxgemm_stream_read(const void *src, size_t bytes, void *sink, hipStream_t stream)
+{
+    if (!src || !sink)
+        return MXGEMM_ERR_INVALID_ARG;
+    if (bytes == 0 || bytes % 16 || bytes >= ((size_t)1 << 31))
+        return MXGEMM_ERR_SHAPE;
+    if (!aligned(src, 16) || !aligned(sink, 4))
+        return MXGEMM_ERR_ALIGN;
+    DeviceInfo *d = nullptr;
+    mxgemm_status st = device_info(&d);
+    if (st != MXGEMM_OK)
+        return st;
+    mx::launch_stream_read((const uint8_t *)src, bytes, (uint32_t *)sink, stream);
+    if (hipGetLastError() != hipSuccess)
+        return MXGEMM_ERR_HIP;
+    return MXGEMM_OK;
+}
+
 mxgemm_status mxgemm_release_workspaces(void)
 {
     std::lock_guard<std::mutex> lock(g_mutex);

@@ -402,6 +402,22 @@ mxgemm_status mxgemm_plan_ex(int M, int N, int K, const mxgemm_strides *strides,
 mxgemm_status mxgemm_query_ex(int M, int N, int K, const mxgemm_strides *strides, int split_k,
                               mxgemm_info *out);
 
+/* ---- measurement ------------------------------------------------------------ */
+
+/*
+ * Read `bytes` of device memory at src once, with the 16-byte non-temporal
+ * loads the skinny kernels stream B with, and nothing else (sink, a 4-byte
+ * device word, is written only if the XOR of everything read equals a fixed
+ * constant).  A kernel whose minimum DRAM traffic is `bytes` cannot finish
+ * faster on this chip ("Optimizing GEMM in HIP", background: the GEMM's
+ * arithmetic intensity against its minimum required traffic), so its time
+ * is the achievable ceiling the benchmark reports next to the published HBM
+ * bandwidth.  bytes: a multiple of 16, below 2^31 (else
+ * MXGEMM_ERR_SHAPE); src 16-byte and sink 4-byte aligned (else
+ * MXGEMM_ERR_ALIGN).  Asynchronous on `stream`; allocates nothing.
+ */
+mxgemm_status mxgemm_stream_read(const void *src, size_t bytes, void *sink, hipStream_t stream);
+
 /* Free the library-owned split-K workspaces (after synchronizing their
  * streams).  Later calls allocate again. */
 mxgemm_status mxgemm_release_workspaces(void);

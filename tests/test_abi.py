@@ -304,3 +304,12 @@ def test_run_bf16a_validation_before_any_hip_call():
     assert f(strides=st(split_mode=mx.SPLIT_BF16_ATOMIC)) == -1
     assert f(ldx=480) == -2                      # ldx < K
     assert f(X=0x2008) == -3 and f(ldx=516) == -3  # 16-byte rows of X
+
+
+def test_stream_read_validation_before_any_hip_call():
+    f = lambda **kw: mx.mxgemm_stream_read(**dict(dict(src=0x1000, nbytes=4096, sink=0x2000, stream=0), **kw),
+                                           check=False)
+    assert f(src=None) == -1 and f(sink=None) == -1
+    assert f(nbytes=0) == -2 and f(nbytes=4100) == -2 and f(nbytes=1 << 31) == -2
+    assert f(src=0x1008) == -3 and f(sink=0x2002) == -3
+    assert f() not in (-1, -2, -3)
