@@ -46,18 +46,20 @@ def log(*a):
 
 def measured_traffic(workload):
     """HBM bytes per launch from the committed counter runs (profiles/traffic.json),
-    or None when the kernels have changed since those counters were taken."""
-    from block_scaled_precision_mxfp4_amd.kernel_hash import kernel_source_hash
+    or None when the workload's kernel family has changed since those
+    counters were taken (each entry carries the fingerprint of its family's
+    sources)."""
+    from block_scaled_precision_mxfp4_amd.kernel_hash import FAMILY_FILES, kernel_family_hash
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != kernel_source_hash():
-        return None
     w = t.get("workloads", {}).get(workload)
-    return None if w is None else w["traffic_bytes"]
+    if w is None or w.get("family") not in FAMILY_FILES or w.get("source_hash") != kernel_family_hash(w["family"]):
+        return None
+    return w["traffic_bytes"]
 
 
 def algorithmic_bytes(M, N, K, beta, a_bits=4):
@@ -534,6 +536,7 @@ def main():
     ap.add_argument("--only", action="store_true", help="time only --workload (profiling runs)")
     ap.add_argument("--b-layout", choices=("nk", "kn"), default="nk",
                     help="B of --workload stored K-major (nk, the default) or MN-major (kn, scales packed)")
+    ap.add_argument("--packed", action="store_true", help="pre-shuffle B of --workload (and A scales if M > 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (counter runs)")
     ap.add_argument("--soak-ms", type=float, default=500.0,
@@ -576,7 +579,7 @@ def main():
 
     head = time_workload(args.workload, args.steps, args.warmup, split_k=args.split_k, eager=args.eager,
                          soak_ms=args.soak_ms, b_layout=int(args.b_layout == "kn"),
-                         packed=True if args.b_layout == "kn" else None)
+                         packed=True if (args.b_layout == "kn" or args.packed) else None)
     others = []
     if not args.only:
         for name in inputs.WORKLOADS:
@@ -632,12 +635,13 @@ def main():
         for name, b_layout, packed in (("square_8192", 1, True), ("skinny_64x7168x16384", 0, True)):
             r = time_workload(name, args.steps, args.warmup, eager=args.eager, soak_ms=args.soak_ms,
                               b_layout=b_layout, packed=packed)
+            key = name + ("_kn" if b_layout else "_packed")
             if r["M"] > 64:
                 roof = {"bound": "mfma", "achieved": r["tflops"], "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s",
-                        "frac": r["tflops"] / PEAK_MXFP4_TFLOPS, "traffic": None}
+                        "frac": r["tflops"] / PEAK_MXFP4_TFLOPS, "traffic": measured_traffic(key)}
             else:
                 roof = {"bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": r["gbs"] / PEAK_HBM_GBS, "traffic": None}
+                        "frac": r["gbs"] / PEAK_HBM_GBS, "traffic": measured_traffic(key)}
             layouts.append({"workload": name, "b_layout": r["b_layout"], "b_packed": r["b_packed"],
                             "sa_packed": r["sa_packed"], "kernel": r["kernel"], "tile": r["tile"],
                             "split_k": r["split_k"], "us_per_step": r["us_per_step"], "tflops": r["tflops"],

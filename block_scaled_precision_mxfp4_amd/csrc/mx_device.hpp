@@ -245,8 +245,9 @@ struct Epilogue {
 };
 
 // Epilogue for beta == 0 through a private LDS region of the wave
-// (16*FM x 16*FN bf16, 16-byte chunks of a row XOR-swizzled by the row
-// index): the fragments are rounded and written to LDS in their own layout,
+// (16*FM x 16*FN bf16, 16-byte chunks of a row XOR-swizzled by row / 2:
+// with 8-byte writes served 32 lanes per cycle, rows r and r + 8 of the 16
+// a write instruction covers must not share a slot): the fragments are rounded and written to LDS in their own layout,
 // then read back row-wise and written to D with 16-byte stores, each
 // instruction covering whole 16*FN-column row segments (full 128-byte lines
 // for FN = 4) instead of 32-byte pieces of 16 rows.  Same values as
@@ -270,12 +271,12 @@ __device__ __forceinline__ void store_tile_staged(const Epilogue &ep, int m_base
             v2u o;
             o[0] = bf16x2_rne(ep.alpha * acc[fn][fm][0], ep.alpha * acc[fn][fm][1]);
             o[1] = bf16x2_rne(ep.alpha * acc[fn][fm][2], ep.alpha * acc[fn][fm][3]);
-            *reinterpret_cast<v2u *>(lds + r * RB + ((j ^ (r & (CH - 1))) * 16) + ((lane >> 4) & 1) * 8) = o;
+            *reinterpret_cast<v2u *>(lds + r * RB + ((j ^ ((r >> 1) & (CH - 1))) * 16) + ((lane >> 4) & 1) * 8) = o;
         }
 #pragma unroll
     for (int i = 0; i < FM * 16 / RPI; ++i) {
         const int r = i * RPI + lane / CH, c = lane & (CH - 1);
-        const v4i v = *reinterpret_cast<const v4i *>(lds + r * RB + ((c ^ (r & (CH - 1))) * 16));
+        const v4i v = *reinterpret_cast<const v4i *>(lds + r * RB + ((c ^ ((r >> 1) & (CH - 1))) * 16));
         const int m = m_base + r, n = n_base + c * 8;
         if (m >= ep.M || n >= ep.N)
             continue;

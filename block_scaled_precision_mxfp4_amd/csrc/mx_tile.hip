@@ -101,14 +101,14 @@ __device__ __forceinline__ void store_whole_tile_staged(uint16_t *D, int64_t ldd
             v2u o;
             o[0] = bf16x2_rne(alpha * acc[fn][fm][0], alpha * acc[fn][fm][1]);
             o[1] = bf16x2_rne(alpha * acc[fn][fm][2], alpha * acc[fn][fm][3]);
-            *reinterpret_cast<v2u *>(lds + r * RB + ((j ^ (r & (CH - 1))) * 16) + ((lane >> 4) & 1) * 8) = o;
+            *reinterpret_cast<v2u *>(lds + r * RB + ((j ^ ((r >> 1) & (CH - 1))) * 16) + ((lane >> 4) & 1) * 8) = o;
         }
     const int r0 = lane / CH, c = lane & (CH - 1);
     uint16_t *d0 = D + (int64_t)(m_base + r0) * ldd + n_base + c * 8;
 #pragma unroll
     for (int i = 0; i < FM * 16 / RPI; ++i) {
         const int r = i * RPI + r0;
-        const v4i v = *reinterpret_cast<const v4i *>(lds + r * RB + ((c ^ (r & (CH - 1))) * 16));
+        const v4i v = *reinterpret_cast<const v4i *>(lds + r * RB + ((c ^ ((r >> 1) & (CH - 1))) * 16));
         __builtin_nontemporal_store(v, reinterpret_cast<v4i *>(d0 + (int64_t)(i * RPI) * ldd));
     }
 }
@@ -207,19 +207,25 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     uint32_t a_bytes, b_bytes;
     __amdgpu_buffer_rsrc_t rsa, rsb;
     // Row-major operands move in whole 128-byte lines: one load instruction
-    // covers 8 rows x the stage's 128 bytes (lane l: row l/8, 16-byte chunk
-    // (l%8) ^ (l/8) ^ h for the h-th 8-row half of a 16-row group).  The
+    // covers 8 rows x the stage's 128 bytes (lane l: row l/8 of the h-th
+    // 8-row half of a 16-row group, 16-byte chunk (l%8) ^ sw(row)).  The
     // resulting LDS layout of a 16-row group (2 KiB) puts row r, chunk c at
-    // 16-byte slot (r/8)*64 + (r%8)*8 + (c ^ (r%8) ^ (r/8)): the 16 rows of
-    // one chunk fall in 16 different bank groups, so fragment reads stay
-    // conflict-free.
-    const uint32_t a_lane = (uint32_t)((lane >> 3) * g.lda_b + (((lane & 7) ^ (lane >> 3)) * 16));
+    // 16-byte slot (r/8)*64 + (r%8)*8 + (c ^ sw(r)), sw(r) = 2*bit1(r) +
+    // 4*bit3(r).  A 16-byte LDS read serves 16 lanes per cycle: lanes 0-31
+    // and 32-63 separately, each split by the parity of lane bits 2-4
+    // (measured on gfx950 with two-lane bank probes).  Under that grouping a
+    // fragment read (row lane%16, chunk 4ks + lane/16) touches 16 distinct
+    // 16-byte bank slots, i.e. all 64 banks once; the earlier swizzle
+    // c ^ (r%8) ^ (r/8), laid out for lanes 0-15 per cycle, doubled every
+    // fragment read (measured 2-way with the LDS conflict counters).
+    const int kc_lane = (lane & 7) ^ (2 * ((lane >> 4) & 1));  // chunk of lane l in a half-0 load
+    const uint32_t a_lane = (uint32_t)((lane >> 3) * g.lda_b + kc_lane * 16);
     uint32_t b_lane, b_rg_stride;
     if constexpr (BPACK) {
         b_lane = (uint32_t)(lane * 16);
         b_rg_stride = (uint32_t)(g.ks_total * 1024);
     } else {
-        b_lane = (uint32_t)((lane >> 3) * g.ldb_b + (((lane & 7) ^ (lane >> 3)) * 16));
+        b_lane = (uint32_t)((lane >> 3) * g.ldb_b + kc_lane * 16);
         b_rg_stride = (uint32_t)(16 * g.ldb_b);
     }
     auto load_src = [&](int lg) __attribute__((always_inline)) {
@@ -293,7 +299,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
                                           on ? (uint32_t)(min(256, (kb_end - kb_s) * 32) * g.ldb_b) : 0u)
                             : make_rsrc(b_base + b_k, on ? b_bytes - b_k : 0u);
         // chunk (K-block of the stage) a row-major lane loads in half h
-        const int kc0 = (lane & 7) ^ (lane >> 3), kc1 = kc0 ^ 1;
+        const int kc0 = kc_lane, kc1 = kc0 ^ 4;
 #pragma unroll
         for (int i = 0; i < A_CH / NW; ++i) {
             const int c = i * NW + wave;
@@ -402,7 +408,8 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     // its 16-row group (row lane%16, K-block lane/16 of step 0; step 1 flips
     // chunk bit 2)
     const int fr = lane & 15;
-    const uint32_t rl0 = (uint32_t)(((fr >> 3) * 64 + (fr & 7) * 8 + ((lane >> 4) ^ (fr & 7) ^ (fr >> 3))) * 16);
+    const int sw_fr = 2 * ((fr >> 1) & 1) + 4 * ((fr >> 3) & 1);
+    const uint32_t rl0 = (uint32_t)(((fr >> 3) * 64 + (fr & 7) * 8 + ((lane >> 4) ^ sw_fr)) * 16);
     const uint32_t rl1 = rl0 ^ 64u;
     // MN-major fragment reads: lane (group g, row i) names K-row 32g + i of
     // the step (call 1; call 2 is 16 K-rows further), whose chunks are

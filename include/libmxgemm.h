@@ -282,8 +282,9 @@ mxgemm_status mxgemm_pack_scales(void *Sp, const void *S, int rows, int K, int64
  * Quantize a bf16 matrix X [M][ldx] (row-major, ldx in bf16 elements) to the
  * operand format of A: packed E2M1 codes A [M][lda/2] bytes (lda in fp4
  * elements, element 2i in the low nibble of byte i) and E8M0 scales
- * scaleA [M][ldsa] bytes, one per 32 consecutive K elements ([F4] "Data
- * layouts").  The outputs can be passed to mxgemm_run as A and scaleA.
+ * scaleA [M][ldsa] bytes, one per 32 consecutive K elements (asm_f4gemm
+ * README, "Data layouts").  The outputs can be passed to mxgemm_run as A and
+ * scaleA.
  *
  * The pages fix the encodings but not how a scale is chosen for real input;
  * the conversion follows the OCP Microscaling Formats v1.0 specification,
@@ -376,9 +377,12 @@ typedef struct mxgemm_info {
 
 /*
  * Plan for the current device: the kernel, tile and split mxgemm_run would
- * use for these arguments, and the buffer sizes it needs.  Returns
- * MXGEMM_ERR_UNSUPPORTED_DEVICE unless the current device is gfx950.
- * split_k as for mxgemm_run.
+ * use for these arguments, and the buffer sizes it needs.  The plan follows
+ * the asm_f4gemm README's "Tile selection heuristic" (count the rounds of
+ * workgroups the compute units need per tile shape, prefer fewer rounds of
+ * larger tiles, iterate candidates in a fixed order), weighted by a per-tile
+ * cost that also prices split-K.  Returns MXGEMM_ERR_UNSUPPORTED_DEVICE
+ * unless the current device is gfx950.  split_k as for mxgemm_run.
  */
 mxgemm_status mxgemm_query(int M, int N, int K, int b_packed, int split_k,
                            mxgemm_info *out);

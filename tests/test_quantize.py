@@ -124,3 +124,52 @@ def test_quantized_activations_feed_the_gemm(M):
     d = gemm_gpu(p, split_k=-1)
     ref, mag, _ = oracle_ref(p)
     assert_parity(d, ref, mag, "quantized A, M=%d" % M)
+
+
+# scale exponents X of the exhaustive sweep: the clamped bottom (-127, block
+# maxima down in bf16's subnormals), the bottom and top of the normal range,
+# and points in between
+SWEEP_X = [-127, -126, -125, -124, -100, -60, -20, -3, -2, -1, 0, 1, 2, 3, 20, 60, 100, 124, 125]
+
+
+def exhaustive_blocks(X):
+    """Every bf16 magnitude below 8 * 2^X (both signs) in 32-blocks whose
+    maximum fixes the scale exponent at X: element 0 of every block is
+    2^(X+2) (the smallest magnitude with floor(log2) - 2 = X), the other 31
+    are the sweep.  For X = -127 (clamped) the blocks' maximum is the
+    largest bf16 below 2^-124 instead and the sweep stops below it."""
+    if X > -127:
+        top = 0x3F80 + ((X + 3) << 7)          # bits of 2^(X+3): the sweep ends below it
+        head = 0x3F80 + ((X + 2) << 7)         # 2^(X+2)
+    else:
+        top = 0x3F80 + ((-124) << 7)            # 2^-124: maxima below it all clamp to X = -127
+        head = top - 1                          # largest bf16 below 2^-124
+    mags = np.arange(0, top, dtype=np.uint32)
+    vals = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+    pad = (-len(vals)) % 31
+    vals = np.concatenate([vals, np.zeros(pad, dtype=np.uint16)]).reshape(-1, 31)
+    blocks = np.concatenate([np.full((vals.shape[0], 1), head, dtype=np.uint16), vals], axis=1)
+    return blocks.reshape(-1)
+
+
+def test_quantize_every_bf16_magnitude_per_scale_exponent():
+    """Exhaustive check of the conversion for 19 scale exponents: every bf16
+    magnitude below 8 * 2^X, with both signs, quantized under scale 2^X
+    (normal and clamped-subnormal scales), byte for byte against the
+    oracle.  About 568,000 distinct (value, scale) inputs; ties, values
+    that saturate at 6, values that round to zero (code 0x8 when negative)
+    and every bf16 subnormal included."""
+    flat = np.concatenate([exhaustive_blocks(X) for X in SWEEP_X])
+    K = 8192
+    pad = (-len(flat)) % K
+    flat = np.concatenate([flat, np.zeros(pad, dtype=np.uint16)])
+    Xm = flat.reshape(-1, K)
+    M = Xm.shape[0]
+    say("case quantize exhaustive", M, "x", K, "distinct inputs", len(flat) - pad)
+    A, S = quantize_gpu(Xm, M, K)
+    Ar, Sr = oracle.quantize_mxfp4(Xm)
+    assert np.array_equal(S, Sr), "scales differ in %d places" % int((S != Sr).sum())
+    assert np.array_equal(A, Ar), "codes differ in %d bytes" % int((A != Ar).sum())
+    # every block's scale is the intended one
+    Xs = [X for X in SWEEP_X for _ in range(len(exhaustive_blocks(X)) // 32)]
+    assert np.array_equal(Sr.reshape(-1)[:len(Xs)], np.array(Xs) + 127)
