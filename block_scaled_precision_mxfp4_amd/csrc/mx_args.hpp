@@ -63,12 +63,13 @@ void launch_tile_deep(const GemmArgs &g, int grid, hipStream_t s);
 // Host-side table of the tiled kernels, in the planner's preference order.
 const TileKernel *tile_kernels(int *count);
 
-// Tiled kernel with 8-bit A (FP8 E4M3, BF8 E5M2; B FP4, row-major A scales):
-// launchers indexed by a_format - 1
+// Tiled kernel with 8-bit A (FP8 E4M3, BF8 E5M2, or FP6 E2M3 / E3M2 in the
+// padded layout of launch_fp6_pad; B FP4, row-major A scales): launchers
+// indexed by a_format - 1
 struct TileKernelA8 {
     int bm, bn;
     int occupancy;
-    LaunchFn plain[2], packed[2];
+    LaunchFn plain[4], packed[4];
     const char *name;
 };
 const TileKernelA8 *tile_kernels_a8(int *count);
@@ -90,11 +91,13 @@ void launch_skinny_bf16a(int nr, bool b_packed, const GemmArgs &g, int grid, hip
 
 // Skinny kernel for 16 < M <= 64 with the waves splitting B's rows and A
 // staged once per workgroup in LDS: mg 16-row groups of A, nrw 16-row groups
-// of B per wave, u 128-K steps per batch, ns ring slots.  index: mg - 2.
+// of B per wave, u 128-K steps per batch; launchers and names per A format
+// (index a_format - 0: FP4, FP8 E4M3, BF8 E5M2, FP6 E2M3, FP6 E3M2).
+// index: mg - 2.
 struct RowsKernel {
-    int mg, nrw, u, ns;
-    LaunchFn plain, packed;
-    const char *name;
+    int mg, nrw, u;
+    LaunchFn plain[5], packed[5];
+    const char *name[5];
 };
 const RowsKernel *rows_kernels(int *count);
 
@@ -138,15 +141,17 @@ void launch_stream_read(const uint8_t *src, size_t bytes, uint32_t *sink, hipStr
 
 // Fixed device scratch of the allocation-free entry point (mx_scratch.hip):
 // kScratchBytes per device; the first kScratchCounterBytes hold split-K
-// arrival counters, the rest partial sums and FP6 A's FP8 copy.
+// arrival counters, the rest partial sums and FP6 A's re-laid copy.
 constexpr size_t kScratchBytes = (size_t)32 << 20;
 constexpr size_t kScratchCounterBytes = (size_t)64 << 10;
 // This device's scratch address (looked up once per device, with the device
 // current); never the array's host-side name.
 hipError_t scratch_address(void **ptr);
 
-// FP6 A (E2M3 or E3M2, rows of lda_b bytes) -> FP8 A (E4M3 or E5M2 respectively,
-// rows of K bytes) in `out`, exactly; K % 16 == 0, lda_b % 4 == 0
-void launch_fp6_to_fp8(int a_fmt, const uint8_t *A, int64_t lda_b, uint8_t *out, int M, int K, hipStream_t s);
+// FP6 A (rows of lda_b bytes, lda_b % 8 == 0) -> the padded layout the
+// 8-bit tiled kernel reads with A's FP6 format code (32 bytes per K-block,
+// rows of fp6_pad_pitch(K) bytes) in `out`; codes unchanged
+int64_t fp6_pad_pitch(int K);
+void launch_fp6_pad(const uint8_t *A, int64_t lda_b, uint8_t *out, int M, int K, hipStream_t s);
 
 }  // namespace mx

@@ -51,6 +51,15 @@ __device__ __forceinline__ v4i lds_read16(uint32_t base)
 }
 
 template <int OFF>
+__device__ __forceinline__ v2u lds_read8(uint32_t base)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+    v2u r;
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(base), "n"(OFF) : "memory");
+    return r;
+}
+
+template <int OFF>
 __device__ __forceinline__ uint32_t lds_read4(uint32_t base)
 {
     static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
@@ -81,6 +90,7 @@ __device__ __forceinline__ void static_for(F &&f)
 }
 
 __device__ __forceinline__ void asm_pass(v4i &r) { asm volatile("" : "+v"(r)); }
+__device__ __forceinline__ void asm_pass(v2u &r) { asm volatile("" : "+v"(r)); }
 __device__ __forceinline__ void asm_pass(uint32_t &r) { asm volatile("" : "+v"(r)); }
 template <typename T, int N>
 __device__ __forceinline__ void asm_pass(T (&r)[N])

@@ -12,9 +12,22 @@
 // registers.  A workgroup covers 4x more rows of B for the same A bytes, and
 // no cross-wave reduction is needed: each wave stores its own columns of D.
 //
-// Batches of U 128-K steps are double-buffered; one barrier per batch hands
-// the A stage over.  A scales (row-major, 16-byte aligned rows) are staged
-// the same way; other scale layouts are loaded by each wave.
+// Batches of U 128-K steps rotate through a ring of LDS slots; one barrier
+// per batch hands a slot over.  A scales (row-major, 16-byte aligned rows)
+// are staged the same way; other scale layouts are loaded by each wave.
+// Row-major B goes through a wave-private part of the same slot: each load
+// instruction covers whole 128-byte lines (4 rows x the batch's 256 bytes)
+// instead of 64-byte halves of 16 rows, which the load path serves at a
+// fraction of the whole-line rate; packed B (1 KiB contiguous per operand)
+// is loaded straight into registers.
+//
+// A of a wider format (AFMT 1, 2: FP8 E4M3 / BF8 E5M2; 3, 4: FP6 E2M3 /
+// E3M2; B stays FP4, "CDNA4 dense MFMA builtins", "Mixed-precision with
+// scaling") is staged the same way, its rows of the batch being 8U or 6U
+// 16-byte chunks (dense FP6: 24 bytes per K-block) in 32-slot LDS rows.  A
+// lane's operand for K-block g of a step: FP8, the two 16-element runs K
+// 16g.. and 64+16g.. of the step (two 16-byte reads); FP6, the block's 24
+// bytes (three 8-byte reads).
 #include "mx_args.hpp"
 #include "mx_device.hpp"
 #include "mx_pipe.hpp"
@@ -25,17 +38,23 @@ namespace mx {
 
 // SAM: 0 = row-major A scales staged in LDS (16-byte aligned rows, K-block
 // count a multiple of 16); 1 = row-major A scales loaded per wave (any
-// alignment); 2 = packed A scales loaded per wave.
+// alignment); 2 = packed A scales loaded per wave (FP4 A only).
 // U: 128-K steps per batch; NS: ring slots (NS - 1 batches in flight).
-template <int MG, int NRW, int U, int NS, bool BPACK, bool SVEC, int SAM>
+// AFMT: A's format (0 FP4, 1 FP8 E4M3, 2 BF8 E5M2, 3 FP6 E2M3, 4 FP6 E3M2);
+// FP6 needs an even K-block count (chunks then never straddle the K end).
+template <int MG, int NRW, int U, int NS, bool BPACK, bool SVEC, int SAM, int AFMT>
 __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
 {
-    static_assert(U % 4 == 0 && NS >= 2, "whole 4-step scale groups per batch");
+    static_assert(U == 4 && NS >= 2, "one 4-step scale group per batch");
+    static_assert(AFMT == 0 || SAM != 2, "wider A with row-major A scales");
     constexpr int G = U / 4;               // 4-step scale groups per batch
     constexpr int RW = 16 * NRW;           // B rows per wave
     constexpr int R = 4 * RW;              // B rows per workgroup
     constexpr int AR = MG * 16;            // A rows staged
-    constexpr int CPR = U * 4;             // 16-byte chunks of an A row per batch
+    constexpr int AW = kFmtBits[AFMT];     // A element bits = dwords of a lane's operand
+    constexpr int AKB = 4 * AW;            // bytes of one A K-block
+    constexpr int ACU = U * AW;            // 16-byte chunks of an A row per batch
+    constexpr int CPR = ACU <= 16 ? 16 : 32;  // LDS slots per A row (FP6: 24 of 32 used)
     constexpr int RPI = 64 / CPR;          // A rows per 1 KiB load instruction
     constexpr int A_BYTES = AR * CPR * 16;
     static_assert(A_BYTES % 4096 == 0, "the A stage splits evenly over the four waves");
@@ -44,8 +63,14 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
     constexpr int SA_ALLOC = SAM == 0 ? (SA_BYTES + 1023) / 1024 * 1024 : 16;
     constexpr int SA_PARTS = SAM == 0 ? SA_ALLOC / 1024 : 1;  // 1 KiB loads of the A scale stage
     static_assert(SA_ALLOC <= 4096, "one 16-byte lane per A scale chunk");
+    constexpr bool BST = !BPACK;           // row-major B staged in LDS
+    constexpr int CPB = U * 4;             // 16-byte chunks of a B row per batch
+    constexpr int RPB = 64 / CPB;          // B rows per 1 KiB load instruction
+    constexpr int B_WAVE = RW * CPB * 16;  // a wave's B bytes per batch
+    constexpr int B_SLOT = BST ? 4 * B_WAVE : 0;
     __shared__ __attribute__((aligned(1024))) uint8_t s_a[NS * A_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t s_sa[NS * SA_ALLOC];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_b[BST ? NS * B_SLOT : 16];
 
     // memory instructions one batch issues per wave: a later batch's loads
     // may stay in flight while the wave waits for an earlier one
@@ -83,7 +108,7 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
 
     // one batch's per-wave loads
     struct Regs {
-        v4i b[U][NRW];
+        v4i b[BST ? 1 : U][NRW];
         uint32_t sbp[BPACK ? U / 2 : 1][NRW];  // packed B scales: one word per step pair
         v4i sbr[BPACK ? 1 : G][NRW];           // row-major B scales: raw 4-step groups
         uint32_t sap[SAM == 2 ? U / 2 : 1][MG];
@@ -95,13 +120,17 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
         const int kb0 = kb_begin + bi * 4 * U;  // first K-block of the batch (a multiple of 16)
         const int kbe = bi < nb ? kb_end : 0;   // batches past the chunk load nothing
         // A stage: whole 128-byte lines; slot s of row r holds chunk s ^ (r % 16)
+        // of the row's batch (chunk c starts in K-block c * 16 / AKB; FP6
+        // slots past the 6U chunks load nothing)
         uint8_t *da = s_a + SLOT * A_BYTES;
 #pragma unroll
         for (int i = 0; i < A_DMA; ++i) {
             const int q = i * 4 + wave;  // 1 KiB instruction of the stage
             const int row = q * RPI + lane / CPR;
-            const int kb = kb0 + ((lane % CPR) ^ (row & 15));
-            load16_to_lds(ra, (lds_void *)(da + q * 1024), kb < kbe ? (uint32_t)(row * g.lda_b + kb * 16) : kOOB);
+            const int c = (lane % CPR) ^ (row & 15);
+            const bool ok = c < ACU && kb0 + c * 16 / AKB < kbe;
+            load16_to_lds(ra, (lds_void *)(da + q * 1024),
+                          ok ? (uint32_t)(row * g.lda_b + kb0 * AKB + c * 16) : kOOB);
         }
         if constexpr (SAM == 0) {
             // [AR][U*4] scale bytes, one 16-byte lane each (a lane past the
@@ -132,17 +161,25 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
             }
         }
         // this wave's rows of B and their scales
+        if constexpr (BST) {
+            // RPB rows x the batch's CPB chunks per instruction; slot s of
+            // row r holds the row's chunk (K-block of the batch) s ^ (r % 16)
+            uint8_t *db = s_b + SLOT * B_SLOT + wave * B_WAVE;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int ks = kb0 / 4 + u;
-            const int kb = ks * 4 + (lane >> 4);
-            const bool ok = kb < kbe;
+            for (int i = 0; i < RW / RPB; ++i) {
+                const int row = i * RPB + lane / CPB;
+                const int kb = kb0 + ((lane % CPB) ^ (row & 15));
+                load16_to_lds_stream(rb, (lds_void *)(db + i * 1024),
+                                     kb < kbe ? (uint32_t)(row * g.ldb_b + kb * 16) : kOOB);
+            }
+        } else {
 #pragma unroll
-            for (int nr = 0; nr < NRW; ++nr) {
-                if constexpr (BPACK)
+            for (int u = 0; u < U; ++u) {
+                const int ks = kb0 / 4 + u;
+                const bool ok = ks * 4 + (lane >> 4) < kbe;
+#pragma unroll
+                for (int nr = 0; nr < NRW; ++nr)
                     r.b[u][nr] = load16_stream(rb, ok ? (uint32_t)(((nr * g.ks_total + ks) * 64 + lane) * 16) : kOOB);
-                else
-                    r.b[u][nr] = load16_stream(rb, ok ? (uint32_t)((nr * 16 + (lane & 15)) * g.ldb_b + kb * 16) : kOOB);
             }
         }
         if constexpr (BPACK) {
@@ -177,6 +214,7 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
     // included, and drain the ring
     const uint32_t a_base = lds_addr(s_a) + (uint32_t)((lane & 15) * CPR * 16);
     const uint32_t sa_base = lds_addr(s_sa) + (uint32_t)((lane & 15) * U * 4);
+    const uint32_t b_base = lds_addr(s_b) + (uint32_t)(wave * B_WAVE + (lane & 15) * CPB * 16);
     auto compute = [&](auto slotc, const Regs &r) __attribute__((always_inline)) {
         constexpr int SLOT = decltype(slotc)::value;
         uint32_t saw[G][MG];
@@ -201,24 +239,72 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
                 for (int mg = 0; mg < MG; ++mg)
                     saw[gi][mg] = scale_group_word<false>(r.sar[gi][mg], lane);
         }
-        // A fragments of step u: row mg*16 + lane%16, chunk 4u + lane/16 at
-        // slot chunk ^ (row % 16); one step is read ahead of the multiplies
+        // staged B: this wave's fragments of the whole batch, read first
+        // (row nr*16 + lane%16, chunk 4u + lane/16 at slot chunk ^ (row % 16))
+        v4i bst[BST ? U : 1][NRW];
+        if constexpr (BST) {
+            static_for<U>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                const uint32_t a = b_base + (uint32_t)((((u * 4) + (lane >> 4)) ^ (lane & 15)) * 16);
+                static_for<NRW>([&](auto nc) {
+                    constexpr int nr = decltype(nc)::value;
+                    bst[u][nr] = lds_read16<SLOT * B_SLOT + nr * 16 * CPB * 16>(a);
+                });
+            });
+        }
+        // A fragments of step u, row mg*16 + lane%16, K-block g = lane/16 of
+        // the step, each 16-byte chunk c at slot c ^ (row % 16): FP4 chunk
+        // 4u + g; FP8 chunks 8u + g and 8u + g + 4; FP6 the 8-byte pieces at
+        // bytes 96u + 24g + 8j, j = 0..2.  One step is read ahead of the
+        // multiplies.
         const uint32_t slot_base = a_base + SLOT * A_BYTES;
-        v4i af[2][MG];
-        auto read_step = [&](auto uc, v4i(&dst)[MG]) __attribute__((always_inline)) {
+        constexpr int NA = AW == 4 ? 1 : AW == 8 ? 2 : 3;  // reads per fragment
+        struct AStep {
+            v4i x[AW == 6 ? 1 : NA][MG];
+            v2u y[AW == 6 ? NA : 1][MG];
+        };
+        AStep af[2];
+        auto read_step = [&](auto uc, AStep &dst) __attribute__((always_inline)) {
             constexpr int u = decltype(uc)::value;
-            const uint32_t a = slot_base + (uint32_t)((((u * 4) + (lane >> 4)) ^ (lane & 15)) * 16);
-            static_for<MG>([&](auto mc) { dst[mc.value] = lds_read16<decltype(mc)::value * 16 * CPR * 16>(a); });
+            const int gq = lane >> 4, row = lane & 15;
+            if constexpr (AW == 6) {
+                static_for<NA>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    const int byte = 24 * gq + 8 * j;  // within the step's 96 bytes
+                    const uint32_t a =
+                        slot_base + (uint32_t)((((u * 6) + (byte >> 4)) ^ row) * 16 + (byte & 8));
+                    static_for<MG>([&](auto mc) {
+                        dst.y[j][mc.value] = lds_read8<decltype(mc)::value * 16 * CPR * 16>(a);
+                    });
+                });
+            } else {
+                static_for<NA>([&](auto jc) {
+                    constexpr int j = decltype(jc)::value;
+                    const uint32_t a = slot_base + (uint32_t)((((u * 4 * NA) + gq + 4 * j) ^ row) * 16);
+                    static_for<MG>([&](auto mc) {
+                        dst.x[j][mc.value] = lds_read16<decltype(mc)::value * 16 * CPR * 16>(a);
+                    });
+                });
+            }
+        };
+        auto wait_step = [&](auto nc, AStep &st) __attribute__((always_inline)) {
+            if constexpr (AW == 6)
+                lds_wait_n<decltype(nc)::value>(st.y);
+            else
+                lds_wait_n<decltype(nc)::value>(st.x);
         };
         read_step(std::integral_constant<int, 0>{}, af[0]);
         static_for<U>([&](auto uc) {
             constexpr int u = decltype(uc)::value;
+            if constexpr (u == 0 && BST)
+                lds_wait_n<NA * MG>(bst);  // the B reads went out before step 0's
             if constexpr (u + 1 < U) {
                 read_step(std::integral_constant<int, u + 1>{}, af[(u + 1) & 1]);
-                lds_wait_n<MG>(af[u & 1]);
+                wait_step(std::integral_constant<int, NA * MG>{}, af[u & 1]);
             } else {
-                lds_wait_n<0>(af[u & 1]);
+                wait_step(std::integral_constant<int, 0>{}, af[u & 1]);
             }
+            const AStep &cur = af[u & 1];
 #pragma unroll
             for (int nr = 0; nr < NRW; ++nr)
 #pragma unroll
@@ -229,7 +315,20 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
                                                : scale_group_word<SVEC>(r.sbr[u / 4][nr], lane);
                     const int oa = SAM == 2 ? (u & 1) * 2 : (u & 3);
                     const uint32_t sar = SAM == 2 ? r.sap[u / 2][mg] >> (8 * (mg & 1)) : saw[u / 4][mg];
-                    acc[nr][mg] = mma_sel(ob, oa, r.b[u][nr], af[u & 1][mg], acc[nr][mg], (int)sbr, (int)sar);
+                    const v4i bf = BST ? bst[BST ? u : 0][nr] : r.b[BST ? 0 : u][nr];
+                    if constexpr (AW == 4) {
+                        acc[nr][mg] = mma_sel(ob, oa, bf, cur.x[0][mg], acc[nr][mg], (int)sbr, (int)sar);
+                    } else {
+                        v8i a;
+                        if constexpr (AW == 8) {
+                            const v4i lo = cur.x[0][mg], hi = cur.x[1][mg];
+                            a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        } else {
+                            const v2u p0 = cur.y[0][mg], p1 = cur.y[1][mg], p2 = cur.y[2][mg];
+                            a = v8i{(int)p0[0], (int)p0[1], (int)p1[0], (int)p1[1], (int)p2[0], (int)p2[1], 0, 0};
+                        }
+                        acc[nr][mg] = mma_sel_wide<kFmtHw[AFMT]>(ob, oa, bf, a, acc[nr][mg], (int)sbr, (int)sar);
+                    }
                 }
         });
     };
@@ -299,40 +398,57 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
         }
 }
 
-template <int MG, int NRW, int U, int NS, bool BPACK>
+template <int MG, int NRW, int U, int NS, bool BPACK, int AFMT>
 static void launch_rows(const GemmArgs &g, int grid, hipStream_t s)
 {
-    // A-scale source: packed words, 16-byte aligned row groups staged in LDS,
-    // or per-wave byte loads; B scales: 16-byte groups when aligned
+    // A-scale source: packed words (FP4 A), 16-byte aligned row groups
+    // staged in LDS, or per-wave byte loads; B scales: 16-byte groups when
+    // aligned
     if constexpr (BPACK) {
-        if (g.sa_packed)
-            hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, true, true, 2>), dim3(grid), dim3(256), 0, s, g);
-        else if (g.sa16)
-            hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, true, true, 0>), dim3(grid), dim3(256), 0, s, g);
+        if constexpr (AFMT == 0) {
+            if (g.sa_packed) {
+                hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, true, true, 2, 0>), dim3(grid), dim3(256), 0, s, g);
+                return;
+            }
+        }
+        if (g.sa16)
+            hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, true, true, 0, AFMT>), dim3(grid), dim3(256), 0, s, g);
         else
-            hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, true, true, 1>), dim3(grid), dim3(256), 0, s, g);
+            hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, true, true, 1, AFMT>), dim3(grid), dim3(256), 0, s, g);
     } else {
         if (g.sa16) {
             if (g.sb16)
-                hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, false, true, 0>), dim3(grid), dim3(256), 0, s, g);
+                hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, false, true, 0, AFMT>), dim3(grid), dim3(256), 0, s, g);
             else
-                hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, false, false, 0>), dim3(grid), dim3(256), 0, s, g);
+                hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, false, false, 0, AFMT>), dim3(grid), dim3(256), 0, s,
+                                   g);
         } else {
             if (g.sb16)
-                hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, false, true, 1>), dim3(grid), dim3(256), 0, s, g);
+                hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, false, true, 1, AFMT>), dim3(grid), dim3(256), 0, s, g);
             else
-                hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, false, false, 1>), dim3(grid), dim3(256), 0, s, g);
+                hipLaunchKernelGGL((mx_rows_kernel<MG, NRW, U, NS, false, false, 1, AFMT>), dim3(grid), dim3(256), 0, s,
+                                   g);
         }
     }
 }
 
-#define MX_ROWS(MG, NRW, U, NS)                                                                 \
-    {MG, NRW, U, NS, launch_rows<MG, NRW, U, NS, false>, launch_rows<MG, NRW, U, NS, true>, \
-     "rows_m" #MG "x16_n4x" #NRW "x16_u" #U "_r" #NS}
+// Ring depth per A format: four slots, three for a wider A of 48 or 64 rows
+// (A's 32-slot rows, B and the A scales then fill 123-147 KiB of LDS).
+#define MX_ROWS(MG, NRW, U, NSW)                                                                               \
+    {MG, NRW, U,                                                                                             \
+     {launch_rows<MG, NRW, U, 4, false, 0>, launch_rows<MG, NRW, U, NSW, false, 1>,                          \
+      launch_rows<MG, NRW, U, NSW, false, 2>, launch_rows<MG, NRW, U, NSW, false, 3>,                        \
+      launch_rows<MG, NRW, U, NSW, false, 4>},                                                               \
+     {launch_rows<MG, NRW, U, 4, true, 0>, launch_rows<MG, NRW, U, NSW, true, 1>,                            \
+      launch_rows<MG, NRW, U, NSW, true, 2>, launch_rows<MG, NRW, U, NSW, true, 3>,                          \
+      launch_rows<MG, NRW, U, NSW, true, 4>},                                                                \
+     {"rows_m" #MG "x16_n4x" #NRW "x16_u" #U "_r4", "rows_fp8_m" #MG "x16_n4x" #NRW "x16_u" #U "_r" #NSW,  \
+      "rows_bf8_m" #MG "x16_n4x" #NRW "x16_u" #U "_r" #NSW, "rows_fp6_m" #MG "x16_n4x" #NRW "x16_u" #U "_r" #NSW, \
+      "rows_fp6_m" #MG "x16_n4x" #NRW "x16_u" #U "_r" #NSW}}
 const RowsKernel *rows_kernels(int *count)
 {
     static const RowsKernel table[] = {
-        MX_ROWS(2, 1, 4, 4), MX_ROWS(3, 1, 4, 4), MX_ROWS(4, 1, 4, 4),
+        MX_ROWS(2, 1, 4, 4), MX_ROWS(3, 1, 4, 3), MX_ROWS(4, 1, 4, 3),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

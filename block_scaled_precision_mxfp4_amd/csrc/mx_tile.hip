@@ -113,11 +113,14 @@ __device__ __forceinline__ void store_whole_tile_staged(uint16_t *D, int64_t ldd
     }
 }
 
-// AFMT: A's format (0 FP4; 1 FP8 E4M3 or 2 BF8 E5M2; B is FP4).  An 8-bit
-// A row holds 256 bytes per 256-K stage: the stage is two FP4-shaped A
-// tiles, one per 128-K step (rows of 128 bytes, the same swizzle), and a
-// lane's operand for step ks is chunks g and g+4 of that step's tile -- the
-// two 16-element runs K 16g.. and 64+16g.. the 8-bit instruction reads.
+// AFMT: A's format (0 FP4; 1 FP8 E4M3 or 2 BF8 E5M2; 3 FP6 E2M3 or 4 FP6
+// E3M2 in the padded layout of mx_fp6.hip; B is FP4).  An 8-bit A row holds
+// 256 bytes per 256-K stage: the stage is two FP4-shaped A tiles, one per
+// 128-K step (rows of 128 bytes, the same swizzle), and a lane's operand for
+// step ks is chunks g and g+4 of that step's tile -- the two 16-element runs
+// K 16g.. and 64+16g.. the 8-bit instruction reads.  A padded FP6 row has the
+// same shape, with K-block g's 24 bytes in those two chunks (the first 8
+// bytes of chunk g+4), so the same reads feed the FP6 instruction.
 // PERSIST (a tile with one workgroup per CU; launched for 256 x 256 with
 // packed B and A scales): one workgroup per CU walks its tiles in the order
 // the plain grid runs them (hardware id blockIdx + i * grid, through the same
@@ -143,7 +146,7 @@ __device__ __forceinline__ void store_whole_tile_staged(uint16_t *D, int64_t ldd
 template <int BM, int BN, int WM, int WN, int BLAY, bool SVEC, bool SAPACK, int AFMT = 0, bool PERSIST = false>
 __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
 {
-    static_assert(AFMT == 0 || ((AFMT == 1 || AFMT == 2) && !SAPACK), "8-bit A with row-major A scales");
+    static_assert(AFMT == 0 || (AFMT >= 1 && AFMT <= 4 && !SAPACK), "8-bit or padded FP6 A with row-major A scales");
     static_assert(BLAY >= 0 && BLAY <= 3 && (AFMT == 0 || BLAY <= 1), "B layouts");
     constexpr bool BPACK = BLAY == 1;                 // packed codes
     constexpr bool BKN = BLAY >= 2;                   // MN-major codes
@@ -309,8 +312,10 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
             if constexpr (AREG > 1)
                 off += (uint32_t)(reg * 128);
             if constexpr (!SVEC) {  // K tail: blocks at or past the chunk end read as zero
+                // (the K-block chunk kc of the step's tile holds: 8-bit A
+                // chunk kc covers block kc / 2, padded FP6 block kc % 4)
                 const int kc = h ? kc1 : kc0;
-                off = kb_s + (AREG == 1 ? kc : 4 * reg + kc / 2) < kb_end ? off : kOOB;
+                off = kb_s + (AREG == 1 ? kc : 4 * reg + (AFMT >= 3 ? kc & 3 : kc / 2)) < kb_end ? off : kOOB;
             }
             load16_to_lds(ra, (lds_void *)(dst_a + c * 1024), off);
         }
@@ -735,8 +740,10 @@ static void launch_tile_a8(const GemmArgs &g, int grid, hipStream_t s)
 
 #define MX_TILE_A8(BM, BN, WM, WN, OCC)                                                                    \
     {BM, BN, OCC,                                                                                          \
-     {launch_tile_a8<BM, BN, WM, WN, false, 1>, launch_tile_a8<BM, BN, WM, WN, false, 2>},                 \
-     {launch_tile_a8<BM, BN, WM, WN, true, 1>, launch_tile_a8<BM, BN, WM, WN, true, 2>}, "tile_a8_" #BM "x" #BN}
+     {launch_tile_a8<BM, BN, WM, WN, false, 1>, launch_tile_a8<BM, BN, WM, WN, false, 2>,                  \
+      launch_tile_a8<BM, BN, WM, WN, false, 3>, launch_tile_a8<BM, BN, WM, WN, false, 4>},                 \
+     {launch_tile_a8<BM, BN, WM, WN, true, 1>, launch_tile_a8<BM, BN, WM, WN, true, 2>,                    \
+      launch_tile_a8<BM, BN, WM, WN, true, 3>, launch_tile_a8<BM, BN, WM, WN, true, 4>}, "tile_a8_" #BM "x" #BN}
 
 const TileKernelA8 *tile_kernels_a8(int *count)
 {

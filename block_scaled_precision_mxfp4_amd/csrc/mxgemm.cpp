@@ -81,7 +81,7 @@ constexpr int kMinSkinnyChunk = 64;
 constexpr double kCuL2 = 64.0 * 2.4e9;
 
 Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool tiled_only = false,
-              int force_nr = 0)
+              int force_nr = 0, int a_format = MXGEMM_FMT_FP4)
 {
     const int KB = K / 32;
     if (num_cu <= 0)
@@ -133,7 +133,7 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool
         best.tiles_m = 1;
         best.tiles_n = tiles;
         best.grid = (int64_t)tiles * eff;
-        best.name = rows[idx].name;
+        best.name = rows[idx].name[a_format];
         const size_t part = (size_t)rows_wg * mg * 16 * 4;
         best.counter_bytes = best.split > 1 ? (size_t)tiles * 4 : 0;
         best.ws_bytes = best.split > 1 ? (size_t)tiles * best.split * part : 0;
@@ -236,8 +236,9 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool
 // Tiled plan for 8-bit A (family 3): the cost model of the FP4 tiles with
 // the matrix time doubled (the 8-bit scaled instruction runs at half the
 // FP4 rate, "CDNA4 dense MFMA builtins", "Instruction throughput") and A's
-// bytes doubled.
-Plan plan_a8(int M, int N, int K, int split_req, int num_cu)
+// bytes doubled.  FP6 A in its padded 8-bit-sized layout (fp6 = true)
+// keeps the FP4 matrix rate (the same table gives FP6 the FP4 cycles).
+Plan plan_a8(int M, int N, int K, int split_req, int num_cu, bool fp6 = false)
 {
     const int KB = K / 32;
     if (num_cu <= 0)
@@ -258,7 +259,7 @@ Plan plan_a8(int M, int N, int K, int split_req, int num_cu)
                 continue;
             const int64_t wgs = tiles * eff;
             const double rounds = (double)((wgs + (int64_t)num_cu * tk.occupancy - 1) / ((int64_t)num_cu * tk.occupancy));
-            const double t_math = 2.0 * 2.0 * tk.bm * tk.bn * 256.0 * tk.occupancy / (kCuFlops * kMatrixFraction);
+            const double t_math = (fp6 ? 1.0 : 2.0) * 2.0 * tk.bm * tk.bn * 256.0 * tk.occupancy / (kCuFlops * kMatrixFraction);
             const double t_load = (double)(2 * tk.bm + tk.bn) * 128.0 * tk.occupancy / kCuLoadRate;
             double t = rounds * (per / 8) * std::max(t_math, t_load);
             if (eff > 1)
@@ -286,21 +287,26 @@ Plan plan_a8(int M, int N, int K, int split_req, int num_cu)
 }
 
 // The plan mxgemm_run follows for these options: FP4 A by the cost model
-// (the tiled kernel only in the bf16-atomic mode); 8-bit A with M > 16 on
-// the 8-bit tiles; any other wider A on the skinny kernel per 16 rows.
+// (the tiled kernel only in the bf16-atomic mode); a wider A with
+// 16 < M <= 64 on the rows kernel (FP6: an even K-block count); otherwise
+// with M > 16 on the 8-bit tiles, FP6 re-laid first; any other wider A on
+// the skinny kernel per 16 rows.
 Plan plan_run(int M, int N, int K, const mxgemm_strides &s, int split_k, int num_cu)
 {
     // an MN-major B is read through the tiled kernel's transposed LDS loads
     if (s.a_format == MXGEMM_FMT_FP4)
         return plan_for(M, N, K, s.b_packed, split_k, num_cu,
                         s.split_mode == MXGEMM_SPLIT_BF16_ATOMIC || s.b_layout == MXGEMM_B_KN);
+    const bool fp6 = s.a_format == MXGEMM_FMT_FP6_E2M3 || s.a_format == MXGEMM_FMT_FP6_E3M2;
+    if (M > 16 && M <= 64 && (!fp6 || (K / 32) % 2 == 0))
+        return plan_for(M, N, K, s.b_packed, split_k, num_cu, false, 0, s.a_format);
     if ((s.a_format == MXGEMM_FMT_FP8_E4M3 || s.a_format == MXGEMM_FMT_FP8_E5M2) && M > 16)
         return plan_a8(M, N, K, split_k, num_cu);
-    // FP6 with M > 16: A converted exactly to FP8 (rows of K bytes), then the
-    // 8-bit tiles, while a 256-row tile of the converted A stays below 2^31 bytes
-    if ((s.a_format == MXGEMM_FMT_FP6_E2M3 || s.a_format == MXGEMM_FMT_FP6_E3M2) && M > 16 &&
-        (int64_t)256 * K < ((int64_t)1 << 31))
-        return plan_a8(M, N, K, split_k, num_cu);
+    // FP6 with M > 16: A re-laid into 32-byte blocks (rows of K bytes rounded
+    // up to 128), then the 8-bit tiles with the FP6 instruction, while a
+    // 256-row tile of the re-laid A stays below 2^31 bytes
+    if (fp6 && M > 16 && (int64_t)256 * mx::fp6_pad_pitch(K) < ((int64_t)1 << 31))
+        return plan_a8(M, N, K, split_k, num_cu, true);
     return plan_for(std::min(M, 16), N, K, s.b_packed, split_k, num_cu, false, 1);
 }
 
@@ -376,7 +382,7 @@ struct DeviceBuffer {
 };
 struct StreamBuffers {
     DeviceBuffer partials, counters;
-    DeviceBuffer conv;  // FP6 A converted to FP8 (M x K bytes)
+    DeviceBuffer conv;  // FP6 A re-laid in 32-byte blocks (M x fp6_pad_pitch(K) bytes)
 };
 std::map<std::pair<int, hipStream_t>, StreamBuffers> g_ws;
 
@@ -433,7 +439,7 @@ mxgemm_status get_split_buffers(hipStream_t stream, size_t counter_need, size_t 
     return MXGEMM_OK;
 }
 
-// The per-stream buffer for FP6 A converted to FP8.
+// The per-stream buffer for FP6 A re-laid for the 8-bit tiles.
 mxgemm_status get_conv_buffer(hipStream_t stream, size_t need, void **conv)
 {
     int dev = 0;
@@ -679,9 +685,9 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     if (st != MXGEMM_OK)
         return st;
     Plan p = plan_run(M, N, K, s, split_k, d->num_cu);
-    // a wider A not on the 8-bit tiles: the skinny kernel (one 16-row
-    // group, nr 1), one launch per 16 rows of A
-    const bool wide = s.a_format != MXGEMM_FMT_FP4 && p.family != 3;
+    // a wider A on the skinny kernel (one 16-row group, nr 1): one launch
+    // per 16 rows of A
+    const bool wide = s.a_format != MXGEMM_FMT_FP4 && p.family == 1;
 
     GemmArgs g;
     std::memset(&g, 0, sizeof g);
@@ -722,9 +728,9 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     g.sb16 = !s.b_packed && aligned(scaleB, 16) && s.ldsb % 16 == 0 && KB % 16 == 0;
     g.group_m = 4;
 
-    // FP6 A on the 8-bit tiles is first copied to FP8 (M x K bytes)
+    // FP6 A on the 8-bit tiles is first re-laid into 32-byte blocks
     const bool fp6_conv = p.family == 3 && (s.a_format == MXGEMM_FMT_FP6_E2M3 || s.a_format == MXGEMM_FMT_FP6_E3M2);
-    const size_t conv_bytes = fp6_conv ? (size_t)M * (size_t)K : 0;
+    const size_t conv_bytes = fp6_conv ? (size_t)M * (size_t)mx::fp6_pad_pitch(K) : 0;
     // the allocation-free form: counters, partials and the FP6 copy come
     // from the device's fixed scratch (counters first, then partials, then
     // the copy); a plan that needs more is refused before any launch
@@ -791,9 +797,8 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     } else if (p.family == 3) {
         int n = 0;
         const mx::TileKernelA8 &k = mx::tile_kernels_a8(&n)[p.index];
-        int fmt8 = s.a_format;
         if (fp6_conv) {
-            // exact FP6 -> FP8 copy of A (E2M3 -> E4M3, E3M2 -> E5M2), same scales
+            // FP6 A re-laid into the 8-bit operand shape, codes and scales unchanged
             void *conv = nullptr;
             if (noalloc) {
                 conv = scr + mx::kScratchCounterBytes + scr_part;
@@ -802,12 +807,11 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
                 if (st != MXGEMM_OK)
                     return st;
             }
-            mx::launch_fp6_to_fp8(s.a_format, (const uint8_t *)A, lda_bytes, (uint8_t *)conv, M, K, stream);
+            mx::launch_fp6_pad((const uint8_t *)A, lda_bytes, (uint8_t *)conv, M, K, stream);
             g.A = (const uint8_t *)conv;
-            g.lda_b = K;
-            fmt8 = s.a_format == MXGEMM_FMT_FP6_E2M3 ? MXGEMM_FMT_FP8_E4M3 : MXGEMM_FMT_FP8_E5M2;
+            g.lda_b = mx::fp6_pad_pitch(K);
         }
-        (s.b_packed ? k.packed : k.plain)[fmt8 - 1](g, (int)p.grid, stream);
+        (s.b_packed ? k.packed : k.plain)[s.a_format - 1](g, (int)p.grid, stream);
     } else if (p.family == 0) {
         int n = 0;
         const mx::TileKernel &k = mx::tile_kernels(&n)[p.index];
@@ -841,7 +845,7 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     } else {
         int n = 0;
         const mx::RowsKernel &k = mx::rows_kernels(&n)[p.index];
-        (s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
+        (s.b_packed ? k.packed : k.plain)[s.a_format](g, (int)p.grid, stream);
     }
     if (hipGetLastError() != hipSuccess)
         return MXGEMM_ERR_HIP;

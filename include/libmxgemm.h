@@ -89,17 +89,21 @@ const char *mxgemm_status_string(mxgemm_status status);
  *              A's format; the byte pitch lda*w/8 must be a whole multiple of
  *              16 (of 8 for the FP6 formats, whose dense rows are 24 bytes
  *              per 32 elements).  Kernels: for M <= 16 the skinny kernel
- *              (the speed of the FP4 case); for M > 16 the 8-bit formats
- *              run on the tiled kernel with 8-bit A tiles.  FP6 A with
- *              M > 16 is first copied, exactly, to FP8 (E2M3 to E4M3, E3M2
- *              to E5M2: every FP6 value is an FP8 value, scales unchanged)
- *              into a library-owned M x K-byte buffer per (device, stream),
- *              allocated on first use like the split-K buffers and freed by
- *              mxgemm_release_workspaces, then runs on the same 8-bit tiles
- *              (for K >= 2^23, once per 16 rows on the skinny kernel
- *              instead).  Needs sa_packed = 0 and split_mode =
- *              MXGEMM_SPLIT_FP32 (else MXGEMM_ERR_INVALID_ARG); size a caller
- *              workspace with mxgemm_query_ex.
+ *              and for 16 < M <= 64 the rows kernel (both at the speed of
+ *              the FP4 case; FP6 on the rows kernel needs an even K/32);
+ *              otherwise, for M > 16, the 8-bit formats run on the tiled
+ *              kernel with 8-bit A tiles, and FP6 A is first re-laid,
+ *              codes unchanged, into
+ *              32-byte slots per 32-element block (rows of K bytes rounded
+ *              up to 128) in a library-owned buffer per (device, stream),
+ *              allocated on first use like the split-K buffers and freed
+ *              by mxgemm_release_workspaces, then runs on the same tiles
+ *              with the FP6 operand format of the scaled instruction, at
+ *              its FP4 rate (when 256 re-laid rows reach 2^31 bytes, once
+ *              per 16 rows on the skinny kernel instead).  Needs
+ *              sa_packed = 0 and split_mode = MXGEMM_SPLIT_FP32 (else
+ *              MXGEMM_ERR_INVALID_ARG); size a caller workspace with
+ *              mxgemm_query_ex.
  *   c_f32      C is float32 instead of bf16.  The README's "C / bias" note
  *              says aiter documents its bias operand as f32; with c_f32 = 1
  *              the epilogue reads that type (D stays bf16; one rounding of

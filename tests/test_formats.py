@@ -120,15 +120,17 @@ def test_fp8_tiled_large_sampled():
     assert_parity(d[rows], ref, mag, "tiled 2048x2048x4096")
 
 
-# FP6 A with M > 16: A converted exactly to FP8 (E2M3 -> E4M3, E3M2 -> E5M2),
-# then the tiled kernel with 8-bit A tiles
+# FP6 A with M > 16: A re-laid into 32-byte blocks (codes unchanged), then the
+# tiled kernel's 8-bit A tiles with the FP6 operand format
 @pytest.mark.parametrize("fmt", [mx.FMT_FP6_E2M3, mx.FMT_FP6_E3M2], ids=lambda f: NAMES[f])
-def test_fp6_all_codes_through_the_8bit_tiles(fmt):
+@pytest.mark.parametrize("M,kernel", [(32, 2), (80, 3)], ids=["rows", "tiles"])
+def test_fp6_all_codes_through_the_wide_kernels(fmt, M, kernel):
     """B = I (FP4 1.0 on the diagonal, unit scales): D is A dequantized, and
     every FP6 value has at most 4 significant bits, so D must equal the
-    oracle's bf16 result bit for bit.  The 32 rows hold all 64 codes, each
-    row a different rotation, with varied scales."""
-    M, K = 32, 64
+    oracle's bf16 result bit for bit.  The rows hold all 64 codes, each row
+    a different rotation, with varied scales: 32 rows on the rows kernel
+    (dense FP6 staged in LDS), 80 on the 8-bit tiles (re-laid FP6)."""
+    K = 64
     N = K
     codes = np.array([[(r + k) % 64 for k in range(K)] for r in range(M)], dtype=np.uint64)
     A = np.zeros((M, K * 6 // 8), dtype=np.uint8)
@@ -145,8 +147,8 @@ def test_fp6_all_codes_through_the_8bit_tiles(fmt):
     SB = np.full((N, K // 32), 127, dtype=np.uint8)
     p = dict(M=M, N=N, K=K, A=A, SA=SA, B=B, SB=SB, alpha=1.0, beta=0.0, C=None, a_fmt=fmt)
     st = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32, a_format=fmt)
-    assert mx.mxgemm_plan_ex(M, N, K, st, -1, 256)["kernel"] == 3
-    say("case fp6 identity", NAMES[fmt])
+    assert mx.mxgemm_plan_ex(M, N, K, st, -1, 256)["kernel"] == kernel
+    say("case fp6 identity", NAMES[fmt], M)
     d = gemm_gpu(p)
     _, _, dref = oracle_ref(p)
     same = (d == dref) | (((d | dref) & 0x7FFF) == 0)  # +0 and -0 are equal
@@ -154,7 +156,9 @@ def test_fp6_all_codes_through_the_8bit_tiles(fmt):
 
 
 FP6_TILED = [
-    (300, 520, 1056, -1, False, "bf16"),  # K tail, C
+    (300, 520, 1056, -1, False, "bf16"),  # K tail (one block past 128), C
+    (40, 96, 608, -1, False, None),       # small tile, K tail of three blocks
+    (130, 256, 2080, 2, False, "f32"),    # split-K, f32 C, K tail
     (2048, 2048, 4096, 1, True, None),    # packed B, sampled
 ]
 
@@ -177,8 +181,7 @@ def test_fp6_tiled_matches_oracle(case, fmt):
 
 
 def test_fp6_conversion_buffers_are_per_stream():
-    """FP6 A with M > 16 is copied to FP8 in a buffer owned per (device,
-    stream).  Two problems of different sizes and formats on two streams,
+    """FP6 A with M > 16 is re-laid in a buffer owned per (device, stream).  Two problems of different sizes and formats on two streams,
     each launched twice with no synchronization in between, must both match
     the oracle."""
     from mxgpu import dev_u8, host_bits

@@ -197,7 +197,7 @@ def test_overflow_to_infinity():
 
 
 @pytest.mark.parametrize("fmt", [1, 2], ids=["e4m3", "e5m2"])
-@pytest.mark.parametrize("M", [1, 8, 300])
+@pytest.mark.parametrize("M", [1, 8, 40, 300])
 def test_fp8_nan_and_inf_codes(fmt, M):
     """A in FP8 E4M3 (NaN codes 0x7F, 0xFF) or BF8 E5M2 (+-inf 0x7C, 0xFC and
     NaN 0x7D, 0xFE) mixed into otherwise finite codes: NaN and signed
