@@ -91,11 +91,10 @@ void launch_skinny_bf16a(int nr, bool b_packed, const GemmArgs &g, int grid, hip
 
 // Skinny kernel for 16 < M <= 64 with the waves splitting B's rows and A
 // staged once per workgroup in LDS: mg 16-row groups of A, nrw 16-row groups
-// of B per wave, u 128-K steps per batch; launchers and names per A format
-// (index a_format - 0: FP4, FP8 E4M3, BF8 E5M2, FP6 E2M3, FP6 E3M2).
-// index: mg - 2.
+// of B per wave; launchers and names per A format (index a_format: FP4, FP8
+// E4M3, BF8 E5M2, FP6 E2M3, FP6 E3M2).  index: mg - 2.
 struct RowsKernel {
-    int mg, nrw, u;
+    int mg, nrw;
     LaunchFn plain[5], packed[5];
     const char *name[5];
 };

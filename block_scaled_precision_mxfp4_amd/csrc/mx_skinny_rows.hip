@@ -45,7 +45,7 @@ namespace mx {
 template <int MG, int NRW, int U, int NS, bool BPACK, bool SVEC, int SAM, int AFMT>
 __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
 {
-    static_assert(U == 4 && NS >= 2, "one 4-step scale group per batch");
+    static_assert(U % 4 == 0 && NS >= 2, "whole 4-step scale groups per batch");
     static_assert(AFMT == 0 || SAM != 2, "wider A with row-major A scales");
     constexpr int G = U / 4;               // 4-step scale groups per batch
     constexpr int RW = 16 * NRW;           // B rows per wave
@@ -55,6 +55,7 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
     constexpr int AKB = 4 * AW;            // bytes of one A K-block
     constexpr int ACU = U * AW;            // 16-byte chunks of an A row per batch
     constexpr int CPR = ACU <= 16 ? 16 : 32;  // LDS slots per A row (FP6: 24 of 32 used)
+    static_assert(ACU <= CPR, "a batch's A row fits its LDS slots");
     constexpr int RPI = 64 / CPR;          // A rows per 1 KiB load instruction
     constexpr int A_BYTES = AR * CPR * 16;
     static_assert(A_BYTES % 4096 == 0, "the A stage splits evenly over the four waves");
@@ -243,12 +244,13 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
         // (row nr*16 + lane%16, chunk 4u + lane/16 at slot chunk ^ (row % 16))
         v4i bst[BST ? U : 1][NRW];
         if constexpr (BST) {
+            const uint32_t bslot = b_base + (uint32_t)(SLOT * B_SLOT);
             static_for<U>([&](auto uc) {
                 constexpr int u = decltype(uc)::value;
-                const uint32_t a = b_base + (uint32_t)((((u * 4) + (lane >> 4)) ^ (lane & 15)) * 16);
+                const uint32_t a = bslot + (uint32_t)((((u * 4) + (lane >> 4)) ^ (lane & 15)) * 16);
                 static_for<NRW>([&](auto nc) {
                     constexpr int nr = decltype(nc)::value;
-                    bst[u][nr] = lds_read16<SLOT * B_SLOT + nr * 16 * CPB * 16>(a);
+                    bst[u][nr] = lds_read16<nr * 16 * CPB * 16>(a);
                 });
             });
         }
@@ -432,23 +434,24 @@ static void launch_rows(const GemmArgs &g, int grid, hipStream_t s)
     }
 }
 
-// Ring depth per A format: four slots, three for a wider A of 48 or 64 rows
-// (A's 32-slot rows, B and the A scales then fill 123-147 KiB of LDS).
-#define MX_ROWS(MG, NRW, U, NSW)                                                                               \
-    {MG, NRW, U,                                                                                             \
-     {launch_rows<MG, NRW, U, 4, false, 0>, launch_rows<MG, NRW, U, NSW, false, 1>,                          \
-      launch_rows<MG, NRW, U, NSW, false, 2>, launch_rows<MG, NRW, U, NSW, false, 3>,                        \
-      launch_rows<MG, NRW, U, NSW, false, 4>},                                                               \
-     {launch_rows<MG, NRW, U, 4, true, 0>, launch_rows<MG, NRW, U, NSW, true, 1>,                            \
-      launch_rows<MG, NRW, U, NSW, true, 2>, launch_rows<MG, NRW, U, NSW, true, 3>,                          \
-      launch_rows<MG, NRW, U, NSW, true, 4>},                                                                \
-     {"rows_m" #MG "x16_n4x" #NRW "x16_u" #U "_r4", "rows_fp8_m" #MG "x16_n4x" #NRW "x16_u" #U "_r" #NSW,  \
-      "rows_bf8_m" #MG "x16_n4x" #NRW "x16_u" #U "_r" #NSW, "rows_fp6_m" #MG "x16_n4x" #NRW "x16_u" #U "_r" #NSW, \
-      "rows_fp6_m" #MG "x16_n4x" #NRW "x16_u" #U "_r" #NSW}}
+// Batch and ring shape per A format: FP4 A takes U4 steps per batch in NS4
+// slots; a wider A four steps per batch in NSW slots (A's 32-slot rows, B
+// and the A scales then fill 123-147 KiB of LDS).
+#define MX_ROWS(MG, NRW, U4, NS4, NSW)                                                                            \
+    {MG, NRW,                                                                                                  \
+     {launch_rows<MG, NRW, U4, NS4, false, 0>, launch_rows<MG, NRW, 4, NSW, false, 1>,                         \
+      launch_rows<MG, NRW, 4, NSW, false, 2>, launch_rows<MG, NRW, 4, NSW, false, 3>,                          \
+      launch_rows<MG, NRW, 4, NSW, false, 4>},                                                                 \
+     {launch_rows<MG, NRW, U4, NS4, true, 0>, launch_rows<MG, NRW, 4, NSW, true, 1>,                           \
+      launch_rows<MG, NRW, 4, NSW, true, 2>, launch_rows<MG, NRW, 4, NSW, true, 3>,                            \
+      launch_rows<MG, NRW, 4, NSW, true, 4>},                                                                  \
+     {"rows_m" #MG "x16_n4x" #NRW "x16_u" #U4 "_r" #NS4, "rows_fp8_m" #MG "x16_n4x" #NRW "x16_u4_r" #NSW,      \
+      "rows_bf8_m" #MG "x16_n4x" #NRW "x16_u4_r" #NSW, "rows_fp6_m" #MG "x16_n4x" #NRW "x16_u4_r" #NSW,       \
+      "rows_fp6_m" #MG "x16_n4x" #NRW "x16_u4_r" #NSW}}
 const RowsKernel *rows_kernels(int *count)
 {
     static const RowsKernel table[] = {
-        MX_ROWS(2, 1, 4, 4), MX_ROWS(3, 1, 4, 3), MX_ROWS(4, 1, 4, 3),
+        MX_ROWS(2, 1, 4, 4, 4), MX_ROWS(3, 1, 4, 4, 3), MX_ROWS(4, 1, 4, 4, 3),
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;
