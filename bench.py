@@ -267,6 +267,7 @@ def time_f16(steps, warmup, soak_ms=0.0, M=8192, N=8192, K=8192):
 
 
 FORMAT_NAMES = {0: "fp4", 1: "fp8_e4m3", 2: "fp8_e5m2", 3: "fp6_e2m3", 4: "fp6_e3m2"}
+FORMAT_CODES = {v: k for k, v in FORMAT_NAMES.items()}
 # mixed-format lines: (workload, A format) -- decode and a small batch with
 # FP8 and FP6 activations against FP4 weights
 MIXED = [("gemv_1x8192x8192", 1), ("gemv_1x8192x8192", 3), ("skinny_64x7168x16384", 1), ("square_8192", 1),
@@ -537,6 +538,8 @@ def main():
     ap.add_argument("--b-layout", choices=("nk", "kn"), default="nk",
                     help="B of --workload stored K-major (nk, the default) or MN-major (kn, scales packed)")
     ap.add_argument("--packed", action="store_true", help="pre-shuffle B of --workload (and A scales if M > 64)")
+    ap.add_argument("--a-format", choices=sorted(FORMAT_CODES), default="fp4",
+                    help="A of --workload in this format (profiling runs of the mixed-format lines)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch steps one by one (counter runs)")
     ap.add_argument("--soak-ms", type=float, default=500.0,
@@ -579,7 +582,8 @@ def main():
 
     head = time_workload(args.workload, args.steps, args.warmup, split_k=args.split_k, eager=args.eager,
                          soak_ms=args.soak_ms, b_layout=int(args.b_layout == "kn"),
-                         packed=True if (args.b_layout == "kn" or args.packed) else None)
+                         packed=True if (args.b_layout == "kn" or args.packed) else None,
+                         a_fmt=FORMAT_CODES[args.a_format])
     others = []
     if not args.only:
         for name in inputs.WORKLOADS:
@@ -618,11 +622,11 @@ def main():
             if r["M"] > 64:  # a contraction: the matrix peak of A's format (FP6 runs at the FP4 rate)
                 peak = PEAK_FP8_TFLOPS if fmt in (1, 2) else PEAK_MXFP4_TFLOPS
                 roof = {"bound": "mfma", "achieved": r["tflops"], "peak": peak, "unit": "TFLOP/s",
-                        "frac": r["tflops"] / peak, "traffic": None}
+                        "frac": r["tflops"] / peak, "traffic": measured_traffic(name + "_" + FORMAT_NAMES[fmt])}
                 value, unit = r["tflops"], "TFLOP/s"
             else:
                 roof = {"bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": r["gbs"] / PEAK_HBM_GBS, "traffic": None}
+                        "frac": r["gbs"] / PEAK_HBM_GBS, "traffic": measured_traffic(name + "_" + FORMAT_NAMES[fmt])}
                 value, unit = r["gbs"], "GB/s"
             mixed.append({"workload": name, "a_format": FORMAT_NAMES[fmt], "us_per_step": r["us_per_step"],
                           "value": value, "unit": unit, "tflops": r["tflops"],
