@@ -93,9 +93,9 @@ const char *mxgemm_status_string(mxgemm_status status);
  *              the FP4 case; FP6 on the rows kernel needs an even K/32);
  *              otherwise, for M > 16, the 8-bit formats run on the tiled
  *              kernel with 8-bit A tiles, and FP6 A is first re-laid,
- *              codes unchanged, into
- *              32-byte slots per 32-element block (rows of K bytes rounded
- *              up to 128) in a library-owned buffer per (device, stream),
+ *              codes unchanged, into 32-byte slots per 32-element block
+ *              (rows of K bytes rounded up to 128) in a library-owned
+ *              buffer per (device, stream),
  *              allocated on first use like the split-K buffers and freed
  *              by mxgemm_release_workspaces, then runs on the same tiles
  *              with the FP6 operand format of the scaled instruction, at
@@ -220,8 +220,9 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B,
  * array per GPU of MXGEMM_NOALLOC_SCRATCH_BYTES (32 MiB), which the library
  * holds from load until the process ends: the split-K arrival counters
  * (first 64 KiB: 4 bytes per output tile of a split plan), the split-K fp32
- * partials unless strides->workspace brings them, and the FP8 copy of an FP6
- * A with M > 16 (M*K bytes).  Same arguments, plans, kernels and results as
+ * partials unless strides->workspace brings them, and the re-laid copy of
+ * an FP6 A on the tiled kernel (M * K bytes, K rounded up to 128).  Same
+ * arguments, plans, kernels and results as
  * mxgemm_run, bit for bit.  Never calls hipMalloc or hipFree (the first call
  * on a device looks up that device's array once).  A plan that needs more
  * than the array holds returns MXGEMM_ERR_SCRATCH before any launch;
