@@ -69,6 +69,19 @@ def algorithmic_bytes(M, N, K, beta, a_bits=4):
     return b
 
 
+def workload_roofline(r):
+    """The roofline of one timed workload: its algorithmic flops against the
+    MXFP4 matrix peak where its arithmetic intensity is above the ridge point
+    (peak flops / 8 TB/s), else its algorithmic bytes against HBM; traffic
+    from the committed counter runs while they match the kernel sources."""
+    intensity = 2.0 * r["M"] * r["N"] * r["K"] / r["algorithmic_bytes"]
+    if intensity >= PEAK_MXFP4_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        return {"bound": "mfma", "achieved": r["tflops"], "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s",
+                "frac": r["tflops"] / PEAK_MXFP4_TFLOPS, "traffic": measured_traffic(r["workload"])}
+    return {"bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": r["gbs"] / PEAK_HBM_GBS, "traffic": measured_traffic(r["workload"])}
+
+
 def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soak_ms=0.0, a_fmt=0, b_layout=0,
                   packed=None):
     import numpy as np
@@ -686,8 +699,9 @@ def main():
         "b_layouts": layouts,
         "device": {"arch": head["arch"], "num_cu": head["num_cu"], "clock_hz": head["clock_hz"],
                    "derived_peak_tflops": head["peak_flops_device"] / 1e12},
-        "workloads": [{k: o[k] for k in ("workload", "kernel", "tile", "split_k", "us_per_step",
-                                         "tflops", "gbs", "copies", "timing")} for o in [head] + others],
+        "workloads": [dict({k: o[k] for k in ("workload", "kernel", "tile", "split_k", "us_per_step",
+                                              "tflops", "gbs", "copies", "timing")},
+                           roofline=workload_roofline(o)) for o in [head] + others],
     }
     skinny = next((o for o in others if o["workload"] == "skinny_64x7168x16384"), None)
     if skinny is not None:

@@ -5,12 +5,12 @@
 // quarter of K, and A is read from L2 once per 16*NR rows of B.  At M = 64
 // that A traffic equals the B stream itself.  Here the four waves of a
 // workgroup share one K chunk and own different rows of B (16*NRW each):
-// each 128-K step's A fragments are loaded once per workgroup into LDS with
-// whole-line direct-to-LDS loads (8 or 16 rows x the batch's bytes per
-// instruction, XOR-swizzled like the tiled kernel's row-major operands) and
-// read by all four waves, while each wave streams its own B rows into
-// registers.  A workgroup covers 4x more rows of B for the same A bytes, and
-// no cross-wave reduction is needed: each wave stores its own columns of D.
+// each batch's A rows are loaded once per workgroup into LDS with whole-line
+// direct-to-LDS loads (2 or 4 rows x the batch's bytes per instruction,
+// XOR-swizzled per 16-row group) and read by all four waves, while each wave
+// streams its own B rows.  A workgroup covers 4x more rows of B for the same
+// A bytes, and no cross-wave reduction is needed: each wave stores its own
+// columns of D.
 //
 // Batches of U 128-K steps rotate through a ring of LDS slots; one barrier
 // per batch hands a slot over.  A scales (row-major, 16-byte aligned rows)
