@@ -97,6 +97,10 @@ struct RowsKernel {
     int mg, nrw;
     LaunchFn plain[5], packed[5];
     const char *name[5];
+    // FP4 A, row-major B, a ring of two slots: two workgroups fit a CU's
+    // LDS, for grids with more workgroups than CUs
+    LaunchFn lean;
+    const char *lean_name;
 };
 const RowsKernel *rows_kernels(int *count);
 

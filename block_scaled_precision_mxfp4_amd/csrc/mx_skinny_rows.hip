@@ -436,7 +436,9 @@ static void launch_rows(const GemmArgs &g, int grid, hipStream_t s)
 
 // Batch and ring shape per A format: FP4 A takes U4 steps per batch in NS4
 // slots; a wider A four steps per batch in NSW slots (A's 32-slot rows, B
-// and the A scales then fill 123-147 KiB of LDS).
+// and the A scales then fill 123-147 KiB of LDS).  The lean entry (FP4 A,
+// row-major B, two slots: 66 KiB at four steps) lets two workgroups share a
+// CU when the grid has more workgroups than CUs.
 #define MX_ROWS(MG, NRW, U4, NS4, NSW)                                                                            \
     {MG, NRW,                                                                                                  \
      {launch_rows<MG, NRW, U4, NS4, false, 0>, launch_rows<MG, NRW, 4, NSW, false, 1>,                         \
@@ -447,7 +449,8 @@ static void launch_rows(const GemmArgs &g, int grid, hipStream_t s)
       launch_rows<MG, NRW, 4, NSW, true, 4>},                                                                  \
      {"rows_m" #MG "x16_n4x" #NRW "x16_u" #U4 "_r" #NS4, "rows_fp8_m" #MG "x16_n4x" #NRW "x16_u4_r" #NSW,      \
       "rows_bf8_m" #MG "x16_n4x" #NRW "x16_u4_r" #NSW, "rows_fp6_m" #MG "x16_n4x" #NRW "x16_u4_r" #NSW,       \
-      "rows_fp6_m" #MG "x16_n4x" #NRW "x16_u4_r" #NSW}}
+      "rows_fp6_m" #MG "x16_n4x" #NRW "x16_u4_r" #NSW},                                                   \
+     launch_rows<MG, NRW, U4, 2, false, 0>, "rows_m" #MG "x16_n4x" #NRW "x16_u" #U4 "_r2"}
 const RowsKernel *rows_kernels(int *count)
 {
     static const RowsKernel table[] = {

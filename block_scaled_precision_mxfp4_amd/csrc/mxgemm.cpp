@@ -40,6 +40,7 @@ struct Plan {
     int kb_per_split = 0;
     int tiles_m = 0, tiles_n = 0;
     int64_t grid = 0;
+    bool lean = false;  // rows kernel: the two-slot ring (two workgroups per CU)
     size_t counter_bytes = 0;
     size_t ws_bytes = 0;
     const char *name = "";
@@ -134,6 +135,14 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool
         best.tiles_n = tiles;
         best.grid = (int64_t)tiles * eff;
         best.name = rows[idx].name[a_format];
+        // more workgroups than CUs: with FP4 A and row-major B the four-slot
+        // ring's 132 KiB of LDS leaves one workgroup per CU, the two-slot
+        // ring fits two (64x28672x8192, 448 workgroups: 37.4 -> 34.1 us on
+        // MI355X; at or below one workgroup per CU the deeper ring is faster)
+        if (a_format == MXGEMM_FMT_FP4 && !b_packed && best.grid > num_cu) {
+            best.lean = true;
+            best.name = rows[idx].lean_name;
+        }
         const size_t part = (size_t)rows_wg * mg * 16 * 4;
         best.counter_bytes = best.split > 1 ? (size_t)tiles * 4 : 0;
         best.ws_bytes = best.split > 1 ? (size_t)tiles * best.split * part : 0;
@@ -845,7 +854,7 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     } else {
         int n = 0;
         const mx::RowsKernel &k = mx::rows_kernels(&n)[p.index];
-        (s.b_packed ? k.packed : k.plain)[s.a_format](g, (int)p.grid, stream);
+        (s.b_packed ? k.packed[s.a_format] : p.lean ? k.lean : k.plain[s.a_format])(g, (int)p.grid, stream);
     }
     if (hipGetLastError() != hipSuccess)
         return MXGEMM_ERR_HIP;

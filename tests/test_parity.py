@@ -270,3 +270,27 @@ def test_rows_kernel_variants(shape):
             assert_parity(d, ref, mag, "rows %s packed=%s,%s split=%d" % (shape, packed, sa_packed, s))
             outs.append(d)
         assert np.array_equal(gemm_gpu(p, split_k=4, b_packed=packed, sa_packed=sa_packed), outs[2])
+
+
+LEAN_CASES = [(17, 16500, 1024, 1), (40, 20000, 1056, 1), (64, 17000, 2048, 1), (50, 8200, 2048, 4)]
+
+
+@pytest.mark.parametrize("case", LEAN_CASES, ids=lambda c: "%dx%dx%d_split%d" % c)
+def test_rows_lean_ring(case):
+    """More workgroups than CUs with row-major B: the rows kernel with a
+    two-slot ring (two workgroups per CU) for every 16-row group count,
+    A scales staged (K-block count a multiple of 16) and per wave (K =
+    1056), unsplit and split K; the same values as the packed-B launch,
+    which keeps the four-slot ring."""
+    M, N, K, s = case
+    p = inputs.make_problem(M, N, K, seed=0x1EA4 + M + N, dist="half_zero", e=(112, 140),
+                            beta=1.0, c_sigma=1.0)
+    p["alpha"], p["beta"] = 1.5, -0.75
+    ref, mag, _ = oracle_ref(p)
+    name = mx.mxgemm_plan(M, N, K, 0, s, 256)["kernel_name"]
+    assert name == "rows_m%dx16_n4x1x16_u4_r2" % -(-M // 16), name
+    assert mx.mxgemm_plan(M, N, K, 1, s, 256)["kernel_name"].endswith("_r4")
+    say("case rows lean", case)
+    d = gemm_gpu(p, split_k=s)
+    assert_parity(d, ref, mag, "rows lean %s" % (case,))
+    assert np.array_equal(gemm_gpu(p, split_k=s, b_packed=True), d)
