@@ -71,6 +71,10 @@ struct TileKernelA8 {
     int occupancy;
     LaunchFn plain[4], packed[4];
     const char *name;
+    // FP6 A only, in the dense operand order of launch_fp6_pack (g.lda_b =
+    // bytes per 16-row group), with packed B and packed A scales: launchers
+    // packed[2], packed[3]; the others are null
+    bool fp6_dense;
 };
 const TileKernelA8 *tile_kernels_a8(int *count);
 
@@ -156,5 +160,11 @@ hipError_t scratch_address(void **ptr);
 // rows of fp6_pad_pitch(K) bytes) in `out`; codes unchanged
 int64_t fp6_pad_pitch(int K);
 void launch_fp6_pad(const uint8_t *A, int64_t lda_b, uint8_t *out, int M, int K, hipStream_t s);
+// FP6 A -> the dense operand order of the 256 x 256 FP6 tile: per 16-row
+// group, fp6_pack_steps(K) 128-K steps of 1536 bytes (the 64 lanes' 24-byte
+// operands), fp6_pack_group_bytes(K) per group; zeros past M and K
+int fp6_pack_steps(int K);
+int64_t fp6_pack_group_bytes(int K);
+void launch_fp6_pack(const uint8_t *A, int64_t lda_b, uint8_t *out, int M, int K, hipStream_t s);
 
 }  // namespace mx

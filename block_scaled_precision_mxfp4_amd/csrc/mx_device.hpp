@@ -247,7 +247,9 @@ struct Epilogue {
 // Epilogue for beta == 0 through a private LDS region of the wave
 // (16*FM x 16*FN bf16, 16-byte chunks of a row XOR-swizzled by row / 2:
 // with 8-byte writes served 32 lanes per cycle, rows r and r + 8 of the 16
-// a write instruction covers must not share a slot): the fragments are rounded and written to LDS in their own layout,
+// a write instruction covers must not share a slot; rows of 256 bytes (FN =
+// 8) all start on bank 0 and are swizzled by row % 16 instead): the
+// fragments are rounded and written to LDS in their own layout,
 // then read back row-wise and written to D with 16-byte stores, each
 // instruction covering whole 16*FN-column row segments (full 128-byte lines
 // for FN = 4) instead of 32-byte pieces of 16 rows.  Same values as
@@ -260,7 +262,8 @@ __device__ __forceinline__ void store_tile_staged(const Epilogue &ep, int m_base
     constexpr int RB = FN * 32;       // bytes per row of the wave tile
     constexpr int CH = RB / 16;       // 16-byte chunks per row (power of two)
     constexpr int RPI = 64 / CH;      // rows per copy-out instruction
-    static_assert(CH == 2 || CH == 4 || CH == 8, "row chunking");
+    static_assert(CH == 2 || CH == 4 || CH == 8 || CH == 16, "row chunking");
+    auto sw = [](int r) { return CH == 16 ? (r & 15) : ((r >> 1) & (CH - 1)); };
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
@@ -271,12 +274,12 @@ __device__ __forceinline__ void store_tile_staged(const Epilogue &ep, int m_base
             v2u o;
             o[0] = bf16x2_rne(ep.alpha * acc[fn][fm][0], ep.alpha * acc[fn][fm][1]);
             o[1] = bf16x2_rne(ep.alpha * acc[fn][fm][2], ep.alpha * acc[fn][fm][3]);
-            *reinterpret_cast<v2u *>(lds + r * RB + ((j ^ ((r >> 1) & (CH - 1))) * 16) + ((lane >> 4) & 1) * 8) = o;
+            *reinterpret_cast<v2u *>(lds + r * RB + ((j ^ sw(r)) * 16) + ((lane >> 4) & 1) * 8) = o;
         }
 #pragma unroll
     for (int i = 0; i < FM * 16 / RPI; ++i) {
         const int r = i * RPI + lane / CH, c = lane & (CH - 1);
-        const v4i v = *reinterpret_cast<const v4i *>(lds + r * RB + ((c ^ ((r >> 1) & (CH - 1))) * 16));
+        const v4i v = *reinterpret_cast<const v4i *>(lds + r * RB + ((c ^ sw(r)) * 16));
         const int m = m_base + r, n = n_base + c * 8;
         if (m >= ep.M || n >= ep.N)
             continue;
@@ -404,9 +407,9 @@ __device__ __forceinline__ v4f load16_coherent(__amdgpu_buffer_rsrc_t r, uint32_
 // with store16_coherent.  Returns true in exactly one workgroup of the tile
 // (the last to arrive), whose threads may then read all partials with
 // load16_coherent.  The counter is returned to zero for the next call.
-__device__ __forceinline__ bool split_arrive_last(int *counter, int splits)
+// `flag`: an int in LDS that no thread accesses meanwhile.
+__device__ __forceinline__ bool split_arrive_last_via(int *counter, int splits, int *flag)
 {
-    __shared__ int s_last;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are complete
     __syncthreads();                      // ... and so are every other thread's
     if (threadIdx.x == 0) {
@@ -414,10 +417,16 @@ __device__ __forceinline__ bool split_arrive_last(int *counter, int splits)
         const int last = prev == splits - 1;
         if (last)
             __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = last;
+        *flag = last;
     }
     __syncthreads();
-    return s_last != 0;
+    return *flag != 0;
+}
+
+__device__ __forceinline__ bool split_arrive_last(int *counter, int splits)
+{
+    __shared__ int s_last;
+    return split_arrive_last_via(counter, splits, &s_last);
 }
 
 }  // namespace mx

@@ -1,4 +1,6 @@
-// FP6 A (E2M3 or E3M2) re-laid for the 8-bit tiled kernel, codes unchanged.
+// FP6 A (E2M3 or E3M2) re-laid for the tiled kernels, codes unchanged: the
+// padded layout of the 8-bit tiles, and the dense operand order of the
+// 256 x 256 FP6 tile (below).
 //
 // The scaled matrix instruction takes FP6 operands at the FP4 rate ("CDNA4
 // dense MFMA builtins", "Instruction throughput"): a lane's operand is the 32
@@ -33,6 +35,45 @@ __global__ void __launch_bounds__(256) mx_fp6_pad_kernel(const uint8_t *__restri
 }
 
 int64_t fp6_pad_pitch(int K) { return (int64_t)(K + 127) / 128 * 128; }
+
+// Dense operand order for the 256 x 256 tile: per 16-row group and 128-K
+// step, the 64 lanes' 24-byte operands back to back (lane l: row l % 16 of
+// the group, K-block l / 16 of the step), 1536 bytes; the steps of a group
+// follow each other, so a 256-K stage of a group is 3 KiB in one run and
+// every direct-to-LDS load a whole 1 KiB.  Steps are counted up to an even
+// number; rows past M and K-blocks past K are zero.  A workgroup copies four
+// steps of one group, 8 bytes per thread and pass: 48 consecutive threads
+// read one row's 384 contiguous bytes.
+__global__ void __launch_bounds__(256) mx_fp6_pack_kernel(const uint8_t *__restrict__ A, int64_t lda_b,
+                                                          uint8_t *__restrict__ out, int M, int KB, int ks_pad)
+{
+    const int quads = (ks_pad + 3) / 4;
+    const int grp = blockIdx.x / quads, s0 = (blockIdx.x - grp * quads) * 4;
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+        const int q = pass * 256 + threadIdx.x;  // 16 rows x 48 words
+        const int r = q / 48, wr = q - r * 48;
+        const int s = s0 + wr / 12, w = wr % 12;  // step, word of the row's 96 bytes in it
+        if (s >= ks_pad)
+            continue;
+        const int row = grp * 16 + r, blk = 4 * s + w / 3;
+        v2u v = v2u{0u, 0u};
+        if (row < M && blk < KB)
+            v = *reinterpret_cast<const v2u *>(A + (int64_t)row * lda_b + (int64_t)s * 96 + w * 8);
+        const int l = (w / 3) * 16 + r;
+        *reinterpret_cast<v2u *>(out + ((int64_t)grp * ks_pad + s) * 1536 + l * 24 + (w % 3) * 8) = v;
+    }
+}
+
+int fp6_pack_steps(int K) { return (K / 32 + 7) / 8 * 2; }
+int64_t fp6_pack_group_bytes(int K) { return (int64_t)fp6_pack_steps(K) * 1536; }
+
+void launch_fp6_pack(const uint8_t *A, int64_t lda_b, uint8_t *out, int M, int K, hipStream_t s)
+{
+    const int ks_pad = fp6_pack_steps(K);
+    const int64_t grid = (int64_t)((M + 15) / 16) * ((ks_pad + 3) / 4);
+    hipLaunchKernelGGL(mx_fp6_pack_kernel, dim3((unsigned)grid), dim3(256), 0, s, A, lda_b, out, M, K / 32, ks_pad);
+}
 
 void launch_fp6_pad(const uint8_t *A, int64_t lda_b, uint8_t *out, int M, int K, hipStream_t s)
 {

@@ -143,10 +143,13 @@ __device__ __forceinline__ void store_whole_tile_staged(uint16_t *D, int64_t ldd
 // page's "Hardware constraints" splits the K positions over the two calls),
 // K-rows 32g .. 32g+15 and 32g+16 .. 32g+31 of the step for lane group g,
 // which is the K-block g the instruction reads from lane group g.
-template <int BM, int BN, int WM, int WN, int BLAY, bool SVEC, bool SAPACK, int AFMT = 0, bool PERSIST = false>
+template <int BM, int BN, int WM, int WN, int BLAY, bool SVEC, bool SAPACK, int AFMT = 0, bool PERSIST = false,
+          bool A6D = false>
 __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
 {
-    static_assert(AFMT == 0 || (AFMT >= 1 && AFMT <= 4 && !SAPACK), "8-bit or padded FP6 A with row-major A scales");
+    static_assert(AFMT == 0 || (AFMT >= 1 && AFMT <= 4 && (!SAPACK || A6D)),
+                  "8-bit or padded FP6 A with row-major A scales, or dense FP6 A");
+    static_assert(!A6D || (AFMT >= 3 && BLAY == 1 && SAPACK && !PERSIST), "dense FP6 A with packed B and scales");
     static_assert(BLAY >= 0 && BLAY <= 3 && (AFMT == 0 || BLAY <= 1), "B layouts");
     constexpr bool BPACK = BLAY == 1;                 // packed codes
     constexpr bool BKN = BLAY >= 2;                   // MN-major codes
@@ -166,9 +169,10 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     constexpr int FM = TM / 16, FN = TN / 16;  // 16-row fragments per wave
     static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(FM % 2 == 0 && FN % 2 == 0, "scale words cover 32-row groups");
-    constexpr int A_CH = BM / 8 * AREG, B_CH = BN / 8;  // 1 KiB chunks per stage
+    // bytes per stage (dense FP6 A: 16-row groups of two 1536-byte steps)
+    constexpr int A_STAGE = A6D ? BM * 192 : BM * 128 * AREG, B_STAGE = BN * 128;
+    constexpr int A_CH = A_STAGE / 1024, B_CH = BN / 8;  // 1 KiB chunks per stage
     static_assert(A_CH % NW == 0 && B_CH % NW == 0, "chunks split evenly over waves");
-    constexpr int A_STAGE = BM * 128 * AREG, B_STAGE = BN * 128;  // bytes per stage
     constexpr int SA_W = BM / 32 * 64, SB_W = BN / 32 * 64;  // scale words per stage
     constexpr int SC_W = SA_W + SB_W + 64;                   // + a scratch row for idle threads
     constexpr int SBP_PER_THREAD = (SB_W + NT - 1) / NT;     // packed-scale words per thread
@@ -183,8 +187,10 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     __shared__ __attribute__((aligned(1024))) uint8_t s_a1[A_STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t s_b0[B_STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t s_b1[B_STAGE];
-    __shared__ uint32_t s_sc0[SC_W];  // [SA words | SB words | scratch]
-    __shared__ uint32_t s_sc1[SC_W];
+    // [SA words | SB words | scratch]; the dense FP6 tile's operands fill
+    // the LDS, and its waves load their scale words into registers instead
+    __shared__ uint32_t s_sc0[A6D ? 1 : SC_W];
+    __shared__ uint32_t s_sc1[A6D ? 1 : SC_W];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS/chunk math scalar
@@ -249,8 +255,15 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         // (every range below is under 2^31 bytes: the host rejects strides
         // and K for which a 256-row tile's would not be)
         const int rows_a = min(BM, g.M - m0);
-        a_base = g.A + (int64_t)m0 * g.lda_b;
-        a_bytes = (uint32_t)((int64_t)rows_a * g.lda_b);
+        if constexpr (A6D) {
+            // lda_b: bytes per 16-row group
+            const int grp16 = min(BM / 16, (g.M + 15) / 16 - m0 / 16);
+            a_base = g.A + (int64_t)(m0 / 16) * g.lda_b;
+            a_bytes = (uint32_t)((int64_t)grp16 * g.lda_b);
+        } else {
+            a_base = g.A + (int64_t)m0 * g.lda_b;
+            a_bytes = (uint32_t)((int64_t)rows_a * g.lda_b);
+        }
         if constexpr (SAPACK) {
             const int m32 = m0 / 32, grp32 = min(BM / 32, (g.M + 31) / 32 - m32);
             rsa = make_rsrc(g.SA + (int64_t)m32 * g.sn8 * 256, (uint32_t)((int64_t)grp32 * g.sn8 * 256));
@@ -292,8 +305,9 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         uint8_t *dst_a = BUF ? s_a1 : s_a0;
         uint8_t *dst_b = BUF ? s_b1 : s_b0;
         const int kb_s = kb_begin + kt * 8;
-        // K offset of the stage: bytes along a row (row-major) or 1 KiB steps (packed)
-        const uint32_t a_k = (uint32_t)kb_s * 16 * AREG;
+        // K offset of the stage: bytes along a row (row-major), 1 KiB steps
+        // (packed B) or 1536-byte steps (dense FP6 A)
+        const uint32_t a_k = A6D ? (uint32_t)(kb_s >> 2) * 1536 : (uint32_t)kb_s * 16 * AREG;
         const uint32_t b_k = BPACK ? (uint32_t)(kb_s >> 2) * 1024 : (uint32_t)kb_s * 16;
         const auto ra = make_rsrc(a_base + a_k, on ? a_bytes - a_k : 0u);
         // MN-major: the stage's K-rows kb_s*32 .. up to the chunk end; rows
@@ -303,9 +317,22 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
                             : make_rsrc(b_base + b_k, on ? b_bytes - b_k : 0u);
         // chunk (K-block of the stage) a row-major lane loads in half h
         const int kc0 = kc_lane, kc1 = kc0 ^ 4;
+        // dense FP6: the lane's byte offset, opaque per stage, so that the
+        // compiler forms each load's offset when it issues it instead of
+        // keeping ten loop-invariant offsets live (which spilled them)
+        uint32_t lane16 = (uint32_t)lane * 16;
+        if constexpr (A6D)
+            asm volatile("" : "+v"(lane16));
 #pragma unroll
         for (int i = 0; i < A_CH / NW; ++i) {
             const int c = i * NW + wave;
+            if constexpr (A6D) {
+                // dense FP6: 1 KiB piece c % 3 of 16-row group c / 3's 3 KiB
+                // stage (zeros past M and K are in the copy itself)
+                load16_to_lds(ra, (lds_void *)(dst_a + c * 1024),
+                              (uint32_t)((c / 3) * g.lda_b) + (uint32_t)((c % 3) * 1024) + lane16);
+                continue;
+            }
             const int reg = AREG == 1 ? 0 : c / (BM / 8), cc = AREG == 1 ? c : c % (BM / 8);  // A tile, chunk
             const int rows8 = cc * 8, h = cc & 1;            // 8-row half h of group cc/2
             uint32_t off = a_lane + (uint32_t)(rows8 * g.lda_b) + (h ? (uint32_t)((kc1 - kc0) * 16) : 0u);
@@ -326,7 +353,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
             if constexpr (BPACK) {
                 // packed B: 1 KiB instruction operands, contiguous
                 const int rg = c >> 1, ks = c & 1;
-                off = b_lane + (uint32_t)rg * b_rg_stride + (uint32_t)(ks * 1024);
+                off = (A6D ? lane16 : b_lane) + (uint32_t)rg * b_rg_stride + (uint32_t)(ks * 1024);
             } else if constexpr (BKN) {
                 // MN-major: instruction c fills K-rows c * KN_RPI .. (a range
                 // below 2^31 - 2^31 + this, so past-N lanes stay out of range)
@@ -353,8 +380,23 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
 
     ScaleRows sa_rows, sb_rows;
     uint32_t sbp[SBP_PER_THREAD], sap[SAP_PER_THREAD];
-    auto issue_scales = [&](int kt, bool on) __attribute__((always_inline)) {
+    // dense FP6: this wave's packed scale words of a stage (its 32-row groups
+    // of A and of B), one register set per buffer
+    uint32_t rsaw[2][FM / 2], rsbw[2][FN / 2];
+    auto issue_scales = [&](int kt, bool on, auto bufc) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(bufc)::value;
         const int kb_s = kb_begin + kt * 8;
+        if constexpr (A6D) {
+            // (past the last stage these read the next chunk's words or, past
+            // the scale rows, zeros from the range check: never used)
+#pragma unroll
+            for (int p = 0; p < FM / 2; ++p)
+                rsaw[BUF][p] = load4(rsa, (uint32_t)((((wave_m * (FM / 2) + p) * g.sn8 + (kb_s >> 3)) * 64 + lane) * 4));
+#pragma unroll
+            for (int p = 0; p < FN / 2; ++p)
+                rsbw[BUF][p] = load4(rsb, (uint32_t)((((wave_n * (FN / 2) + p) * g.sn8 + (kb_s >> 3)) * 64 + lane) * 4));
+            return;
+        }
         if constexpr (SAPACK) {
             // packed words are already the LDS words: word q of the stage is
             // word q & 63 of 32-row group q / 64's chunk for this 8-block step
@@ -384,6 +426,8 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
     };
     auto commit_scales = [&](auto bufc) __attribute__((always_inline)) {
         constexpr int BUF = decltype(bufc)::value;
+        if constexpr (A6D)
+            return;
         uint32_t *dsc = BUF ? s_sc1 : s_sc0;
         if constexpr (SAPACK) {
 #pragma unroll
@@ -448,7 +492,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
             if constexpr (LOADS_AT >= 0)
                 __builtin_amdgcn_sched_barrier(0);
             issue_operands(kt + 1, more, Next{});
-            issue_scales(kt + 1, more);
+            issue_scales(kt + 1, more, Next{});
             if constexpr (LOADS_AT >= 0)
                 __builtin_amdgcn_sched_barrier(0);
         };
@@ -460,10 +504,52 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         uint32_t saw[FM / 2], sbw[FN / 2];
 #pragma unroll
         for (int p = 0; p < FM / 2; ++p)
-            saw[p] = ssc[(wave_m * (FM / 2) + p) * 64 + lane];
+            saw[p] = A6D ? rsaw[BUF][p] : ssc[(wave_m * (FM / 2) + p) * 64 + lane];
 #pragma unroll
         for (int p = 0; p < FN / 2; ++p)
-            sbw[p] = ssc[SA_W + (wave_n * (FN / 2) + p) * 64 + lane];
+            sbw[p] = A6D ? rsbw[BUF][p] : ssc[SA_W + (wave_n * (FN / 2) + p) * 64 + lane];
+        if constexpr (A6D) {
+            // dense FP6, per 128-K step: the four A operands (three 8-byte
+            // reads each at a 24-byte lane stride: 32 lanes per cycle on 64
+            // distinct banks), then the eight B fragments, each read one
+            // fragment ahead of its multiplies.  A scheduling barrier after
+            // each fragment's multiplies keeps the compiler from issuing all
+            // of a step's reads up front, which spilled.
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                v8i af[FM];
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    const uint8_t *t = sa_tile + (wave_m * FM + fm) * 3072 + ks * 1536 + lane * 24;
+                    const v2u p0 = *reinterpret_cast<const v2u *>(t);
+                    const v2u p1 = *reinterpret_cast<const v2u *>(t + 8);
+                    const v2u p2 = *reinterpret_cast<const v2u *>(t + 16);
+                    af[fm] = v8i{(int)p0[0], (int)p0[1], (int)p1[0], (int)p1[1], (int)p2[0], (int)p2[1], 0, 0};
+                }
+                auto read_b = [&](int fn) __attribute__((always_inline)) {
+                    return *reinterpret_cast<const v4i *>(sb_tile + ((wave_n * FN + fn) * 2 + ks) * 1024 + lane * 16);
+                };
+                v4i bq[2];
+                bq[0] = read_b(0);
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    if constexpr (LOADS_AT > 0) {
+                        if (ks * FN + fn == LOADS_AT)
+                            prefetch();
+                    }
+                    if (fn + 1 < FN)
+                        bq[(fn + 1) & 1] = read_b(fn + 1);
+                    const v4i bf = bq[fn & 1];
+#pragma unroll
+                    for (int fm = 0; fm < FM; ++fm)
+                        acc[fn][fm] = mma_sel_wide<kFmtHw[AFMT]>(
+                            ks * 2 + (fn & 1), ks * 2 + (fm & 1), bf, af[fm],
+                            FIRST && ks == 0 ? v4f{0.f, 0.f, 0.f, 0.f} : acc[fn][fm], (int)sbw[fn >> 1],
+                            (int)saw[fm >> 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        } else {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             using a_t = typename std::conditional<AFMT == 0, v4i, v8i>::type;
@@ -513,13 +599,14 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        }
         wait_vmem();
         commit_scales(Next{});
         __syncthreads();
     };
 
     issue_operands(0, true, B0{});
-    issue_scales(0, true);
+    issue_scales(0, true, B0{});
     wait_vmem();
     commit_scales(B0{});
     __syncthreads();
@@ -568,7 +655,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
             // (its last readers passed the barrier ending stage nst - 2)
             load_src(xcd_remap(next_hw, units));
             issue_operands(0, true, B0{});
-            issue_scales(0, true);
+            issue_scales(0, true, B0{});
         }
         // staged epilogue in the last stage's A buffer: each wave stages
         // 1/PARTS of its tile at a time in a private region of s_a1.  Naming
@@ -658,7 +745,10 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         for (int fm = 0; fm < FM; ++fm)
             store16_coherent(rws, z * PART + (uint32_t)((((wave * FN + fn) * FM + fm) * 64 + lane) * 16),
                              acc[fn][fm]);
-    if (!split_arrive_last(g.counters + t, g.split))
+    // (the dense FP6 tile's operand buffers fill the LDS: its flag takes a
+    // word of the A buffer, free after the last stage's barrier)
+    if (!(A6D ? split_arrive_last_via(g.counters + t, g.split, reinterpret_cast<int *>(s_a0))
+              : split_arrive_last(g.counters + t, g.split)))
         return;
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
@@ -738,19 +828,39 @@ static void launch_tile_a8(const GemmArgs &g, int grid, hipStream_t s)
         hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BLAY, false, false, AFMT>), dim3(grid), dim3(64 * WM * WN), 0, s, g);
 }
 
+// FP6 A in the dense operand order (launch_fp6_pack), packed B and packed A
+// scales; SVEC: whole 8-block stages
+template <int BM, int BN, int WM, int WN, int AFMT>
+static void launch_tile_fp6_dense(const GemmArgs &g, int grid, hipStream_t s)
+{
+    if (g.KB % 8 == 0)
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, 1, true, true, AFMT, false, true>), dim3(grid),
+                           dim3(64 * WM * WN), 0, s, g);
+    else
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, 1, false, true, AFMT, false, true>), dim3(grid),
+                           dim3(64 * WM * WN), 0, s, g);
+}
+
 #define MX_TILE_A8(BM, BN, WM, WN, OCC)                                                                    \
     {BM, BN, OCC,                                                                                          \
      {launch_tile_a8<BM, BN, WM, WN, false, 1>, launch_tile_a8<BM, BN, WM, WN, false, 2>,                  \
       launch_tile_a8<BM, BN, WM, WN, false, 3>, launch_tile_a8<BM, BN, WM, WN, false, 4>},                 \
      {launch_tile_a8<BM, BN, WM, WN, true, 1>, launch_tile_a8<BM, BN, WM, WN, true, 2>,                    \
-      launch_tile_a8<BM, BN, WM, WN, true, 3>, launch_tile_a8<BM, BN, WM, WN, true, 4>}, "tile_a8_" #BM "x" #BN}
+      launch_tile_a8<BM, BN, WM, WN, true, 3>, launch_tile_a8<BM, BN, WM, WN, true, 4>}, "tile_a8_" #BM "x" #BN, \
+     false}
 
 const TileKernelA8 *tile_kernels_a8(int *count)
 {
+    // the dense FP6 tile: 8 waves of 64 x 128 (four A fragments of 24 bytes
+    // and eight B fragments per step, the registers the FP4 tile's 128 x 64
+    // waves use)
     static const TileKernelA8 table[] = {
         MX_TILE_A8(128, 256, 2, 4, 1),
         MX_TILE_A8(128, 128, 2, 2, 1),
         MX_TILE_A8(64, 64, 2, 2, 3),
+        {256, 256, 1, {nullptr, nullptr, nullptr, nullptr},
+         {nullptr, nullptr, launch_tile_fp6_dense<256, 256, 4, 2, 3>, launch_tile_fp6_dense<256, 256, 4, 2, 4>},
+         "tile_fp6_256x256", true},
     };
     *count = (int)(sizeof(table) / sizeof(table[0]));
     return table;

@@ -245,19 +245,32 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool
 // Tiled plan for 8-bit A (family 3): the cost model of the FP4 tiles with
 // the matrix time doubled (the 8-bit scaled instruction runs at half the
 // FP4 rate, "CDNA4 dense MFMA builtins", "Instruction throughput") and A's
-// bytes doubled.  FP6 A in its padded 8-bit-sized layout (fp6 = true)
-// keeps the FP4 matrix rate (the same table gives FP6 the FP4 cycles).
-Plan plan_a8(int M, int N, int K, int split_req, int num_cu, bool fp6 = false)
+// bytes doubled.  FP6 A (fp6 = true) keeps the FP4 matrix rate (the same
+// table gives FP6 the FP4 cycles), in its padded 8-bit-sized layout or, on
+// the dense FP6 tile, with 24 bytes per K-block (a row-major B is packed
+// for it first, at the cost of a pass over B).
+// MXGEMM_A8_TILE=<kernel name> restricts the choice to that tile where it
+// applies (a test hook).
+Plan plan_a8(int M, int N, int K, int split_req, int num_cu, bool fp6 = false, bool b_packed = false)
 {
     const int KB = K / 32;
     if (num_cu <= 0)
         num_cu = 256;
     int n = 0;
     const mx::TileKernelA8 *tile = mx::tile_kernels_a8(&n);
+    const char *only = std::getenv("MXGEMM_A8_TILE");
+    bool only_ok = false;
+    for (int k = 0; only && k < n; ++k)
+        only_ok |= std::strcmp(only, tile[k].name) == 0 && (!tile[k].fp6_dense || fp6);
     Plan best;
     double best_t = 1e300;
     for (int k = 0; k < n; ++k) {
         const mx::TileKernelA8 &tk = tile[k];
+        if (tk.fp6_dense && !fp6)
+            continue;
+        if (only_ok && std::strcmp(only, tk.name) != 0)
+            continue;
+        const double a_rows = tk.fp6_dense ? 1.5 : 2.0;  // A bytes per stage, in FP4 tile rows
         const int tm = cdiv(M, tk.bm), tn = cdiv(N, tk.bn);
         const int64_t tiles = (int64_t)tm * tn;
         for (int s : kSplits) {
@@ -269,8 +282,13 @@ Plan plan_a8(int M, int N, int K, int split_req, int num_cu, bool fp6 = false)
             const int64_t wgs = tiles * eff;
             const double rounds = (double)((wgs + (int64_t)num_cu * tk.occupancy - 1) / ((int64_t)num_cu * tk.occupancy));
             const double t_math = (fp6 ? 1.0 : 2.0) * 2.0 * tk.bm * tk.bn * 256.0 * tk.occupancy / (kCuFlops * kMatrixFraction);
-            const double t_load = (double)(2 * tk.bm + tk.bn) * 128.0 * tk.occupancy / kCuLoadRate;
+            const double t_load = (a_rows * tk.bm + tk.bn) * 128.0 * tk.occupancy / kCuLoadRate;
             double t = rounds * (per / 8) * std::max(t_math, t_load);
+            // the dense FP6 tile's stages run like the FP4 256 x 256 tile's:
+            // 8192^3 in 314-316 us against 438-440 us on the 128 x 256
+            // 8-bit tile, 4096^3 in 52.8 against 64.6-65.4 us (MI355X)
+            if (tk.fp6_dense)
+                t = t * 0.7 + (b_packed ? 0.0 : (double)N * K / kHbm);  // B's codes read and written once
             if (eff > 1)
                 t += kSplitChunkCost * eff + (double)tiles * eff * tk.bm * tk.bn * 4 * 2 / kHbm +
                      (double)eff * tk.bm * tk.bn * 4 / kCuL2;
@@ -315,7 +333,7 @@ Plan plan_run(int M, int N, int K, const mxgemm_strides &s, int split_k, int num
     // up to 128), then the 8-bit tiles with the FP6 instruction, while a
     // 256-row tile of the re-laid A stays below 2^31 bytes
     if (fp6 && M > 16 && (int64_t)256 * mx::fp6_pad_pitch(K) < ((int64_t)1 << 31))
-        return plan_a8(M, N, K, split_k, num_cu, true);
+        return plan_a8(M, N, K, split_k, num_cu, true, s.b_packed != 0);
     return plan_for(std::min(M, 16), N, K, s.b_packed, split_k, num_cu, false, 1);
 }
 
@@ -737,9 +755,21 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     g.sb16 = !s.b_packed && aligned(scaleB, 16) && s.ldsb % 16 == 0 && KB % 16 == 0;
     g.group_m = 4;
 
-    // FP6 A on the 8-bit tiles is first re-laid into 32-byte blocks
+    // FP6 A on the 8-bit tiles is first re-laid into 32-byte blocks; on the
+    // dense FP6 tile into its operand order, with the A scales shuffled
+    // behind it
     const bool fp6_conv = p.family == 3 && (s.a_format == MXGEMM_FMT_FP6_E2M3 || s.a_format == MXGEMM_FMT_FP6_E3M2);
-    const size_t conv_bytes = fp6_conv ? (size_t)M * (size_t)mx::fp6_pad_pitch(K) : 0;
+    int n_a8 = 0;
+    const bool fp6_dense = fp6_conv && mx::tile_kernels_a8(&n_a8)[p.index].fp6_dense;
+    const size_t a6_bytes = fp6_dense ? align_up((size_t)cdiv(M, 16) * (size_t)mx::fp6_pack_group_bytes(K), 256) : 0;
+    // [A dense | A scales packed | B packed | B scales packed]: a row-major
+    // B is packed too, the tile reads only the packed layout
+    const bool pack_b_here = fp6_dense && !s.b_packed;
+    const size_t sap_bytes = fp6_dense ? align_up(packed_sb_bytes(M, K), 256) : 0;
+    const size_t bp_bytes = pack_b_here ? align_up(packed_b_bytes(N, K), 256) : 0;
+    const size_t conv_bytes = !fp6_conv ? 0
+                              : fp6_dense ? a6_bytes + sap_bytes + bp_bytes + (pack_b_here ? packed_sb_bytes(N, K) : 0)
+                                          : (size_t)M * (size_t)mx::fp6_pad_pitch(K);
     // the allocation-free form: counters, partials and the FP6 copy come
     // from the device's fixed scratch (counters first, then partials, then
     // the copy); a plan that needs more is refused before any launch
@@ -816,11 +846,28 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
                 if (st != MXGEMM_OK)
                     return st;
             }
-            mx::launch_fp6_pad((const uint8_t *)A, lda_bytes, (uint8_t *)conv, M, K, stream);
-            g.A = (const uint8_t *)conv;
-            g.lda_b = mx::fp6_pad_pitch(K);
+            if (fp6_dense) {
+                uint8_t *sap = (uint8_t *)conv + a6_bytes;
+                mx::launch_fp6_pack((const uint8_t *)A, lda_bytes, (uint8_t *)conv, M, K, stream);
+                mx::launch_pack_sb((uint32_t *)sap, (const uint8_t *)scaleA, M, KB, s.ldsa, stream);
+                g.A = (const uint8_t *)conv;
+                g.lda_b = mx::fp6_pack_group_bytes(K);
+                g.SA = sap;
+                g.sa_packed = 1;
+                if (pack_b_here) {
+                    uint8_t *bp = sap + sap_bytes, *sbp = bp + bp_bytes;
+                    mx::launch_pack_b(bp, (const uint8_t *)B, N, KB, s.ldb / 2, stream);
+                    mx::launch_pack_sb((uint32_t *)sbp, (const uint8_t *)scaleB, N, KB, s.ldsb, stream);
+                    g.B = bp;
+                    g.SB = sbp;
+                }
+            } else {
+                mx::launch_fp6_pad((const uint8_t *)A, lda_bytes, (uint8_t *)conv, M, K, stream);
+                g.A = (const uint8_t *)conv;
+                g.lda_b = mx::fp6_pad_pitch(K);
+            }
         }
-        (s.b_packed ? k.packed : k.plain)[s.a_format - 1](g, (int)p.grid, stream);
+        (s.b_packed || fp6_dense ? k.packed : k.plain)[s.a_format - 1](g, (int)p.grid, stream);
     } else if (p.family == 0) {
         int n = 0;
         const mx::TileKernel &k = mx::tile_kernels(&n)[p.index];

@@ -180,6 +180,69 @@ def test_fp6_tiled_matches_oracle(case, fmt):
         assert_parity(d[rows], ref, mag, "fp6 tiled %s %s" % (NAMES[fmt], case))
 
 
+# FP6 A on the 256 x 256 dense FP6 tile: A re-laid into the instruction's
+# operand order (24 bytes per lane and K-block), A scales shuffled, a
+# row-major B packed by the library; forced through the planner's test hook
+# on shapes the oracle checks in full
+FP6_DENSE = [
+    (300, 520, 1056, -1, True, "bf16"),  # ragged M and N, K tail (33 blocks), C
+    (300, 520, 1056, -1, False, None),   # the same with row-major B
+    (512, 512, 2048, 1, True, None),     # whole tiles, staged epilogue
+    (130, 256, 2080, 2, True, "f32"),    # split-K with a K tail, f32 C
+    (256, 300, 8192, 4, False, None),    # split-K over whole stages, row-major B
+]
+
+
+@pytest.mark.parametrize("fmt", [mx.FMT_FP6_E2M3, mx.FMT_FP6_E3M2], ids=lambda f: NAMES[f])
+@pytest.mark.parametrize("case", FP6_DENSE, ids=lambda c: "%dx%dx%d_s%d%s" % (c[:4] + ("_packed" if c[4] else "",)))
+def test_fp6_dense_tile_matches_oracle(case, fmt, monkeypatch):
+    """Against the oracle, and bit for bit against the 128 x 256 8-bit tile
+    on the padded copy of A: both feed each accumulator the same operands in
+    the same K order."""
+    M, N, K, split, packed, c = case
+    st = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32, b_packed=int(packed), a_format=fmt)
+    p = problem(case, fmt, seed=0xD6D6 + 13 * fmt + M + N)
+    monkeypatch.setenv("MXGEMM_A8_TILE", "tile_fp6_256x256")
+    assert mx.mxgemm_plan_ex(M, N, K, st, split, 256)["kernel_name"] == "tile_fp6_256x256"
+    say("case fp6 dense", NAMES[fmt], case)
+    d = gemm_gpu(p, split_k=split, b_packed=packed)
+    ref, mag, _ = oracle_ref(p)
+    assert_parity(d, ref, mag, "fp6 dense %s %s" % (NAMES[fmt], case))
+    monkeypatch.setenv("MXGEMM_A8_TILE", "tile_a8_128x256")
+    assert mx.mxgemm_plan_ex(M, N, K, st, split, 256)["kernel_name"] == "tile_a8_128x256"
+    assert np.array_equal(gemm_gpu(p, split_k=split, b_packed=packed), d)
+
+
+@pytest.mark.parametrize("fmt", [mx.FMT_FP6_E2M3, mx.FMT_FP6_E3M2], ids=lambda f: NAMES[f])
+def test_fp6_dense_tile_all_codes(fmt, monkeypatch):
+    """B = I through the dense FP6 tile: every FP6 code in every lane
+    position of a K-block, D equal to the oracle's bf16 result bit for bit."""
+    M, K = 272, 256
+    N = K
+    codes = np.array([[(3 * r + k) % 64 for k in range(K)] for r in range(M)], dtype=np.uint64)
+    A = np.zeros((M, K * 6 // 8), dtype=np.uint8)
+    for r in range(M):
+        acc = 0
+        for k in range(K):
+            acc |= int(codes[r, k]) << (6 * k)
+        A[r] = np.frombuffer(acc.to_bytes(K * 6 // 8, "little"), dtype=np.uint8)
+    rng = np.random.default_rng(16 + fmt)
+    SA = rng.integers(118, 136, (M, K // 32)).astype(np.uint8)
+    B = np.zeros((N, K // 2), dtype=np.uint8)
+    for j in range(N):
+        B[j, j // 2] |= 0x2 << (4 * (j % 2))
+    SB = np.full((N, K // 32), 127, dtype=np.uint8)
+    p = dict(M=M, N=N, K=K, A=A, SA=SA, B=B, SB=SB, alpha=1.0, beta=0.0, C=None, a_fmt=fmt)
+    monkeypatch.setenv("MXGEMM_A8_TILE", "tile_fp6_256x256")
+    st = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32, b_packed=1, a_format=fmt)
+    assert mx.mxgemm_plan_ex(M, N, K, st, -1, 256)["kernel_name"] == "tile_fp6_256x256"
+    say("case fp6 dense identity", NAMES[fmt])
+    d = gemm_gpu(p, b_packed=True)
+    _, _, dref = oracle_ref(p)
+    same = (d == dref) | (((d | dref) & 0x7FFF) == 0)  # +0 and -0 are equal
+    assert same.all(), "%d of %d elements differ" % (int((~same).sum()), d.size)
+
+
 def test_fp6_conversion_buffers_are_per_stream():
     """FP6 A with M > 16 is re-laid in a buffer owned per (device, stream).  Two problems of different sizes and formats on two streams,
     each launched twice with no synchronization in between, must both match
