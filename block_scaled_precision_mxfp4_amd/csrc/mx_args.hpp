@@ -162,9 +162,11 @@ int64_t fp6_pad_pitch(int K);
 void launch_fp6_pad(const uint8_t *A, int64_t lda_b, uint8_t *out, int M, int K, hipStream_t s);
 // FP6 A -> the dense operand order of the 256 x 256 FP6 tile: per 16-row
 // group, fp6_pack_steps(K) 128-K steps of 1536 bytes (the 64 lanes' 24-byte
-// operands), fp6_pack_group_bytes(K) per group; zeros past M and K
+// operands), fp6_pack_group_bytes(K) per group; zeros past M and K.  The A
+// scales (rows of ldsa bytes) go to sa_out in the shuffled scale layout.
 int fp6_pack_steps(int K);
 int64_t fp6_pack_group_bytes(int K);
-void launch_fp6_pack(const uint8_t *A, int64_t lda_b, uint8_t *out, int M, int K, hipStream_t s);
+void launch_fp6_pack(const uint8_t *A, int64_t lda_b, const uint8_t *SA, int64_t ldsa, uint8_t *out,
+                     uint32_t *sa_out, int M, int K, hipStream_t s);
 
 }  // namespace mx

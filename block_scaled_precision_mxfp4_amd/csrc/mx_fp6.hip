@@ -36,51 +36,119 @@ __global__ void __launch_bounds__(256) mx_fp6_pad_kernel(const uint8_t *__restri
 
 int64_t fp6_pad_pitch(int K) { return (int64_t)(K + 127) / 128 * 128; }
 
-// Dense operand order for the 256 x 256 tile: per 16-row group and 128-K
-// step, the 64 lanes' 24-byte operands back to back (lane l: row l % 16 of
-// the group, K-block l / 16 of the step), 1536 bytes; the steps of a group
-// follow each other, so a 256-K stage of a group is 3 KiB in one run and
-// every direct-to-LDS load a whole 1 KiB.  Steps are counted up to an even
-// number; rows past M and K-blocks past K are zero.  A workgroup copies four
-// steps of one group, 8 bytes per thread and pass: 48 consecutive threads
-// read one row's 384 contiguous bytes.
-__global__ void __launch_bounds__(256) mx_fp6_pack_kernel(const uint8_t *__restrict__ A, int64_t lda_b,
-                                                          uint8_t *__restrict__ out, int M, int KB, int ks_pad)
-{
-    const int quads = (ks_pad + 3) / 4;
-    const int grp = blockIdx.x / quads, s0 = (blockIdx.x - grp * quads) * 4;
-#pragma unroll
-    for (int pass = 0; pass < 3; ++pass) {
-        const int q = pass * 256 + threadIdx.x;  // 16 rows x 48 words
-        const int r = q / 48, wr = q - r * 48;
-        const int s = s0 + wr / 12, w = wr % 12;  // step, word of the row's 96 bytes in it
-        if (s >= ks_pad)
-            continue;
-        const int row = grp * 16 + r, blk = 4 * s + w / 3;
-        v2u v = v2u{0u, 0u};
-        if (row < M && blk < KB)
-            v = *reinterpret_cast<const v2u *>(A + (int64_t)row * lda_b + (int64_t)s * 96 + w * 8);
-        const int l = (w / 3) * 16 + r;
-        *reinterpret_cast<v2u *>(out + ((int64_t)grp * ks_pad + s) * 1536 + l * 24 + (w % 3) * 8) = v;
-    }
-}
-
-int fp6_pack_steps(int K) { return (K / 32 + 7) / 8 * 2; }
-int64_t fp6_pack_group_bytes(int K) { return (int64_t)fp6_pack_steps(K) * 1536; }
-
-void launch_fp6_pack(const uint8_t *A, int64_t lda_b, uint8_t *out, int M, int K, hipStream_t s)
-{
-    const int ks_pad = fp6_pack_steps(K);
-    const int64_t grid = (int64_t)((M + 15) / 16) * ((ks_pad + 3) / 4);
-    hipLaunchKernelGGL(mx_fp6_pack_kernel, dim3((unsigned)grid), dim3(256), 0, s, A, lda_b, out, M, K / 32, ks_pad);
-}
-
 void launch_fp6_pad(const uint8_t *A, int64_t lda_b, uint8_t *out, int M, int K, hipStream_t s)
 {
     const int KB = K / 32;
     const int64_t threads = (int64_t)M * KB;
     hipLaunchKernelGGL(mx_fp6_pad_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, A, lda_b, out,
                        fp6_pad_pitch(K), M, KB);
+}
+
+// Dense operand order for the 256 x 256 tile: per 16-row group and 128-K
+// step, the 64 lanes' 24-byte operands back to back (lane l: row l % 16 of
+// the group, K-block l / 16 of the step), 1536 bytes; the steps of a group
+// follow each other, so a 256-K stage of a group is 3 KiB in one run and
+// every direct-to-LDS load a whole 1 KiB.  Steps are counted up to an even
+// number; rows past M and K-blocks past K are zero.
+//
+// A workgroup moves 32 rows x 4 steps: the rows' 384-byte runs are read in
+// 16-byte pieces (24 consecutive threads per row; 8-byte pieces when the row
+// pitch is not a multiple of 16) whose 8-byte words are dropped into LDS at
+// their operand-order places, then each of the two groups' 6 KiB runs is
+// written with 16-byte stores.  The same workgroup writes the A scales of
+// its 32 rows and two 8-block steps in the shuffled scale layout (the one
+// mxgemm_pack_scales writes: word (row group, step, lane) holds rows 16j +
+// lane % 16 at K-block 4i + lane / 16 of the step, byte 2i + j; 0x7F past M
+// and K).
+template <bool V16>
+__global__ void __launch_bounds__(256) mx_fp6_pack_kernel(const uint8_t *__restrict__ A, int64_t lda_b,
+                                                          const uint8_t *__restrict__ SA, int64_t ldsa,
+                                                          uint8_t *__restrict__ out, uint32_t *__restrict__ sa_out,
+                                                          int M, int KB, int ks_pad)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t s_out[2 * 4 * 1536];
+    const int quads = (ks_pad + 3) / 4;
+    const int g32 = blockIdx.x / quads, s0 = (blockIdx.x - g32 * quads) * 4;
+    const int tid = threadIdx.x;
+    // word w (of 12) of step s of row r -> its place in the group's run
+    auto place = [&](int r, int s, int w, v2u v) __attribute__((always_inline)) {
+        const int l = (w / 3) * 16 + (r & 15);
+        *reinterpret_cast<v2u *>(s_out + (r >> 4) * 6144 + s * 1536 + l * 24 + (w % 3) * 8) = v;
+    };
+    if constexpr (V16) {
+#pragma unroll
+        for (int pass = 0; pass < 3; ++pass) {
+            const int q = pass * 256 + tid;  // 32 rows x 24 pieces
+            const int r = q / 24, c = q - r * 24;
+            const int s = c / 6, w = (c % 6) * 2;  // step of the four, first word of the piece in it
+            const int row = g32 * 32 + r, blk0 = 4 * (s0 + s) + w / 3, blk1 = 4 * (s0 + s) + (w + 1) / 3;
+            const uint8_t *src = A + (int64_t)row * lda_b + (int64_t)(s0 + s) * 96 + w * 8;
+            v2u lo = v2u{0u, 0u}, hi = v2u{0u, 0u};
+            if (row < M && blk1 < KB) {
+                const v4i v = *reinterpret_cast<const v4i *>(src);
+                lo = v2u{(uint32_t)v[0], (uint32_t)v[1]};
+                hi = v2u{(uint32_t)v[2], (uint32_t)v[3]};
+            } else if (row < M && blk0 < KB) {
+                lo = *reinterpret_cast<const v2u *>(src);
+            }
+            place(r, s, w, lo);
+            place(r, s, w + 1, hi);
+        }
+    } else {
+#pragma unroll
+        for (int pass = 0; pass < 6; ++pass) {
+            const int q = pass * 256 + tid;  // 32 rows x 48 words
+            const int r = q / 48, wr = q - r * 48;
+            const int s = wr / 12, w = wr % 12;  // step of the four, word of the row's 96 bytes in it
+            const int row = g32 * 32 + r, blk = 4 * (s0 + s) + w / 3;
+            v2u v = v2u{0u, 0u};
+            if (row < M && blk < KB)
+                v = *reinterpret_cast<const v2u *>(A + (int64_t)row * lda_b + (int64_t)(s0 + s) * 96 + w * 8);
+            place(r, s, w, v);
+        }
+    }
+    if (tid < 128) {
+        const int d3 = s0 / 2 + (tid >> 6), lane = tid & 63;
+        if (d3 < ks_pad / 2) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = g32 * 32 + (j & 1) * 16 + (lane & 15);
+                const int col = d3 * 8 + (j >> 1) * 4 + (lane >> 4);
+                const uint32_t b = row < M && col < KB ? SA[(int64_t)row * ldsa + col] : 0x7Fu;
+                word |= b << (8 * j);
+            }
+            sa_out[((int64_t)g32 * (ks_pad / 2) + d3) * 64 + lane] = word;
+        }
+    }
+    __syncthreads();
+    const int groups = (M + 15) / 16;
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+        const int q = pass * 256 + tid;  // 768 chunks of 16 bytes
+        const int gi = q / 384, off = (q - gi * 384) * 16;
+        const int grp = g32 * 2 + gi, s = s0 + off / 1536;
+        if (grp < groups && s < ks_pad)
+            *reinterpret_cast<v4i *>(out + ((int64_t)grp * ks_pad + s0) * 1536 + off) =
+                *reinterpret_cast<const v4i *>(s_out + gi * 6144 + off);
+    }
+}
+
+int fp6_pack_steps(int K) { return (K / 32 + 7) / 8 * 2; }
+int64_t fp6_pack_group_bytes(int K) { return (int64_t)fp6_pack_steps(K) * 1536; }
+
+void launch_fp6_pack(const uint8_t *A, int64_t lda_b, const uint8_t *SA, int64_t ldsa, uint8_t *out,
+                     uint32_t *sa_out, int M, int K, hipStream_t s)
+{
+    const int ks_pad = fp6_pack_steps(K);
+    const int64_t grid = (int64_t)((M + 31) / 32) * ((ks_pad + 3) / 4);
+    // (A is 16-byte aligned; 16-byte pieces need 16-byte rows as well)
+    if (lda_b % 16 == 0)
+        hipLaunchKernelGGL(mx_fp6_pack_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, A, lda_b, SA, ldsa, out,
+                           sa_out, M, K / 32, ks_pad);
+    else
+        hipLaunchKernelGGL(mx_fp6_pack_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, A, lda_b, SA, ldsa, out,
+                           sa_out, M, K / 32, ks_pad);
 }
 
 }  // namespace mx

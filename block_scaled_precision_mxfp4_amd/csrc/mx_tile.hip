@@ -91,7 +91,9 @@ __device__ __forceinline__ void store_whole_tile_staged(uint16_t *D, int64_t ldd
     constexpr int RB = FN * 32;  // bytes per row of the wave tile
     constexpr int CH = RB / 16;  // 16-byte chunks per row
     constexpr int RPI = 64 / CH; // rows per copy-out instruction
-    static_assert(CH == 2 || CH == 4 || CH == 8, "row chunking");
+    static_assert(CH == 2 || CH == 4 || CH == 8 || CH == 16, "row chunking");
+    // (the swizzle of store_tile_staged)
+    auto sw = [](int r) { return CH == 16 ? (r & 15) : ((r >> 1) & (CH - 1)); };
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
@@ -101,14 +103,14 @@ __device__ __forceinline__ void store_whole_tile_staged(uint16_t *D, int64_t ldd
             v2u o;
             o[0] = bf16x2_rne(alpha * acc[fn][fm][0], alpha * acc[fn][fm][1]);
             o[1] = bf16x2_rne(alpha * acc[fn][fm][2], alpha * acc[fn][fm][3]);
-            *reinterpret_cast<v2u *>(lds + r * RB + ((j ^ ((r >> 1) & (CH - 1))) * 16) + ((lane >> 4) & 1) * 8) = o;
+            *reinterpret_cast<v2u *>(lds + r * RB + ((j ^ sw(r)) * 16) + ((lane >> 4) & 1) * 8) = o;
         }
     const int r0 = lane / CH, c = lane & (CH - 1);
     uint16_t *d0 = D + (int64_t)(m_base + r0) * ldd + n_base + c * 8;
 #pragma unroll
     for (int i = 0; i < FM * 16 / RPI; ++i) {
         const int r = i * RPI + r0;
-        const v4i v = *reinterpret_cast<const v4i *>(lds + r * RB + ((c ^ ((r >> 1) & (CH - 1))) * 16));
+        const v4i v = *reinterpret_cast<const v4i *>(lds + r * RB + ((c ^ sw(r)) * 16));
         __builtin_nontemporal_store(v, reinterpret_cast<v4i *>(d0 + (int64_t)(i * RPI) * ldd));
     }
 }
@@ -149,7 +151,7 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
 {
     static_assert(AFMT == 0 || (AFMT >= 1 && AFMT <= 4 && (!SAPACK || A6D)),
                   "8-bit or padded FP6 A with row-major A scales, or dense FP6 A");
-    static_assert(!A6D || (AFMT >= 3 && BLAY == 1 && SAPACK && !PERSIST), "dense FP6 A with packed B and scales");
+    static_assert(!A6D || (AFMT >= 3 && BLAY == 1 && SAPACK), "dense FP6 A with packed B and scales");
     static_assert(BLAY >= 0 && BLAY <= 3 && (AFMT == 0 || BLAY <= 1), "B layouts");
     constexpr bool BPACK = BLAY == 1;                 // packed codes
     constexpr bool BKN = BLAY >= 2;                   // MN-major codes
@@ -639,8 +641,11 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_kernel(GemmArgs g)
         // (0, 2); (0, 1), (1, 3), (0, 4), (0, 5) and (0, 6) were slower.  The K-tail
         // variant (!SVEC) keeps one issue point: its larger address state
         // spills inside the loop when the loop is instantiated twice.
+        // (the dense FP6 tile, eight fragment steps per 128-K step: waves
+        // 4-7 at the second step's start, 8192^3 304-305 us against
+        // 311-315 us at step 3 and 313-314 us at step 1)
         if (wave >= 4)
-            run(std::integral_constant<int, 3>{});
+            run(std::integral_constant<int, A6D ? 8 : 3>{});
         else
             run(std::integral_constant<int, 0>{});
     } else {
@@ -829,11 +834,15 @@ static void launch_tile_a8(const GemmArgs &g, int grid, hipStream_t s)
 }
 
 // FP6 A in the dense operand order (launch_fp6_pack), packed B and packed A
-// scales; SVEC: whole 8-block stages
+// scales; SVEC: whole 8-block stages; persistent under the conditions of the
+// FP4 256 x 256 tile
 template <int BM, int BN, int WM, int WN, int AFMT>
 static void launch_tile_fp6_dense(const GemmArgs &g, int grid, hipStream_t s)
 {
-    if (g.KB % 8 == 0)
+    if (g.persist_grid > 0 && g.KB % 8 == 0)
+        hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, 1, true, true, AFMT, true, true>), dim3(g.persist_grid),
+                           dim3(64 * WM * WN), 0, s, g);
+    else if (g.KB % 8 == 0)
         hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, 1, true, true, AFMT, false, true>), dim3(grid),
                            dim3(64 * WM * WN), 0, s, g);
     else

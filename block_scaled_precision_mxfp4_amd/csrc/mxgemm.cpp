@@ -354,7 +354,9 @@ int64_t persist_grid(const Plan &p, int M, int N, int K, int num_cu, bool d_stag
     const char *pipe = std::getenv("MXGEMM_TILE_PIPELINE");
     if (pipe && std::strcmp(pipe, "deep") == 0)
         return 0;
-    const bool tile_ok = p.family == 0 && p.bm == 256 && p.bn == 256 && sa_packed;
+    // (the dense FP6 tile, family 3's only 256 x 256 one, always reads
+    // packed A scales)
+    const bool tile_ok = p.bm == 256 && p.bn == 256 && ((p.family == 0 && sa_packed) || p.family == 3);
     if (!tile_ok || p.split != 1 || !d_stage || !svec)
         return 0;
     if (M % p.bm || N % p.bn || (K / 32) % 16 || num_cu % 8 || p.grid <= num_cu)
@@ -516,7 +518,8 @@ static void fill_info(const Plan &p, int M, int N, int K, int num_cu, const mxge
     std::memset(out, 0, sizeof *out);
     // what mxgemm_run launches for beta == 0 and 16-byte aligned pointers
     const int KB = K / 32;
-    const bool svec = KB % 8 == 0 && (s.sa_packed || s.ldsa % 8 == 0) && (s.b_packed || s.ldsb % 8 == 0);
+    const bool dense6 = p.family == 3 && p.bm == 256;  // scales packed by the library
+    const bool svec = KB % 8 == 0 && (dense6 || ((s.sa_packed || s.ldsa % 8 == 0) && (s.b_packed || s.ldsb % 8 == 0)));
     out->persist_grid = s.b_layout == MXGEMM_B_KN ? 0 : persist_grid(p, M, N, K, num_cu, s.ldd % 8 == 0, svec,
                                                                      s.sa_packed != 0);
     out->kernel = p.family;
@@ -848,12 +851,13 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
             }
             if (fp6_dense) {
                 uint8_t *sap = (uint8_t *)conv + a6_bytes;
-                mx::launch_fp6_pack((const uint8_t *)A, lda_bytes, (uint8_t *)conv, M, K, stream);
-                mx::launch_pack_sb((uint32_t *)sap, (const uint8_t *)scaleA, M, KB, s.ldsa, stream);
+                mx::launch_fp6_pack((const uint8_t *)A, lda_bytes, (const uint8_t *)scaleA, s.ldsa, (uint8_t *)conv,
+                                    (uint32_t *)sap, M, K, stream);
                 g.A = (const uint8_t *)conv;
                 g.lda_b = mx::fp6_pack_group_bytes(K);
                 g.SA = sap;
                 g.sa_packed = 1;
+                g.persist_grid = (int)persist_grid(p, M, N, K, d->num_cu, g.d_stage != 0, KB % 8 == 0, true);
                 if (pack_b_here) {
                     uint8_t *bp = sap + sap_bytes, *sbp = bp + bp_bytes;
                     mx::launch_pack_b(bp, (const uint8_t *)B, N, KB, s.ldb / 2, stream);

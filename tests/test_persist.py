@@ -4,9 +4,10 @@ The persistent form (one workgroup per CU walking its tiles, the next tile's
 first stage loaded while the last tile's D is written) runs the same matrix
 instructions in the same order as the plain grid, so D must match the plain
 grid's bit for bit (MXGEMM_TILE_PERSIST=0 selects it), and sampled rows and
-columns must match the oracle.  The persistent tile is FP4 256 x 256 with
-packed B and A scales; cases cover an uneven last round (400 tiles on 256
-CUs), two and four whole rounds, and the 8192^3 shape.
+columns must match the oracle.  The persistent tiles are FP4 256 x 256 with
+packed B and A scales, and the dense FP6 256 x 256 tile (B packed by the
+caller or by the library); cases cover an uneven last round (400 tiles on
+256 CUs), two and four whole rounds, and the 8192^3 shape.
 """
 import os
 import sys
@@ -28,6 +29,8 @@ CASES = [
     (4096, 8192, 1024, 0, (256, 256), [(True, True)]),
     (8192, 8192, 1024, 0, (256, 256), [(True, True)]),
     (8192, 8192, 8192, 0, (256, 256), [(True, True)]),
+    (5120, 5120, 512, 3, (256, 256), [(True, False), (False, False)]),
+    (4096, 8192, 1024, 4, (256, 256), [(True, False), (False, False)]),
 ]
 
 
@@ -56,7 +59,7 @@ def plain_grid(p, **kw):
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "%dx%dx%d_f%d" % c[:4])
 def test_persistent_matches_plain_grid_and_oracle(case):
     M, N, K, fmt, tile, layouts = case
-    e = (118, 136) if fmt == 0 else (110, 130)
+    e = (110, 130) if fmt in (1, 2) else (118, 136)
     p = inputs.make_problem(M, N, K, seed=0x9E51 + M + N + K + fmt, e=e, a_fmt=fmt)
     p["alpha"] = -0.75
     rng = np.random.default_rng(M + N + fmt)
