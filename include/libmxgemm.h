@@ -93,12 +93,16 @@ const char *mxgemm_status_string(mxgemm_status status);
  *              the FP4 case; FP6 on the rows kernel needs an even K/32);
  *              otherwise, for M > 16, the 8-bit formats run on the tiled
  *              kernel with 8-bit A tiles, and FP6 A is first re-laid,
- *              codes unchanged, into 32-byte slots per 32-element block
- *              (rows of K bytes rounded up to 128) in a library-owned
- *              buffer per (device, stream),
- *              allocated on first use like the split-K buffers and freed
- *              by mxgemm_release_workspaces, then runs on the same tiles
- *              with the FP6 operand format of the scaled instruction, at
+ *              codes unchanged, in a library-owned buffer per (device,
+ *              stream), allocated on first use like the split-K buffers
+ *              and freed by mxgemm_release_workspaces: on large shapes
+ *              into the scaled instruction's operand order (24 bytes per
+ *              lane, 1536 bytes per 16 rows and 128 K; its A scales
+ *              shuffled beside it, and a row-major B and its scales packed
+ *              as mxgemm_pack_b packs them) for a 256 x 256 FP6 tile,
+ *              otherwise into 32-byte slots per 32-element block (rows of
+ *              K bytes rounded up to 128) for the 8-bit tiles; both pass
+ *              the FP6 operand format to the instruction, which runs it at
  *              its FP4 rate (when 256 re-laid rows reach 2^31 bytes, once
  *              per 16 rows on the skinny kernel instead).  Needs
  *              sa_packed = 0 and split_mode = MXGEMM_SPLIT_FP32 (else
@@ -221,7 +225,9 @@ mxgemm_status mxgemm_run(void *D, const void *C, const void *A, const void *B,
  * holds from load until the process ends: the split-K arrival counters
  * (first 64 KiB: 4 bytes per output tile of a split plan), the split-K fp32
  * partials unless strides->workspace brings them, and the re-laid copy of
- * an FP6 A on the tiled kernel (M * K bytes, K rounded up to 128).  Same
+ * an FP6 A on the tiled kernels (M * K bytes, K rounded up to 128, on the
+ * 8-bit tiles; about 3/4 of that plus M * K / 32 scale bytes on the FP6
+ * tile, plus N * K * 17/32 bytes when B is row-major).  Same
  * arguments, plans, kernels and results as
  * mxgemm_run, bit for bit.  Never calls hipMalloc or hipFree (the first call
  * on a device looks up that device's array once).  A plan that needs more
