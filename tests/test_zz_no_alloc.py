@@ -69,6 +69,26 @@ def test_noalloc_matches_run_on_consecutive_calls(seq):
         assert_parity(d[:, cols], ref, mag, "noalloc %s" % ((M, N, K, split, fmt),))
 
 
+def test_noalloc_fp6_dense_tile(monkeypatch):
+    """The dense FP6 tile (forced through the planner's test hook) keeps its
+    re-laid A, shuffled A scales and the packed copy of a row-major B in the
+    scratch: bit for bit mxgemm_run's output on two consecutive calls, the
+    second smaller."""
+    mx.lib()
+    monkeypatch.setenv("MXGEMM_A8_TILE", "tile_fp6_256x256")
+    for M, N, K, split, fmt in [(512, 520, 2048, 1, 3), (300, 300, 1056, 2, 4)]:
+        p = inputs.make_problem(M, N, K, seed=0xD6A1 + M + fmt, e=(118, 136), beta=1.0, c_sigma=2.0, a_fmt=fmt)
+        p["alpha"], p["beta"] = 0.75, -0.5
+        ops = operands(p)
+        assert mx.mxgemm_plan_ex(M, N, K, ops["st"], split, 256)["kernel_name"] == "tile_fp6_256x256"
+        say("case noalloc fp6 dense", (M, N, K), "split", split, "a_format", fmt)
+        d_ref = run(mx.mxgemm_run, p, ops, split)
+        d = run(mx.mxgemm_run_noalloc, p, ops, split)
+        assert np.array_equal(d, d_ref), "%d of %d elements differ from mxgemm_run" % (int((d != d_ref).sum()), d.size)
+        ref, mag, _ = oracle_ref(p)
+        assert_parity(d, ref, mag, "noalloc fp6 dense %s" % ((M, N, K, split, fmt),))
+
+
 def test_noalloc_refuses_plans_beyond_its_scratch():
     mx.lib()
     M, N, K = 4096, 4096, 8192
