@@ -12,7 +12,8 @@
 //     the four bytes one lane needs for two 16-row groups x two 128-K steps
 //     (the word layout of the asm_f4gemm README's scale shuffle, "Data
 //     layouts"), so one 4-byte LDS read feeds four matrix instructions and
-//     op_sel picks the byte.
+//     op_sel picks the byte (the dense FP6 tile keeps those words in
+//     registers).
 // Out-of-range rows and K blocks are zero-filled by the buffer loads'
 // range check, so no caller padding is needed.
 //
@@ -123,8 +124,12 @@ __device__ __forceinline__ void store_whole_tile_staged(uint16_t *D, int64_t ldd
 // K 16g.. and 64+16g.. the 8-bit instruction reads.  A padded FP6 row has the
 // same shape, with K-block g's 24 bytes in those two chunks (the first 8
 // bytes of chunk g+4), so the same reads feed the FP6 instruction.
+// A6D (FP6 A in the dense operand order of mx_fp6.hip, 256 x 256, packed B
+// and scales): a stage of A is 3 KiB per 16-row group, the lanes' 24-byte
+// operands back to back, read as three 8-byte pieces per lane; A and B fill
+// the LDS, so each wave loads its scale words into registers.
 // PERSIST (a tile with one workgroup per CU; launched for 256 x 256 with
-// packed B and A scales): one workgroup per CU walks its tiles in the order
+// packed B and A scales, FP4 or dense FP6): one workgroup per CU walks its tiles in the order
 // the plain grid runs them (hardware id blockIdx + i * grid, through the same
 // XCD remap).  After a tile's last stage (which reads buffer 1) it issues the
 // next tile's first stage into buffer 0, then writes D through buffer 1's A
