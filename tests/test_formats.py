@@ -213,6 +213,52 @@ def test_fp6_dense_tile_matches_oracle(case, fmt, monkeypatch):
     assert np.array_equal(gemm_gpu(p, split_k=split, b_packed=packed), d)
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor_b", "packed_b"])
+def test_fp6_dense_tile_strided(packed, monkeypatch):
+    """Padded A rows (a byte pitch that is a multiple of 8, not of 16: the
+    re-layout's 8-byte reads; and one that is a multiple of 16), padded B
+    rows and scale rows at odd pitches and addresses, padded C and D, on the
+    dense FP6 tile."""
+    from mxgpu import dev_bf16, dev_u8, host_bits
+    fmt = mx.FMT_FP6_E2M3
+    M, N, K = 272, 300, 2048
+    p = problem((M, N, K, 1, packed, "bf16"), fmt, seed=0x57D6 + int(packed))
+    ref, mag, _ = oracle_ref(p)
+    monkeypatch.setenv("MXGEMM_A8_TILE", "tile_fp6_256x256")
+    for lda in (K + 32, K + 64):
+        a_row = lda * 6 // 8
+        ldb, ldsa, ldsb, ldc, ldd = K + 96, K // 32 + 3, K // 32 + 5, N + 3, N + 1
+
+        def pad(X, cols, fill):
+            out = np.full((X.shape[0], cols), fill, dtype=X.dtype)
+            out[:, : X.shape[1]] = X
+            return out
+        A = dev_u8(pad(p["A"], a_row, 0x55))
+        SA_buf = dev_u8(np.concatenate([[0xFF], pad(p["SA"], ldsa, 0xFF).ravel()]))
+        C = dev_bf16(pad(p["C"], ldc, 0x7FC0))
+        D = torch.zeros((M, ldd), dtype=torch.bfloat16, device="cuda")
+        if packed:
+            info = mx.mxgemm_plan(M, N, K, 1, -1, 256)
+            B = torch.empty(info["packed_b_bytes"], dtype=torch.uint8, device="cuda")
+            SBp = torch.empty(info["packed_sb_bytes"], dtype=torch.uint8, device="cuda")
+            mx.mxgemm_pack_b(B, SBp, dev_u8(p["B"]), dev_u8(p["SB"]), N, K)
+            sb_ptr, ldb_e, ldsb_e = SBp.data_ptr(), K, K // 32
+        else:
+            B = dev_u8(pad(p["B"], ldb // 2, 0x77))
+            SB_buf = dev_u8(np.concatenate([[0xFF], pad(p["SB"], ldsb, 0xFF).ravel()]))
+            sb_ptr, ldb_e, ldsb_e = SB_buf.data_ptr() + 1, ldb, ldsb
+        st = mx.make_strides(ldd=ldd, ldc=ldc, lda=lda, ldb=ldb_e, ldsa=ldsa, ldsb=ldsb_e, b_packed=int(packed),
+                             a_format=fmt)
+        assert mx.mxgemm_plan_ex(M, N, K, st, 1, 256)["kernel_name"] == "tile_fp6_256x256"
+        say("case fp6 dense strided", "lda", lda, "packed", packed)
+        mx.mxgemm_run(D, C, A, B, SA_buf.data_ptr() + 1, sb_ptr, p["alpha"], p["beta"], M, N, K, strides=st,
+                      split_k=1)
+        torch.cuda.synchronize()
+        d = host_bits(D)
+        assert_parity(d[:, :N], ref, mag, "fp6 dense strided lda %d packed %s" % (lda, packed))
+        assert (d[:, N:] == 0).all()  # padding columns untouched
+
+
 @pytest.mark.parametrize("fmt", [mx.FMT_FP6_E2M3, mx.FMT_FP6_E3M2], ids=lambda f: NAMES[f])
 def test_fp6_dense_tile_all_codes(fmt, monkeypatch):
     """B = I through the dense FP6 tile: every FP6 code in every lane
