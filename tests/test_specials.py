@@ -4,8 +4,9 @@ The E8M0 scale codes at the ends of the range -- 0x00 (2^-127 by reading S1
 of the pages' formula 2^(e-127)), 0x01, 0xFE (2^127) and 0xFF (NaN) -- and
 the FP8 NaN / infinity codes of a wider A run through every kernel family
 (M = 1 and M <= 16: skinny; 16 < M <= 64: rows; M > 64: tiled two-stage,
-four-slot ring and persistent 256 x 256), row-major, packed B and packed B
-with packed A scales, unsplit and split K, and are compared element by
+four-slot ring and persistent 256 x 256; FP6 A on the dense FP6 tile and
+the 8-bit tile), row-major, packed B and packed B with packed A scales,
+unsplit and split K, and are compared element by
 element with the oracle under the rules of tests/mxgpu.py (NaN must match
 NaN, infinities must match the oracle's bf16 rounding, bf16 subnormals are
 compared with an absolute half-spacing, and the fp32 accumulation's own
@@ -112,6 +113,27 @@ def test_special_scale_codes_persistent():
     ref, mag, _ = oracle_ref(p, rows=rows)
     assert np.isnan(ref).any() and (np.abs(ref) > 2.0 ** 128).any()
     assert_parity(d[rows], ref, mag, "persistent special scales")
+
+
+@pytest.mark.parametrize("tile", ["tile_fp6_256x256", "tile_a8_128x256"])
+def test_special_scale_codes_fp6_tiles(tile, monkeypatch):
+    """The same mixture with FP6 E2M3 A on the dense FP6 tile (its A scales
+    shuffled by the re-layout and held in registers) and on the 8-bit tile
+    (the padded copy), row-major and packed B, unsplit and split K."""
+    monkeypatch.setenv("MXGEMM_A8_TILE", tile)
+    M, N, K = 300, 520, 2048
+    fmt = mx.FMT_FP6_E2M3
+    p = with_special_scales(inputs.make_problem(M, N, K, seed=0xF6 + len(tile), e=(118, 136), a_fmt=fmt),
+                            seed=0xF6 + len(tile))
+    ref, mag, _ = oracle_ref(p)
+    assert np.isnan(ref).any() and (np.abs(ref) > 2.0 ** 128).any()
+    for packed in (False, True):
+        st = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32, b_packed=int(packed), a_format=fmt)
+        assert mx.mxgemm_plan_ex(M, N, K, st, 1, 256)["kernel_name"] == tile
+        for s in (1, 2):
+            say("case special scales fp6", tile, "packed", packed, "split", s)
+            d = gemm_gpu(p, split_k=s, b_packed=packed)
+            assert_parity(d, ref, mag, "fp6 %s packed=%s split=%d" % (tile, packed, s))
 
 
 @pytest.mark.parametrize("shape", SHAPES[:4], ids=lambda s: "%dx%dx%d" % s)
