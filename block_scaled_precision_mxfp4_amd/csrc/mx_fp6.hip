@@ -52,10 +52,10 @@ void launch_fp6_pad(const uint8_t *A, int64_t lda_b, uint8_t *out, int M, int K,
 // number; rows past M and K-blocks past K are zero.
 //
 // A workgroup moves 32 rows x 4 steps: the rows' 384-byte runs are read in
-// 16-byte pieces (24 consecutive threads per row; 8-byte pieces when the row
-// pitch is not a multiple of 16) whose 8-byte words are dropped into LDS at
-// their operand-order places, then each of the two groups' 6 KiB runs is
-// written with 16-byte stores.  The same workgroup writes the A scales of
+// 16-byte pieces (24 consecutive threads per row, streaming loads; 8-byte
+// pieces when the row pitch is not a multiple of 16) whose 8-byte words are
+// dropped into LDS at their operand-order places, then each of the two
+// groups' 6 KiB runs is written with 16-byte stores.  The same workgroup writes the A scales of
 // its 32 rows and two 8-block steps in the shuffled scale layout (the one
 // mxgemm_pack_scales writes: word (row group, step, lane) holds rows 16j +
 // lane % 16 at K-block 4i + lane / 16 of the step, byte 2i + j; 0x7F past M
@@ -70,6 +70,18 @@ __global__ void __launch_bounds__(256) mx_fp6_pack_kernel(const uint8_t *__restr
     const int quads = (ks_pad + 3) / 4;
     const int g32 = blockIdx.x / quads, s0 = (blockIdx.x - g32 * quads) * 4;
     const int tid = threadIdx.x;
+    // the A-scale bytes of this thread's shuffled word (threads 0-127: two
+    // 8-block steps x 64 lanes), loaded before the operand bytes so that
+    // their latency overlaps the operands' instead of following it
+    const int d3 = s0 / 2 + (tid >> 6), slane = tid & 63;
+    const bool sc_on = tid < 128 && d3 < ks_pad / 2;
+    uint32_t sb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = g32 * 32 + (j & 1) * 16 + (slane & 15);
+        const int col = d3 * 8 + (j >> 1) * 4 + (slane >> 4);
+        sb[j] = sc_on && row < M && col < KB ? SA[(int64_t)row * ldsa + col] : 0x7Fu;
+    }
     // word w (of 12) of step s of row r -> its place in the group's run
     auto place = [&](int r, int s, int w, v2u v) __attribute__((always_inline)) {
         const int l = (w / 3) * 16 + (r & 15);
@@ -85,7 +97,7 @@ __global__ void __launch_bounds__(256) mx_fp6_pack_kernel(const uint8_t *__restr
             const uint8_t *src = A + (int64_t)row * lda_b + (int64_t)(s0 + s) * 96 + w * 8;
             v2u lo = v2u{0u, 0u}, hi = v2u{0u, 0u};
             if (row < M && blk1 < KB) {
-                const v4i v = *reinterpret_cast<const v4i *>(src);
+                const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i *>(src));
                 lo = v2u{(uint32_t)v[0], (uint32_t)v[1]};
                 hi = v2u{(uint32_t)v[2], (uint32_t)v[3]};
             } else if (row < M && blk0 < KB) {
@@ -107,20 +119,8 @@ __global__ void __launch_bounds__(256) mx_fp6_pack_kernel(const uint8_t *__restr
             place(r, s, w, v);
         }
     }
-    if (tid < 128) {
-        const int d3 = s0 / 2 + (tid >> 6), lane = tid & 63;
-        if (d3 < ks_pad / 2) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = g32 * 32 + (j & 1) * 16 + (lane & 15);
-                const int col = d3 * 8 + (j >> 1) * 4 + (lane >> 4);
-                const uint32_t b = row < M && col < KB ? SA[(int64_t)row * ldsa + col] : 0x7Fu;
-                word |= b << (8 * j);
-            }
-            sa_out[((int64_t)g32 * (ks_pad / 2) + d3) * 64 + lane] = word;
-        }
-    }
+    if (sc_on)
+        sa_out[((int64_t)g32 * (ks_pad / 2) + d3) * 64 + slane] = sb[0] | sb[1] << 8 | sb[2] << 16 | sb[3] << 24;
     __syncthreads();
     const int groups = (M + 15) / 16;
 #pragma unroll
