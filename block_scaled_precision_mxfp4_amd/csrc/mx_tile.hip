@@ -811,10 +811,11 @@ static void launch_tile(const GemmArgs &g, int grid, hipStream_t s)
     // need only the former)
     const bool sa_ok = SAPACK ? g.KB % 8 == 0 : g.sa_fast != 0;
     const bool sb_ok = SBPACK ? g.KB % 8 == 0 : g.sb_fast != 0;
-    // persistent form: 256 x 256 with packed B and A scales (its other
-    // layouts spill in the tile loop; the 256 x 128 tile and the 8-bit
-    // 128 x 256 tile measured no faster persistent)
-    if constexpr (BM == 256 && BN == 256 && BLAY == 1 && SAPACK) {
+    // persistent form: 256 x 256 with packed A and B scales, B's codes
+    // packed or MN-major (its other layouts spill in the tile loop; the
+    // 256 x 128 tile and the 8-bit 128 x 256 tile measured no faster
+    // persistent)
+    if constexpr (BM == 256 && BN == 256 && (BLAY == 1 || BLAY == 3) && SAPACK) {
         if (g.persist_grid > 0 && sa_ok && sb_ok) {
             hipLaunchKernelGGL((mx_tile_kernel<BM, BN, WM, WN, BLAY, true, SAPACK, 0, true>), dim3(g.persist_grid),
                                dim3(64 * WM * WN), 0, s, g);

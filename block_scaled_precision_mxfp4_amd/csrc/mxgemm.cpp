@@ -340,7 +340,8 @@ Plan plan_run(int M, int N, int K, const mxgemm_strides &s, int split_k, int num
 size_t packed_b_bytes(int N, int K) { return (size_t)cdiv(N, 16) * 16 * (size_t)cdiv(K / 32, 4) * 64; }
 size_t packed_sb_bytes(int N, int K) { return (size_t)cdiv(N, 32) * 32 * (size_t)cdiv(K / 32, 8) * 8; }
 
-// The two-stage tiled kernel's 256 x 256 tile with packed B and A scales runs
+// The two-stage tiled kernel's 256 x 256 tile with packed A and B scales (B's
+// codes packed or MN-major; or the dense FP6 tile) runs
 // persistent (one workgroup per CU walking its tiles) when every tile is
 // whole and unsplit, the epilogue is staged (d_stage), whole 8-block stages
 // with 8-byte scale loads apply (svec), each tile has an even number of
@@ -520,8 +521,7 @@ static void fill_info(const Plan &p, int M, int N, int K, int num_cu, const mxge
     const int KB = K / 32;
     const bool dense6 = p.family == 3 && p.bm == 256;  // scales packed by the library
     const bool svec = KB % 8 == 0 && (dense6 || ((s.sa_packed || s.ldsa % 8 == 0) && (s.b_packed || s.ldsb % 8 == 0)));
-    out->persist_grid = s.b_layout == MXGEMM_B_KN ? 0 : persist_grid(p, M, N, K, num_cu, s.ldd % 8 == 0, svec,
-                                                                     s.sa_packed != 0);
+    out->persist_grid = persist_grid(p, M, N, K, num_cu, s.ldd % 8 == 0, svec, s.sa_packed != 0);
     out->kernel = p.family;
     out->tile_m = p.bm;
     out->tile_n = p.bn;
@@ -887,7 +887,7 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
             else if (std::strcmp(e, "deep") == 0)
                 deep = deep_ok && !g.split_atomic && !b_kn;
         }
-        if (!deep && !b_kn) {
+        if (!deep) {
             const bool svec = (s.sa_packed ? KB % 8 == 0 : g.sa_fast != 0) &&
                               (s.b_packed ? KB % 8 == 0 : g.sb_fast != 0);
             g.persist_grid = (int)persist_grid(p, M, N, K, d->num_cu, g.d_stage != 0, svec, s.sa_packed != 0);

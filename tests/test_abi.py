@@ -283,6 +283,11 @@ def test_persistent_form_is_planned_only_where_it_applies(monkeypatch):
     assert pg(4096, 4096, 4096, st(4096, 4096)) == 0               # one round of tiles
     assert pg(8192, 8192, 8192, st(8192, 8192, ldd=8196)) == 0     # unstaged epilogue
     assert mx.mxgemm_plan_ex(8192, 8192, 8192, st(8192, 8192), -1, 128)["persist_grid"] == 128
+    # MN-major B codes with packed scales: persistent too; with row-major scales not
+    kn = lambda pk: mx.make_strides(ldd=8192, ldc=8192, lda=8192, ldb=8192, ldsa=256, ldsb=256, b_packed=pk,
+                                    sa_packed=pk, b_layout=mx.B_KN)
+    assert pg(8192, 8192, 8192, kn(1)) == 256
+    assert pg(8192, 8192, 8192, kn(0)) == 0
     monkeypatch.setenv("MXGEMM_TILE_PERSIST", "0")
     assert pg(8192, 8192, 8192, st(8192, 8192)) == 0
 

@@ -12,7 +12,7 @@ result (same matrix instructions in the same order).  Cases: ragged M, N
 and K (K-block counts that are not multiples of 8), M = 1, every tile
 shape, row-major and packed B scales, packed A scales, split 1/2/4, row
 pitches wider than N holding large codes that must never be read, and the
-8192^3 shape.
+8192^3 shape, and the persistent form against its plain grid.
 """
 import os
 import sys
@@ -102,6 +102,29 @@ def test_mn_major_square_8192(monkeypatch):
     rows = np.array([0, 1, 255, 256, 4095, 8191], dtype=np.int64)
     ref, mag, _ = oracle_ref(p, rows=rows)
     assert_parity(d[rows], ref, mag, "kn 8192^3")
+
+
+def test_mn_major_persistent_matches_plain_grid(monkeypatch):
+    """MN-major B with packed scales on 400 whole 256 x 256 tiles (an uneven
+    last round on 256 CUs): the persistent form equals the plain grid and the
+    K-major result bit for bit, and sampled rows match the oracle."""
+    M = N = 5120
+    K = 512
+    p = kn_problem(M, N, K, seed=0x5120)
+    st = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=p["ldb_kn"], ldsa=K // 32, ldsb=K // 32, b_packed=1, sa_packed=1,
+                         b_layout=mx.B_KN)
+    assert mx.mxgemm_query_ex(M, N, K, st, -1)["persist_grid"] > 0
+    say("case kn persistent")
+    d = gemm_gpu(p, split_k=-1, b_packed=True, sa_packed=True)
+    monkeypatch.setenv("MXGEMM_TILE_PERSIST", "0")
+    say("case kn plain grid")
+    d_plain = gemm_gpu(p, split_k=-1, b_packed=True, sa_packed=True)
+    monkeypatch.delenv("MXGEMM_TILE_PERSIST")
+    assert np.array_equal(d, d_plain), "%d elements differ from the plain grid" % int((d != d_plain).sum())
+    assert np.array_equal(d, gemm_gpu(k_major(p), split_k=-1, b_packed=True, sa_packed=True))
+    rows = np.array([0, 255, 256, 2600, M - 1], dtype=np.int64)
+    ref, mag, _ = oracle_ref(p, rows=rows)
+    assert_parity(d[rows], ref, mag, "kn persistent")
 
 
 def test_mn_major_strides_and_offsets():
