@@ -388,16 +388,33 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(GemmArgs g)
             store16_coherent(rws, z * PART + (uint32_t)((((wave * NRW + nr) * MG + mg) * 64 + lane) * 16), acc[nr][mg]);
     if (!split_arrive_last(g.counters + t, g.split))
         return;
+    // every fragment's partial of a chunk is requested before any is added,
+    // so that one memory latency per chunk is paid, not one per fragment;
+    // each element still adds the chunks in z order
+    v4f sum[NRW][MG];
 #pragma unroll
     for (int nr = 0; nr < NRW; ++nr)
 #pragma unroll
-        for (int mg = 0; mg < MG; ++mg) {
-            const uint32_t idx = (uint32_t)((((wave * NRW + nr) * MG + mg) * 64 + lane) * 16);
-            v4f sum = load16_coherent(rws, idx);
-            for (int zz = 1; zz < g.split; ++zz)
-                sum += load16_coherent(rws, zz * PART + idx);
-            store_quad(ep, mb + mg * 16, nb4 + nr * 16, sum);
-        }
+        for (int mg = 0; mg < MG; ++mg)
+            sum[nr][mg] = load16_coherent(rws, (uint32_t)((((wave * NRW + nr) * MG + mg) * 64 + lane) * 16));
+    for (int zz = 1; zz < g.split; ++zz) {
+        v4f part[NRW][MG];
+#pragma unroll
+        for (int nr = 0; nr < NRW; ++nr)
+#pragma unroll
+            for (int mg = 0; mg < MG; ++mg)
+                part[nr][mg] = load16_coherent(rws, zz * PART + (uint32_t)((((wave * NRW + nr) * MG + mg) * 64 + lane) * 16));
+#pragma unroll
+        for (int nr = 0; nr < NRW; ++nr)
+#pragma unroll
+            for (int mg = 0; mg < MG; ++mg)
+                sum[nr][mg] += part[nr][mg];
+    }
+#pragma unroll
+    for (int nr = 0; nr < NRW; ++nr)
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg)
+            store_quad(ep, mb + mg * 16, nb4 + nr * 16, sum[nr][mg]);
 }
 
 template <int MG, int NRW, int U, int NS, bool BPACK, int AFMT>

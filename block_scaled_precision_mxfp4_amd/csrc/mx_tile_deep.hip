@@ -310,15 +310,29 @@ __global__ void __launch_bounds__(64 * WM * WN) mx_tile_deep_kernel(GemmArgs g)
                              acc[fn][fm]);
     if (!split_arrive_last(g.counters + t, g.split))
         return;
+    // (as in mx_tile_kernel: a group's partials of a chunk requested
+    // together, each element adding the chunks in z order)
+    constexpr int FG = FM < 4 ? FM : 4;  // fragments per group
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const uint32_t idx = (uint32_t)((((wave * FN + fn) * FM + fm) * 64 + lane) * 16);
-            v4f sum = load16_coherent(rws, idx);
-            for (int zz = 1; zz < g.split; ++zz)
-                sum += load16_coherent(rws, zz * PART + idx);
-            store_quad(ep, mb + fm * 16, nb + fn * 16, sum);
+        for (int f0 = 0; f0 < FM; f0 += FG) {
+            v4f sum[FG];
+#pragma unroll
+            for (int i = 0; i < FG; ++i)
+                sum[i] = load16_coherent(rws, (uint32_t)((((wave * FN + fn) * FM + f0 + i) * 64 + lane) * 16));
+            for (int zz = 1; zz < g.split; ++zz) {
+                v4f part[FG];
+#pragma unroll
+                for (int i = 0; i < FG; ++i)
+                    part[i] = load16_coherent(rws, zz * PART + (uint32_t)((((wave * FN + fn) * FM + f0 + i) * 64 + lane) * 16));
+#pragma unroll
+                for (int i = 0; i < FG; ++i)
+                    sum[i] += part[i];
+            }
+#pragma unroll
+            for (int i = 0; i < FG; ++i)
+                store_quad(ep, mb + (f0 + i) * 16, nb + fn * 16, sum[i]);
         }
 }
 
