@@ -59,21 +59,34 @@ std::pair<int, int> split_chunks(int KB, int s, int gran)
     return {per, cdiv(KB, per)};
 }
 
-// Cost model of the tiled kernel, per 256-K stage of a round of workgroups:
-// the larger of the matrix time (2*bm*bn*256 flop per tile at 40 % of a
-// CU's peak, the fraction the 256x256 tile sustains in its main loop) and
-// the operand load time ((bm + bn) * 128 bytes per tile at 65 GB/s per CU,
-// what one stage of direct-to-LDS loads reaches), times the tiles a CU runs
-// at once; plus, for split K, the partial round trip and 2 us per chunk for
-// its serialized tail.  Fitted on MI355X to a sweep of every tile and split
-// over eight shapes (128x256x512 ... 2048x8192x8192): the choices it makes
-// there are within 11 % of the best measured (3 % on average).  The rates
-// only rank candidates; the bench reports measured numbers.
+// Cost model of the tiled kernel: a measured time per 256-K stage for one
+// round of workgroups of each tile (its occupancy's workgroups per CU at
+// once), scaled down to 0.5 + 0.5 * the filled fraction when a single round
+// leaves slots idle; times the rounds and stages; plus, for split K, 1 us per
+// chunk, the partials' round trip at 5 TB/s and the last workgroup's reads.
+// Fitted on MI355X to a sweep of every tile at splits 1, 2, 4, 8 over 15
+// shapes (128x256x512 ... 8192x8192x2048, 2048x2048x8192, 1024x4096x16384,
+// 4352^2 x 4096): it picks the measured best on all of them.  The times only
+// rank candidates; the bench reports measured numbers.
+double tile_stage_seconds(int bm, int bn)
+{
+    if (bm == 256 && bn == 256)
+        return 1.6e-6;
+    if (bm == 256)
+        return 1.4e-6;
+    if (bm == 128)
+        return 1.2e-6;
+    return 1.0e-6;
+}
+constexpr double kTileChunkCost = 1e-6;
+constexpr double kHbm = 5.0e12;
+// the 8-bit tiles' model: matrix time at 40 % of a CU's peak against the
+// operand loads at 65 GB/s per CU, 2 us per split chunk (fitted before the
+// split fix-up batched its loads)
 constexpr double kCuFlops = 4.0 * 4096.0 * 2.4e9;
 constexpr double kMatrixFraction = 0.4;
 constexpr double kCuLoadRate = 65e9;
 constexpr double kSplitChunkCost = 2e-6;
-constexpr double kHbm = 5.0e12;
 // The skinny kernels split K only into chunks of at least 64 scale blocks
 // (2048 K): a sweep of splits 1..16 over 20 shapes with M <= 64 on MI355X
 // found every shorter chunk slower than the next smaller split (the
@@ -212,14 +225,18 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool
             if (split_req <= 0 && s > 1 && eff < s)
                 continue;
             const int64_t wgs = tiles * eff;
-            const double rounds = (double)((wgs + (int64_t)num_cu * tk.occupancy - 1) / ((int64_t)num_cu * tk.occupancy));
-            const double t_math = 2.0 * tk.bm * tk.bn * 256.0 * tk.occupancy / (kCuFlops * kMatrixFraction);
-            const double t_load = (double)(tk.bm + tk.bn) * 128.0 * tk.occupancy / kCuLoadRate;
-            double t = rounds * (per / 8) * std::max(t_math, t_load);
+            const int64_t slots = (int64_t)num_cu * tk.occupancy;
+            const int64_t rounds = (wgs + slots - 1) / slots;
+            // a single, partly filled round runs its stages faster
+            const double fill = std::min(1.0, (double)wgs / (double)slots);
+            const double ts = tile_stage_seconds(tk.bm, tk.bn) * (rounds == 1 ? 0.5 + 0.5 * fill : 1.0);
+            double t = (double)rounds * (per / 8) * ts;
             if (eff > 1)
-                t += kSplitChunkCost * eff + (double)tiles * eff * tk.bm * tk.bn * 4 * 2 / kHbm +
+                t += kTileChunkCost * eff + (double)tiles * eff * tk.bm * tk.bn * 4 * 2 / kHbm +
                      (double)eff * tk.bm * tk.bn * 4 / kCuL2;
-            if (t < best_t * 0.97 || split_req > 0) {
+            // (on a tie the later candidate -- smaller tile, larger split --
+            // wins: measured ties went to the one with more workgroups)
+            if (t <= best_t * 1.005 || split_req > 0) {
                 if (split_req > 0 && t >= best_t)
                     continue;
                 best_t = t;

@@ -276,7 +276,10 @@ def test_persistent_form_is_planned_only_where_it_applies(monkeypatch):
     assert mx.mxgemm_plan(8192, 8192, 8192, 1, -1, 256)["persist_grid"] == 0    # row-major A scales
     assert pg(5120, 5120, 512, st(5120, 512, pk=0)) == 0            # 256 x 256 needs packed B and A scales
     assert pg(5120, 5120, 512, st(5120, 512)) == 256
+    monkeypatch.setenv("MXGEMM_FORCE_TILE", "1")
     assert pg(4352, 4352, 1024, st(4352, 1024)) == 0                # 256 x 128 tile: plain grid
+    monkeypatch.delenv("MXGEMM_FORCE_TILE")
+    assert pg(4352, 4352, 1024, st(4352, 1024)) == 256
     assert pg(8192, 8192, 8192, st(8192, 8192), split=2) == 0      # split K
     assert pg(8192, 8192, 8448, st(8192, 8448)) == 0               # 264 blocks: odd stage count
     assert pg(8192, 8200, 8192, st(8200, 8192)) == 0               # ragged N tile
