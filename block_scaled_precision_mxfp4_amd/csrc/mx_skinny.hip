@@ -437,9 +437,19 @@ __global__ void __launch_bounds__(256) mx_skinny_kernel(GemmArgs g)
         const int f = i * 4 + wave;
         if (f < NF) {
             const uint32_t idx = (uint32_t)((f * 64 + lane) * 16);
+            // four chunks in flight at a time, added in z order (a chunk
+            // past the split reads zeros from past the range and is not added)
             v4f tot = load16_coherent(rws, idx);
-            for (int zz = 1; zz < g.split; ++zz)
-                tot += load16_coherent(rws, zz * PART + idx);
+            for (int zz = 1; zz < g.split; zz += 4) {
+                v4f part[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    part[h] = load16_coherent(rws, zz + h < g.split ? (zz + h) * PART + idx : kOOB);
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    if (zz + h < g.split)
+                        tot += part[h];
+            }
             int m, n;
             block_mn(f, m, n);
             store_quad(ep, m, n, tot);
