@@ -114,8 +114,8 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool
         // and share one K chunk, with A staged once per workgroup.  The split
         // is the smallest that gives most CUs a workgroup while every chunk
         // keeps at least two batches (measured on MI355X: 64x7168x16384
-        // fastest at split 2, where a third of the time is the partial-sum
-        // tail and a larger split costs more than it gains).
+        // fastest at split 2; split 4 moves the data faster with two
+        // workgroups per CU but its partial-sum tail costs more than that).
         const int mg = cdiv(M, 16);
         const int idx = mg - 2;
         const int rows_wg = 64 * rows[idx].nrw;
