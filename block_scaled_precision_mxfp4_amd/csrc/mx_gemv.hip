@@ -1,0 +1,215 @@
+// Single-row MXFP4 GEMV (M == 1, FP4 A, row-major FP4 B) on gfx950.
+//
+// The cost is reading B once from HBM.  A plain streaming read of B's bytes
+// runs fastest in small pieces: many workgroups, each wave a few KiB.  This
+// kernel gives a workgroup 4 rows of B (4 columns of D) and the whole of K;
+// its four waves take 2048-K chunks of those rows in turn (chunk c to wave
+// c mod 4), 4 KiB of B per chunk, and add their sums through LDS in wave
+// order.  One chunk per wave at K = 8192.
+//
+// One scaled 16x16x128 FP4 instruction ("CDNA4 dense MFMA builtins",
+// "Mixed-precision with scaling") covers 4 rows x 4 consecutive 128-K steps
+// of B against all 16 steps of the chunk's A:
+//   - B operand lane l (row x = l % 16 of the instruction's first operand,
+//     K-block l / 16): B row x / 4, step 4t + x % 4 of the chunk for
+//     instruction t = 0..3.  One load instruction then reads 256 contiguous
+//     bytes of each of the 4 rows, and the four of a chunk the rows' whole
+//     1 KiB.
+//   - A operand lane l (column y = l % 16): step y of the chunk, K-block
+//     l / 16 -- the chunk's 1 KiB of A in one load, the same for all four
+//     instructions.
+// Output (x, y) of instruction t is B row x / 4 at step 4t + x % 4 against A
+// at step y; it is a term of the GEMV only where y = 4t + x % 4.  Lane l
+// holds outputs x = 4 (l / 16) + i, y = l % 16 (i = 0..3), so its term is
+// accumulator i = l % 4 of instruction t = (l % 16) / 4, for B row l / 16:
+// each row's 16 terms sit in one 16-lane row of the wave.  The other outputs
+// (an A step against a different B step) are never read.
+//
+// Scales follow their operand lanes: lane l's A scale is A's K-block
+// (step l % 16, block l / 16); its B scale for instruction t is that of B
+// row (l % 16) / 4, step 4t + l % 4, block l / 16.  Each lane loads one
+// dword of scale bytes (A: step l % 16's four blocks; B: row l / 16, step
+// l % 16) and the B words reach their operand lanes by a cross-lane permute;
+// the lane's byte is shifted down for op_sel 0.
+//
+// XQ: A is a bf16 row (the decode step), quantized on load with the
+// activation quantizer's rule: each A operand lane loads its whole 32-element
+// block (64 bytes) and encodes it itself, so its codes and scale byte are
+// exactly the operand and scale the lane passes to the instruction.
+//
+// Requires K % 2048 == 0 (every chunk whole: no range checks inside K, no
+// scale bytes of a neighbouring row), 16-byte aligned scale rows, split 1.
+#include "mx_args.hpp"
+#include "mx_device.hpp"
+#include "mx_quantize.hpp"
+
+namespace mx {
+
+constexpr int kGemvRows = 4;     // rows of B (columns of D) per workgroup
+constexpr int kGemvChunk = 2048; // K per chunk: 16 steps of 128
+
+template <bool XQ>
+struct GemvChunk {
+    v4i b[4];        // B operand of instruction t
+    v4i a;           // A operand, all 16 steps of the chunk
+    uint32_t sa;     // A scale bytes of step l % 16
+    uint32_t sb;     // B scale bytes of row l / 16, step l % 16
+    v4i x[XQ ? 4 : 1];  // XQ: the lane's bf16 block of A
+};
+
+// Loads of chunk c (nothing, without memory traffic, when !on).  The scale
+// words and the A operand go first: the scale permutes can then start while
+// B is still arriving, and each multiply waits only for its own B operand.
+template <bool XQ>
+__device__ __forceinline__ void gemv_issue(GemvChunk<XQ> &ch, int c, bool on, __amdgpu_buffer_rsrc_t rb,
+                                           __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rsa,
+                                           __amdgpu_buffer_rsrc_t rsb, uint32_t b_lane, uint32_t sb_lane,
+                                           int lane)
+{
+    const uint32_t bc = (uint32_t)c * (kGemvChunk / 2);
+    ch.sb = load4(rsb, on && sb_lane != kOOB ? sb_lane + (uint32_t)c * 64 : kOOB);
+    if constexpr (XQ) {
+        // bf16 elements c * 2048 + (l % 16) * 128 + (l / 16) * 32 ... + 31
+        const uint32_t xo = 4 * bc + (lane & 15) * 256 + (lane >> 4) * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            ch.x[i] = load16(ra, on ? xo + i * 16 : kOOB);
+    } else {
+        ch.sa = load4(rsa, on ? (uint32_t)c * 64 + (lane & 15) * 4 : kOOB);
+        ch.a = load16(ra, on ? bc + (lane & 15) * 64 + (lane >> 4) * 16 : kOOB);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        ch.b[t] = load16_stream(rb, on && b_lane != kOOB ? b_lane + bc + t * 256 : kOOB);
+}
+
+template <bool XQ>
+__device__ __forceinline__ void gemv_compute(const GemvChunk<XQ> &ch, v4f (&acc)[4], int lane)
+{
+    const int sh = 8 * (lane >> 4);
+    v4i a = ch.a;
+    int sa;
+    if constexpr (XQ) {
+        uint32_t s8;
+        quantize_block(ch.x, a, s8);
+        sa = (int)s8;
+    } else {
+        sa = (int)(ch.sa >> sh);
+    }
+    const int q = lane & 15;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        // this lane's B scale word: row q / 4, step 4t + q % 4 of the chunk
+        const int src = (q >> 2) * 16 + 4 * t + (q & 3);
+        const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)ch.sb);
+        acc[t] = mfma_fp4<0, 0>(ch.b[t], a, acc[t], (int)(w >> sh), sa);
+    }
+}
+
+// LOOP = false: at most one chunk per wave (K <= 8192), one register set,
+// so that more waves fit a SIMD
+template <bool XQ, bool LOOP>
+__global__ void __launch_bounds__(256) mx_gemv_kernel(GemmArgs g)
+{
+    __shared__ float s_part[4][kGemvRows];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n0 = blockIdx.x * kGemvRows;
+    const int rows = min(kGemvRows, g.N - n0);
+    const uint32_t kbytes = (uint32_t)(g.K / 2);
+    const auto rb = make_rsrc(g.B + (int64_t)n0 * g.ldb_b, (uint32_t)((rows - 1) * g.ldb_b) + kbytes);
+    const auto rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)((rows - 1) * g.ldsb + g.KB));
+    const auto ra = make_rsrc(g.A, XQ ? 4 * kbytes : kbytes);  // XQ: K bf16
+    const auto rsa = make_rsrc(g.SA, (uint32_t)g.KB);
+
+    // per-lane offsets inside a chunk: B row (l % 16) / 4 at step l % 4 of
+    // the instruction's four, K-block l / 16; B scale dword: row l / 16,
+    // step l % 16.  Rows past N load nothing.
+    const int br = (lane & 15) >> 2;
+    const uint32_t b_lane = br < rows ? (uint32_t)(br * g.ldb_b) + (lane & 3) * 64 + (lane >> 4) * 16 : kOOB;
+    const int sr = lane >> 4;
+    const uint32_t sb_lane = sr < rows ? (uint32_t)(sr * g.ldsb) + (lane & 15) * 4 : kOOB;
+
+    v4f acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int chunks = g.K / kGemvChunk;
+    int c = wave;
+    if (c < chunks) {
+        GemvChunk<XQ> x;
+        gemv_issue(x, c, true, rb, ra, rsa, rsb, b_lane, sb_lane, lane);
+        if (!LOOP) {
+            gemv_compute(x, acc, lane);
+        } else if (c + 4 >= chunks) {
+            gemv_compute(x, acc, lane);  // one chunk for this wave (K <= 8192)
+        } else {
+            // two register sets: each chunk's loads are issued before the
+            // previous chunk's multiplies.  Every pass issues and multiplies
+            // both sets (a chunk past K loads nothing and adds zeros), so no
+            // load is conditional and each multiply waits only for its own
+            // operands.
+            GemvChunk<XQ> y;
+            const int mine = (chunks - wave + 3) / 4;  // this wave's chunks
+            for (int i = 0; i < mine; i += 2) {
+                gemv_issue(y, c + 4, c + 4 < chunks, rb, ra, rsa, rsb, b_lane, sb_lane, lane);
+                gemv_compute(x, acc, lane);
+                gemv_issue(x, c + 8, c + 8 < chunks, rb, ra, rsa, rsb, b_lane, sb_lane, lane);
+                gemv_compute(y, acc, lane);
+                c += 8;
+            }
+        }
+    }
+
+    // the lane's term: accumulator l % 4 of instruction (l % 16) / 4
+    const int ti = (lane & 15) >> 2, ii = lane & 3;
+    float v = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (t == ti && i == ii)
+                v = acc[t][i];
+    // sum of the 16 lanes of each row: quad (lane ^ 1, lane ^ 2), then the
+    // mirrored half-row and row partners, so every lane ends with its row's
+    // total in one fixed order
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));
+    if ((lane & 15) == 0)
+        s_part[wave][lane >> 4] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        v4f tot;
+#pragma unroll
+        for (int r = 0; r < kGemvRows; ++r) {
+            float s = s_part[0][r];
+#pragma unroll
+            for (int w = 1; w < 4; ++w)
+                s += s_part[w][r];
+            tot[r] = s;
+        }
+        Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec, g.c_f32};
+        store_quad(ep, 0, n0, tot);
+    }
+}
+
+void launch_gemv(const GemmArgs &g, int grid, hipStream_t s)
+{
+    if (g.K <= 4 * kGemvChunk)
+        hipLaunchKernelGGL((mx_gemv_kernel<false, false>), dim3(grid), dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((mx_gemv_kernel<false, true>), dim3(grid), dim3(256), 0, s, g);
+}
+
+void launch_gemv_bf16a(const GemmArgs &g, int grid, hipStream_t s)
+{
+    if (g.K <= 4 * kGemvChunk)
+        hipLaunchKernelGGL((mx_gemv_kernel<true, false>), dim3(grid), dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((mx_gemv_kernel<true, true>), dim3(grid), dim3(256), 0, s, g);
+}
+
+}  // namespace mx

@@ -33,7 +33,8 @@ constexpr int kMaxDevices = 64;
 constexpr int kSplits[] = {1, 2, 4, 8, 16};
 
 struct Plan {
-    int family = 0;  // 0 tiled, 1 skinny (M <= 16), 2 skinny rows (16 < M <= 64)
+    int family = 0;  // 0 tiled, 1 skinny (M <= 16), 2 skinny rows (16 < M <= 64), 3 tiled with
+                     // a wider A, 4 single-row GEMV (M == 1)
     int index = 0;   // index into the kernel table of the family
     int bm = 0, bn = 0;
     int split = 1;
@@ -94,8 +95,21 @@ constexpr double kSplitChunkCost = 2e-6;
 constexpr int kMinSkinnyChunk = 64;
 constexpr double kCuL2 = 64.0 * 2.4e9;
 
+// The single-row GEMV (mx_gemv.hip) takes M == 1 with FP4 A and row-major B
+// when K is a multiple of its 2048-K chunk and its 4-row workgroups fill at
+// least one per CU (N >= 4 * CUs); unsplit.  MXGEMM_GEMV=0 keeps such shapes
+// on the skinny kernel.
+bool gemv_applies(int M, int N, int K, int b_packed, int split_req, int num_cu, int a_format)
+{
+    if (M != 1 || a_format != MXGEMM_FMT_FP4 || b_packed || K % 2048 || split_req > 1 ||
+        (int64_t)cdiv(N, 4) < num_cu)
+        return false;
+    const char *e = std::getenv("MXGEMM_GEMV");
+    return !(e && std::strcmp(e, "0") == 0) && !std::getenv("MXGEMM_FORCE_NR");
+}
+
 Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool tiled_only = false,
-              int force_nr = 0, int a_format = MXGEMM_FMT_FP4)
+              int force_nr = 0, int a_format = MXGEMM_FMT_FP4, bool allow_gemv = true)
 {
     const int KB = K / 32;
     if (num_cu <= 0)
@@ -159,6 +173,19 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool
         const size_t part = (size_t)rows_wg * mg * 16 * 4;
         best.counter_bytes = best.split > 1 ? (size_t)tiles * 4 : 0;
         best.ws_bytes = best.split > 1 ? (size_t)tiles * best.split * part : 0;
+        return best;
+    }
+    if (!tiled_only && allow_gemv && force_nr == 0 &&
+        gemv_applies(M, N, K, b_packed, split_req, num_cu > 0 ? num_cu : 256, a_format)) {
+        best.family = 4;
+        best.bm = 1;
+        best.bn = 4;
+        best.split = 1;
+        best.kb_per_split = KB;
+        best.tiles_m = 1;
+        best.tiles_n = cdiv(N, 4);
+        best.grid = best.tiles_n;
+        best.name = "gemv_m1_n4";
         return best;
     }
     if (M <= 16 && !tiled_only) {
@@ -335,12 +362,13 @@ Plan plan_a8(int M, int N, int K, int split_req, int num_cu, bool fp6 = false, b
 // 16 < M <= 64 on the rows kernel (FP6: an even K-block count); otherwise
 // with M > 16 on the 8-bit tiles, FP6 re-laid first; any other wider A on
 // the skinny kernel per 16 rows.
-Plan plan_run(int M, int N, int K, const mxgemm_strides &s, int split_k, int num_cu)
+Plan plan_run(int M, int N, int K, const mxgemm_strides &s, int split_k, int num_cu, bool allow_gemv = true)
 {
     // an MN-major B is read through the tiled kernel's transposed LDS loads
     if (s.a_format == MXGEMM_FMT_FP4)
         return plan_for(M, N, K, s.b_packed, split_k, num_cu,
-                        s.split_mode == MXGEMM_SPLIT_BF16_ATOMIC || s.b_layout == MXGEMM_B_KN);
+                        s.split_mode == MXGEMM_SPLIT_BF16_ATOMIC || s.b_layout == MXGEMM_B_KN, 0,
+                        MXGEMM_FMT_FP4, allow_gemv);
     const bool fp6 = s.a_format == MXGEMM_FMT_FP6_E2M3 || s.a_format == MXGEMM_FMT_FP6_E3M2;
     if (M > 16 && M <= 64 && (!fp6 || (K / 32) % 2 == 0))
         return plan_for(M, N, K, s.b_packed, split_k, num_cu, false, 0, s.a_format);
@@ -731,7 +759,10 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     st = device_info(&d);
     if (st != MXGEMM_OK)
         return st;
-    Plan p = plan_run(M, N, K, s, split_k, d->num_cu);
+    // the GEMV reads the scale rows as aligned dwords (16-byte aligned rows,
+    // as the skinny kernel's vector scale path); a bf16 A has no scale row
+    const bool gemv_ok = (X || (aligned(scaleA, 16) && s.ldsa % 16 == 0)) && aligned(scaleB, 16) && s.ldsb % 16 == 0;
+    Plan p = plan_run(M, N, K, s, split_k, d->num_cu, gemv_ok);
     // a wider A on the skinny kernel (one 16-row group, nr 1): one launch
     // per 16 rows of A
     const bool wide = s.a_format != MXGEMM_FMT_FP4 && p.family == 1;
@@ -837,9 +868,13 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     if (g.split_atomic)
         mx::launch_d_init(g, stream);
     if (X) {
-        if (p.family != 1)  // M == 1 with the fp32 split reduction plans the skinny kernel
+        // M == 1 with the fp32 split reduction plans the GEMV or the skinny kernel
+        if (p.family == 4)
+            mx::launch_gemv_bf16a(g, (int)p.grid, stream);
+        else if (p.family == 1)
+            mx::launch_skinny_bf16a(p.bn / 16, s.b_packed != 0, g, (int)p.grid, stream);
+        else
             return MXGEMM_ERR_INVALID_ARG;
-        mx::launch_skinny_bf16a(p.bn / 16, s.b_packed != 0, g, (int)p.grid, stream);
     } else if (wide) {
         // stream-ordered launches over 16-row blocks of A, C and D; the split
         // counters return to zero at the end of each
@@ -915,6 +950,8 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
             (s.sa_packed ? k.deep_packed_sa : s.b_packed ? k.deep_packed : k.deep_plain)(g, (int)p.grid, stream);
         else
             (s.sa_packed ? k.packed_sa : s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
+    } else if (p.family == 4) {
+        mx::launch_gemv(g, (int)p.grid, stream);
     } else if (p.family == 1) {
         int n = 0;
         const mx::SkinnyKernel &k = mx::skinny_kernels(&n)[p.index];

@@ -328,10 +328,10 @@ mxgemm_status mxgemm_quantize(void *A, void *scaleA, const void *X, int M, int K
  * and split_k as for mxgemm_run; strides->lda / ldsa are ignored, and
  * a_format, sa_packed and split_mode must be 0 (else
  * MXGEMM_ERR_INVALID_ARG).
- *   M == 1 (decode), K-major B: one launch.  The skinny kernel loads the
- *     bf16 row and quantizes each 32-block in registers with the quantizer's
- *     rule, so D is bit for bit what mxgemm_quantize followed by mxgemm_run
- *     gives.
+ *   M == 1 (decode), K-major B: one launch.  The kernel mxgemm_run would
+ *     plan (the single-row GEMV or the skinny kernel) loads the bf16 row and
+ *     quantizes each 32-block in registers with the quantizer's rule, so D
+ *     is bit for bit what mxgemm_quantize followed by mxgemm_run gives.
  *   M > 1, or an MN-major B (b_layout = MXGEMM_B_KN): mxgemm_quantize into a library-owned buffer of
  *     M*K/2 + M*K/32 bytes per (device, stream) (allocated on first use like
  *     the split-K buffers, freed by mxgemm_release_workspaces), then
@@ -367,7 +367,10 @@ mxgemm_status mxgemm_f16_run(void *C, const void *A, const void *B, int M, int N
 typedef struct mxgemm_info {
     int32_t kernel;          /* kernel family: 0 = tiled (LDS, M > 64); 1 = skinny (M <= 16,
                                 streams B); 2 = skinny rows (16 < M <= 64, streams B, A
-                                shared through LDS) */
+                                shared through LDS); 3 = tiled with an FP8/FP6 A; 4 =
+                                single-row GEMV (M == 1, row-major B, K % 2048 == 0,
+                                N >= 4 x num_cu, unsplit; 4 rows of B per workgroup; with
+                                16-byte aligned scale rows, else the skinny kernel) */
     int32_t tile_m, tile_n;  /* output tile per workgroup */
     int32_t split_k;         /* K chunks the plan uses */
     int64_t grid;            /* workgroups launched */

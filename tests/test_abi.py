@@ -220,7 +220,11 @@ def test_plan_for_workloads(name):
     for b_packed in (0, 1):
         p = mx.mxgemm_plan(M, N, K, b_packed, -1, 256)
         assert p["split_k"] in (1, 2, 4, 8, 16)
-        if M <= 16:
+        if M == 1 and not b_packed and K % 2048 == 0 and cdiv(N, 4) >= 256:
+            # the single-row GEMV: 4 rows of B per workgroup, unsplit
+            assert p["kernel"] == 4 and p["kernel_name"] == "gemv_m1_n4"
+            assert (p["tile_m"], p["tile_n"], p["split_k"]) == (1, 4, 1)
+        elif M <= 16:
             assert p["kernel"] == 1 and p["kernel_name"].startswith("skinny")
             assert p["tile_m"] >= M
         elif M <= 64:

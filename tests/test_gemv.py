@@ -1,0 +1,189 @@
+"""GPU parity of the single-row GEMV (`gemv_m1_n4`: M == 1, FP4 A, row-major
+FP4 B, K a multiple of 2048), through the C-ABI, against the oracle.
+
+The planner sends M == 1 with a row-major B to this kernel when K % 2048 == 0
+and its 4-row workgroups give every compute unit one (N >= 4 x CUs);
+MXGEMM_GEMV=0 keeps such shapes on the skinny kernel.  Cases: one chunk per
+wave (K = 2048, 6144 -- one wave idle -- and 8192), several chunks per wave
+(K = 16384 and 28672: the two-register-set loop, waves with unequal chunk
+counts), ragged N (a last workgroup with 1, 2 or 3 rows), beta with bf16
+and float32 C, D aliasing C, padded rows of every operand, the E8M0
+special scale codes, and the fused bf16-A decode (quantize-on-load), bit
+for bit against mxgemm_quantize followed by mxgemm_run and element by
+element against the oracle's quantizer and GEMM.  Source of the operation:
+asm_f4gemm README, problem statement and "Data layouts"; the decode's
+quantizer: OCP Microscaling Formats v1.0, section 6.3 (as in test_quantize).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import block_scaled_precision_mxfp4_amd as mx
+import oracle
+from block_scaled_precision_mxfp4_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from mxgpu import assert_parity, dev_bf16, dev_u8, gemm_gpu, host_bits, oracle_ref  # noqa: E402
+from test_decode import problem, run_fused, run_two_step  # noqa: E402
+from test_specials import with_special_scales  # noqa: E402
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib_loaded():
+    mx.lib()
+    yield
+    mx.mxgemm_release_workspaces()
+
+
+def planned(M, N, K, b_packed=0, split=-1):
+    return mx.mxgemm_query(M, N, K, b_packed, split)["kernel_name"]
+
+
+# (N, K): chunks per wave 1 (K <= 8192) or several; N % 4 = 0..3
+SHAPES = [(1024, 2048), (1027, 6144), (8192, 8192), (2050, 16384), (1025, 28672), (8193, 2048)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "1x%dx%d" % s)
+@pytest.mark.parametrize("beta", [0.0, 1.0])
+def test_gemv_matches_oracle(shape, beta):
+    N, K = shape
+    assert planned(1, N, K) == "gemv_m1_n4"
+    p = inputs.make_problem(1, N, K, seed=0x6E00 + N + K, e=(120, 134), beta=beta, c_sigma=2.0 if beta else None)
+    p["alpha"] = 0.5
+    if beta:
+        p["beta"] = -0.75
+    say("case gemv", shape, "beta", beta)
+    d = gemm_gpu(p)
+    ref, mag, _ = oracle_ref(p)
+    assert_parity(d, ref, mag, "gemv %s beta=%g" % (shape, beta))
+
+
+def test_gemv_f32_C_and_in_place():
+    N, K = 1030, 8192
+    p = inputs.make_problem(1, N, K, seed=0x6EF3, beta=1.0, c_sigma=2.0)
+    p["C"] = (np.random.default_rng(3).standard_normal((1, N)) * 2.0).astype(np.float32)
+    say("case gemv f32 C")
+    assert_parity(gemm_gpu(p), *oracle_ref(p)[:2], "gemv f32 C")
+    # D aliasing a bf16 C
+    p = inputs.make_problem(1, N, K, seed=0x6EA1, beta=1.0, c_sigma=2.0)
+    p["alpha"], p["beta"] = 2.0, -1.0
+    ref, mag, _ = oracle_ref(p)
+    A, B, SA, SB = dev_u8(p["A"]), dev_u8(p["B"]), dev_u8(p["SA"]), dev_u8(p["SB"])
+    CD = dev_bf16(p["C"])
+    say("case gemv in place")
+    mx.mxgemm_run(CD, CD, A, B, SA, SB, 2.0, -1.0, 1, N, K)
+    torch.cuda.synchronize()
+    assert_parity(host_bits(CD), ref, mag, "gemv in place")
+
+
+def test_gemv_padded_rows():
+    """B rows, scale rows and D with pitches beyond their lengths (B pitch a
+    multiple of 32 elements, scale pitches multiples of 16 bytes: the GEMV's
+    requirements)."""
+    N, K = 1100, 4096
+    ldb, ldsb, ldd = K + 64, K // 32 + 16, N + 6
+    p = inputs.make_problem(1, N, K, seed=0x6EBD, e=(118, 136))
+    ref, mag, _ = oracle_ref(p)
+    Bpad = np.zeros((N, ldb // 2), dtype=np.uint8)
+    Bpad[:, : K // 2] = p["B"]
+    SBpad = np.full((N, ldsb), 0xFF, dtype=np.uint8)  # NaN scale bytes past each row's K
+    SBpad[:, : K // 32] = p["SB"]
+    A, SA = dev_u8(p["A"]), dev_u8(p["SA"])
+    B, SB = dev_u8(Bpad), dev_u8(SBpad)
+    D = torch.full((1, ldd), float("nan"), dtype=torch.bfloat16, device="cuda")
+    st = mx.make_strides(ldd=ldd, ldc=ldd, lda=K, ldb=ldb, ldsa=K // 32, ldsb=ldsb)
+    assert mx.mxgemm_query_ex(1, N, K, st, -1)["kernel_name"] == "gemv_m1_n4"
+    say("case gemv padded")
+    mx.mxgemm_run(D, None, A, B, SA, SB, p["alpha"], 0.0, 1, N, K, strides=st)
+    torch.cuda.synchronize()
+    bits = host_bits(D)
+    assert_parity(bits[:, :N], ref, mag, "gemv padded")
+    assert (bits[:, N:] == host_bits(torch.full((1, ldd - N), float("nan"), dtype=torch.bfloat16))).all()
+
+
+def test_gemv_special_scale_codes():
+    """About 2 % of the scale bytes of A and B replaced by 0x00, 0x01, 0xFE
+    or 0xFF (A: not 0xFF, which would make every output NaN)."""
+    N, K = 1040, 6144
+    p = with_special_scales(inputs.make_problem(1, N, K, seed=0x6E5C, e=(118, 136)), seed=0x6E5C)
+    p["SA"][p["SA"] == 0xFF] = 0xFE
+    ref, mag, _ = oracle_ref(p)
+    say("case gemv special scales")
+    assert planned(1, N, K) == "gemv_m1_n4"
+    assert_parity(gemm_gpu(p), ref, mag, "gemv special scales")
+    assert np.isnan(ref).any() and (np.abs(ref) > 2.0 ** 128).any()
+
+
+def test_gemv_and_skinny_agree(monkeypatch):
+    """The same problem on the skinny kernel (MXGEMM_GEMV=0): both within the
+    oracle's tolerance; their K orders differ, so bits may differ."""
+    N, K = 4096, 16384
+    p = inputs.make_problem(1, N, K, seed=0x6E6E, e=(120, 134))
+    ref, mag, _ = oracle_ref(p)
+    d_gemv = gemm_gpu(p)
+    monkeypatch.setenv("MXGEMM_GEMV", "0")
+    assert planned(1, N, K).startswith("skinny")
+    d_skinny = gemm_gpu(p)
+    assert_parity(d_gemv, ref, mag, "gemv")
+    assert_parity(d_skinny, ref, mag, "skinny")
+
+
+def test_gemv_plan_conditions():
+    """Only M == 1, row-major B, K % 2048 == 0, unsplit, N >= 4 x CUs."""
+    ncu = mx.mxgemm_query(1, 8192, 8192)["num_cu"]
+    assert planned(1, 4 * ncu, 2048) == "gemv_m1_n4"
+    assert planned(1, 4 * ncu - 4, 2048) != "gemv_m1_n4"
+    assert planned(1, 8192, 8192, b_packed=1) != "gemv_m1_n4"
+    assert planned(1, 8192, 8192 + 1024) != "gemv_m1_n4"
+    assert planned(2, 8192, 8192) != "gemv_m1_n4"
+    assert planned(1, 8192, 8192, split=2) != "gemv_m1_n4"
+    assert planned(1, 8192, 8192, split=1) == "gemv_m1_n4"
+
+
+# (N, K, beta): the fused decode on the GEMV
+DECODE = [(8192, 8192, 0.0), (1027, 6144, 1.0), (2050, 16384, 1.0)]
+
+
+@pytest.mark.parametrize("case", DECODE, ids=lambda c: "1x%dx%d%s" % (c[0], c[1], "_c" if c[2] else ""))
+def test_gemv_fused_decode(case):
+    N, K, beta = case
+    p = problem(1, N, K, seed=0x6ED0 + N + K, beta=beta)
+    say("case gemv fused decode", case)
+    d = run_fused(p)
+    d2 = run_two_step(p)
+    assert np.array_equal(d, d2), "%d of %d elements differ" % (int((d != d2).sum()), d.size)
+    p["A"], p["SA"] = oracle.quantize_mxfp4(p["X"])
+    ref, mag, _ = oracle_ref(p)
+    assert_parity(d, ref, mag, "gemv fused decode %s" % (case,))
+
+
+def test_gemv_fused_decode_special_values():
+    """NaN / inf blocks (scale 0xFF: every output NaN), then the finite
+    specials (-0, zero blocks, ties, subnormal blocks) on the fused GEMV."""
+    N, K = 1024, 4096
+    p = problem(1, N, K, seed=0x6E5E, specials=True)
+    say("case gemv fused decode specials")
+    d = run_fused(p)
+    assert np.array_equal(d, run_two_step(p))
+    p["A"], p["SA"] = oracle.quantize_mxfp4(p["X"])
+    assert (p["SA"] == 0xFF).any()
+    ref, mag, _ = oracle_ref(p)
+    assert np.isnan(ref).all()
+    assert_parity(d, ref, mag, "gemv fused specials")
+    X = p["X"].copy()
+    nonfinite = (X & 0x7F80) == 0x7F80
+    X[nonfinite] = 0x3F80 | (X[nonfinite] & 0x8000)
+    p["X"] = X
+    d = run_fused(p)
+    assert np.array_equal(d, run_two_step(p))
+    p["A"], p["SA"] = oracle.quantize_mxfp4(X)
+    ref, mag, _ = oracle_ref(p)
+    assert np.isfinite(ref).all()
+    assert_parity(d, ref, mag, "gemv fused finite specials")
