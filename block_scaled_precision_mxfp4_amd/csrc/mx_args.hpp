@@ -108,12 +108,6 @@ struct RowsKernel {
 };
 const RowsKernel *rows_kernels(int *count);
 
-// Single-row GEMV (M == 1, FP4 A, row-major B, K % 2048 == 0, 16-byte
-// aligned scale rows, split 1): one workgroup per 4 rows of B.
-void launch_gemv(const GemmArgs &g, int grid, hipStream_t s);
-// the same with A a bf16 row (g.A) quantized to MXFP4 on load; g.SA unused
-void launch_gemv_bf16a(const GemmArgs &g, int grid, hipStream_t s);
-
 void launch_pack_b(uint8_t *Bp, const uint8_t *B, int N, int KB, int64_t ldb_b, hipStream_t s);
 // p[0 .. words) = 0, on stream s
 void launch_zero_words(uint32_t *p, size_t words, hipStream_t s);

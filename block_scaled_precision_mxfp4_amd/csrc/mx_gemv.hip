@@ -32,84 +32,57 @@
 // l % 16) and the B words reach their operand lanes by a cross-lane permute;
 // the lane's byte is shifted down for op_sel 0.
 //
-// XQ: A is a bf16 row (the decode step), quantized on load with the
-// activation quantizer's rule: each A operand lane loads its whole 32-element
-// block (64 bytes) and encodes it itself, so its codes and scale byte are
-// exactly the operand and scale the lane passes to the instruction.
-//
 // Requires K % 2048 == 0 (every chunk whole: no range checks inside K, no
 // scale bytes of a neighbouring row), 16-byte aligned scale rows, split 1.
 #include "mx_args.hpp"
 #include "mx_device.hpp"
-#include "mx_quantize.hpp"
 
 namespace mx {
 
 constexpr int kGemvRows = 4;     // rows of B (columns of D) per workgroup
 constexpr int kGemvChunk = 2048; // K per chunk: 16 steps of 128
 
-template <bool XQ>
 struct GemvChunk {
-    v4i b[4];        // B operand of instruction t
-    v4i a;           // A operand, all 16 steps of the chunk
-    uint32_t sa;     // A scale bytes of step l % 16
-    uint32_t sb;     // B scale bytes of row l / 16, step l % 16
-    v4i x[XQ ? 4 : 1];  // XQ: the lane's bf16 block of A
+    v4i b[4];     // B operand of instruction t
+    v4i a;        // A operand, all 16 steps of the chunk
+    uint32_t sa;  // A scale bytes of step l % 16
+    uint32_t sb;  // B scale bytes of row l / 16, step l % 16
 };
 
 // Loads of chunk c (nothing, without memory traffic, when !on).  The scale
 // words and the A operand go first: the scale permutes can then start while
 // B is still arriving, and each multiply waits only for its own B operand.
-template <bool XQ>
-__device__ __forceinline__ void gemv_issue(GemvChunk<XQ> &ch, int c, bool on, __amdgpu_buffer_rsrc_t rb,
+__device__ __forceinline__ void gemv_issue(GemvChunk &ch, int c, bool on, __amdgpu_buffer_rsrc_t rb,
                                            __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rsa,
                                            __amdgpu_buffer_rsrc_t rsb, uint32_t b_lane, uint32_t sb_lane,
                                            int lane)
 {
     const uint32_t bc = (uint32_t)c * (kGemvChunk / 2);
     ch.sb = load4(rsb, on && sb_lane != kOOB ? sb_lane + (uint32_t)c * 64 : kOOB);
-    if constexpr (XQ) {
-        // bf16 elements c * 2048 + (l % 16) * 128 + (l / 16) * 32 ... + 31
-        const uint32_t xo = 4 * bc + (lane & 15) * 256 + (lane >> 4) * 64;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ch.x[i] = load16(ra, on ? xo + i * 16 : kOOB);
-    } else {
-        ch.sa = load4(rsa, on ? (uint32_t)c * 64 + (lane & 15) * 4 : kOOB);
-        ch.a = load16(ra, on ? bc + (lane & 15) * 64 + (lane >> 4) * 16 : kOOB);
-    }
+    ch.sa = load4(rsa, on ? (uint32_t)c * 64 + (lane & 15) * 4 : kOOB);
+    ch.a = load16(ra, on ? bc + (lane & 15) * 64 + (lane >> 4) * 16 : kOOB);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
         ch.b[t] = load16_stream(rb, on && b_lane != kOOB ? b_lane + bc + t * 256 : kOOB);
 }
 
-template <bool XQ>
-__device__ __forceinline__ void gemv_compute(const GemvChunk<XQ> &ch, v4f (&acc)[4], int lane)
+__device__ __forceinline__ void gemv_compute(const GemvChunk &ch, v4f (&acc)[4], int lane)
 {
     const int sh = 8 * (lane >> 4);
-    v4i a = ch.a;
-    int sa;
-    if constexpr (XQ) {
-        uint32_t s8;
-        quantize_block(ch.x, a, s8);
-        sa = (int)s8;
-    } else {
-        sa = (int)(ch.sa >> sh);
-    }
+    const int sa = (int)(ch.sa >> sh);
     const int q = lane & 15;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         // this lane's B scale word: row q / 4, step 4t + q % 4 of the chunk
         const int src = (q >> 2) * 16 + 4 * t + (q & 3);
         const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)ch.sb);
-        acc[t] = mfma_fp4<0, 0>(ch.b[t], a, acc[t], (int)(w >> sh), sa);
+        acc[t] = mfma_fp4<0, 0>(ch.b[t], ch.a, acc[t], (int)(w >> sh), sa);
     }
 }
 
-// LOOP = false: at most one chunk per wave (K <= 8192), one register set,
-// so that more waves fit a SIMD
-template <bool XQ, bool LOOP>
-__global__ void __launch_bounds__(256) mx_gemv_kernel(GemmArgs g)
+// LOOP = false: at most one chunk per wave (K <= 8192), one register set.
+template <bool LOOP>
+__device__ __forceinline__ void gemv_body(const GemmArgs &g)
 {
     __shared__ float s_part[4][kGemvRows];
     const int lane = threadIdx.x & 63;
@@ -119,7 +92,7 @@ __global__ void __launch_bounds__(256) mx_gemv_kernel(GemmArgs g)
     const uint32_t kbytes = (uint32_t)(g.K / 2);
     const auto rb = make_rsrc(g.B + (int64_t)n0 * g.ldb_b, (uint32_t)((rows - 1) * g.ldb_b) + kbytes);
     const auto rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)((rows - 1) * g.ldsb + g.KB));
-    const auto ra = make_rsrc(g.A, XQ ? 4 * kbytes : kbytes);  // XQ: K bf16
+    const auto ra = make_rsrc(g.A, kbytes);
     const auto rsa = make_rsrc(g.SA, (uint32_t)g.KB);
 
     // per-lane offsets inside a chunk: B row (l % 16) / 4 at step l % 4 of
@@ -138,7 +111,7 @@ __global__ void __launch_bounds__(256) mx_gemv_kernel(GemmArgs g)
     const int chunks = g.K / kGemvChunk;
     int c = wave;
     if (c < chunks) {
-        GemvChunk<XQ> x;
+        GemvChunk x;
         gemv_issue(x, c, true, rb, ra, rsa, rsb, b_lane, sb_lane, lane);
         if (!LOOP) {
             gemv_compute(x, acc, lane);
@@ -150,7 +123,7 @@ __global__ void __launch_bounds__(256) mx_gemv_kernel(GemmArgs g)
             // both sets (a chunk past K loads nothing and adds zeros), so no
             // load is conditional and each multiply waits only for its own
             // operands.
-            GemvChunk<XQ> y;
+            GemvChunk y;
             const int mine = (chunks - wave + 3) / 4;  // this wave's chunks
             for (int i = 0; i < mine; i += 2) {
                 gemv_issue(y, c + 4, c + 4 < chunks, rb, ra, rsa, rsb, b_lane, sb_lane, lane);
@@ -196,20 +169,24 @@ __global__ void __launch_bounds__(256) mx_gemv_kernel(GemmArgs g)
     }
 }
 
+__global__ void __launch_bounds__(256) mx_gemv_kernel(GemmArgs g)
+{
+    gemv_body<true>(g);
+}
+
+// One chunk per wave: at most 64 registers, so that eight waves fit a SIMD
+// and all 2048 workgroups of N = 8192 are resident at once.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) mx_gemv1_kernel(GemmArgs g)
+{
+    gemv_body<false>(g);
+}
+
 void launch_gemv(const GemmArgs &g, int grid, hipStream_t s)
 {
     if (g.K <= 4 * kGemvChunk)
-        hipLaunchKernelGGL((mx_gemv_kernel<false, false>), dim3(grid), dim3(256), 0, s, g);
+        hipLaunchKernelGGL(mx_gemv1_kernel, dim3(grid), dim3(256), 0, s, g);
     else
-        hipLaunchKernelGGL((mx_gemv_kernel<false, true>), dim3(grid), dim3(256), 0, s, g);
-}
-
-void launch_gemv_bf16a(const GemmArgs &g, int grid, hipStream_t s)
-{
-    if (g.K <= 4 * kGemvChunk)
-        hipLaunchKernelGGL((mx_gemv_kernel<true, false>), dim3(grid), dim3(256), 0, s, g);
-    else
-        hipLaunchKernelGGL((mx_gemv_kernel<true, true>), dim3(grid), dim3(256), 0, s, g);
+        hipLaunchKernelGGL(mx_gemv_kernel, dim3(grid), dim3(256), 0, s, g);
 }
 
 }  // namespace mx

@@ -11,13 +11,13 @@
 
 namespace mx {
 
-// Magnitude maximum (bf16 magnitude bits, which order like the values for
-// finite inputs) and NaN/infinity flag (an all-ones exponent field) of the 8
-// bf16 in x.
-__device__ __forceinline__ void quarter_stats(v4i x, uint32_t &amag, uint32_t &special)
+// Encode one 32-block: x holds this lane's 8 bf16 (a quarter of the block);
+// the four lanes of the block combine their maximum and NaN/inf flag.
+__device__ __forceinline__ void quantize_quarter(v4i x, uint32_t &word, uint8_t &scale)
 {
-    amag = 0;
-    special = 0;
+    // bf16 magnitude bits order like the values for finite inputs; an
+    // all-ones exponent field is an infinity or a NaN
+    uint32_t amag = 0, special = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
 #pragma unroll
@@ -27,27 +27,22 @@ __device__ __forceinline__ void quarter_stats(v4i x, uint32_t &amag, uint32_t &s
             amag = max(amag, hb & 0x7FFFu);
         }
     }
-}
+    // the block's four lanes are one aligned quad: quad permutes (lane ^ 1,
+    // lane ^ 2) exchange within it without going through LDS
+    amag = max(amag, (uint32_t)__builtin_amdgcn_mov_dpp((int)amag, 0xB1, 0xF, 0xF, true));
+    amag = max(amag, (uint32_t)__builtin_amdgcn_mov_dpp((int)amag, 0x4E, 0xF, 0xF, true));
+    special |= (uint32_t)__builtin_amdgcn_mov_dpp((int)special, 0xB1, 0xF, 0xF, true);
+    special |= (uint32_t)__builtin_amdgcn_mov_dpp((int)special, 0x4E, 0xF, 0xF, true);
 
-// The block's scale exponent X from its magnitude maximum: floor(log2 amax)
-// from the bf16 fields (subnormal: from the top set mantissa bit), minus 2,
-// clamped; -127 for an all-zero block.
-__device__ __forceinline__ int block_exponent(uint32_t amag)
-{
+    // floor(log2 amax) from the bf16 fields (subnormal: from the top set
+    // mantissa bit), then the scale exponent
     int xs = -127;
     if (amag != 0) {
         const int ef = (int)(amag >> 7);
         const int fl = ef > 0 ? ef - 127 : -133 + (31 - __builtin_clz(amag & 0x7Fu));
         xs = min(127, max(-127, fl - 2));
     }
-    return xs;
-}
-
-// E2M1 codes of the 8 bf16 in x at scale 2^xs (element 2w in the low nibble
-// of byte w); all zero for a NaN/infinity block.
-__device__ __forceinline__ uint32_t encode_quarter(v4i x, int xs, uint32_t special)
-{
-    uint32_t word = 0;
+    word = 0;
     if (!special && xs > -127) {
         // v_cvt_scalef32_pk_fp4_bf16: two bf16 divided by the scale, rounded
         // to nearest even E2M1 with saturation at 6, sign kept -- the rule
@@ -86,43 +81,7 @@ __device__ __forceinline__ uint32_t encode_quarter(v4i x, int xs, uint32_t speci
             }
         }
     }
-    return word;
-}
-
-// Encode one 32-block: x holds this lane's 8 bf16 (a quarter of the block);
-// the four lanes of the block combine their maximum and NaN/inf flag.
-__device__ __forceinline__ void quantize_quarter(v4i x, uint32_t &word, uint8_t &scale)
-{
-    uint32_t amag, special;
-    quarter_stats(x, amag, special);
-    // the block's four lanes are one aligned quad: quad permutes (lane ^ 1,
-    // lane ^ 2) exchange within it without going through LDS
-    amag = max(amag, (uint32_t)__builtin_amdgcn_mov_dpp((int)amag, 0xB1, 0xF, 0xF, true));
-    amag = max(amag, (uint32_t)__builtin_amdgcn_mov_dpp((int)amag, 0x4E, 0xF, 0xF, true));
-    special |= (uint32_t)__builtin_amdgcn_mov_dpp((int)special, 0xB1, 0xF, 0xF, true);
-    special |= (uint32_t)__builtin_amdgcn_mov_dpp((int)special, 0x4E, 0xF, 0xF, true);
-    const int xs = block_exponent(amag);
-    word = encode_quarter(x, xs, special);
     scale = special ? (uint8_t)0xFF : (uint8_t)(xs + 127);
-}
-
-// Encode one 32-block held whole by this lane (x[i]: elements 8i..8i+7):
-// codes[i] holds elements 8i..8i+7, the same rule as quantize_quarter.
-__device__ __forceinline__ void quantize_block(const v4i (&x)[4], v4i &codes, uint32_t &scale)
-{
-    uint32_t amag = 0, special = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t a, sp;
-        quarter_stats(x[i], a, sp);
-        amag = max(amag, a);
-        special |= sp;
-    }
-    const int xs = block_exponent(amag);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        codes[i] = (int)encode_quarter(x[i], xs, special);
-    scale = special ? 0xFFu : (uint32_t)(xs + 127);
 }
 
 }  // namespace mx

@@ -23,6 +23,12 @@
 
 #include "mx_args.hpp"
 
+namespace mx {
+// Single-row GEMV (mx_gemv.hip): M == 1, FP4 A, row-major B, K % 2048 == 0,
+// 16-byte aligned scale rows, split 1; one workgroup per 4 rows of B.
+void launch_gemv(const GemmArgs &g, int grid, hipStream_t s);
+}  // namespace mx
+
 namespace {
 
 using mx::GemmArgs;
@@ -760,8 +766,11 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     if (st != MXGEMM_OK)
         return st;
     // the GEMV reads the scale rows as aligned dwords (16-byte aligned rows,
-    // as the skinny kernel's vector scale path); a bf16 A has no scale row
-    const bool gemv_ok = (X || (aligned(scaleA, 16) && s.ldsa % 16 == 0)) && aligned(scaleB, 16) && s.ldsb % 16 == 0;
+    // as the skinny kernel's vector scale path).  A bf16 A row stays on the
+    // skinny kernel's quantize-on-load: the GEMV's 4-row workgroups would
+    // each load and encode the whole row (2048 times at N = 8192, 32 MiB of
+    // bf16 from L2), which measured 10.2-10.4 us against 8.8 us
+    const bool gemv_ok = !X && aligned(scaleA, 16) && s.ldsa % 16 == 0 && aligned(scaleB, 16) && s.ldsb % 16 == 0;
     Plan p = plan_run(M, N, K, s, split_k, d->num_cu, gemv_ok);
     // a wider A on the skinny kernel (one 16-row group, nr 1): one launch
     // per 16 rows of A
@@ -868,13 +877,9 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     if (g.split_atomic)
         mx::launch_d_init(g, stream);
     if (X) {
-        // M == 1 with the fp32 split reduction plans the GEMV or the skinny kernel
-        if (p.family == 4)
-            mx::launch_gemv_bf16a(g, (int)p.grid, stream);
-        else if (p.family == 1)
-            mx::launch_skinny_bf16a(p.bn / 16, s.b_packed != 0, g, (int)p.grid, stream);
-        else
+        if (p.family != 1)  // M == 1 with the fp32 split reduction plans the skinny kernel
             return MXGEMM_ERR_INVALID_ARG;
+        mx::launch_skinny_bf16a(p.bn / 16, s.b_packed != 0, g, (int)p.grid, stream);
     } else if (wide) {
         // stream-ordered launches over 16-row blocks of A, C and D; the split
         // counters return to zero at the end of each

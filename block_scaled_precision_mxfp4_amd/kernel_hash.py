@@ -14,7 +14,7 @@ _COMMON = ("mx_args.hpp", "mx_device.hpp", "mx_pipe.hpp")
 FAMILY_FILES = {
     "tile": _COMMON + ("mx_tile.hip", "mx_tile_deep.hip"),
     "skinny": _COMMON + ("mx_skinny.hip", "mx_quantize.hpp"),
-    "gemv": _COMMON + ("mx_gemv.hip", "mx_quantize.hpp"),
+    "gemv": _COMMON + ("mx_gemv.hip",),
     "rows": _COMMON + ("mx_skinny_rows.hip",),
     "quant": _COMMON + ("mx_quant.hip", "mx_quantize.hpp"),
     "stream": _COMMON + ("mx_stream.hip",),

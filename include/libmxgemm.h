@@ -328,10 +328,12 @@ mxgemm_status mxgemm_quantize(void *A, void *scaleA, const void *X, int M, int K
  * and split_k as for mxgemm_run; strides->lda / ldsa are ignored, and
  * a_format, sa_packed and split_mode must be 0 (else
  * MXGEMM_ERR_INVALID_ARG).
- *   M == 1 (decode), K-major B: one launch.  The kernel mxgemm_run would
- *     plan (the single-row GEMV or the skinny kernel) loads the bf16 row and
- *     quantizes each 32-block in registers with the quantizer's rule, so D
- *     is bit for bit what mxgemm_quantize followed by mxgemm_run gives.
+ *   M == 1 (decode), K-major B: one launch.  The skinny kernel loads the
+ *     bf16 row and quantizes each 32-block in registers with the quantizer's
+ *     rule, so D is bit for bit what mxgemm_quantize followed by mxgemm_run
+ *     gives where mxgemm_run plans the skinny kernel too; where it plans the
+ *     single-row GEMV (kernel family 4, another K order) the two agree
+ *     within the fp32 accumulation's rounding.
  *   M > 1, or an MN-major B (b_layout = MXGEMM_B_KN): mxgemm_quantize into a library-owned buffer of
  *     M*K/2 + M*K/32 bytes per (device, stream) (allocated on first use like
  *     the split-K buffers, freed by mxgemm_release_workspaces), then

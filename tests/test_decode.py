@@ -2,8 +2,10 @@
 GEMM (quantize-on-load at M = 1, the decode step), through the C-ABI.
 
 The fused kernel quantizes with the quantizer's own block routine, so its D
-must equal mxgemm_quantize followed by mxgemm_run bit for bit (same codes,
-same scales, same matrix instructions in the same order); it is also checked
+must equal mxgemm_quantize followed by mxgemm_run on the same (skinny)
+kernel bit for bit (same codes, same scales, same matrix instructions in the
+same order; MXGEMM_GEMV=0 keeps the two-step path off the single-row GEMV,
+whose K order differs); it is also checked
 against the oracle's quantizer and GEMM.  Shapes cover the 1 x 8192 x 8192
 decode, ragged N, a K tail (K % 128 != 0), forced split-K, packed B, C with
 beta and float32 C, special values (NaN, +-inf, -0, zero blocks, exact
@@ -106,8 +108,11 @@ DECODE = [
 
 @pytest.mark.parametrize("case", DECODE, ids=lambda c: "1x%dx%d%s_s%d%s" % (
     c[0], c[1], "_packed" if c[2] else "", c[3], "_c32" if c[5] else ("_c" if c[4] else "")))
-def test_fused_decode_matches_quantize_then_gemm(case):
+def test_fused_decode_matches_quantize_then_gemm(case, monkeypatch):
     N, K, packed, split, beta, c_f32 = case
+    # the two-step path on the skinny kernel (it would run the single-row
+    # GEMV at 1 x 8192 x 8192, whose K order differs; tests/test_gemv.py)
+    monkeypatch.setenv("MXGEMM_GEMV", "0")
     p = problem(1, N, K, seed=0xDEC0 + N + K, beta=beta, c_f32=c_f32)
     say("case fused decode", case)
     d = run_fused(p, packed, split)
