@@ -32,19 +32,29 @@
 // l % 16) and the B words reach their operand lanes by a cross-lane permute;
 // the lane's byte is shifted down for op_sel 0.
 //
+// AF: A's format (0 FP4; 1 FP8 E4M3, 2 BF8 E5M2, 3 FP6 E2M3, 4 FP6 E3M2;
+// B is FP4).  A wider A operand lane holds its K-block as the skinny kernel
+// does: 8-bit, the two 16-byte runs at bytes 16g and 64 + 16g of its step
+// (g = l / 16); FP6, the block's 24 bytes.  A chunk of A is then 2 KiB or
+// 1.5 KiB instead of 1 KiB; B and the scales are unchanged.
+//
 // Requires K % 2048 == 0 (every chunk whole: no range checks inside K, no
 // scale bytes of a neighbouring row), 16-byte aligned scale rows, split 1.
 #include "mx_args.hpp"
 #include "mx_device.hpp"
+
+#include <type_traits>
 
 namespace mx {
 
 constexpr int kGemvRows = 4;     // rows of B (columns of D) per workgroup
 constexpr int kGemvChunk = 2048; // K per chunk: 16 steps of 128
 
+template <int AF>
 struct GemvChunk {
+    using a_t = typename std::conditional<AF == 0, v4i, v8i>::type;
     v4i b[4];     // B operand of instruction t
-    v4i a;        // A operand, all 16 steps of the chunk
+    a_t a;        // A operand, all 16 steps of the chunk
     uint32_t sa;  // A scale bytes of step l % 16
     uint32_t sb;  // B scale bytes of row l / 16, step l % 16
 };
@@ -52,7 +62,8 @@ struct GemvChunk {
 // Loads of chunk c (nothing, without memory traffic, when !on).  The scale
 // words and the A operand go first: the scale permutes can then start while
 // B is still arriving, and each multiply waits only for its own B operand.
-__device__ __forceinline__ void gemv_issue(GemvChunk &ch, int c, bool on, __amdgpu_buffer_rsrc_t rb,
+template <int AF>
+__device__ __forceinline__ void gemv_issue(GemvChunk<AF> &ch, int c, bool on, __amdgpu_buffer_rsrc_t rb,
                                            __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rsa,
                                            __amdgpu_buffer_rsrc_t rsb, uint32_t b_lane, uint32_t sb_lane,
                                            int lane)
@@ -60,13 +71,27 @@ __device__ __forceinline__ void gemv_issue(GemvChunk &ch, int c, bool on, __amdg
     const uint32_t bc = (uint32_t)c * (kGemvChunk / 2);
     ch.sb = load4(rsb, on && sb_lane != kOOB ? sb_lane + (uint32_t)c * 64 : kOOB);
     ch.sa = load4(rsa, on ? (uint32_t)c * 64 + (lane & 15) * 4 : kOOB);
-    ch.a = load16(ra, on ? bc + (lane & 15) * 64 + (lane >> 4) * 16 : kOOB);
+    constexpr int AKB = 4 * kFmtBits[AF];  // bytes of an A K-block
+    const uint32_t ac = (uint32_t)c * 64 * AKB + (lane & 15) * 4 * AKB;  // the lane's step
+    if constexpr (AF == 0) {
+        ch.a = load16(ra, on ? ac + (lane >> 4) * 16 : kOOB);
+    } else if constexpr (kFmtBits[AF] == 8) {
+        const uint32_t o = ac + (lane >> 4) * 16;
+        const v4i lo = load16(ra, on ? o : kOOB), hi = load16(ra, on ? o + 64 : kOOB);
+        ch.a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+        const uint32_t o = ac + (lane >> 4) * 24;
+        const v4i lo = load16(ra, on ? o : kOOB);
+        const v2u hi = load8(ra, on ? o + 16 : kOOB);
+        ch.a = v8i{lo[0], lo[1], lo[2], lo[3], (int)hi[0], (int)hi[1], 0, 0};
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
         ch.b[t] = load16_stream(rb, on && b_lane != kOOB ? b_lane + bc + t * 256 : kOOB);
 }
 
-__device__ __forceinline__ void gemv_compute(const GemvChunk &ch, v4f (&acc)[4], int lane)
+template <int AF>
+__device__ __forceinline__ void gemv_compute(const GemvChunk<AF> &ch, v4f (&acc)[4], int lane)
 {
     const int sh = 8 * (lane >> 4);
     const int sa = (int)(ch.sa >> sh);
@@ -76,12 +101,15 @@ __device__ __forceinline__ void gemv_compute(const GemvChunk &ch, v4f (&acc)[4],
         // this lane's B scale word: row q / 4, step 4t + q % 4 of the chunk
         const int src = (q >> 2) * 16 + 4 * t + (q & 3);
         const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)ch.sb);
-        acc[t] = mfma_fp4<0, 0>(ch.b[t], ch.a, acc[t], (int)(w >> sh), sa);
+        if constexpr (AF == 0)
+            acc[t] = mfma_fp4<0, 0>(ch.b[t], ch.a, acc[t], (int)(w >> sh), sa);
+        else
+            acc[t] = mfma_fp4_wide<kFmtHw[AF], 0, 0>(ch.b[t], ch.a, acc[t], (int)(w >> sh), sa);
     }
 }
 
 // LOOP = false: at most one chunk per wave (K <= 8192), one register set.
-template <bool LOOP>
+template <int AF, bool LOOP>
 __device__ __forceinline__ void gemv_body(const GemmArgs &g)
 {
     __shared__ float s_part[4][kGemvRows];
@@ -92,7 +120,7 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
     const uint32_t kbytes = (uint32_t)(g.K / 2);
     const auto rb = make_rsrc(g.B + (int64_t)n0 * g.ldb_b, (uint32_t)((rows - 1) * g.ldb_b) + kbytes);
     const auto rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)((rows - 1) * g.ldsb + g.KB));
-    const auto ra = make_rsrc(g.A, kbytes);
+    const auto ra = make_rsrc(g.A, (uint32_t)((int64_t)g.K * kFmtBits[AF] / 8));
     const auto rsa = make_rsrc(g.SA, (uint32_t)g.KB);
 
     // per-lane offsets inside a chunk: B row (l % 16) / 4 at step l % 4 of
@@ -111,7 +139,7 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
     const int chunks = g.K / kGemvChunk;
     int c = wave;
     if (c < chunks) {
-        GemvChunk x;
+        GemvChunk<AF> x;
         gemv_issue(x, c, true, rb, ra, rsa, rsb, b_lane, sb_lane, lane);
         if (!LOOP) {
             gemv_compute(x, acc, lane);
@@ -123,7 +151,7 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
             // both sets (a chunk past K loads nothing and adds zeros), so no
             // load is conditional and each multiply waits only for its own
             // operands.
-            GemvChunk y;
+            GemvChunk<AF> y;
             const int mine = (chunks - wave + 3) / 4;  // this wave's chunks
             for (int i = 0; i < mine; i += 2) {
                 gemv_issue(y, c + 4, c + 4 < chunks, rb, ra, rsa, rsb, b_lane, sb_lane, lane);
@@ -169,24 +197,38 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
     }
 }
 
+template <int AF>
 __global__ void __launch_bounds__(256) mx_gemv_kernel(GemmArgs g)
 {
-    gemv_body<true>(g);
+    gemv_body<AF, true>(g);
 }
 
 // One chunk per wave: at most 64 registers, so that eight waves fit a SIMD
 // and all 2048 workgroups of N = 8192 are resident at once.
+template <int AF>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) mx_gemv1_kernel(GemmArgs g)
 {
-    gemv_body<false>(g);
+    gemv_body<AF, false>(g);
 }
 
-void launch_gemv(const GemmArgs &g, int grid, hipStream_t s)
+template <int AF>
+static void launch_gemv_fmt(const GemmArgs &g, int grid, hipStream_t s)
 {
     if (g.K <= 4 * kGemvChunk)
-        hipLaunchKernelGGL(mx_gemv1_kernel, dim3(grid), dim3(256), 0, s, g);
+        hipLaunchKernelGGL(mx_gemv1_kernel<AF>, dim3(grid), dim3(256), 0, s, g);
     else
-        hipLaunchKernelGGL(mx_gemv_kernel, dim3(grid), dim3(256), 0, s, g);
+        hipLaunchKernelGGL(mx_gemv_kernel<AF>, dim3(grid), dim3(256), 0, s, g);
+}
+
+void launch_gemv(int a_fmt, const GemmArgs &g, int grid, hipStream_t s)
+{
+    switch (a_fmt) {
+    case 0: launch_gemv_fmt<0>(g, grid, s); break;
+    case 1: launch_gemv_fmt<1>(g, grid, s); break;
+    case 2: launch_gemv_fmt<2>(g, grid, s); break;
+    case 3: launch_gemv_fmt<3>(g, grid, s); break;
+    default: launch_gemv_fmt<4>(g, grid, s); break;
+    }
 }
 
 }  // namespace mx

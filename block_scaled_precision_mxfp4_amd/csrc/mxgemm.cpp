@@ -24,9 +24,10 @@
 #include "mx_args.hpp"
 
 namespace mx {
-// Single-row GEMV (mx_gemv.hip): M == 1, FP4 A, row-major B, K % 2048 == 0,
+// Single-row GEMV (mx_gemv.hip): M == 1, A in format a_fmt (0 FP4, 1..4
+// FP8 E4M3, BF8 E5M2, FP6 E2M3, FP6 E3M2), row-major B, K % 2048 == 0,
 // 16-byte aligned scale rows, split 1; one workgroup per 4 rows of B.
-void launch_gemv(const GemmArgs &g, int grid, hipStream_t s);
+void launch_gemv(int a_fmt, const GemmArgs &g, int grid, hipStream_t s);
 }  // namespace mx
 
 namespace {
@@ -101,13 +102,14 @@ constexpr double kSplitChunkCost = 2e-6;
 constexpr int kMinSkinnyChunk = 64;
 constexpr double kCuL2 = 64.0 * 2.4e9;
 
-// The single-row GEMV (mx_gemv.hip) takes M == 1 with FP4 A and row-major B
-// when K is a multiple of its 2048-K chunk and its 4-row workgroups fill at
-// least one per CU (N >= 4 * CUs); unsplit.  MXGEMM_GEMV=0 keeps such shapes
-// on the skinny kernel.
+// The single-row GEMV (mx_gemv.hip) takes M == 1 (A in any format) with a
+// row-major B when K is a multiple of its 2048-K chunk and its 4-row
+// workgroups fill at least one per CU (N >= 4 * CUs); unsplit.
+// MXGEMM_GEMV=0 keeps such shapes on the skinny kernel.
 bool gemv_applies(int M, int N, int K, int b_packed, int split_req, int num_cu, int a_format)
 {
-    if (M != 1 || a_format != MXGEMM_FMT_FP4 || b_packed || K % 2048 || split_req > 1 ||
+    (void)a_format;
+    if (M != 1 || b_packed || K % 2048 || split_req > 1 ||
         (int64_t)cdiv(N, 4) < num_cu)
         return false;
     const char *e = std::getenv("MXGEMM_GEMV");
@@ -181,7 +183,7 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool
         best.ws_bytes = best.split > 1 ? (size_t)tiles * best.split * part : 0;
         return best;
     }
-    if (!tiled_only && allow_gemv && force_nr == 0 &&
+    if (!tiled_only && allow_gemv && force_nr <= 1 &&
         gemv_applies(M, N, K, b_packed, split_req, num_cu > 0 ? num_cu : 256, a_format)) {
         best.family = 4;
         best.bm = 1;
@@ -385,7 +387,7 @@ Plan plan_run(int M, int N, int K, const mxgemm_strides &s, int split_k, int num
     // 256-row tile of the re-laid A stays below 2^31 bytes
     if (fp6 && M > 16 && (int64_t)256 * mx::fp6_pad_pitch(K) < ((int64_t)1 << 31))
         return plan_a8(M, N, K, split_k, num_cu, true, s.b_packed != 0);
-    return plan_for(std::min(M, 16), N, K, s.b_packed, split_k, num_cu, false, 1);
+    return plan_for(std::min(M, 16), N, K, s.b_packed, split_k, num_cu, false, 1, s.a_format, allow_gemv);
 }
 
 size_t packed_b_bytes(int N, int K) { return (size_t)cdiv(N, 16) * 16 * (size_t)cdiv(K / 32, 4) * 64; }
@@ -956,7 +958,7 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
         else
             (s.sa_packed ? k.packed_sa : s.b_packed ? k.packed : k.plain)(g, (int)p.grid, stream);
     } else if (p.family == 4) {
-        mx::launch_gemv(g, (int)p.grid, stream);
+        mx::launch_gemv(s.a_format, g, (int)p.grid, stream);
     } else if (p.family == 1) {
         int n = 0;
         const mx::SkinnyKernel &k = mx::skinny_kernels(&n)[p.index];

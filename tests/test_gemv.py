@@ -1,7 +1,8 @@
 """GPU parity of the single-row GEMV (`gemv_m1_n4`: M == 1, FP4 A, row-major
 FP4 B, K a multiple of 2048), through the C-ABI, against the oracle.
 
-The planner sends M == 1 with a row-major B to this kernel when K % 2048 == 0
+The planner sends M == 1 with a row-major B (A in FP4, FP8, BF8 or either
+FP6) to this kernel when K % 2048 == 0
 and its 4-row workgroups give every compute unit one (N >= 4 x CUs);
 MXGEMM_GEMV=0 keeps such shapes on the skinny kernel.  Cases: one chunk per
 wave (K = 2048, 6144 -- one wave idle -- and 8192), several chunks per wave
@@ -61,6 +62,26 @@ def test_gemv_matches_oracle(shape, beta):
     d = gemm_gpu(p)
     ref, mag, _ = oracle_ref(p)
     assert_parity(d, ref, mag, "gemv %s beta=%g" % (shape, beta))
+
+
+FORMATS = {1: "e4m3", 2: "e5m2", 3: "e2m3", 4: "e3m2"}
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS), ids=lambda f: FORMATS[f])
+@pytest.mark.parametrize("shape", [(1027, 6144), (2050, 16384)], ids=lambda s: "1x%dx%d" % s)
+def test_gemv_wider_A_matches_oracle(shape, fmt):
+    """A in FP8 E4M3, BF8 E5M2, FP6 E2M3 or FP6 E3M2 ("CDNA4 dense MFMA
+    builtins", "Mixed-precision with scaling"), B FP4, on the GEMV: one chunk
+    per wave and the two-set loop, ragged N, C with beta."""
+    N, K = shape
+    st = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=K, ldsa=K // 32, ldsb=K // 32, a_format=fmt)
+    assert mx.mxgemm_query_ex(1, N, K, st, -1)["kernel_name"] == "gemv_m1_n4"
+    e = (120, 134) if fmt in (3, 4) else (110, 130)
+    p = inputs.make_problem(1, N, K, seed=0x6EF0 + 31 * fmt + N, e=e, beta=1.0, c_sigma=2.0, a_fmt=fmt)
+    p["alpha"], p["beta"] = 0.5, -0.75
+    say("case gemv", FORMATS[fmt], shape)
+    ref, mag, _ = oracle_ref(p)
+    assert_parity(gemm_gpu(p), ref, mag, "gemv %s %s" % (FORMATS[fmt], shape))
 
 
 def test_gemv_f32_C_and_in_place():
