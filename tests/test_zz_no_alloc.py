@@ -42,7 +42,8 @@ def run(fn, p, ops, split, D=None):
 # (M, N, K, split, A format): the skinny split path, the rows kernel's split,
 # the tiled split, FP6 A on the 8-bit tiles (its re-laid copy in the
 # scratch), the rows kernel's split with FP8 and FP6 A, the rows kernel's
-# two-slot ring (516 workgroups) split; each is followed by a smaller call
+# two-slot ring (516 workgroups) split, the single-row GEMV (no scratch)
+# with FP4 and FP8 A; each is followed by a smaller call
 CASES = [
     [(64, 7168, 16384, 2, 0), (40, 1000, 2048, 4, 0)],
     [(300, 520, 4096, 4, 0), (17, 200, 2048, 2, 0)],
@@ -50,6 +51,7 @@ CASES = [
     [(300, 520, 2048, 2, 3), (100, 260, 1024, 1, 3)],
     [(64, 2048, 4096, 2, 1), (33, 500, 2048, 4, 3)],
     [(50, 8200, 2048, 4, 0), (40, 1000, 1024, 2, 0)],
+    [(1, 8192, 8192, -1, 0), (1, 2050, 4096, -1, 1)],
 ]
 
 
