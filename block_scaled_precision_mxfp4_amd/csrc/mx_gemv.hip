@@ -1,4 +1,5 @@
-// Single-row MXFP4 GEMV (M == 1, FP4 A, row-major FP4 B) on gfx950.
+// Single-row block-scaled GEMV (M == 1, row-major FP4 B; A in FP4, or FP8 /
+// BF8 / FP6 below) on gfx950.
 //
 // The cost is reading B once from HBM.  A plain streaming read of B's bytes
 // runs fastest in small pieces: many workgroups, each wave a few KiB.  This
@@ -16,8 +17,8 @@
 //     bytes of each of the 4 rows, and the four of a chunk the rows' whole
 //     1 KiB.
 //   - A operand lane l (column y = l % 16): step y of the chunk, K-block
-//     l / 16 -- the chunk's 1 KiB of A in one load, the same for all four
-//     instructions.
+//     l / 16 -- the chunk's 1 KiB of FP4 A in one load, the same for all
+//     four instructions.
 // Output (x, y) of instruction t is B row x / 4 at step 4t + x % 4 against A
 // at step y; it is a term of the GEMV only where y = 4t + x % 4.  Lane l
 // holds outputs x = 4 (l / 16) + i, y = l % 16 (i = 0..3), so its term is
