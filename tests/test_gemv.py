@@ -6,8 +6,8 @@ FP6) to this kernel when K % 2048 == 0
 and its 4-row workgroups give every compute unit one (N >= 4 x CUs);
 MXGEMM_GEMV=0 keeps such shapes on the skinny kernel.  Cases: one chunk per
 wave (K = 2048, 6144 -- one wave idle -- and 8192), several chunks per wave
-(K = 16384 and 28672: the two-register-set loop, waves with unequal chunk
-counts), ragged N (a last workgroup with 1, 2 or 3 rows), beta with bf16
+(K = 16384, 28672 and 2^18: the two-register-set loop, waves with unequal
+chunk counts), ragged N (a last workgroup with 1, 2 or 3 rows), beta with bf16
 and float32 C, D aliasing C, padded rows of every operand, the E8M0
 special scale codes, and quantize-then-GEMM beside the fused bf16-A
 decode (which stays on the skinny kernel).  Source of the operation:
@@ -82,6 +82,18 @@ def test_gemv_wider_A_matches_oracle(shape, fmt):
     say("case gemv", FORMATS[fmt], shape)
     ref, mag, _ = oracle_ref(p)
     assert_parity(gemm_gpu(p), ref, mag, "gemv %s %s" % (FORMATS[fmt], shape))
+
+
+def test_gemv_long_K():
+    """K = 2^18 (128 chunks, 32 per wave through the two-set loop; 128 MiB
+    of B): against the oracle element by element."""
+    N, K = 1024, 1 << 18
+    assert planned(1, N, K) == "gemv_m1_n4"
+    p = inputs.make_problem(1, N, K, seed=0x6E18, e=(120, 134))
+    say("case gemv long K", (1, N, K))
+    d = gemm_gpu(p)
+    ref, mag, _ = oracle_ref(p)
+    assert_parity(d, ref, mag, "gemv long K")
 
 
 def test_gemv_f32_C_and_in_place():
