@@ -106,9 +106,8 @@ constexpr double kCuL2 = 64.0 * 2.4e9;
 // row-major B when K is a multiple of its 2048-K chunk and its 4-row
 // workgroups fill at least one per CU (N >= 4 * CUs); unsplit.
 // MXGEMM_GEMV=0 keeps such shapes on the skinny kernel.
-bool gemv_applies(int M, int N, int K, int b_packed, int split_req, int num_cu, int a_format)
+bool gemv_applies(int M, int N, int K, int b_packed, int split_req, int num_cu)
 {
-    (void)a_format;
     if (M != 1 || b_packed || K % 2048 || split_req > 1 ||
         (int64_t)cdiv(N, 4) < num_cu)
         return false;
@@ -184,7 +183,7 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool
         return best;
     }
     if (!tiled_only && allow_gemv && force_nr <= 1 &&
-        gemv_applies(M, N, K, b_packed, split_req, num_cu > 0 ? num_cu : 256, a_format)) {
+        gemv_applies(M, N, K, b_packed, split_req, num_cu > 0 ? num_cu : 256)) {
         best.family = 4;
         best.bm = 1;
         best.bn = 4;
@@ -368,8 +367,9 @@ Plan plan_a8(int M, int N, int K, int split_req, int num_cu, bool fp6 = false, b
 // The plan mxgemm_run follows for these options: FP4 A by the cost model
 // (the tiled kernel only in the bf16-atomic mode); a wider A with
 // 16 < M <= 64 on the rows kernel (FP6: an even K-block count); otherwise
-// with M > 16 on the 8-bit tiles, FP6 re-laid first; any other wider A on
-// the skinny kernel per 16 rows.
+// with M > 16 on the 8-bit tiles, FP6 re-laid first; any other wider A at
+// M == 1 on the single-row GEMV where it applies, else on the skinny kernel
+// per 16 rows.
 Plan plan_run(int M, int N, int K, const mxgemm_strides &s, int split_k, int num_cu, bool allow_gemv = true)
 {
     // an MN-major B is read through the tiled kernel's transposed LDS loads

@@ -88,8 +88,10 @@ const char *mxgemm_status_string(mxgemm_status status);
  *              scale per 32 elements as for FP4.  lda counts elements of
  *              A's format; the byte pitch lda*w/8 must be a whole multiple of
  *              16 (of 8 for the FP6 formats, whose dense rows are 24 bytes
- *              per 32 elements).  Kernels: for M <= 16 the skinny kernel
- *              and for 16 < M <= 64 the rows kernel (both at the speed of
+ *              per 32 elements).  Kernels: for M == 1 the single-row GEMV
+ *              where it applies (kernel family 4), else for M <= 16 the
+ *              skinny kernel, and for 16 < M <= 64 the rows kernel (all at
+ *              the speed of
  *              the FP4 case; FP6 on the rows kernel needs an even K/32);
  *              otherwise, for M > 16, the 8-bit formats run on the tiled
  *              kernel with 8-bit A tiles, and FP6 A is first re-laid,
