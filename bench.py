@@ -83,7 +83,7 @@ def workload_roofline(r):
 
 
 def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soak_ms=0.0, a_fmt=0, b_layout=0,
-                  packed=None):
+                  packed=None, a_packed=False):
     import numpy as np
     import torch
 
@@ -108,7 +108,8 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soa
     if a_fmt or b_layout:
         info = mx.mxgemm_query_ex(M, N, K, mx.make_strides(ldd=N, ldc=N, lda=K, ldb=ldb, ldsa=K // 32, ldsb=K // 32,
                                                           b_packed=int(packed), sa_packed=int(sa_packed),
-                                                          a_format=a_fmt, b_layout=b_layout), split_k)
+                                                          a_format=a_fmt, b_layout=b_layout,
+                                                          a_packed=int(a_packed)), split_k)
         info["packed_b_bytes"] = mx.mxgemm_query(M, N, K, int(packed), split_k)["packed_b_bytes"]
         info["packed_sb_bytes"] = mx.mxgemm_query(M, N, K, int(packed), split_k)["packed_sb_bytes"]
     else:
@@ -141,12 +142,18 @@ def time_workload(name, steps, warmup, split_k=-1, rotate=True, eager=False, soa
             SAp = torch.empty(info["packed_sa_bytes"], dtype=torch.uint8, device="cuda")
             mx.mxgemm_pack_scales(SAp, SA, M, K)
             SA = SAp
+        if a_packed:  # FP6 A and its scales put into the dense tile's order once, like a packed B
+            Ap = torch.empty(mx.mxgemm_pack_a_bytes(M, K), dtype=torch.uint8, device="cuda")
+            SAp = torch.empty(info["packed_sa_bytes"], dtype=torch.uint8, device="cuda")
+            mx.mxgemm_pack_a(Ap, SAp, A, SA, M, K, a_fmt)
+            A, SA = Ap, SAp
         sets.append((D, C, A, B, SA, SB))
     del A0, SA0, B0, SB0, C0
     wsp = torch.zeros(max(info["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
     strides = mx.make_strides(ldd=N, ldc=N, lda=K, ldb=ldb, ldsa=K // 32, ldsb=K // 32,
                               b_packed=int(packed), sa_packed=int(sa_packed), workspace=wsp,
-                              workspace_bytes=wsp.numel(), a_format=a_fmt, b_layout=b_layout)
+                              workspace_bytes=wsp.numel(), a_format=a_fmt, b_layout=b_layout,
+                              a_packed=int(a_packed))
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
@@ -551,6 +558,8 @@ def main():
     ap.add_argument("--b-layout", choices=("nk", "kn"), default="nk",
                     help="B of --workload stored K-major (nk, the default) or MN-major (kn, scales packed)")
     ap.add_argument("--packed", action="store_true", help="pre-shuffle B of --workload (and A scales if M > 64)")
+    ap.add_argument("--a-packed", action="store_true",
+                    help="FP6 A of --workload put into the dense tile's order once (mxgemm_pack_a; profiling runs)")
     ap.add_argument("--a-format", choices=sorted(FORMAT_CODES), default="fp4",
                     help="A of --workload in this format (profiling runs of the mixed-format lines)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -596,7 +605,7 @@ def main():
     head = time_workload(args.workload, args.steps, args.warmup, split_k=args.split_k, eager=args.eager,
                          soak_ms=args.soak_ms, b_layout=int(args.b_layout == "kn"),
                          packed=True if (args.b_layout == "kn" or args.packed) else None,
-                         a_fmt=FORMAT_CODES[args.a_format])
+                         a_fmt=FORMAT_CODES[args.a_format], a_packed=args.a_packed)
     others = []
     if not args.only:
         for name in inputs.WORKLOADS:
@@ -630,18 +639,23 @@ def main():
 
     mixed = []
     if not args.only:
-        for name, fmt in MIXED:
-            r = time_workload(name, args.steps, args.warmup, eager=args.eager, soak_ms=args.soak_ms, a_fmt=fmt)
+        # (the last entry: the FP6 square with A put into the dense tile's
+        # order once by mxgemm_pack_a, outside the timed call, as B is)
+        for name, fmt, a_packed in [(n, f, False) for n, f in MIXED] + [("square_8192", 3, True)]:
+            r = time_workload(name, args.steps, args.warmup, eager=args.eager, soak_ms=args.soak_ms, a_fmt=fmt,
+                              a_packed=a_packed)
             if r["M"] > 64:  # a contraction: the matrix peak of A's format (FP6 runs at the FP4 rate)
                 peak = PEAK_FP8_TFLOPS if fmt in (1, 2) else PEAK_MXFP4_TFLOPS
                 roof = {"bound": "mfma", "achieved": r["tflops"], "peak": peak, "unit": "TFLOP/s",
-                        "frac": r["tflops"] / peak, "traffic": measured_traffic(name + "_" + FORMAT_NAMES[fmt])}
+                        "frac": r["tflops"] / peak,
+                        "traffic": measured_traffic(name + "_" + FORMAT_NAMES[fmt] + ("_packed_a" if a_packed else ""))}
                 value, unit = r["tflops"], "TFLOP/s"
             else:
                 roof = {"bound": "hbm", "achieved": r["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": r["gbs"] / PEAK_HBM_GBS, "traffic": measured_traffic(name + "_" + FORMAT_NAMES[fmt])}
                 value, unit = r["gbs"], "GB/s"
-            mixed.append({"workload": name, "a_format": FORMAT_NAMES[fmt], "us_per_step": r["us_per_step"],
+            mixed.append({"workload": name, "a_format": FORMAT_NAMES[fmt], "a_packed": a_packed,
+                          "us_per_step": r["us_per_step"],
                           "value": value, "unit": unit, "tflops": r["tflops"],
                           "algorithmic_bytes": r["algorithmic_bytes"], "kernel": r["kernel"], "roofline": roof})
 

@@ -18,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
 
 # C-ABI entry points declared in include/libmxgemm.h
-EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_run_noalloc", "mxgemm_run_bf16a", "mxgemm_pack_b", "mxgemm_pack_scales", "mxgemm_quantize",
+EXPORTS = ("mxgemm_status_string", "mxgemm_run", "mxgemm_run_noalloc", "mxgemm_run_bf16a", "mxgemm_pack_b", "mxgemm_pack_scales", "mxgemm_pack_a",
+           "mxgemm_pack_a_bytes", "mxgemm_quantize",
            "mxgemm_f16_run", "mxgemm_query", "mxgemm_plan", "mxgemm_query_ex", "mxgemm_plan_ex",
            "mxgemm_stream_read", "mxgemm_release_workspaces")
 
@@ -40,7 +41,7 @@ class Strides(ctypes.Structure):
                 ("b_packed", ctypes.c_int32), ("sa_packed", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("c_f32", ctypes.c_int32), ("split_mode", ctypes.c_int32),
-                ("a_format", ctypes.c_int32), ("b_layout", ctypes.c_int32)]
+                ("a_format", ctypes.c_int32), ("b_layout", ctypes.c_int32), ("a_packed", ctypes.c_int32)]
 
 
 SPLIT_FP32 = 0         # MXGEMM_SPLIT_FP32
@@ -94,6 +95,10 @@ def lib():
         L.mxgemm_pack_b.restype = i32
         L.mxgemm_pack_scales.argtypes = [vp, vp, i32, i32, i64, vp]
         L.mxgemm_pack_scales.restype = i32
+        L.mxgemm_pack_a.argtypes = [vp, vp, vp, vp, i32, i32, i64, i64, i32, vp]
+        L.mxgemm_pack_a.restype = i32
+        L.mxgemm_pack_a_bytes.argtypes = [i32, i32]
+        L.mxgemm_pack_a_bytes.restype = ctypes.c_size_t
         L.mxgemm_quantize.argtypes = [vp, vp, vp, i32, i32, i64, i64, i64, vp]
         L.mxgemm_quantize.restype = i32
         L.mxgemm_f16_run.argtypes = [vp, vp, vp, i32, i32, i32, i64, i64, i64, vp]
@@ -144,9 +149,9 @@ def _check(status, where):
 
 
 def make_strides(*, ldd, ldc, lda, ldb, ldsa, ldsb, b_packed=0, sa_packed=0, workspace=None,
-                 workspace_bytes=0, c_f32=0, split_mode=SPLIT_FP32, a_format=FMT_FP4, b_layout=B_NK):
+                 workspace_bytes=0, c_f32=0, split_mode=SPLIT_FP32, a_format=FMT_FP4, b_layout=B_NK, a_packed=0):
     return Strides(ldd, ldc, lda, ldb, ldsa, ldsb, b_packed, sa_packed, _ptr(workspace), workspace_bytes,
-                   c_f32, split_mode, a_format, b_layout)
+                   c_f32, split_mode, a_format, b_layout, a_packed)
 
 
 def mxgemm_status_string(status: int) -> str:
@@ -196,6 +201,22 @@ def mxgemm_pack_scales(Sp, S, rows, K, lds=None, stream=None, check=True):
     if check:
         _check(st, "mxgemm_pack_scales")
     return st
+
+
+def mxgemm_pack_a(Ap, SAp, A, scaleA, M, K, a_format, lda=None, ldsa=None, stream=None, check=True):
+    """Put an FP6 A and its scales into the dense FP6 tile's order, for
+    mxgemm_run with a_packed = 1 (asynchronous)."""
+    lda = K if lda is None else lda
+    ldsa = K // 32 if ldsa is None else ldsa
+    st = lib().mxgemm_pack_a(_ptr(Ap), _ptr(SAp), _ptr(A), _ptr(scaleA), int(M), int(K), int(lda), int(ldsa),
+                             int(a_format), _stream(stream))
+    if check:
+        _check(st, "mxgemm_pack_a")
+    return st
+
+
+def mxgemm_pack_a_bytes(M, K) -> int:
+    return int(lib().mxgemm_pack_a_bytes(int(M), int(K)))
 
 
 def mxgemm_run_bf16a(D, C, X, B, scaleB, alpha, beta, M, N, K, ldx=None, strides=None, split_k=-1,

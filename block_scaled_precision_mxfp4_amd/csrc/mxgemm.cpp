@@ -302,7 +302,8 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool
 // for it first, at the cost of a pass over B).
 // MXGEMM_A8_TILE=<kernel name> restricts the choice to that tile where it
 // applies (a test hook).
-Plan plan_a8(int M, int N, int K, int split_req, int num_cu, bool fp6 = false, bool b_packed = false)
+Plan plan_a8(int M, int N, int K, int split_req, int num_cu, bool fp6 = false, bool b_packed = false,
+             bool dense_only = false)
 {
     const int KB = K / 32;
     if (num_cu <= 0)
@@ -317,7 +318,7 @@ Plan plan_a8(int M, int N, int K, int split_req, int num_cu, bool fp6 = false, b
     double best_t = 1e300;
     for (int k = 0; k < n; ++k) {
         const mx::TileKernelA8 &tk = tile[k];
-        if (tk.fp6_dense && !fp6)
+        if ((tk.fp6_dense && !fp6) || (dense_only && !tk.fp6_dense))
             continue;
         if (only_ok && std::strcmp(only, tk.name) != 0)
             continue;
@@ -378,6 +379,10 @@ Plan plan_run(int M, int N, int K, const mxgemm_strides &s, int split_k, int num
                         s.split_mode == MXGEMM_SPLIT_BF16_ATOMIC || s.b_layout == MXGEMM_B_KN, 0,
                         MXGEMM_FMT_FP4, allow_gemv);
     const bool fp6 = s.a_format == MXGEMM_FMT_FP6_E2M3 || s.a_format == MXGEMM_FMT_FP6_E3M2;
+    // an A already in the dense FP6 operand order (mxgemm_pack_a) is read
+    // by the dense FP6 tile only
+    if (fp6 && s.a_packed)
+        return plan_a8(M, N, K, split_k, num_cu, true, s.b_packed != 0, true);
     if (M > 16 && M <= 64 && (!fp6 || (K / 32) % 2 == 0))
         return plan_for(M, N, K, s.b_packed, split_k, num_cu, false, 0, s.a_format);
     if ((s.a_format == MXGEMM_FMT_FP8_E4M3 || s.a_format == MXGEMM_FMT_FP8_E5M2) && M > 16)
@@ -611,7 +616,9 @@ static bool valid_options(const mxgemm_strides &s)
            (s.split_mode == MXGEMM_SPLIT_FP32 || s.split_mode == MXGEMM_SPLIT_BF16_ATOMIC) &&
            s.a_format >= MXGEMM_FMT_FP4 && s.a_format <= MXGEMM_FMT_FP6_E3M2 &&
            (s.b_layout == MXGEMM_B_NK || (s.b_layout == MXGEMM_B_KN && s.a_format == MXGEMM_FMT_FP4)) &&
-           (s.a_format == MXGEMM_FMT_FP4 || (!s.sa_packed && s.split_mode == MXGEMM_SPLIT_FP32));
+           (s.a_format == MXGEMM_FMT_FP4 || (!s.sa_packed && s.split_mode == MXGEMM_SPLIT_FP32)) &&
+           (s.a_packed == 0 ||
+            (s.a_packed == 1 && (s.a_format == MXGEMM_FMT_FP6_E2M3 || s.a_format == MXGEMM_FMT_FP6_E3M2)));
 }
 
 mxgemm_status mxgemm_plan_ex(int M, int N, int K, const mxgemm_strides *strides, int split_k, int num_cu,
@@ -621,7 +628,7 @@ mxgemm_status mxgemm_plan_ex(int M, int N, int K, const mxgemm_strides *strides,
     std::memset(&s, 0, sizeof s);
     if (strides)
         s = *strides;
-    if (!out || !valid_split(split_k) || num_cu < 1 || !valid_options(s))
+    if (!out || !valid_split(split_k) || num_cu < 1 || !valid_options(s) || (s.a_packed && M <= 64))
         return MXGEMM_ERR_INVALID_ARG;
     mxgemm_status st = check_shape(M, N, K);
     if (st != MXGEMM_OK)
@@ -709,6 +716,14 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
             return MXGEMM_ERR_INVALID_ARG;
         if (s.a_format != MXGEMM_FMT_FP4 && (s.sa_packed || s.split_mode != MXGEMM_SPLIT_FP32))
             return MXGEMM_ERR_INVALID_ARG;
+        // a pre-packed FP6 A feeds the dense FP6 tile, which runs for M > 64
+        if ((s.a_packed != 0 && s.a_packed != 1) ||
+            (s.a_packed && (X || M <= 64 || (s.a_format != MXGEMM_FMT_FP6_E2M3 && s.a_format != MXGEMM_FMT_FP6_E3M2))))
+            return MXGEMM_ERR_INVALID_ARG;
+        if (s.a_packed) {  // lda and ldsa are not used: the layout is fixed by M and K
+            s.lda = K;
+            s.ldsa = K / 32;
+        }
     } else {
         std::memset(&s, 0, sizeof s);
         s.ldd = s.ldc = N;
@@ -747,7 +762,7 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     if (!aligned(A, 16) || !aligned(B, 16) || lda_bytes % (a_bits == 6 ? 8 : 16) ||
         (b_rows && (s.ldb / 2) % 16))
         return MXGEMM_ERR_ALIGN;
-    if ((s.b_packed && !aligned(scaleB, 4)) || (!X && s.sa_packed && !aligned(scaleA, 4)))
+    if ((s.b_packed && !aligned(scaleB, 4)) || (!X && (s.sa_packed || s.a_packed) && !aligned(scaleA, 4)))
         return MXGEMM_ERR_ALIGN;
     if (!aligned(D, 2) || (C && beta != 0.0f && !aligned(C, s.c_f32 ? 4 : 2)))
         return MXGEMM_ERR_ALIGN;
@@ -823,11 +838,13 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
     const bool fp6_conv = p.family == 3 && (s.a_format == MXGEMM_FMT_FP6_E2M3 || s.a_format == MXGEMM_FMT_FP6_E3M2);
     int n_a8 = 0;
     const bool fp6_dense = fp6_conv && mx::tile_kernels_a8(&n_a8)[p.index].fp6_dense;
-    const size_t a6_bytes = fp6_dense ? align_up((size_t)cdiv(M, 16) * (size_t)mx::fp6_pack_group_bytes(K), 256) : 0;
+    // (a pre-packed A is read where it is: no copy of A or its scales)
+    const bool a_here = fp6_dense && !s.a_packed;
+    const size_t a6_bytes = a_here ? align_up((size_t)cdiv(M, 16) * (size_t)mx::fp6_pack_group_bytes(K), 256) : 0;
     // [A dense | A scales packed | B packed | B scales packed]: a row-major
     // B is packed too, the tile reads only the packed layout
     const bool pack_b_here = fp6_dense && !s.b_packed;
-    const size_t sap_bytes = fp6_dense ? align_up(packed_sb_bytes(M, K), 256) : 0;
+    const size_t sap_bytes = a_here ? align_up(packed_sb_bytes(M, K), 256) : 0;
     const size_t bp_bytes = pack_b_here ? align_up(packed_b_bytes(N, K), 256) : 0;
     const size_t conv_bytes = !fp6_conv ? 0
                               : fp6_dense ? a6_bytes + sap_bytes + bp_bytes + (pack_b_here ? packed_sb_bytes(N, K) : 0)
@@ -903,18 +920,23 @@ mxgemm_status run_impl(void *D, const void *C, const void *A, const void *B, con
             void *conv = nullptr;
             if (noalloc) {
                 conv = scr + mx::kScratchCounterBytes + scr_part;
-            } else {
+            } else if (conv_bytes > 0) {
                 st = get_conv_buffer(stream, conv_bytes, &conv);
                 if (st != MXGEMM_OK)
                     return st;
             }
             if (fp6_dense) {
                 uint8_t *sap = (uint8_t *)conv + a6_bytes;
-                mx::launch_fp6_pack((const uint8_t *)A, lda_bytes, (const uint8_t *)scaleA, s.ldsa, (uint8_t *)conv,
-                                    (uint32_t *)sap, M, K, stream);
-                g.A = (const uint8_t *)conv;
+                if (a_here) {
+                    mx::launch_fp6_pack((const uint8_t *)A, lda_bytes, (const uint8_t *)scaleA, s.ldsa,
+                                        (uint8_t *)conv, (uint32_t *)sap, M, K, stream);
+                    g.A = (const uint8_t *)conv;
+                    g.SA = sap;
+                } else {  // mxgemm_pack_a's output, read in place
+                    g.A = (const uint8_t *)A;
+                    g.SA = (const uint8_t *)scaleA;
+                }
                 g.lda_b = mx::fp6_pack_group_bytes(K);
-                g.SA = sap;
                 g.sa_packed = 1;
                 g.persist_grid = (int)persist_grid(p, M, N, K, d->num_cu, g.d_stage != 0, KB % 8 == 0, true);
                 if (pack_b_here) {
@@ -1069,6 +1091,38 @@ mxgemm_status mxgemm_pack_scales(void *Sp, const void *S, int rows, int K, int64
     if (st != MXGEMM_OK)
         return st;
     mx::launch_pack_sb((uint32_t *)Sp, (const uint8_t *)S, rows, K / 32, lds, stream);
+    if (hipGetLastError() != hipSuccess)
+        return MXGEMM_ERR_HIP;
+    return MXGEMM_OK;
+}
+
+size_t mxgemm_pack_a_bytes(int M, int K)
+{
+    if (check_shape(M, 1, K) != MXGEMM_OK)
+        return 0;
+    return (size_t)cdiv(M, 16) * (size_t)mx::fp6_pack_group_bytes(K);
+}
+
+mxgemm_status mxgemm_pack_a(void *Ap, void *SAp, const void *A, const void *scaleA, int M, int K, int64_t lda,
+                            int64_t ldsa, int a_format, hipStream_t stream)
+{
+    if (!Ap || !SAp || !A || !scaleA ||
+        (a_format != MXGEMM_FMT_FP6_E2M3 && a_format != MXGEMM_FMT_FP6_E3M2))
+        return MXGEMM_ERR_INVALID_ARG;
+    mxgemm_status st = check_shape(M, 1, K);
+    if (st != MXGEMM_OK)
+        return st;
+    if (lda < K || ldsa < K / 32)
+        return MXGEMM_ERR_SHAPE;
+    // FP6 rows: lda * 6 / 8 bytes, in whole 8-byte units, as mxgemm_run reads them
+    if ((lda * 6) % 8 || (lda * 6 / 8) % 8 || !aligned(A, 16) || !aligned(Ap, 16) || !aligned(SAp, 4))
+        return MXGEMM_ERR_ALIGN;
+    DeviceInfo *d = nullptr;
+    st = device_info(&d);
+    if (st != MXGEMM_OK)
+        return st;
+    mx::launch_fp6_pack((const uint8_t *)A, lda * 6 / 8, (const uint8_t *)scaleA, ldsa, (uint8_t *)Ap,
+                        (uint32_t *)SAp, M, K, stream);
     if (hipGetLastError() != hipSuccess)
         return MXGEMM_ERR_HIP;
     return MXGEMM_OK;

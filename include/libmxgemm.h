@@ -173,6 +173,10 @@ typedef struct mxgemm_strides {
     int32_t split_mode; /* MXGEMM_SPLIT_FP32 or MXGEMM_SPLIT_BF16_ATOMIC */
     int32_t a_format;   /* MXGEMM_FMT_* */
     int32_t b_layout;   /* MXGEMM_B_NK (B's rows hold K) or MXGEMM_B_KN (B's rows hold N) */
+    int32_t a_packed;   /* 0: A and scaleA as above; 1: an FP6 A (a_format MXGEMM_FMT_FP6_*)
+                           and its scales as mxgemm_pack_a wrote them (lda, ldsa and
+                           sa_packed ignored; M > 64, where the dense FP6 tile runs; not
+                           with mxgemm_run_bf16a): the call skips its re-layout of A */
 } mxgemm_strides;
 
 /* ---- the GEMM ------------------------------------------------------------- */
@@ -288,6 +292,30 @@ mxgemm_status mxgemm_pack_b(void *Bp, void *SBp, const void *B, const void *scal
  */
 mxgemm_status mxgemm_pack_scales(void *Sp, const void *S, int rows, int K, int64_t lds,
                                  hipStream_t stream);
+
+/*
+ * An FP6 A (a_format MXGEMM_FMT_FP6_E2M3 or _E3M2; the layout does not depend
+ * on which) and its scales, put once into the order the dense FP6 tile reads:
+ * what mxgemm_run does to a row-major FP6 A on every call with M > 64
+ * (for an A used in several calls, or written that way by its producer).
+ * Codes: per 16-row group of A and 128-K step, 1536 bytes in the scaled
+ * matrix instruction's operand order ("CDNA4 dense MFMA builtins",
+ * "Mixed-precision with scaling": lane l holds row l%16, K-block l/16 of the
+ * step, 24 bytes of FP6 codes, unchanged), steps padded to an even count,
+ * groups in order; rows past M and blocks past K/32 are code 0.  Scales:
+ * mxgemm_pack_scales' shuffle of scaleA (padding 0x7F).  A: [M][lda] FP6
+ * elements (byte pitch lda*6/8 a multiple of 8; A 16-byte aligned);
+ * scaleA: [M][ldsa] bytes.  Ap: mxgemm_pack_a_bytes(M, K) bytes, 16-byte
+ * aligned; SAp: ceil(M/32)*32 * ceil(K/256)*8 bytes (packed_sa_bytes),
+ * 4-byte aligned; neither overlaps A or scaleA.  Pass Ap as A and SAp as
+ * scaleA to mxgemm_run with a_packed = 1.  Asynchronous on `stream`; errors
+ * as mxgemm_run (MXGEMM_ERR_INVALID_ARG for another a_format).
+ */
+mxgemm_status mxgemm_pack_a(void *Ap, void *SAp, const void *A, const void *scaleA, int M, int K,
+                            int64_t lda, int64_t ldsa, int a_format, hipStream_t stream);
+
+/* Bytes of mxgemm_pack_a's Ap for an M x K FP6 A (0 for an invalid shape). */
+size_t mxgemm_pack_a_bytes(int M, int K);
 
 /* ---- activation quantizer -------------------------------------------------------- */
 

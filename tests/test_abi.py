@@ -325,3 +325,24 @@ def test_stream_read_validation_before_any_hip_call():
     assert f(nbytes=0) == -2 and f(nbytes=4100) == -2 and f(nbytes=1 << 31) == -2
     assert f(src=0x1008) == -3 and f(sink=0x2002) == -3
     assert f() not in (-1, -2, -3)
+
+
+def test_prepacked_fp6_A_plan_and_sizes():
+    """a_packed = 1 (an FP6 A from mxgemm_pack_a): planned on the dense FP6
+    tile whatever the cost model would pick, refused for FP4/FP8 A and for
+    M <= 64; mxgemm_pack_a_bytes = ceil(M/16) x even 128-K steps x 1536."""
+    def st(fmt, a_packed):
+        return mx.make_strides(ldd=2048, ldc=2048, lda=4096, ldb=4096, ldsa=128, ldsb=128, b_packed=1,
+                               a_format=fmt, a_packed=a_packed)
+    # the cost model keeps 2048 x 2048 x 4096 FP6 on the 128 x 128 tile
+    assert mx.mxgemm_plan_ex(2048, 2048, 4096, st(mx.FMT_FP6_E2M3, 0))["kernel_name"] != "tile_fp6_256x256"
+    for fmt in (mx.FMT_FP6_E2M3, mx.FMT_FP6_E3M2):
+        assert mx.mxgemm_plan_ex(2048, 2048, 4096, st(fmt, 1))["kernel_name"] == "tile_fp6_256x256"
+    for fmt, M in ((mx.FMT_FP4, 2048), (mx.FMT_FP8_E4M3, 2048), (mx.FMT_FP6_E2M3, 64), (mx.FMT_FP6_E2M3, 1)):
+        with pytest.raises(mx.MxGemmError):
+            mx.mxgemm_plan_ex(M, 2048, 4096, st(fmt, 1))
+    with pytest.raises(mx.MxGemmError):
+        mx.mxgemm_plan_ex(2048, 2048, 4096, st(mx.FMT_FP6_E2M3, 2))
+    assert mx.mxgemm_pack_a_bytes(33, 1056) == 3 * 10 * 1536  # 33 blocks -> 5 8-block stages -> 10 steps
+    assert mx.mxgemm_pack_a_bytes(8192, 8192) == 512 * 64 * 1536
+    assert mx.mxgemm_pack_a_bytes(0, 1024) == 0
