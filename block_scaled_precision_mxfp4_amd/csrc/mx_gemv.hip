@@ -39,6 +39,16 @@
 // (g = l / 16); FP6, the block's 24 bytes.  A chunk of A is then 2 KiB or
 // 1.5 KiB instead of 1 KiB; B and the scales are unchanged.
 //
+// MR: 2 <= M <= 4 (FP4 A), the small-batch decode.  The A operand's lanes
+// then pair like B's: lane y = l % 16 carries A row y / 4 at step 4t + y % 4
+// (one 16-byte load per lane and instruction: 256 contiguous bytes of each
+// of the 4 rows, rows past M loading nothing), and its scale words reach
+// their lanes by the same permute as B's.  Output (x, y) is a term where the
+// two steps agree, x % 4 = y % 4, for B row x / 4 and A row y / 4; those
+// positions are the same in every instruction, so one accumulator sums the
+// chunk: lane l's term is element l % 4, for A row (l % 16) / 4 and B row
+// l / 16, and each (A row, B row) pair's four terms sit in one lane quad.
+//
 // Requires K % 2048 == 0 (every chunk whole: no range checks inside K, no
 // scale bytes of a neighbouring row), 16-byte aligned scale rows, split 1.
 #include "mx_args.hpp"
@@ -51,26 +61,37 @@ namespace mx {
 constexpr int kGemvRows = 4;     // rows of B (columns of D) per workgroup
 constexpr int kGemvChunk = 2048; // K per chunk: 16 steps of 128
 
-template <int AF>
+template <int AF, bool MR>
 struct GemvChunk {
     using a_t = typename std::conditional<AF == 0, v4i, v8i>::type;
     v4i b[4];     // B operand of instruction t
-    a_t a;        // A operand, all 16 steps of the chunk
-    uint32_t sa;  // A scale bytes of step l % 16
+    a_t a;        // A operand, all 16 steps of the chunk (one row)
+    v4i am[MR ? 4 : 1];  // MR: A operand of instruction t (4 rows x 4 steps)
+    uint32_t sa;  // A scale bytes of step l % 16 (MR: of row l / 16)
     uint32_t sb;  // B scale bytes of row l / 16, step l % 16
 };
 
 // Loads of chunk c (nothing, without memory traffic, when !on).  The scale
 // words and the A operand go first: the scale permutes can then start while
 // B is still arriving, and each multiply waits only for its own B operand.
-template <int AF>
-__device__ __forceinline__ void gemv_issue(GemvChunk<AF> &ch, int c, bool on, __amdgpu_buffer_rsrc_t rb,
+template <int AF, bool MR>
+__device__ __forceinline__ void gemv_issue(GemvChunk<AF, MR> &ch, int c, bool on, __amdgpu_buffer_rsrc_t rb,
                                            __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rsa,
                                            __amdgpu_buffer_rsrc_t rsb, uint32_t b_lane, uint32_t sb_lane,
-                                           int lane)
+                                           uint32_t a_lane, uint32_t sa_lane, int lane)
 {
     const uint32_t bc = (uint32_t)c * (kGemvChunk / 2);
     ch.sb = load4(rsb, on && sb_lane != kOOB ? sb_lane + (uint32_t)c * 64 : kOOB);
+    if constexpr (MR) {
+        ch.sa = load4(rsa, on && sa_lane != kOOB ? sa_lane + (uint32_t)c * 64 : kOOB);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            ch.am[t] = load16(ra, on && a_lane != kOOB ? a_lane + bc + t * 256 : kOOB);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            ch.b[t] = load16_stream(rb, on && b_lane != kOOB ? b_lane + bc + t * 256 : kOOB);
+        return;
+    }
     ch.sa = load4(rsa, on ? (uint32_t)c * 64 + (lane & 15) * 4 : kOOB);
     constexpr int AKB = 4 * kFmtBits[AF];  // bytes of an A K-block
     const uint32_t ac = (uint32_t)c * 64 * AKB + (lane & 15) * 4 * AKB;  // the lane's step
@@ -91,12 +112,24 @@ __device__ __forceinline__ void gemv_issue(GemvChunk<AF> &ch, int c, bool on, __
         ch.b[t] = load16_stream(rb, on && b_lane != kOOB ? b_lane + bc + t * 256 : kOOB);
 }
 
-template <int AF>
-__device__ __forceinline__ void gemv_compute(const GemvChunk<AF> &ch, v4f (&acc)[4], int lane)
+template <int AF, bool MR>
+__device__ __forceinline__ void gemv_compute(const GemvChunk<AF, MR> &ch, v4f (&acc)[4], int lane)
 {
     const int sh = 8 * (lane >> 4);
-    const int sa = (int)(ch.sa >> sh);
     const int q = lane & 15;
+    if constexpr (MR) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            // B's and A's scale words of this lane: row q / 4 of each, step
+            // 4t + q % 4 of the chunk
+            const int src = (q >> 2) * 16 + 4 * t + (q & 3);
+            const uint32_t wb = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)ch.sb);
+            const uint32_t wa = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)ch.sa);
+            acc[0] = mfma_fp4<0, 0>(ch.b[t], ch.am[t], acc[0], (int)(wb >> sh), (int)(wa >> sh));
+        }
+        return;
+    }
+    const int sa = (int)(ch.sa >> sh);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         // this lane's B scale word: row q / 4, step 4t + q % 4 of the chunk
@@ -110,10 +143,10 @@ __device__ __forceinline__ void gemv_compute(const GemvChunk<AF> &ch, v4f (&acc)
 }
 
 // LOOP = false: at most one chunk per wave (K <= 8192), one register set.
-template <int AF, bool LOOP>
+template <int AF, bool LOOP, bool MR>
 __device__ __forceinline__ void gemv_body(const GemmArgs &g)
 {
-    __shared__ float s_part[4][kGemvRows];
+    __shared__ float s_part[4][MR ? 4 : 1][kGemvRows];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n0 = blockIdx.x * kGemvRows;
@@ -121,8 +154,8 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
     const uint32_t kbytes = (uint32_t)(g.K / 2);
     const auto rb = make_rsrc(g.B + (int64_t)n0 * g.ldb_b, (uint32_t)((rows - 1) * g.ldb_b) + kbytes);
     const auto rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)((rows - 1) * g.ldsb + g.KB));
-    const auto ra = make_rsrc(g.A, (uint32_t)((int64_t)g.K * kFmtBits[AF] / 8));
-    const auto rsa = make_rsrc(g.SA, (uint32_t)g.KB);
+    const auto ra = make_rsrc(g.A, (uint32_t)((int64_t)(MR ? g.M - 1 : 0) * g.lda_b + (int64_t)g.K * kFmtBits[AF] / 8));
+    const auto rsa = make_rsrc(g.SA, (uint32_t)((int64_t)(MR ? g.M - 1 : 0) * g.ldsa + g.KB));
 
     // per-lane offsets inside a chunk: B row (l % 16) / 4 at step l % 4 of
     // the instruction's four, K-block l / 16; B scale dword: row l / 16,
@@ -131,6 +164,9 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
     const uint32_t b_lane = br < rows ? (uint32_t)(br * g.ldb_b) + (lane & 3) * 64 + (lane >> 4) * 16 : kOOB;
     const int sr = lane >> 4;
     const uint32_t sb_lane = sr < rows ? (uint32_t)(sr * g.ldsb) + (lane & 15) * 4 : kOOB;
+    // MR: A row (l % 16) / 4 as B's, and its scale dword row l / 16
+    const uint32_t a_lane = MR && br < g.M ? (uint32_t)(br * g.lda_b) + (lane & 3) * 64 + (lane >> 4) * 16 : kOOB;
+    const uint32_t sa_lane = MR && sr < g.M ? (uint32_t)(sr * g.ldsa) + (lane & 15) * 4 : kOOB;
 
     v4f acc[4];
 #pragma unroll
@@ -140,8 +176,8 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
     const int chunks = g.K / kGemvChunk;
     int c = wave;
     if (c < chunks) {
-        GemvChunk<AF> x;
-        gemv_issue(x, c, true, rb, ra, rsa, rsb, b_lane, sb_lane, lane);
+        GemvChunk<AF, MR> x;
+        gemv_issue(x, c, true, rb, ra, rsa, rsb, b_lane, sb_lane, a_lane, sa_lane, lane);
         if (!LOOP) {
             gemv_compute(x, acc, lane);
         } else if (c + 4 >= chunks) {
@@ -152,18 +188,48 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
             // both sets (a chunk past K loads nothing and adds zeros), so no
             // load is conditional and each multiply waits only for its own
             // operands.
-            GemvChunk<AF> y;
+            GemvChunk<AF, MR> y;
             const int mine = (chunks - wave + 3) / 4;  // this wave's chunks
             for (int i = 0; i < mine; i += 2) {
-                gemv_issue(y, c + 4, c + 4 < chunks, rb, ra, rsa, rsb, b_lane, sb_lane, lane);
+                gemv_issue(y, c + 4, c + 4 < chunks, rb, ra, rsa, rsb, b_lane, sb_lane, a_lane, sa_lane, lane);
                 gemv_compute(x, acc, lane);
-                gemv_issue(x, c + 8, c + 8 < chunks, rb, ra, rsa, rsb, b_lane, sb_lane, lane);
+                gemv_issue(x, c + 8, c + 8 < chunks, rb, ra, rsa, rsb, b_lane, sb_lane, a_lane, sa_lane, lane);
                 gemv_compute(y, acc, lane);
                 c += 8;
             }
         }
     }
 
+    if constexpr (MR) {
+        // the lane's term: element l % 4, for A row (l % 16) / 4 and B row
+        // l / 16; a quad (lane ^ 1, lane ^ 2) holds one pair's four terms
+        const int ii = lane & 3;
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (i == ii)
+                v = acc[0][i];
+        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+        if ((lane & 3) == 0)
+            s_part[wave][(lane & 15) >> 2][lane >> 4] = v;
+        __syncthreads();
+        if (threadIdx.x < g.M) {
+            const int m = threadIdx.x;
+            v4f tot;
+#pragma unroll
+            for (int r = 0; r < kGemvRows; ++r) {
+                float s = s_part[0][m][r];
+#pragma unroll
+                for (int w = 1; w < 4; ++w)
+                    s += s_part[w][m][r];
+                tot[r] = s;
+            }
+            Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec, g.c_f32};
+            store_quad(ep, m, n0, tot);
+        }
+        return;
+    }
     // the lane's term: accumulator l % 4 of instruction (l % 16) / 4
     const int ti = (lane & 15) >> 2, ii = lane & 3;
     float v = 0.f;
@@ -181,16 +247,16 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));
     if ((lane & 15) == 0)
-        s_part[wave][lane >> 4] = v;
+        s_part[wave][0][lane >> 4] = v;
     __syncthreads();
     if (threadIdx.x == 0) {
         v4f tot;
 #pragma unroll
         for (int r = 0; r < kGemvRows; ++r) {
-            float s = s_part[0][r];
+            float s = s_part[0][0][r];
 #pragma unroll
             for (int w = 1; w < 4; ++w)
-                s += s_part[w][r];
+                s += s_part[w][0][r];
             tot[r] = s;
         }
         Epilogue ep{g.D, g.C, g.alpha, g.beta, g.M, g.N, g.ldd, g.ldc, g.d_vec, g.c_vec, g.c_f32};
@@ -198,37 +264,41 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
     }
 }
 
-template <int AF>
+template <int AF, bool MR>
 __global__ void __launch_bounds__(256) mx_gemv_kernel(GemmArgs g)
 {
-    gemv_body<AF, true>(g);
+    gemv_body<AF, true, MR>(g);
 }
 
 // One chunk per wave: at most 64 registers, so that eight waves fit a SIMD
 // and all 2048 workgroups of N = 8192 are resident at once.
-template <int AF>
+template <int AF, bool MR>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) mx_gemv1_kernel(GemmArgs g)
 {
-    gemv_body<AF, false>(g);
+    gemv_body<AF, false, MR>(g);
 }
 
-template <int AF>
+template <int AF, bool MR>
 static void launch_gemv_fmt(const GemmArgs &g, int grid, hipStream_t s)
 {
     if (g.K <= 4 * kGemvChunk)
-        hipLaunchKernelGGL(mx_gemv1_kernel<AF>, dim3(grid), dim3(256), 0, s, g);
+        hipLaunchKernelGGL((mx_gemv1_kernel<AF, MR>), dim3(grid), dim3(256), 0, s, g);
     else
-        hipLaunchKernelGGL(mx_gemv_kernel<AF>, dim3(grid), dim3(256), 0, s, g);
+        hipLaunchKernelGGL((mx_gemv_kernel<AF, MR>), dim3(grid), dim3(256), 0, s, g);
 }
 
 void launch_gemv(int a_fmt, const GemmArgs &g, int grid, hipStream_t s)
 {
+    if (g.M > 1) {  // 2 <= M <= 4, FP4 A
+        launch_gemv_fmt<0, true>(g, grid, s);
+        return;
+    }
     switch (a_fmt) {
-    case 0: launch_gemv_fmt<0>(g, grid, s); break;
-    case 1: launch_gemv_fmt<1>(g, grid, s); break;
-    case 2: launch_gemv_fmt<2>(g, grid, s); break;
-    case 3: launch_gemv_fmt<3>(g, grid, s); break;
-    default: launch_gemv_fmt<4>(g, grid, s); break;
+    case 0: launch_gemv_fmt<0, false>(g, grid, s); break;
+    case 1: launch_gemv_fmt<1, false>(g, grid, s); break;
+    case 2: launch_gemv_fmt<2, false>(g, grid, s); break;
+    case 3: launch_gemv_fmt<3, false>(g, grid, s); break;
+    default: launch_gemv_fmt<4, false>(g, grid, s); break;
     }
 }
 

@@ -1,5 +1,6 @@
-"""GPU parity of the single-row GEMV (`gemv_m1_n4`: M == 1, FP4 A, row-major
-FP4 B, K a multiple of 2048), through the C-ABI, against the oracle.
+"""GPU parity of the GEMV (`gemv_m1_n4`: M == 1; `gemv_m4_n4`: 2 <= M <= 4
+with FP4 A; row-major FP4 B, K a multiple of 2048), through the C-ABI,
+against the oracle.
 
 The planner sends M == 1 with a row-major B (A in FP4, FP8, BF8 or either
 FP6) to this kernel when K % 2048 == 0
@@ -96,6 +97,37 @@ def test_gemv_long_K():
     assert_parity(d, ref, mag, "gemv long K")
 
 
+@pytest.mark.parametrize("M", [2, 3, 4])
+@pytest.mark.parametrize("shape", [(1024, 2048), (1027, 6144), (2050, 16384)], ids=lambda s: "x%dx%d" % s)
+def test_gemv_small_batch_matches_oracle(shape, M, monkeypatch):
+    """2 <= M <= 4 (FP4 A): A rows through the B-like operand lanes, one
+    accumulator per chunk; padded A and scale rows (pitches beyond K), C with
+    beta; against the oracle, and the skinny kernel (MXGEMM_GEMV=0) on the
+    same problem within the same tolerance."""
+    N, K = shape
+    assert planned(M, N, K) == "gemv_m4_n4"
+    p = inputs.make_problem(M, N, K, seed=0x6E40 + 17 * M + N, e=(118, 136), beta=1.0, c_sigma=2.0)
+    p["alpha"], p["beta"] = 0.5, -0.75
+    ref, mag, _ = oracle_ref(p)
+    lda, ldsa = K + 128, K // 32 + 16
+    Apad = np.zeros((M, lda // 2), dtype=np.uint8)
+    Apad[:, : K // 2] = p["A"]
+    SApad = np.full((M, ldsa), 0xFF, dtype=np.uint8)  # NaN scale bytes past each row's K
+    SApad[:, : K // 32] = p["SA"]
+    A, SA, B, SB = dev_u8(Apad), dev_u8(SApad), dev_u8(p["B"]), dev_u8(p["SB"])
+    C = dev_bf16(p["C"])
+    st = mx.make_strides(ldd=N, ldc=N, lda=lda, ldb=K, ldsa=ldsa, ldsb=K // 32)
+    assert mx.mxgemm_query_ex(M, N, K, st, -1)["kernel_name"] == "gemv_m4_n4"
+    say("case gemv small batch", (M, N, K))
+    D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    mx.mxgemm_run(D, C, A, B, SA, SB, p["alpha"], p["beta"], M, N, K, strides=st)
+    torch.cuda.synchronize()
+    assert_parity(host_bits(D), ref, mag, "gemv M=%d %s" % (M, shape))
+    monkeypatch.setenv("MXGEMM_GEMV", "0")
+    assert planned(M, N, K).startswith("skinny")
+    assert_parity(gemm_gpu(p), ref, mag, "skinny M=%d %s" % (M, shape))
+
+
 def test_gemv_f32_C_and_in_place():
     N, K = 1030, 8192
     p = inputs.make_problem(1, N, K, seed=0x6EF3, beta=1.0, c_sigma=2.0)
@@ -173,7 +205,8 @@ def test_gemv_plan_conditions():
     assert planned(1, 4 * ncu - 4, 2048) != "gemv_m1_n4"
     assert planned(1, 8192, 8192, b_packed=1) != "gemv_m1_n4"
     assert planned(1, 8192, 8192 + 1024) != "gemv_m1_n4"
-    assert planned(2, 8192, 8192) != "gemv_m1_n4"
+    assert planned(2, 8192, 8192) == "gemv_m4_n4"
+    assert planned(5, 8192, 8192).startswith("skinny")
     assert planned(1, 8192, 8192, split=2) != "gemv_m1_n4"
     assert planned(1, 8192, 8192, split=1) == "gemv_m1_n4"
 
