@@ -88,8 +88,8 @@ const char *mxgemm_status_string(mxgemm_status status);
  *              scale per 32 elements as for FP4.  lda counts elements of
  *              A's format; the byte pitch lda*w/8 must be a whole multiple of
  *              16 (of 8 for the FP6 formats, whose dense rows are 24 bytes
- *              per 32 elements).  Kernels: for M == 1 the single-row GEMV
- *              where it applies (kernel family 4), else for M <= 16 the
+ *              per 32 elements).  Kernels: for M == 1 the GEMV where it
+ *              applies (kernel family 4), else for M <= 16 the
  *              skinny kernel, and for 16 < M <= 64 the rows kernel (all at
  *              the speed of
  *              the FP4 case; FP6 on the rows kernel needs an even K/32);
@@ -400,9 +400,10 @@ typedef struct mxgemm_info {
     int32_t kernel;          /* kernel family: 0 = tiled (LDS, M > 64); 1 = skinny (M <= 16,
                                 streams B); 2 = skinny rows (16 < M <= 64, streams B, A
                                 shared through LDS); 3 = tiled with an FP8/FP6 A; 4 =
-                                single-row GEMV (M == 1, row-major B, K % 2048 == 0,
-                                N >= 4 x num_cu, unsplit; 4 rows of B per workgroup; with
-                                16-byte aligned scale rows, else the skinny kernel) */
+                                GEMV (M == 1, or 2 <= M <= 4 with FP4 A; row-major B,
+                                K % 2048 == 0, N >= 4 x num_cu, unsplit; 4 rows of B per
+                                workgroup; with 16-byte aligned scale rows, else the skinny
+                                kernel) */
     int32_t tile_m, tile_n;  /* output tile per workgroup */
     int32_t split_k;         /* K chunks the plan uses */
     int64_t grid;            /* workgroups launched */
