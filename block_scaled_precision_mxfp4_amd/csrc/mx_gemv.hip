@@ -39,7 +39,9 @@
 // (g = l / 16); FP6, the block's 24 bytes.  A chunk of A is then 2 KiB or
 // 1.5 KiB instead of 1 KiB; B and the scales are unchanged.
 //
-// MR: 2 <= M <= 4 (FP4 A), the small-batch decode.  The A operand's lanes
+// MR (1 or 2): 2 <= M <= 4 * MR (FP4 A), the small-batch decode.  For each
+// group of 4 A rows (one with MR = 1, two with MR = 2, sharing every B
+// operand and B scale word, with an accumulator each) the A operand's lanes
 // then pair like B's: lane y = l % 16 carries A row y / 4 at step 4t + y % 4
 // (one 16-byte load per lane and instruction: 256 contiguous bytes of each
 // of the 4 rows, rows past M loading nothing), and its scale words reach
@@ -61,32 +63,37 @@ namespace mx {
 constexpr int kGemvRows = 4;     // rows of B (columns of D) per workgroup
 constexpr int kGemvChunk = 2048; // K per chunk: 16 steps of 128
 
-template <int AF, bool MR>
+template <int AF, int MR>
 struct GemvChunk {
     using a_t = typename std::conditional<AF == 0, v4i, v8i>::type;
     v4i b[4];     // B operand of instruction t
     a_t a;        // A operand, all 16 steps of the chunk (one row)
-    v4i am[MR ? 4 : 1];  // MR: A operand of instruction t (4 rows x 4 steps)
+    v4i am[MR ? 4 * MR : 1];  // MR: A operand of instruction t, row group h: am[4h + t]
     uint32_t sa;  // A scale bytes of step l % 16 (MR: of row l / 16)
+    uint32_t sa_hi;  // MR = 2: of row 4 + l / 16
     uint32_t sb;  // B scale bytes of row l / 16, step l % 16
 };
 
 // Loads of chunk c (nothing, without memory traffic, when !on).  The scale
 // words and the A operand go first: the scale permutes can then start while
 // B is still arriving, and each multiply waits only for its own B operand.
-template <int AF, bool MR>
+template <int AF, int MR>
 __device__ __forceinline__ void gemv_issue(GemvChunk<AF, MR> &ch, int c, bool on, __amdgpu_buffer_rsrc_t rb,
                                            __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rsa,
                                            __amdgpu_buffer_rsrc_t rsb, uint32_t b_lane, uint32_t sb_lane,
-                                           uint32_t a_lane, uint32_t sa_lane, int lane)
+                                           const uint32_t (&a_lane)[2], const uint32_t (&sa_lane)[2], int lane)
 {
     const uint32_t bc = (uint32_t)c * (kGemvChunk / 2);
     ch.sb = load4(rsb, on && sb_lane != kOOB ? sb_lane + (uint32_t)c * 64 : kOOB);
-    if constexpr (MR) {
-        ch.sa = load4(rsa, on && sa_lane != kOOB ? sa_lane + (uint32_t)c * 64 : kOOB);
+    if constexpr (MR > 0) {
+        ch.sa = load4(rsa, on && sa_lane[0] != kOOB ? sa_lane[0] + (uint32_t)c * 64 : kOOB);
+        if constexpr (MR > 1)
+            ch.sa_hi = load4(rsa, on && sa_lane[1] != kOOB ? sa_lane[1] + (uint32_t)c * 64 : kOOB);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            ch.am[t] = load16(ra, on && a_lane != kOOB ? a_lane + bc + t * 256 : kOOB);
+        for (int h = 0; h < MR; ++h)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                ch.am[4 * h + t] = load16(ra, on && a_lane[h] != kOOB ? a_lane[h] + bc + t * 256 : kOOB);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
             ch.b[t] = load16_stream(rb, on && b_lane != kOOB ? b_lane + bc + t * 256 : kOOB);
@@ -112,20 +119,23 @@ __device__ __forceinline__ void gemv_issue(GemvChunk<AF, MR> &ch, int c, bool on
         ch.b[t] = load16_stream(rb, on && b_lane != kOOB ? b_lane + bc + t * 256 : kOOB);
 }
 
-template <int AF, bool MR>
+template <int AF, int MR>
 __device__ __forceinline__ void gemv_compute(const GemvChunk<AF, MR> &ch, v4f (&acc)[4], int lane)
 {
     const int sh = 8 * (lane >> 4);
     const int q = lane & 15;
-    if constexpr (MR) {
+    if constexpr (MR > 0) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            // B's and A's scale words of this lane: row q / 4 of each, step
-            // 4t + q % 4 of the chunk
+            // B's and A's scale words of this lane: row q / 4 of each (of the
+            // A row group), step 4t + q % 4 of the chunk
             const int src = (q >> 2) * 16 + 4 * t + (q & 3);
             const uint32_t wb = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)ch.sb);
-            const uint32_t wa = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)ch.sa);
-            acc[0] = mfma_fp4<0, 0>(ch.b[t], ch.am[t], acc[0], (int)(wb >> sh), (int)(wa >> sh));
+#pragma unroll
+            for (int h = 0; h < MR; ++h) {
+                const uint32_t wa = (uint32_t)__builtin_amdgcn_ds_bpermute(src * 4, (int)(h ? ch.sa_hi : ch.sa));
+                acc[h] = mfma_fp4<0, 0>(ch.b[t], ch.am[4 * h + t], acc[h], (int)(wb >> sh), (int)(wa >> sh));
+            }
         }
         return;
     }
@@ -143,10 +153,10 @@ __device__ __forceinline__ void gemv_compute(const GemvChunk<AF, MR> &ch, v4f (&
 }
 
 // LOOP = false: at most one chunk per wave (K <= 8192), one register set.
-template <int AF, bool LOOP, bool MR>
+template <int AF, bool LOOP, int MR>
 __device__ __forceinline__ void gemv_body(const GemmArgs &g)
 {
-    __shared__ float s_part[4][MR ? 4 : 1][kGemvRows];
+    __shared__ float s_part[4][MR ? 4 * MR : 1][kGemvRows];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n0 = blockIdx.x * kGemvRows;
@@ -156,6 +166,7 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
     const auto rsb = make_rsrc(g.SB + (int64_t)n0 * g.ldsb, (uint32_t)((rows - 1) * g.ldsb + g.KB));
     const auto ra = make_rsrc(g.A, (uint32_t)((int64_t)(MR ? g.M - 1 : 0) * g.lda_b + (int64_t)g.K * kFmtBits[AF] / 8));
     const auto rsa = make_rsrc(g.SA, (uint32_t)((int64_t)(MR ? g.M - 1 : 0) * g.ldsa + g.KB));
+    static_assert(MR <= 2, "at most two groups of 4 A rows");
 
     // per-lane offsets inside a chunk: B row (l % 16) / 4 at step l % 4 of
     // the instruction's four, K-block l / 16; B scale dword: row l / 16,
@@ -164,9 +175,14 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
     const uint32_t b_lane = br < rows ? (uint32_t)(br * g.ldb_b) + (lane & 3) * 64 + (lane >> 4) * 16 : kOOB;
     const int sr = lane >> 4;
     const uint32_t sb_lane = sr < rows ? (uint32_t)(sr * g.ldsb) + (lane & 15) * 4 : kOOB;
-    // MR: A row (l % 16) / 4 as B's, and its scale dword row l / 16
-    const uint32_t a_lane = MR && br < g.M ? (uint32_t)(br * g.lda_b) + (lane & 3) * 64 + (lane >> 4) * 16 : kOOB;
-    const uint32_t sa_lane = MR && sr < g.M ? (uint32_t)(sr * g.ldsa) + (lane & 15) * 4 : kOOB;
+    // MR: A row 4h + (l % 16) / 4 as B's, and its scale dword row 4h + l / 16
+    uint32_t a_lane[2], sa_lane[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int ar = 4 * h + br, asr = 4 * h + sr;
+        a_lane[h] = MR > h && ar < g.M ? (uint32_t)(ar * g.lda_b) + (lane & 3) * 64 + (lane >> 4) * 16 : kOOB;
+        sa_lane[h] = MR > h && asr < g.M ? (uint32_t)(asr * g.ldsa) + (lane & 15) * 4 : kOOB;
+    }
 
     v4f acc[4];
 #pragma unroll
@@ -200,19 +216,23 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
         }
     }
 
-    if constexpr (MR) {
-        // the lane's term: element l % 4, for A row (l % 16) / 4 and B row
-        // l / 16; a quad (lane ^ 1, lane ^ 2) holds one pair's four terms
+    if constexpr (MR > 0) {
+        // the lane's term of row group h: element l % 4 of accumulator h,
+        // for A row 4h + (l % 16) / 4 and B row l / 16; a quad (lane ^ 1,
+        // lane ^ 2) holds one pair's four terms
         const int ii = lane & 3;
-        float v = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (i == ii)
-                v = acc[0][i];
-        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-        v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
-        if ((lane & 3) == 0)
-            s_part[wave][(lane & 15) >> 2][lane >> 4] = v;
+        for (int h = 0; h < MR; ++h) {
+            float v = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i == ii)
+                    v = acc[h][i];
+            v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+            v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+            if ((lane & 3) == 0)
+                s_part[wave][4 * h + ((lane & 15) >> 2)][lane >> 4] = v;
+        }
         __syncthreads();
         if (threadIdx.x < g.M) {
             const int m = threadIdx.x;
@@ -264,7 +284,7 @@ __device__ __forceinline__ void gemv_body(const GemmArgs &g)
     }
 }
 
-template <int AF, bool MR>
+template <int AF, int MR>
 __global__ void __launch_bounds__(256) mx_gemv_kernel(GemmArgs g)
 {
     gemv_body<AF, true, MR>(g);
@@ -272,13 +292,13 @@ __global__ void __launch_bounds__(256) mx_gemv_kernel(GemmArgs g)
 
 // One chunk per wave: at most 64 registers, so that eight waves fit a SIMD
 // and all 2048 workgroups of N = 8192 are resident at once.
-template <int AF, bool MR>
+template <int AF, int MR>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) mx_gemv1_kernel(GemmArgs g)
 {
     gemv_body<AF, false, MR>(g);
 }
 
-template <int AF, bool MR>
+template <int AF, int MR>
 static void launch_gemv_fmt(const GemmArgs &g, int grid, hipStream_t s)
 {
     if (g.K <= 4 * kGemvChunk)
@@ -289,16 +309,20 @@ static void launch_gemv_fmt(const GemmArgs &g, int grid, hipStream_t s)
 
 void launch_gemv(int a_fmt, const GemmArgs &g, int grid, hipStream_t s)
 {
+    if (g.M > 4) {  // 5 <= M <= 8, FP4 A
+        launch_gemv_fmt<0, 2>(g, grid, s);
+        return;
+    }
     if (g.M > 1) {  // 2 <= M <= 4, FP4 A
-        launch_gemv_fmt<0, true>(g, grid, s);
+        launch_gemv_fmt<0, 1>(g, grid, s);
         return;
     }
     switch (a_fmt) {
-    case 0: launch_gemv_fmt<0, false>(g, grid, s); break;
-    case 1: launch_gemv_fmt<1, false>(g, grid, s); break;
-    case 2: launch_gemv_fmt<2, false>(g, grid, s); break;
-    case 3: launch_gemv_fmt<3, false>(g, grid, s); break;
-    default: launch_gemv_fmt<4, false>(g, grid, s); break;
+    case 0: launch_gemv_fmt<0, 0>(g, grid, s); break;
+    case 1: launch_gemv_fmt<1, 0>(g, grid, s); break;
+    case 2: launch_gemv_fmt<2, 0>(g, grid, s); break;
+    case 3: launch_gemv_fmt<3, 0>(g, grid, s); break;
+    default: launch_gemv_fmt<4, 0>(g, grid, s); break;
     }
 }
 

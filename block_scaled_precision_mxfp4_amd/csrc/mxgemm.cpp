@@ -25,7 +25,7 @@
 
 namespace mx {
 // GEMV (mx_gemv.hip): M == 1 with A in format a_fmt (0 FP4, 1..4 FP8 E4M3,
-// BF8 E5M2, FP6 E2M3, FP6 E3M2), or 2 <= M <= 4 with FP4 A; row-major B,
+// BF8 E5M2, FP6 E2M3, FP6 E3M2), or 2 <= M <= 8 with FP4 A; row-major B,
 // K % 2048 == 0, 16-byte aligned scale rows, split 1; one workgroup per 4
 // rows of B.
 void launch_gemv(int a_fmt, const GemmArgs &g, int grid, hipStream_t s);
@@ -42,7 +42,7 @@ constexpr int kSplits[] = {1, 2, 4, 8, 16};
 
 struct Plan {
     int family = 0;  // 0 tiled, 1 skinny (M <= 16), 2 skinny rows (16 < M <= 64), 3 tiled with
-                     // a wider A, 4 GEMV (M <= 4)
+                     // a wider A, 4 GEMV (M <= 8)
     int index = 0;   // index into the kernel table of the family
     int bm = 0, bn = 0;
     int split = 1;
@@ -103,13 +103,13 @@ constexpr double kSplitChunkCost = 2e-6;
 constexpr int kMinSkinnyChunk = 64;
 constexpr double kCuL2 = 64.0 * 2.4e9;
 
-// The GEMV (mx_gemv.hip) takes M == 1 (A in any format) and 2 <= M <= 4
+// The GEMV (mx_gemv.hip) takes M == 1 (A in any format) and 2 <= M <= 8
 // (FP4 A) with a row-major B when K is a multiple of its 2048-K chunk and
 // its 4-row workgroups fill at least one per CU (N >= 4 * CUs); unsplit.
 // MXGEMM_GEMV=0 keeps such shapes on the skinny kernel.
 bool gemv_applies(int M, int N, int K, int b_packed, int split_req, int num_cu, int a_format)
 {
-    if (M < 1 || M > 4 || (M > 1 && a_format != MXGEMM_FMT_FP4) || b_packed || K % 2048 || split_req > 1 ||
+    if (M < 1 || M > 8 || (M > 1 && a_format != MXGEMM_FMT_FP4) || b_packed || K % 2048 || split_req > 1 ||
         (int64_t)cdiv(N, 4) < num_cu)
         return false;
     const char *e = std::getenv("MXGEMM_GEMV");
@@ -193,7 +193,7 @@ Plan plan_for(int M, int N, int K, int b_packed, int split_req, int num_cu, bool
         best.tiles_m = 1;
         best.tiles_n = cdiv(N, 4);
         best.grid = best.tiles_n;
-        best.name = M == 1 ? "gemv_m1_n4" : "gemv_m4_n4";
+        best.name = M == 1 ? "gemv_m1_n4" : M <= 4 ? "gemv_m4_n4" : "gemv_m8_n4";
         return best;
     }
     if (M <= 16 && !tiled_only) {

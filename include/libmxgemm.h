@@ -400,7 +400,7 @@ typedef struct mxgemm_info {
     int32_t kernel;          /* kernel family: 0 = tiled (LDS, M > 64); 1 = skinny (M <= 16,
                                 streams B); 2 = skinny rows (16 < M <= 64, streams B, A
                                 shared through LDS); 3 = tiled with an FP8/FP6 A; 4 =
-                                GEMV (M == 1, or 2 <= M <= 4 with FP4 A; row-major B,
+                                GEMV (M == 1, or 2 <= M <= 8 with FP4 A; row-major B,
                                 K % 2048 == 0, N >= 4 x num_cu, unsplit; 4 rows of B per
                                 workgroup; with 16-byte aligned scale rows, else the skinny
                                 kernel) */

@@ -350,7 +350,7 @@ def test_prepacked_fp6_A_plan_and_sizes():
 
 def test_gemv_plan_conditions_host():
     """The GEMV's planner conditions on the host (256 CUs): M == 1 (any A
-    format) or 2 <= M <= 4 (FP4 A), row-major B, K % 2048 == 0, unsplit or
+    format) or 2 <= M <= 8 (FP4 A), row-major B, K % 2048 == 0, unsplit or
     split 1, N >= 4 x CUs."""
     name = lambda M, N, K, packed=0, split=-1: mx.mxgemm_plan(M, N, K, packed, split, 256)["kernel_name"]
     assert name(1, 1024, 2048) == "gemv_m1_n4"
@@ -360,10 +360,10 @@ def test_gemv_plan_conditions_host():
     assert name(1, 8192, 8192, packed=1) != "gemv_m1_n4"
     assert name(1, 8192, 8192, split=1) == "gemv_m1_n4"
     assert name(1, 8192, 8192, split=2) != "gemv_m1_n4"
-    for M in (2, 3, 4):  # the small-batch form, FP4 A
-        assert name(M, 8192, 8192) == "gemv_m4_n4"
+    for M in (2, 3, 4, 5, 8):  # the small-batch forms, FP4 A
+        assert name(M, 8192, 8192) == ("gemv_m4_n4" if M <= 4 else "gemv_m8_n4")
         assert mx.mxgemm_plan(M, 8192, 8192, 0, -1, 256)["tile_m"] == M
-    assert name(5, 8192, 8192).startswith("skinny")
+    assert name(9, 8192, 8192).startswith("skinny")
     assert mx.mxgemm_plan(1, 8192, 8192, 0, -1, 128)["grid"] == 2048
     for fmt in (mx.FMT_FP8_E4M3, mx.FMT_FP8_E5M2, mx.FMT_FP6_E2M3, mx.FMT_FP6_E3M2):
         st = mx.make_strides(ldd=8192, ldc=8192, lda=8192, ldb=8192, ldsa=256, ldsb=256, a_format=fmt)

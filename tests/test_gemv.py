@@ -1,5 +1,5 @@
-"""GPU parity of the GEMV (`gemv_m1_n4`: M == 1; `gemv_m4_n4`: 2 <= M <= 4
-with FP4 A; row-major FP4 B, K a multiple of 2048), through the C-ABI,
+"""GPU parity of the GEMV (`gemv_m1_n4`: M == 1; `gemv_m4_n4` and
+`gemv_m8_n4`: 2 <= M <= 8 with FP4 A; row-major FP4 B, K a multiple of 2048), through the C-ABI,
 against the oracle.
 
 The planner sends M == 1 with a row-major B (A in FP4, FP8, BF8 or either
@@ -97,15 +97,16 @@ def test_gemv_long_K():
     assert_parity(d, ref, mag, "gemv long K")
 
 
-@pytest.mark.parametrize("M", [2, 3, 4])
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 7, 8])
 @pytest.mark.parametrize("shape", [(1024, 2048), (1027, 6144), (2050, 16384)], ids=lambda s: "x%dx%d" % s)
 def test_gemv_small_batch_matches_oracle(shape, M, monkeypatch):
-    """2 <= M <= 4 (FP4 A): A rows through the B-like operand lanes, one
-    accumulator per chunk; padded A and scale rows (pitches beyond K), C with
+    """2 <= M <= 8 (FP4 A): A rows through the B-like operand lanes, one
+    accumulator per group of 4 A rows; padded A and scale rows (pitches beyond K), C with
     beta; against the oracle, and the skinny kernel (MXGEMM_GEMV=0) on the
     same problem within the same tolerance."""
     N, K = shape
-    assert planned(M, N, K) == "gemv_m4_n4"
+    kname = "gemv_m4_n4" if M <= 4 else "gemv_m8_n4"
+    assert planned(M, N, K) == kname
     p = inputs.make_problem(M, N, K, seed=0x6E40 + 17 * M + N, e=(118, 136), beta=1.0, c_sigma=2.0)
     p["alpha"], p["beta"] = 0.5, -0.75
     ref, mag, _ = oracle_ref(p)
@@ -117,7 +118,7 @@ def test_gemv_small_batch_matches_oracle(shape, M, monkeypatch):
     A, SA, B, SB = dev_u8(Apad), dev_u8(SApad), dev_u8(p["B"]), dev_u8(p["SB"])
     C = dev_bf16(p["C"])
     st = mx.make_strides(ldd=N, ldc=N, lda=lda, ldb=K, ldsa=ldsa, ldsb=K // 32)
-    assert mx.mxgemm_query_ex(M, N, K, st, -1)["kernel_name"] == "gemv_m4_n4"
+    assert mx.mxgemm_query_ex(M, N, K, st, -1)["kernel_name"] == kname
     say("case gemv small batch", (M, N, K))
     D = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     mx.mxgemm_run(D, C, A, B, SA, SB, p["alpha"], p["beta"], M, N, K, strides=st)
@@ -206,7 +207,8 @@ def test_gemv_plan_conditions():
     assert planned(1, 8192, 8192, b_packed=1) != "gemv_m1_n4"
     assert planned(1, 8192, 8192 + 1024) != "gemv_m1_n4"
     assert planned(2, 8192, 8192) == "gemv_m4_n4"
-    assert planned(5, 8192, 8192).startswith("skinny")
+    assert planned(8, 8192, 8192) == "gemv_m8_n4"
+    assert planned(9, 8192, 8192).startswith("skinny")
     assert planned(1, 8192, 8192, split=2) != "gemv_m1_n4"
     assert planned(1, 8192, 8192, split=1) == "gemv_m1_n4"
 
